@@ -1,0 +1,495 @@
+"""CPU oracle for the variance-normalized KV-cache tile quantizer and its paged
+decode-attention read path.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+CPU-baseline leg may import this module.  The product path (the HIP library
+and its Python binding) never imports it, and it imports nothing from the
+product path: the two share no code.  The only shared module is the seeded
+input generator, which holds no arithmetic of the method.
+
+Everything here is plain NumPy in float64 (the pages fix no precision), one
+tile at a time, in the order the pages give the steps.  It is slow on purpose.
+
+Sources (the pages, cited by title and section):
+
+* [axbrief §diff]  "Huawei's KVarN boosts vLLM KV-cache capacity by 5x without
+  accuracy loss" (axbrief.com), section "기존 방식과 달라진 지점" (what differs
+  from earlier methods).  Its four-step paragraph is the only description of
+  the method: the cache is quantized per fixed-size token tile; each tile,
+  still raw fp16, is rotated along the channel dimension with a Hadamard
+  transform to spread channel-concentrated outliers; a Sinkhorn-like
+  iterative variance normalization then evens out the per-channel variance;
+  finally asymmetric round-to-nearest produces the low-bit cache.
+* [axbrief §flag]  same page, section "별도의 캘리브레이션이나 모델 변경 없이
+  플래그 하나로 적용": restates rotation + iterative variance normalization,
+  and that nothing is calibrated (every statistic comes from the tile itself).
+* [ttj §quant]  "화웨이가 공개한 KVarN — LLM 추론의 '메모리 먹는 하마' KV 캐시를
+  양자화로 길들이기" (ttj.kr), section "양자화로 캐시를 다이어트시킨다": K and V
+  are compressed and restored inside the inference pipeline, with the cache
+  managed in pages.
+* [aitrends §TL;DR], [aitrends §용어 해설]  aitrends.kr article 74976: the
+  attention backend reads compressed KV pages directly instead of
+  re-materializing fp16.
+
+Readings where the pages are silent (each is a documented parameter or choice):
+
+* Hadamard: Sylvester order, orthonormal (divided by sqrt(d)), no random signs,
+  applied to every token row of K and of V.
+* "Variance": population standard deviation (divide by n), mean-centered; the
+  data themselves are only scaled, never shifted (the per-token zero-point of
+  the rounding step absorbs offsets).
+* One iteration = a channel step (each channel divided by its spread over the
+  tile's tokens) followed by a token step (each token divided by its spread
+  over the channels).  The factors multiply into alpha (per channel) and beta
+  (per token), so that R = diag(beta) . Y . diag(alpha) holds exactly.
+* Guard: a channel (token) whose spread is at most GUARD times its RMS is left
+  unscaled (factor 1).  This covers one-token tiles, repeated rows, all-zero
+  rows and nearly constant columns, where dividing by the spread would blow
+  up values instead of evening them out.
+* Rounding granularity: per token row over the 128 channels of the tile; the
+  zero-point is the row minimum (a float, not an integer); the step is
+  (max - min) / (2^bits - 1); ties round to even; a row with zero range gets
+  codes 0 and step 0.
+* Stored metadata, fp32: alpha[128] per tile, and per token the scale
+  S = beta * step and offset O = beta * min, so that the restored rotated row
+  is alpha * (S * code + O) and the restored token is that row rotated back.
+* Tiles are aligned to the start of each sequence; the last one may be
+  partial, and its statistics use only its valid rows.
+
+"parity unpinned" applies to nothing here: every function is pinned by the
+tests in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+HEAD_DIM = 128
+PAGE_TOKENS = 16
+GUARD = 1e-2
+
+
+# ----------------------------------------------------------------------------
+# Step 2 of the tile quantizer: Hadamard rotation along channels [axbrief §diff]
+# ----------------------------------------------------------------------------
+
+def hadamard(d: int = HEAD_DIM) -> np.ndarray:
+    """Orthonormal Sylvester Hadamard matrix of order d (a power of two)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h / math.sqrt(d)
+
+
+def fwht(x: np.ndarray) -> np.ndarray:
+    """Orthonormal fast Walsh-Hadamard transform along the last axis.
+
+    For each bit of the channel index, entries that differ only in that bit
+    are replaced by their sum (bit 0) and difference (bit 1).  Equal to
+    x @ hadamard(d) for every row."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    d = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < d:
+        y = y.reshape(lead + (d // (2 * h), 2, h))
+        lo = y[..., 0, :].copy()
+        hi = y[..., 1, :].copy()
+        y[..., 0, :] = lo + hi
+        y[..., 1, :] = lo - hi
+        y = y.reshape(lead + (d,))
+        h *= 2
+    return y / math.sqrt(d)
+
+
+# ----------------------------------------------------------------------------
+# Step 3: Sinkhorn-like iterative variance normalization [axbrief §diff, §flag]
+# ----------------------------------------------------------------------------
+
+def _spread_and_rms(v: np.ndarray, axis: int):
+    mean = v.mean(axis=axis, keepdims=True)
+    std = np.sqrt(((v - mean) ** 2).mean(axis=axis, keepdims=True))
+    rms = np.sqrt((v ** 2).mean(axis=axis, keepdims=True))
+    return std, rms
+
+
+def _factor(v: np.ndarray, axis: int) -> np.ndarray:
+    std, rms = _spread_and_rms(v, axis)
+    return np.where(std > GUARD * rms, std, 1.0)
+
+
+def sinkhorn(r: np.ndarray, iters: int):
+    """Alternate channel and token variance normalization of a rotated tile.
+
+    r: [n, d] rotated tile (rows are tokens).  Returns (y, alpha[d], beta[n])
+    with r == beta[:, None] * y * alpha[None, :]."""
+    y = np.array(r, dtype=np.float64, copy=True)
+    n, d = y.shape
+    alpha = np.ones(d)
+    beta = np.ones(n)
+    for _ in range(int(iters)):
+        g = _factor(y, axis=0)          # channel step: spread over tokens
+        y = y / g
+        alpha = alpha * g[0]
+        g = _factor(y, axis=1)          # token step: spread over channels
+        y = y / g
+        beta = beta * g[:, 0]
+    return y, alpha, beta
+
+
+# ----------------------------------------------------------------------------
+# Step 4: asymmetric round-to-nearest to low-bit codes [axbrief §diff]
+# ----------------------------------------------------------------------------
+
+def rtn(y: np.ndarray, bits: int):
+    """Per-row asymmetric round-to-nearest.
+
+    Returns (codes uint8 [n, d], step[n], zero[n], pre[n, d]) where pre is the
+    value before rounding, (y - zero) / step."""
+    levels = (1 << bits) - 1
+    zero = y.min(axis=1)
+    step = (y.max(axis=1) - zero) / levels
+    safe = np.where(step > 0, step, 1.0)
+    pre = np.where(step[:, None] > 0, (y - zero[:, None]) / safe[:, None], 0.0)
+    codes = np.clip(np.rint(pre), 0, levels).astype(np.uint8)
+    return codes, step, zero, pre
+
+
+@dataclasses.dataclass
+class TileQuant:
+    codes: np.ndarray     # uint8 [n, d], one code per element
+    alpha: np.ndarray     # float32 [d]
+    scale: np.ndarray     # float32 [n]  (beta * step)
+    offset: np.ndarray    # float32 [n]  (beta * zero)
+    pre: np.ndarray       # float64 [n, d], value before rounding
+    rotated: np.ndarray   # float64 [n, d]
+    normalized: np.ndarray  # float64 [n, d]
+    beta: np.ndarray      # float64 [n]
+
+
+def quantize_tile(x: np.ndarray, bits: int, iters: int) -> TileQuant:
+    """The four steps on one tile of 1..T tokens: x fp16 [n, d]."""
+    x = np.asarray(x)
+    if x.ndim != 2 or x.shape[0] < 1:
+        raise ValueError("tile must be [n>=1, d]")
+    r = fwht(x.astype(np.float64))
+    y, alpha, beta = sinkhorn(r, iters)
+    codes, step, zero, pre = rtn(y, bits)
+    return TileQuant(codes=codes, alpha=alpha.astype(np.float32),
+                     scale=(beta * step).astype(np.float32),
+                     offset=(beta * zero).astype(np.float32),
+                     pre=pre, rotated=r, normalized=y, beta=beta)
+
+
+def dequantize_tile(codes, alpha, scale, offset) -> np.ndarray:
+    """Restore a tile [ttj §quant]: rotated row alpha * (S * code + O), rotated
+    back with the same (self-inverse) Hadamard.  float64 [n, d]."""
+    codes = np.asarray(codes, dtype=np.float64)
+    rot = np.asarray(alpha, np.float64)[None, :] * (
+        np.asarray(scale, np.float64)[:, None] * codes + np.asarray(offset, np.float64)[:, None])
+    return fwht(rot)
+
+
+# ----------------------------------------------------------------------------
+# Code packing (natural order: channel c at bit (c mod (8/bits)) * bits of
+# byte c * bits / 8, low bits first)
+# ----------------------------------------------------------------------------
+
+def pack_natural(codes: np.ndarray, bits: int) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    per = 8 // bits
+    d = codes.shape[-1]
+    out = np.zeros(codes.shape[:-1] + (d // per,), dtype=np.uint8)
+    for c in range(d):
+        out[..., c // per] |= (codes[..., c] & ((1 << bits) - 1)) << ((c % per) * bits)
+    return out
+
+
+def unpack_natural(packed: np.ndarray, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    per = 8 // bits
+    d = packed.shape[-1] * per
+    out = np.zeros(packed.shape[:-1] + (d,), dtype=np.uint8)
+    for c in range(d):
+        out[..., c] = (packed[..., c // per] >> ((c % per) * bits)) & ((1 << bits) - 1)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Dense (logical) layout: one token run whose tile 0 starts at token 0
+# ----------------------------------------------------------------------------
+
+def quantize_dense(x: np.ndarray, tile_tokens: int, bits: int, iters: int):
+    """x fp16 [n, H, d] -> dict(codes packed [n, H, d*bits/8], alpha [ntiles, H, d],
+    scale [n, H], offset [n, H], pre [n, H, d], codes_raw [n, H, d])."""
+    n, heads, d = x.shape
+    ntiles = (n + tile_tokens - 1) // tile_tokens
+    codes = np.zeros((n, heads, d), np.uint8)
+    pre = np.zeros((n, heads, d))
+    alpha = np.zeros((ntiles, heads, d), np.float32)
+    scale = np.zeros((n, heads), np.float32)
+    offset = np.zeros((n, heads), np.float32)
+    for h in range(heads):
+        for j in range(ntiles):
+            a, b = j * tile_tokens, min(n, (j + 1) * tile_tokens)
+            tq = quantize_tile(x[a:b, h, :], bits, iters)
+            codes[a:b, h] = tq.codes
+            pre[a:b, h] = tq.pre
+            alpha[j, h] = tq.alpha
+            scale[a:b, h] = tq.scale
+            offset[a:b, h] = tq.offset
+    return dict(codes=pack_natural(codes, bits), codes_raw=codes, alpha=alpha, scale=scale,
+                offset=offset, pre=pre)
+
+
+def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits: int) -> np.ndarray:
+    """Inverse of quantize_dense from the stored codes and fp32 metadata: float64 [n, H, d]."""
+    q = unpack_natural(codes_packed, bits)
+    n, heads, d = q.shape
+    out = np.zeros((n, heads, d))
+    for h in range(heads):
+        for a in range(0, n, tile_tokens):
+            b = min(n, a + tile_tokens)
+            out[a:b, h] = dequantize_tile(q[a:b, h], alpha[a // tile_tokens, h], scale[a:b, h],
+                                          offset[a:b, h])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Paged layout.  A page holds PAGE_TOKENS consecutive tokens of one sequence;
+# the pool is [num_pages][kv_heads][slot bytes].  A slot is
+#   codes (16 * d * bits / 8 bytes) | scale fp32[16] | offset fp32[16] | alpha slice fp32[16 d / T]
+# The page with index j inside its tile stores alpha[j * 16d/T : (j+1) * 16d/T].
+# Code layouts of a slot (d = 128):
+#   K slots: four blocks of 32 channels; block k holds, token after token, the
+#     32 channels 32k..32k+31 of each of the 16 tokens in natural packing.
+#   V slots: four quads of 4 tokens; quad q holds 16 groups of 8 channels; a
+#     group is 4*bits bytes read as little-endian 32-bit words; word w holds
+#     channels 8m + w*F/4 + j (j < F/4, F = 32/bits fields per word) of the 4
+#     tokens 4q + r, channel j / token r in field 2j + (r >> 1) + (F/2)(r & 1),
+#     a field being bits [bits*f, bits*(f+1)) of the word.
+# Rows of a page past the sequence's end hold code 0, scale 0 and offset 0.
+# ----------------------------------------------------------------------------
+
+def slot_layout(bits: int, tile_tokens: int, d: int = HEAD_DIM, page: int = PAGE_TOKENS):
+    codes = page * d * bits // 8
+    alpha_len = page * d // tile_tokens
+    return dict(codes=codes, scale=codes, offset=codes + 4 * page, alpha=codes + 8 * page,
+                alpha_len=alpha_len, total=codes + 8 * page + 4 * alpha_len)
+
+
+def slot_bytes(bits: int, tile_tokens: int) -> int:
+    return slot_layout(bits, tile_tokens)["total"]
+
+
+def k_codes_to_bytes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes uint8 [16, 128] -> K-slot code bytes."""
+    per_tok = 32 * bits // 8
+    out = np.zeros(PAGE_TOKENS * HEAD_DIM * bits // 8, np.uint8)
+    for k in range(4):
+        blk = pack_natural(codes[:, 32 * k:32 * (k + 1)], bits)   # [16, per_tok]
+        out[k * 16 * per_tok:(k + 1) * 16 * per_tok] = blk.reshape(-1)
+    return out
+
+
+def bytes_to_k_codes(raw: np.ndarray, bits: int) -> np.ndarray:
+    per_tok = 32 * bits // 8
+    codes = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
+    for k in range(4):
+        blk = raw[k * 16 * per_tok:(k + 1) * 16 * per_tok].reshape(16, per_tok)
+        codes[:, 32 * k:32 * (k + 1)] = unpack_natural(blk, bits)
+    return codes
+
+
+def _v_field(bits: int, c: int, r: int):
+    """(byte offset inside a quad, word index, field index) of channel c, token-in-quad r."""
+    f_per_word = 32 // bits
+    ch_per_word = f_per_word // 4
+    m, cw = divmod(c, 8)
+    w, j = divmod(cw, ch_per_word)
+    field = 2 * j + (r >> 1) + (f_per_word // 2) * (r & 1)
+    return m * 4 * bits + 4 * w, field
+
+
+def v_codes_to_bytes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes uint8 [16, 128] -> V-slot code bytes."""
+    quad_bytes = 4 * HEAD_DIM * bits // 8
+    words = np.zeros(PAGE_TOKENS * HEAD_DIM * bits // 32, np.uint64)
+    for t in range(PAGE_TOKENS):
+        q, r = divmod(t, 4)
+        for c in range(HEAD_DIM):
+            off, field = _v_field(bits, c, r)
+            wi = (q * quad_bytes + off) // 4
+            words[wi] |= np.uint64(int(codes[t, c]) & ((1 << bits) - 1)) << np.uint64(bits * field)
+    return words.astype("<u4").view(np.uint8).copy()
+
+
+def bytes_to_v_codes(raw: np.ndarray, bits: int) -> np.ndarray:
+    quad_bytes = 4 * HEAD_DIM * bits // 8
+    words = np.ascontiguousarray(raw).view("<u4")
+    codes = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
+    for t in range(PAGE_TOKENS):
+        q, r = divmod(t, 4)
+        for c in range(HEAD_DIM):
+            off, field = _v_field(bits, c, r)
+            codes[t, c] = (int(words[(q * quad_bytes + off) // 4]) >> (bits * field)) & ((1 << bits) - 1)
+    return codes
+
+
+def new_pool(num_pages: int, kv_heads: int, bits: int, tile_tokens: int) -> np.ndarray:
+    return np.zeros((num_pages, kv_heads, slot_bytes(bits, tile_tokens)), np.uint8)
+
+
+def write_slot(pool, page, head, role, bits, tile_tokens, codes16, scale16, offset16, alpha_slice):
+    lay = slot_layout(bits, tile_tokens)
+    enc = k_codes_to_bytes if role == "K" else v_codes_to_bytes
+    slot = pool[page, head]
+    slot[:lay["codes"]] = enc(codes16, bits)
+    slot[lay["scale"]:lay["offset"]] = np.asarray(scale16, "<f4").view(np.uint8)
+    slot[lay["offset"]:lay["alpha"]] = np.asarray(offset16, "<f4").view(np.uint8)
+    slot[lay["alpha"]:lay["total"]] = np.asarray(alpha_slice, "<f4").view(np.uint8)
+
+
+def read_slot(pool, page, head, role, bits, tile_tokens):
+    lay = slot_layout(bits, tile_tokens)
+    slot = np.ascontiguousarray(pool[page, head])
+    dec = bytes_to_k_codes if role == "K" else bytes_to_v_codes
+    codes = dec(slot[:lay["codes"]], bits)
+    scale = slot[lay["scale"]:lay["offset"]].view("<f4").copy()
+    offset = slot[lay["offset"]:lay["alpha"]].view("<f4").copy()
+    alpha = slot[lay["alpha"]:lay["total"]].view("<f4").copy()
+    return codes, scale, offset, alpha
+
+
+def _store_tile(pool, table_row, head, role, bits, tile_tokens, tile_index, tq: TileQuant):
+    """Write one (possibly partial) quantized tile into its pages."""
+    ppt = tile_tokens // PAGE_TOKENS
+    alen = PAGE_TOKENS * HEAD_DIM // tile_tokens
+    n = tq.codes.shape[0]
+    for j in range(ppt):
+        page = int(table_row[tile_index * ppt + j])
+        if page < 0:
+            raise ValueError("block table has no page for a started tile")
+        codes16 = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
+        scale16 = np.zeros(PAGE_TOKENS, np.float32)
+        offset16 = np.zeros(PAGE_TOKENS, np.float32)
+        a, b = j * PAGE_TOKENS, min(n, (j + 1) * PAGE_TOKENS)
+        if b > a:
+            codes16[:b - a] = tq.codes[a:b]
+            scale16[:b - a] = tq.scale[a:b]
+            offset16[:b - a] = tq.offset[a:b]
+        write_slot(pool, page, head, role, bits, tile_tokens, codes16, scale16, offset16,
+                   tq.alpha[j * alen:(j + 1) * alen])
+
+
+def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iters,
+                      pool_k, pool_v, staging_k=None, staging_v=None):
+    """Quantize every tile of every sequence into the page pools (in place).
+
+    k, v: fp16 [total_tokens, Hkv, d]; table: int32 [S, max_blocks].  A tail
+    that does not fill its tile is also copied, as fp16 rows, to staging
+    [S, T, Hkv, d] so that later appends can re-quantize the partial tile.
+    Returns dict of pre-rounding values per (seq, head, role) for the tests."""
+    heads = k.shape[1]
+    pre = {}
+    for s in range(len(cu_seqlens) - 1):
+        a0, a1 = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        n = a1 - a0
+        for role, x, pool, bits, stg in (("K", k, pool_k, bits_k, staging_k),
+                                         ("V", v, pool_v, bits_v, staging_v)):
+            for h in range(heads):
+                pre_rows = np.zeros((n, HEAD_DIM))
+                for j in range((n + tile_tokens - 1) // tile_tokens):
+                    a, b = j * tile_tokens, min(n, (j + 1) * tile_tokens)
+                    tq = quantize_tile(x[a0 + a:a0 + b, h, :], bits, iters)
+                    pre_rows[a:b] = tq.pre
+                    _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq)
+                pre[(s, h, role)] = pre_rows
+            tail = n % tile_tokens
+            if stg is not None and tail:
+                stg[s, :tail] = x[a1 - tail:a1]
+    return pre
+
+
+def append_and_requant(k_new, v_new, lens_before, table, tile_tokens, bits_k, bits_v, iters,
+                       pool_k, pool_v, staging_k, staging_v):
+    """Append one token per sequence and re-quantize its (partial) tile from the
+    fp16 staging rows.  k_new, v_new fp16 [S, Hkv, d].  Returns pre-rounding
+    values per (seq, head, role) of the re-quantized tile rows."""
+    heads = k_new.shape[1]
+    pre = {}
+    for s in range(k_new.shape[0]):
+        pos = int(lens_before[s])
+        j, r = divmod(pos, tile_tokens)
+        staging_k[s, r] = k_new[s]
+        staging_v[s, r] = v_new[s]
+        for role, stg, pool, bits in (("K", staging_k, pool_k, bits_k), ("V", staging_v, pool_v, bits_v)):
+            for h in range(heads):
+                tq = quantize_tile(stg[s, :r + 1, h, :], bits, iters)
+                _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq)
+                pre[(s, h, role)] = tq.pre
+    return pre
+
+
+def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens):
+    """Decode one (sequence, kv head) from the pages with this module's own
+    reader: returns (restored tokens float64 [L, d], codes [L, d], alpha per
+    tile [ntiles, d], scale [L], offset [L])."""
+    ppt = tile_tokens // PAGE_TOKENS
+    ntiles = (seq_len + tile_tokens - 1) // tile_tokens
+    codes = np.zeros((ntiles * tile_tokens, HEAD_DIM), np.uint8)
+    scale = np.zeros(ntiles * tile_tokens, np.float32)
+    offset = np.zeros(ntiles * tile_tokens, np.float32)
+    alpha = np.zeros((ntiles, HEAD_DIM), np.float32)
+    alen = PAGE_TOKENS * HEAD_DIM // tile_tokens
+    for j in range(ntiles):
+        for p in range(ppt):
+            page = int(table_row[j * ppt + p])
+            c16, s16, o16, a = read_slot(pool, page, head, role, bits, tile_tokens)
+            t0 = j * tile_tokens + p * PAGE_TOKENS
+            codes[t0:t0 + PAGE_TOKENS] = c16
+            scale[t0:t0 + PAGE_TOKENS] = s16
+            offset[t0:t0 + PAGE_TOKENS] = o16
+            alpha[j, p * alen:(p + 1) * alen] = a
+    out = np.zeros((seq_len, HEAD_DIM))
+    for j in range(ntiles):
+        a, b = j * tile_tokens, min(seq_len, (j + 1) * tile_tokens)
+        out[a:b] = dequantize_tile(codes[a:b], alpha[j], scale[a:b], offset[a:b])
+    return out, codes[:seq_len], alpha, scale[:seq_len], offset[:seq_len]
+
+
+# ----------------------------------------------------------------------------
+# Decode attention [aitrends §TL;DR]: one new query per sequence and head over
+# every cached token, reading the quantized pages (here: restoring them in
+# float64 with the reader above; the GPU path never restores fp16).
+# ----------------------------------------------------------------------------
+
+def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Plain single-query softmax attention in float64."""
+    s = sm_scale * (keys.astype(np.float64) @ np.asarray(q, np.float64))
+    s = s - s.max()
+    p = np.exp(s)
+    p = p / p.sum()
+    return p @ values.astype(np.float64)
+
+
+def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
+                      sm_scale=None):
+    """q fp16 [S, Hq, d]; seq_lens count every cached token (the newest included).
+    Query head h reads kv head h // (Hq / Hkv).  Returns float64 [S, Hq, d]."""
+    s_n, hq, d = q.shape
+    hkv = pool_k.shape[1]
+    g = hq // hkv
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+    out = np.zeros((s_n, hq, d))
+    for s in range(s_n):
+        for kh in range(hkv):
+            kx = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens)[0]
+            vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens)[0]
+            for h in range(kh * g, (kh + 1) * g):
+                out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
+    return out

@@ -1,0 +1,402 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formulas: each checks a library routine,
+a closed form worked by hand (tests/golden/), an exact identity, brute force
+on tiny inputs, or an invariant that a plausible mistake (dropped term, wrong
+sign, wrong axis, transposed operand) would break.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.special
+import torch
+
+import oracle as orc
+from kv_cache_quantization_tiles_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- Hadamard
+
+def test_hadamard_equals_scipy():
+    for d in (2, 4, 8, 128):
+        np.testing.assert_array_equal(orc.hadamard(d) * math.sqrt(d), scipy.linalg.hadamard(d))
+
+
+@pytest.mark.parametrize("d", [2, 8, 128])
+def test_fwht_equals_matrix_product(d):
+    x = _rng(1).standard_normal((7, d))
+    np.testing.assert_allclose(orc.fwht(x), x @ (scipy.linalg.hadamard(d) / math.sqrt(d)),
+                               rtol=0, atol=1e-12)
+
+
+def test_hadamard_orthogonal_symmetric_selfinverse():
+    h = orc.hadamard(128)
+    np.testing.assert_allclose(h @ h.T, np.eye(128), atol=1e-13)
+    np.testing.assert_array_equal(h, h.T)
+    x = _rng(2).standard_normal((5, 128))
+    np.testing.assert_allclose(orc.fwht(orc.fwht(x)), x, atol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(orc.fwht(x), axis=1), np.linalg.norm(x, axis=1),
+                               rtol=1e-13)
+
+
+def test_single_channel_spike_is_spread_evenly():
+    # The rotation spreads an outlier concentrated in one channel over all channels.
+    for c in (0, 5, 77, 127):
+        x = np.zeros(128)
+        x[c] = 20.0
+        np.testing.assert_allclose(np.abs(orc.fwht(x)), 20.0 / math.sqrt(128), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- Sinkhorn-like normalization
+
+def test_sinkhorn_hand_example():
+    g = _golden("sinkhorn_2x2.json")
+    r = np.array(g["R"], float)
+    for key, iters in (("iters1", 1), ("iters2", 2)):
+        want = g[key]
+        y, alpha, beta = orc.sinkhorn(r, iters)
+        np.testing.assert_allclose(alpha, want["alpha"], rtol=1e-15)
+        np.testing.assert_allclose(beta, want["beta"], rtol=1e-15)
+        np.testing.assert_allclose(y, want["Y"], rtol=1e-15)
+        codes, step, zero, _ = orc.rtn(y, g["bits"])
+        np.testing.assert_array_equal(codes, want["codes"])
+        np.testing.assert_allclose(beta * step, want["S"], rtol=1e-15)
+        np.testing.assert_allclose(beta * zero, want["O"], rtol=1e-15)
+        restored = alpha[None] * ((beta * step)[:, None] * codes + (beta * zero)[:, None])
+        if iters == 2:
+            np.testing.assert_allclose(restored, r, rtol=1e-15)
+
+
+def test_sinkhorn_factorization_identity():
+    r = orc.fwht(_rng(3).standard_normal((64, 128)) * np.r_[np.full(4, 20.0), np.ones(124)])
+    for iters in (0, 1, 3, 5):
+        y, alpha, beta = orc.sinkhorn(r, iters)
+        np.testing.assert_allclose(beta[:, None] * y * alpha[None, :], r, rtol=1e-12, atol=1e-12)
+
+
+def test_sinkhorn_first_iteration_statistics():
+    # iters=1: alpha is the population std of each column of R over the tokens
+    # (channel step first), beta the population std of each row of R/alpha.
+    r = _rng(4).standard_normal((64, 128)) * 3 + 1
+    _, alpha, beta = orc.sinkhorn(r, 1)
+    np.testing.assert_allclose(alpha, r.std(axis=0, ddof=0), rtol=1e-13)
+    np.testing.assert_allclose(beta, (r / alpha).std(axis=1, ddof=0), rtol=1e-13)
+
+
+def test_sinkhorn_last_step_normalizes_rows_and_columns_converge():
+    r = orc.fwht(_rng(5).standard_normal((64, 128)) * np.r_[np.full(3, 30.0), np.ones(125)])
+    y, _, _ = orc.sinkhorn(r, 3)
+    np.testing.assert_allclose(y.std(axis=1), 1.0, rtol=1e-12)
+    col = y.std(axis=0)
+    assert col.max() / col.min() < 1.05      # channel variances evened out
+    y0, _, _ = orc.sinkhorn(r, 0)
+    col0 = y0.std(axis=0)
+    assert col0.max() / col0.min() > col.max() / col.min()
+
+
+def test_sinkhorn_zero_iterations_is_identity():
+    r = _rng(6).standard_normal((10, 128))
+    y, alpha, beta = orc.sinkhorn(r, 0)
+    np.testing.assert_array_equal(y, r)
+    np.testing.assert_array_equal(alpha, 1.0)
+    np.testing.assert_array_equal(beta, 1.0)
+
+
+def test_sinkhorn_channel_scaling_equivariance():
+    # Scaling rotated channel c by k_c > 0 changes alpha_c by k_c and nothing else.
+    r = _rng(7).standard_normal((64, 128))
+    k = np.exp(_rng(8).uniform(-2, 2, 128))
+    y1, a1, b1 = orc.sinkhorn(r, 3)
+    y2, a2, b2 = orc.sinkhorn(r * k[None], 3)
+    np.testing.assert_allclose(a2, a1 * k, rtol=1e-12)
+    np.testing.assert_allclose(b2, b1, rtol=1e-12)
+    np.testing.assert_allclose(y2, y1, rtol=1e-11, atol=1e-12)
+
+
+def test_sinkhorn_one_token_tile_keeps_alpha_one():
+    r = _rng(9).standard_normal((1, 128))
+    _, alpha, beta = orc.sinkhorn(r, 3)
+    np.testing.assert_array_equal(alpha, 1.0)
+    np.testing.assert_allclose(beta, r.std(), rtol=1e-13)
+
+
+def test_guard_on_repeated_and_zero_rows():
+    row = _rng(10).standard_normal(128)
+    r = np.stack([row, row, row, np.zeros(128)])
+    y, alpha, beta = orc.sinkhorn(r, 3)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(alpha)) and np.all(np.isfinite(beta))
+    np.testing.assert_array_equal(y[3], 0.0)
+    assert beta[3] == 1.0
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_spike_tile_hand_example():
+    g = _golden("spike_tile.json")
+    x = np.zeros((1, 128), np.float16)
+    x[0, g["channel"]] = g["a"]
+    tq = orc.quantize_tile(x, g["bits"], g["iters"])
+    want = np.array([15 if bin(g["channel"] & j).count("1") % 2 == 0 else 0 for j in range(128)])
+    np.testing.assert_array_equal(tq.codes[0], want)
+    np.testing.assert_array_equal(tq.alpha, np.float32(g["alpha"]))
+    assert tq.scale[0] == np.float32(g["S"])
+    assert tq.offset[0] == np.float32(g["O"])
+
+
+def _outlier_tile(seed, n=64):
+    x = _rng(seed).standard_normal((n, 128))
+    x[:, [3, 40, 99]] *= np.array([15.0, 30.0, 45.0])
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_rtn_error_bound_and_code_range(bits):
+    tq = orc.quantize_tile(_outlier_tile(11), bits, 3)
+    y = tq.normalized
+    levels = (1 << bits) - 1
+    step = (y.max(1) - y.min(1)) / levels
+    rec = step[:, None] * tq.codes + y.min(1)[:, None]
+    assert np.all(np.abs(y - rec) <= step[:, None] / 2 * (1 + 1e-12))
+    assert tq.codes.min() == 0 and tq.codes.max() == levels
+    np.testing.assert_array_equal(tq.codes[np.arange(64), y.argmin(1)], 0)
+    np.testing.assert_array_equal(tq.codes[np.arange(64), y.argmax(1)], levels)
+    # In the original domain the error is bounded by (S/2) * ||alpha|| per token.
+    x = orc.dequantize_tile(tq.codes, tq.alpha, tq.scale, tq.offset)
+    err = np.linalg.norm(x - _outlier_tile(11).astype(np.float64), axis=1)
+    bound = tq.scale.astype(np.float64) / 2 * np.linalg.norm(tq.alpha.astype(np.float64))
+    assert np.all(err <= bound * (1 + 1e-6) + 1e-6)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_rtn_brute_force_nearest_level(bits):
+    y = _rng(12).standard_normal((16, 32))
+    codes, step, zero, pre = orc.rtn(y, bits)
+    cand = zero[:, None, None] + step[:, None, None] * np.arange(1 << bits)[None, None, :]
+    best = np.abs(y[:, :, None] - cand).argmin(axis=2)
+    not_tie = np.abs(pre - np.floor(pre) - 0.5) > 1e-9
+    np.testing.assert_array_equal(codes[not_tie], best[not_tie])
+
+
+def test_rtn_negation_symmetry_and_ties_to_even():
+    y = _rng(13).standard_normal((8, 128))
+    c1, _, _, pre = orc.rtn(y, 4)
+    c2, _, _, _ = orc.rtn(-y, 4)
+    not_tie = np.abs(pre - np.floor(pre) - 0.5) > 1e-9
+    np.testing.assert_array_equal((15 - c1)[not_tie], c2[not_tie])
+    # exact ties: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2 (levels 0..3 spanning [0, 3])
+    codes, _, _, _ = orc.rtn(np.array([[0.0, 0.5, 1.5, 2.5, 3.0]]), 2)
+    np.testing.assert_array_equal(codes[0], [0, 0, 2, 2, 3])
+
+
+def test_rounding_is_per_row_and_row_scale_invariant():
+    # Scaling one row of the normalized tile by c > 0 scales that row's step and
+    # zero-point by c and changes no code (the rounding is per token row).
+    y = _rng(14).standard_normal((16, 128))
+    y2 = y.copy()
+    y2[5] *= 7.0
+    c1, s1, z1, _ = orc.rtn(y, 4)
+    c2, s2, z2, _ = orc.rtn(y2, 4)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_allclose(s2[5], 7 * s1[5], rtol=1e-14)
+    np.testing.assert_allclose(z2[5], 7 * z1[5], rtol=1e-14)
+    np.testing.assert_array_equal(np.delete(s2, 5), np.delete(s1, 5))
+
+
+def test_final_token_factor_cancels_in_stored_values():
+    # The last token step's beta cancels: S and O equal the range / minimum of the
+    # rows of R / alpha.  (A kernel may skip that step.)
+    tq = orc.quantize_tile(_outlier_tile(15), 4, 3)
+    z = tq.rotated / tq.alpha.astype(np.float64)[None]
+    np.testing.assert_allclose(tq.offset, z.min(1), rtol=1e-6)
+    np.testing.assert_allclose(tq.scale, (z.max(1) - z.min(1)) / 15, rtol=1e-6)
+
+
+def test_quality_beats_plain_per_token_rtn():
+    x = _outlier_tile(16).astype(np.float64)
+    tq = orc.quantize_tile(x.astype(np.float16), 4, 3)
+    ours = orc.dequantize_tile(tq.codes, tq.alpha, tq.scale, tq.offset)
+    q, step, zero, _ = orc.rtn(x, 4)
+    plain = step[:, None] * q + zero[:, None]
+    rel = lambda a: np.linalg.norm(a - x) / np.linalg.norm(x)   # noqa: E731
+    assert rel(ours) < 0.6 * rel(plain)
+
+
+# ---------------------------------------------------------------- packing and layouts
+
+def test_natural_packing_hand_examples():
+    for ex in _golden("packing.json")["natural"]:
+        packed = orc.pack_natural(np.array(ex["codes"], np.uint8), ex["bits"])
+        assert [int(b) for b in packed] == [int(b, 16) for b in ex["bytes"]]
+        np.testing.assert_array_equal(orc.unpack_natural(packed, ex["bits"]), ex["codes"])
+
+
+def _one_hot_page(t, c, value):
+    codes = np.zeros((16, 128), np.uint8)
+    codes[t, c] = value
+    return codes
+
+
+def test_k_slot_positions_hand_examples():
+    for ex in _golden("packing.json")["k_slot_4bit"]:
+        raw = orc.k_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0xB), 4)
+        want = np.zeros_like(raw)
+        want[ex["byte"]] = 0x0B if ex["nibble"] == "low" else 0xB0
+        np.testing.assert_array_equal(raw, want)
+
+
+def test_v_slot_positions_hand_examples():
+    g = _golden("packing.json")
+    for ex in g["v_slot_4bit"]:
+        raw = orc.v_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0xB), 4)
+        want = np.zeros_like(raw)
+        want[ex["byte"]] = 0x0B if ex["nibble"] == "low" else 0xB0
+        np.testing.assert_array_equal(raw, want)
+    for ex in g["v_slot_2bit"]:
+        raw = orc.v_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0x3), 2)
+        want = np.zeros_like(raw)
+        want[ex["byte"]] = 0x3 << ex["shift"]
+        np.testing.assert_array_equal(raw, want)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_slot_code_layouts_round_trip_and_are_bijective(bits):
+    codes = _rng(17).integers(0, 1 << bits, (16, 128)).astype(np.uint8)
+    for enc, dec in ((orc.k_codes_to_bytes, orc.bytes_to_k_codes),
+                     (orc.v_codes_to_bytes, orc.bytes_to_v_codes)):
+        raw = enc(codes, bits)
+        assert raw.size == 16 * 128 * bits // 8
+        np.testing.assert_array_equal(dec(raw, bits), codes)
+        # every bit of the code area is used by exactly one code
+        ones = enc(np.full((16, 128), (1 << bits) - 1, np.uint8), bits)
+        assert np.all(ones == 0xFF)
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
+def test_slot_sizes(tile):
+    assert orc.slot_bytes(4, 64) == 1280
+    assert orc.slot_bytes(4, tile) == 1024 + 128 + 4 * (16 * 128 // tile)
+    assert orc.slot_bytes(2, tile) == 512 + 128 + 4 * (16 * 128 // tile)
+
+
+def test_pages_hold_the_same_values_as_dense_layout():
+    wl = inputs.workload(1).scaled(seq_len=200)          # ragged: 3 full tiles + 8 rows
+    k = inputs.gen_kv(wl, "K")
+    v = inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    pk = orc.new_pool(npages, wl.hkv, 4, 64)
+    pv = orc.new_pool(npages, wl.hkv, 4, 64)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, 64, 4, 4, 3, pk, pv)
+    for role, x, pool in (("K", k, pk), ("V", v, pv)):
+        dense = orc.quantize_dense(x, 64, 4, 3)
+        ref = orc.dequantize_dense(dense["codes"], dense["alpha"], dense["scale"], dense["offset"], 64, 4)
+        got, codes, alpha, scale, offset = orc.read_sequence(pool, table[0], 200, 0, role, 4, 64)
+        np.testing.assert_array_equal(codes, dense["codes_raw"][:, 0])
+        np.testing.assert_array_equal(alpha, dense["alpha"][:, 0])
+        np.testing.assert_array_equal(scale, dense["scale"][:, 0])
+        np.testing.assert_allclose(got, ref[:, 0], rtol=0, atol=0)
+
+
+def test_append_one_by_one_equals_prefill():
+    wl = inputs.workload(1).scaled(seq_len=80)
+    k = inputs.gen_kv(wl, "K")
+    v = inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    full_k = orc.new_pool(npages, 1, 4, 32)
+    full_v = orc.new_pool(npages, 1, 4, 32)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, 32, 4, 4, 3, full_k, full_v)
+    ak = orc.new_pool(npages, 1, 4, 32)
+    av = orc.new_pool(npages, 1, 4, 32)
+    sk = np.zeros((1, 32, 1, 128), np.float16)
+    sv = np.zeros((1, 32, 1, 128), np.float16)
+    for pos in range(80):
+        orc.append_and_requant(k[pos:pos + 1], v[pos:pos + 1], [pos], table, 32, 4, 4, 3, ak, av, sk, sv)
+    np.testing.assert_array_equal(ak, full_k)
+    np.testing.assert_array_equal(av, full_v)
+
+
+# ---------------------------------------------------------------- attention
+
+def test_query_side_fold_identity():
+    # (H q * alpha) . (S code + O) == q . restored key   (H symmetric, orthonormal)
+    tq = orc.quantize_tile(_outlier_tile(18), 4, 3)
+    key = orc.dequantize_tile(tq.codes, tq.alpha, tq.scale, tq.offset)
+    q = _rng(19).standard_normal(128)
+    qt = orc.fwht(q) * tq.alpha.astype(np.float64)
+    folded = tq.scale.astype(np.float64) * (tq.codes @ qt) + tq.offset.astype(np.float64) * qt.sum()
+    np.testing.assert_allclose(folded, key @ q, rtol=1e-12, atol=1e-10)
+    # value side: the weighted sum of restored values equals H applied once to
+    # the weighted sum of rotated rows
+    p = scipy.special.softmax(_rng(20).standard_normal(64))
+    rot = tq.alpha.astype(np.float64)[None] * (tq.scale.astype(np.float64)[:, None] * tq.codes
+                                               + tq.offset.astype(np.float64)[:, None])
+    np.testing.assert_allclose(orc.fwht(p @ rot), p @ key, atol=1e-12)
+
+
+def test_attention_matches_library_softmax_and_torch_sdpa():
+    rng = _rng(21)
+    q = rng.standard_normal(128)
+    k = rng.standard_normal((37, 128)) * 3
+    v = rng.standard_normal((37, 128))
+    sm = 1 / math.sqrt(128)
+    want = scipy.special.softmax(sm * (k @ q)) @ v
+    np.testing.assert_allclose(orc.attention(q, k, v, sm), want, rtol=1e-12, atol=1e-14)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None, None], torch.tensor(k)[None, None], torch.tensor(v)[None, None])
+    np.testing.assert_allclose(orc.attention(q, k, v, sm), ref[0, 0, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_degenerate_cases():
+    rng = _rng(22)
+    q = rng.standard_normal(128)
+    v = rng.standard_normal((5, 128))
+    np.testing.assert_allclose(orc.attention(q, rng.standard_normal((1, 128)), v[:1], 0.1), v[0])
+    same = np.repeat(rng.standard_normal((1, 128)), 5, axis=0)
+    np.testing.assert_allclose(orc.attention(q, same, v, 0.1), v.mean(0), atol=1e-14)
+
+
+def _paged_case(shuffled, seq_len=150, hkv=2, hq=8):
+    base = inputs.workload(1)
+    import dataclasses
+    wl = dataclasses.replace(base, seq_lens=(seq_len, seq_len - 37), hkv=hkv, hq=hq, tile_tokens=32)
+    k = inputs.gen_kv(wl, "K")
+    v = inputs.gen_kv(wl, "V")
+    table, npages = (inputs.block_table if shuffled else inputs.identity_block_table)(wl)
+    pk = orc.new_pool(npages, hkv, 4, 32)
+    pv = orc.new_pool(npages, hkv, 2, 32)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, 32, 4, 2, 3, pk, pv)
+    q = inputs.gen_q(wl)
+    lens = np.array(wl.seq_lens)
+    out = orc.paged_decode_attn(q, table, lens, pk, pv, 32, 4, 2)
+    return wl, k, v, q, out, (pk, pv, table)
+
+
+def test_paged_attention_equals_brute_force_with_gqa_and_ignores_page_order():
+    wl, k, v, q, out, (pk, pv, table) = _paged_case(True)
+    _, _, _, _, out_id, _ = _paged_case(False)
+    np.testing.assert_array_equal(out, out_id)
+    cu = wl.cu_seqlens()
+    kd = orc.quantize_dense(k[cu[0]:cu[1]], 32, 4, 3)
+    vd = orc.quantize_dense(v[cu[0]:cu[1]], 32, 2, 3)
+    kx = orc.dequantize_dense(kd["codes"], kd["alpha"], kd["scale"], kd["offset"], 32, 4)
+    vx = orc.dequantize_dense(vd["codes"], vd["alpha"], vd["scale"], vd["offset"], 32, 2)
+    # torch SDPA on the restored K/V with grouped heads (query head h -> kv head h // 4)
+    qt = torch.tensor(q[0].astype(np.float64))[:, None, :]               # [Hq, 1, d]
+    kt = torch.tensor(kx).permute(1, 0, 2).repeat_interleave(4, dim=0)   # [Hq, L, d]
+    vt = torch.tensor(vx).permute(1, 0, 2).repeat_interleave(4, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0].numpy()
+    np.testing.assert_allclose(out[0], ref, rtol=1e-10, atol=1e-12)
