@@ -1,0 +1,257 @@
+#!/usr/bin/env python
+"""Throughput of the quantized KV-cache hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. quantize every page of the prefill (K and V, all sequences and heads),
+  2. append one decode token per sequence and re-quantize its tile,
+  3. one decode-attention step over every cached token, read from the pages.
+Default workload: a Qwen3-4B-shaped layer, 8 KV heads / 32 query heads,
+4 sequences x 16K context, 16-token pages, tile 64, 4-bit K and V, 3
+normalization iterations.
+
+Prints one JSON line.  `value` is the step's algorithmic bytes (quantize +
+append + decode) over the step time, in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from kv_cache_quantization_tiles_amd import inputs  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+D = 128
+
+
+# ----------------------------------------------------------------------------- byte model
+def quantize_bytes(n_token_heads: int, bits: int, tile: int) -> float:
+    """Algorithmic bytes of quantizing n token-heads of K or V: fp16 read,
+    codes + scale + offset written, and the tile's channel factors."""
+    return n_token_heads * (2 * D + D * bits / 8 + 8 + 4 * D / tile)
+
+
+def slot_bytes_per_token(bits: int, tile: int) -> float:
+    return D * bits / 8 + 8 + 4 * D / tile
+
+
+def decode_bytes(wl, lens) -> float:
+    """Slot bytes of every page read by one decode step (whole tiles)."""
+    t = wl.tile_tokens
+    tok = sum(int(math.ceil(l / t)) * t for l in lens) * wl.hkv
+    return tok * (slot_bytes_per_token(wl.bits_k, t) + slot_bytes_per_token(wl.bits_v, t))
+
+
+def append_bytes(wl, lens_before) -> float:
+    """Staging rows read and the tile's slots rewritten, K and V."""
+    t = wl.tile_tokens
+    tot = 0.0
+    for l in lens_before:
+        rows = l % t + 1
+        for bits in (wl.bits_k, wl.bits_v):
+            tot += wl.hkv * (rows * 2 * D + 2 * D + t * slot_bytes_per_token(bits, t))
+    return tot
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+def _oracle_quantize_unit(args):
+    import oracle as orc
+    wl, s, h, role = args
+    x = inputs.gen_kv(wl, role, seqs=[s])[:, h:h + 1]
+    n = x.shape[0]
+    table = np.arange(int(math.ceil(n / wl.tile_tokens)) * (wl.tile_tokens // 16), dtype=np.int32)[None]
+    bits = wl.bits_k if role == "K" else wl.bits_v
+    pool = orc.new_pool(table.shape[1], 1, bits, wl.tile_tokens)
+    t0 = time.perf_counter()
+    if role == "K":
+        orc.quantize_to_pages(x, x, np.array([0, n], np.int32), table, wl.tile_tokens, bits, bits, wl.iters,
+                              pool, orc.new_pool(table.shape[1], 1, bits, wl.tile_tokens))
+    else:
+        orc.quantize_to_pages(x, x, np.array([0, n], np.int32), table, wl.tile_tokens, bits, bits, wl.iters,
+                              orc.new_pool(table.shape[1], 1, bits, wl.tile_tokens), pool)
+    return (s, h, role), pool, time.perf_counter() - t0
+
+
+def _oracle_decode_unit(args):
+    import oracle as orc
+    wl, s, h, pk, pv, q = args
+    n = wl.seq_lens[s]
+    table = np.arange(pk.shape[0], dtype=np.int32)[None]
+    t0 = time.perf_counter()
+    orc.paged_decode_attn(q, table, np.array([n], np.int32), pk, pv, wl.tile_tokens, wl.bits_k, wl.bits_v)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, max_seqs: int):
+    """Time the oracle (as it stands) on the host cores, on a bounded sample:
+    the first `max_seqs` sequences of the workload, all heads, K and V
+    quantized, then one decode step over them."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    seqs = list(range(min(max_seqs, wl.num_seqs)))
+    units = [(wl, s, h, role) for s in seqs for h in range(wl.hkv) for role in ("K", "V")]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_quantize_unit, units, chunksize=1)
+        tq = time.perf_counter() - t0
+        pools = {key: p for key, p, _ in res}
+        q = inputs.gen_q(wl)
+        dunits = [(wl, s, h, pools[(s, h, "K")], pools[(s, h, "V")],
+                   q[s:s + 1, h * wl.group:(h + 1) * wl.group]) for s in seqs for h in range(wl.hkv)]
+        t1 = time.perf_counter()
+        pool.map(_oracle_decode_unit, dunits, chunksize=1)
+        td = time.perf_counter() - t1
+    ntok_heads = sum(wl.seq_lens[s] for s in seqs) * wl.hkv
+    qb = quantize_bytes(ntok_heads, wl.bits_k, wl.tile_tokens) + quantize_bytes(ntok_heads, wl.bits_v, wl.tile_tokens)
+    db = decode_bytes(wl, [wl.seq_lens[s] for s in seqs])
+    return {"value": round((qb + db) / (tq + td) / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(seqs)} of {wl.num_seqs} sequences x {wl.seq_lens[0]} tokens, all {wl.hkv} kv heads: "
+                      f"quantize K and V to pages, then one decode step (fp64 NumPy oracle, "
+                      f"{cores} worker processes)",
+            "quantize_s": round(tq, 3), "decode_s": round(td, 3),
+            "machine_cores": os.cpu_count()}
+
+
+# ----------------------------------------------------------------------------- GPU leg
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--cpu-seqs", type=int, default=1, help="sequences in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards "
+              "without communication, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    wl = inputs.workload(args.workload)
+    if wl.layers != 1:
+        raise SystemExit("multi-layer workloads are not bench lines")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seqs)  # before any GPU call
+
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    table, npages = inputs.block_table(wl)
+    k_np, v_np = inputs.gen_kv(wl, "K"), inputs.gen_kv(wl, "V")
+    n_in = 2   # input copies, alternated so that inputs stream from HBM
+    ks = [torch.from_numpy(k_np).to(dev) for _ in range(n_in)]
+    vs = [torch.from_numpy(v_np).to(dev) for _ in range(n_in)]
+    del k_np, v_np
+    cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+    max_len = max(wl.seq_lens)
+    pool_bytes = (npages * wl.hkv * (api.kvq_slot_bytes(cfg, False) + api.kvq_slot_bytes(cfg, True)))
+    n_pools = max(3, int(math.ceil(1.0e9 / pool_bytes)))   # >= 1 GB of pools between reuses
+    caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
+    lens_before = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    lens_after = lens_before + 1
+    kn = torch.from_numpy(inputs.gen_decode_kv(wl, "K", 0)).to(dev)
+    vn = torch.from_numpy(inputs.gen_decode_kv(wl, "V", 0)).to(dev)
+    q = torch.from_numpy(inputs.gen_q(wl)).to(dev)
+    out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+    ws = caches[0].workspace(wl.hq, max_len + 1)
+
+    def step(i, ev=None):
+        c = caches[i % n_pools]
+        if ev is not None:
+            ev[0].record()
+        c.quantize_prefill(ks[i % n_in], vs[i % n_in], cu, max_len)
+        if ev is not None:
+            ev[1].record()
+        c.append(kn, vn, lens_before)
+        if ev is not None:
+            ev[2].record()
+        c.decode(q, lens_after, max_len + 1, out=out, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tq = [e[0].elapsed_time(e[1]) for e in evs]
+    ta = [e[1].elapsed_time(e[2]) for e in evs]
+    td = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+
+    # decode attention alone, pools rotated so every call reads cold pages
+    n_dec = max(20, args.steps)
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dec)]
+    for j in range(n_dec):
+        dev_ev[j][0].record()
+        caches[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws)
+        dev_ev[j][1].record()
+    # bandwidth probe: plain copy of 1 GiB
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    api._lib.kvq_bandwidth_probe(src, dst, nb)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        api._lib.kvq_bandwidth_probe(src, dst, nb)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    td_cold = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+
+    ntok_heads = wl.total_tokens * wl.hkv
+    qbytes = quantize_bytes(ntok_heads, wl.bits_k, wl.tile_tokens) + quantize_bytes(ntok_heads, wl.bits_v, wl.tile_tokens)
+    abytes = append_bytes(wl, wl.seq_lens)
+    dbytes = decode_bytes(wl, [l + 1 for l in wl.seq_lens])
+    q_ms, a_ms, d_ms = float(np.mean(tq)), float(np.mean(ta)), float(np.mean(td))
+    q_gbps = qbytes / (q_ms * 1e-3) / 1e9
+    d_gbps_cold = dbytes / (td_cold * 1e-3) / 1e9
+    value = (qbytes + abytes + dbytes) / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": "quantize GB/s + quantized decode-attn tokens/s at 16K; % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "context": max_len, "kv_heads": wl.hkv,
+                   "q_heads": wl.hq, "head_dim": D, "page_tokens": 16, "tile_tokens": wl.tile_tokens,
+                   "bits_k": wl.bits_k, "bits_v": wl.bits_v, "sinkhorn_iters": wl.iters},
+        "quantize_ms": round(q_ms, 4), "quantize_GBps": round(q_gbps, 1),
+        "quantize_hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+        "append_ms": round(a_ms, 4),
+        "decode_attn_ms": round(d_ms, 4), "decode_attn_cold_ms": round(td_cold, 4),
+        "decode_attn_GBps_cold": round(d_gbps_cold, 1),
+        "decode_hbm_frac_cold": round(d_gbps_cold / HBM_PEAK_GBPS, 4),
+        "decode_tok_per_s": round(wl.num_seqs / ((a_ms + d_ms) * 1e-3), 1),
+        "decode_attn_only_tok_per_s": round(wl.num_seqs / (td_cold * 1e-3), 1),
+        "copy_probe_GBps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "quantize_paged_kernel",
+                     "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(q_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

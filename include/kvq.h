@@ -1,0 +1,221 @@
+/*
+ * kvq.h - C ABI of the MI355X (gfx950) variance-normalized KV-cache tile
+ * quantizer and its paged decode-attention read path.
+ *
+ * The method: the KV cache is quantized one fixed-size token tile at a time;
+ * each raw fp16 tile is rotated along the channel dimension with a Hadamard
+ * transform (spreading channel-concentrated outliers), then put through a
+ * Sinkhorn-like iterative variance normalization that evens out the
+ * per-channel variance, then rounded to nearest, asymmetrically, to a
+ * low-bit cache.  Source: page "Huawei's KVarN boosts vLLM KV-cache capacity
+ * by 5x without accuracy loss" (axbrief.com), section "기존 방식과 달라진
+ * 지점", restated in its section "별도의 캘리브레이션이나 모델 변경 없이
+ * 플래그 하나로 적용" (nothing is calibrated: every statistic comes from the
+ * tile).  K and V are compressed and restored inside the pipeline with the
+ * cache kept in pages (page "화웨이가 공개한 KVarN — LLM 추론의 '메모리 먹는
+ * 하마' KV 캐시를 양자화로 길들이기", ttj.kr, section "양자화로 캐시를
+ * 다이어트시킨다"), and the attention backend reads the compressed pages
+ * directly instead of re-materializing fp16 (aitrends.kr article 74976,
+ * TL;DR and the glossary entries on KV compression and the attention
+ * backend).
+ *
+ * What the pages leave open is fixed here as follows (every function uses it):
+ *   - Hadamard: orthonormal Sylvester order, no random signs, on every token
+ *     row of K and of V (head_dim 128).
+ *   - One normalization iteration = channel step (each channel divided by its
+ *     population std over the tile's valid tokens) then token step (each token
+ *     divided by its population std over the 128 channels).  A channel/token
+ *     whose std is at most 1e-2 times its RMS keeps factor 1.  The channel
+ *     factors alpha[128] are stored per tile; the token factors are folded
+ *     into the per-token scale and offset.
+ *   - Rounding: per token row of the tile, zero-point = row minimum, step =
+ *     (max - min) / (2^bits - 1), round half to even; a zero-range row gets
+ *     codes 0 and step 0.  Stored per token: scale S = beta*step and offset
+ *     O = beta*min (fp32).  Restore: rotated row = alpha * (S * code + O),
+ *     token = Hadamard(rotated row).
+ *   - Tiles start at token 0 of each sequence; the last may be partial and
+ *     its statistics use only its valid rows.
+ *
+ * Conventions for every function:
+ *   - Pointers to data are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), contiguous in the documented layouts, at least 16-byte
+ *     aligned (pools and code buffers: 256-byte aligned recommended).
+ *     `cfg` and scalar arguments live on the host.
+ *   - The caller owns and allocates every buffer.  The library allocates
+ *     nothing, keeps no state between calls except a thread-local error
+ *     message, and never synchronizes: each call enqueues its kernels on
+ *     `stream` (a hipStream_t passed as void*, NULL = default stream) and
+ *     returns.
+ *   - Arguments are validated on the host before any launch.  On a non-OK
+ *     status nothing was launched (except KVQ_ERR_HIP, reported when a
+ *     launch fails) and kvq_last_error() describes the problem.  Contents of
+ *     device arrays (lengths, page ids) are trusted: out-of-range values are
+ *     undefined behaviour, as for any kernel argument.
+ *   - Inputs must be finite.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t kvq_half; /* IEEE 754 binary16 bit pattern */
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,         /* null pointer, non-positive size, inconsistent shapes */
+  KVQ_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 16, tile not 32/64/128,
+                               bits not 2/4, iters outside 0..16, GQA group > 16 */
+  KVQ_ERR_HIP = -3,         /* a kernel launch failed */
+  KVQ_ERR_WORKSPACE = -4    /* workspace smaller than kvq_decode_workspace_bytes() */
+} kvq_status;
+
+typedef struct {
+  int32_t head_dim;       /* must be 128 */
+  int32_t page_tokens;    /* must be 16 */
+  int32_t tile_tokens;    /* 32, 64 or 128 (a multiple of page_tokens) */
+  int32_t bits_k;         /* code width of K: 2 or 4 */
+  int32_t bits_v;         /* code width of V: 2 or 4 */
+  int32_t sinkhorn_iters; /* normalization iterations, 0..16 */
+} kvq_config;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Library version string. */
+const char* kvq_version(void);
+
+/*
+ * Page-pool layout.  A page holds 16 consecutive tokens of one sequence.  A
+ * pool is an array [num_pages][kv_heads][slot] of bytes; a slot is
+ *   codes : 16*128*bits/8 bytes (layout below)
+ *   scale : float32[16]   per token S   (0 for rows past the sequence end)
+ *   offset: float32[16]   per token O   (0 for rows past the sequence end)
+ *   alpha : float32[16*128/tile_tokens] the slice j*L..(j+1)*L-1 (L = 2048/T)
+ *           of the tile's channel factors, j = the page's index in its tile.
+ * K-slot codes: 4 blocks of 32 channels; block k stores, token after token,
+ *   channels 32k..32k+31 of each token packed low bits first (channel c at
+ *   bits (c mod (8/bits))*bits of byte c*bits/8 within the token's block).
+ * V-slot codes: 4 quads of 4 tokens; quad q holds 16 groups of 8 channels;
+ *   group m is 4*bits bytes read as little-endian 32-bit words; word w holds
+ *   channels 8m + w*F/4 + j (j < F/4, F = 32/bits fields per word) of tokens
+ *   4q + r (r < 4), channel j / token r in field f = 2j + (r>>1) + (F/2)(r&1),
+ *   field f being bits [bits*f, bits*(f+1)) of the word.
+ * Rows of a page past the sequence's end hold code 0, scale 0 and offset 0.
+ * Contract: a sequence owns a page for every page of every tile it has
+ * started (pages are allocated in whole tiles), so a partial tile's channel
+ * factors always have a home.  The block table is int32 [num_seqs][max_blocks]
+ * of page ids; page p of sequence s holds its tokens 16p..16p+15.
+ * Returns 0 for an invalid config.
+ */
+size_t kvq_slot_bytes(const kvq_config* cfg, int32_t is_v);
+
+/*
+ * kvq_quantize_tiles - quantize one token run per head in the dense layout.
+ *   x          fp16 [n_tokens][heads][128]; tile j of each head covers tokens
+ *              j*T .. min(n_tokens, (j+1)*T)-1.
+ *   bits       2 or 4 (cfg->bits_k/bits_v are ignored here).
+ *   codes      uint8 [n_tokens][heads][128*bits/8], channels packed low bits
+ *              first (natural order).
+ *   alpha      float32 [ceil(n_tokens/T)][heads][128] channel factors.
+ *   tok_scale  float32 [n_tokens][heads] per token S.
+ *   tok_offset float32 [n_tokens][heads] per token O.
+ * Errors: KVQ_ERR_ARG for null pointers or n_tokens/heads <= 0,
+ * KVQ_ERR_UNSUPPORTED for an unsupported config or bits.
+ */
+kvq_status kvq_quantize_tiles(const kvq_config* cfg, const kvq_half* x, int32_t n_tokens,
+                              int32_t heads, int32_t bits, uint8_t* codes, float* alpha,
+                              float* tok_scale, float* tok_offset, void* stream);
+
+/*
+ * kvq_dequantize - restore fp16 tokens from the dense layout of
+ * kvq_quantize_tiles (same shapes): out[t][h] = Hadamard(alpha * (S*code + O))
+ * computed in fp32 and rounded to nearest-even fp16.
+ */
+kvq_status kvq_dequantize(const kvq_config* cfg, const uint8_t* codes, const float* alpha,
+                          const float* tok_scale, const float* tok_offset, int32_t n_tokens,
+                          int32_t heads, int32_t bits, kvq_half* out, void* stream);
+
+/*
+ * kvq_quantize_to_pages - quantize a prefill of K and V into the page pools.
+ *   k, v         fp16 [total_tokens][kv_heads][128], sequences packed back to
+ *                back; sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1.
+ *   cu_seqlens   int32 [num_seqs+1], device.
+ *   max_seq_len  host upper bound of every sequence length (sizes the grid).
+ *   block_table  int32 [num_seqs][max_blocks], device.
+ *   pool_k/pool_v  K and V pools (layout above; bits from cfg).
+ *   staging_k/staging_v  fp16 [num_seqs][T][kv_heads][128] or NULL: rows
+ *                of a last tile that is not full are copied there (needed
+ *                by kvq_append_and_requant).
+ * K uses cfg->bits_k, V cfg->bits_v; both use cfg->sinkhorn_iters.
+ */
+kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t max_seq_len, int32_t kv_heads,
+                                 const int32_t* block_table, int32_t max_blocks, void* pool_k,
+                                 void* pool_v, kvq_half* staging_k, kvq_half* staging_v,
+                                 void* stream);
+
+/*
+ * kvq_append_and_requant - append one decode token per sequence and
+ * re-quantize the tile it lands in.
+ *   k_new, v_new     fp16 [num_seqs][kv_heads][128].
+ *   seq_lens_before  int32 [num_seqs], device: tokens cached before this one.
+ *   staging_k/_v     fp16 [num_seqs][T][kv_heads][128]: rows 0..r-1 of the
+ *                    partial tile (r = seq_len_before mod T) must hold that
+ *                    tile's fp16 rows (kvq_quantize_to_pages and earlier
+ *                    appends keep them); the new row is written at r.
+ * The whole tile (rows 0..r) is quantized again, as in kvq_quantize_to_pages,
+ * and its pages rewritten.  The caller advances its lengths afterwards.
+ */
+kvq_status kvq_append_and_requant(const kvq_config* cfg, const kvq_half* k_new,
+                                  const kvq_half* v_new, const int32_t* seq_lens_before,
+                                  int32_t num_seqs, int32_t kv_heads, kvq_half* staging_k,
+                                  kvq_half* staging_v, const int32_t* block_table,
+                                  int32_t max_blocks, void* pool_k, void* pool_v, void* stream);
+
+/* Bytes of workspace kvq_paged_decode_attn needs for these sizes. */
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t q_heads,
+                                  int32_t kv_heads, int32_t max_seq_len);
+
+/*
+ * kvq_paged_decode_attn - one decode step of attention straight from the
+ * quantized pages (no fp16 K/V is rebuilt).
+ *   q            fp16 [num_seqs][q_heads][128]; query head h reads kv head
+ *                h / (q_heads / kv_heads).
+ *   seq_lens     int32 [num_seqs], device: tokens to attend (newest included).
+ *   max_seq_len  host upper bound of seq_lens (sizes the grid).
+ *   sm_scale     softmax scale (1/sqrt(128) for standard attention).
+ *   out          float32 [num_seqs][q_heads][128]:
+ *                softmax(sm_scale * q.K^T) V over the restored tokens,
+ *                computed as scores (H q * alpha_K).(S code + O) and values
+ *                Hadamard(sum_t p_t alpha_V (S code + O)), fp32 accumulation.
+ *   workspace    device scratch of at least kvq_decode_workspace_bytes().
+ * Errors: KVQ_ERR_WORKSPACE if the workspace is too small; KVQ_ERR_ARG if
+ * q_heads is not a multiple of kv_heads; KVQ_ERR_UNSUPPORTED if the group is
+ * larger than 16.
+ */
+kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs,
+                                 int32_t q_heads, int32_t kv_heads, const int32_t* block_table,
+                                 int32_t max_blocks, const int32_t* seq_lens,
+                                 int32_t max_seq_len, const void* pool_k, const void* pool_v,
+                                 float sm_scale, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_bandwidth_probe - measurement helper, not part of the method: copies
+ * `bytes` (a positive multiple of 16) from src to dst with a plain streaming
+ * kernel, so that achieved HBM bandwidth and profiler byte counters can be
+ * calibrated against a kernel of known traffic (2 * bytes).
+ */
+kvq_status kvq_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,277 @@
+// C ABI of libkvq: host-side validation, then kernel launches on the
+// caller's stream.  See include/kvq.h for the contract of every function.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvq_status check_config(const kvq_config* cfg, bool need_paged_bits) {
+  if (cfg == nullptr) return fail(KVQ_ERR_ARG, "cfg is NULL");
+  if (cfg->head_dim != kvq::kHeadDim)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d unsupported (must be 128)", cfg->head_dim);
+  if (cfg->page_tokens != kvq::kPage)
+    return fail(KVQ_ERR_UNSUPPORTED, "page_tokens %d unsupported (must be 16)", cfg->page_tokens);
+  if (cfg->tile_tokens != 32 && cfg->tile_tokens != 64 && cfg->tile_tokens != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "tile_tokens %d unsupported (32, 64 or 128)", cfg->tile_tokens);
+  if (cfg->sinkhorn_iters < 0 || cfg->sinkhorn_iters > 16)
+    return fail(KVQ_ERR_UNSUPPORTED, "sinkhorn_iters %d outside 0..16", cfg->sinkhorn_iters);
+  if (need_paged_bits) {
+    if (cfg->bits_k != 2 && cfg->bits_k != 4)
+      return fail(KVQ_ERR_UNSUPPORTED, "bits_k %d unsupported (2 or 4)", cfg->bits_k);
+    if (cfg->bits_v != 2 && cfg->bits_v != 4)
+      return fail(KVQ_ERR_UNSUPPORTED, "bits_v %d unsupported (2 or 4)", cfg->bits_v);
+  }
+  return KVQ_OK;
+}
+
+kvq_status check_bits(int bits) {
+  if (bits != 2 && bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "bits %d unsupported (2 or 4)", bits);
+  return KVQ_OK;
+}
+
+kvq_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KVQ_OK;
+}
+
+#define KVQ_TRY(x)                 \
+  do {                             \
+    kvq_status st_ = (x);          \
+    if (st_ != KVQ_OK) return st_; \
+  } while (0)
+
+#define KVQ_NONNULL(p) \
+  if ((p) == nullptr) return fail(KVQ_ERR_ARG, "%s is NULL", #p)
+
+// Split of the context into partitions of tiles for the decode kernel: enough
+// waves to cover 256 CUs several times over, at least one tile each.
+int tiles_per_partition(int num_seqs, int kv_heads, int max_seq_len, int tile) {
+  const long tiles = (long)((max_seq_len + tile - 1) / tile);
+  const long total = tiles * num_seqs * kv_heads;
+  long tpp = (total + 2047) / 2048;
+  if (tpp < 1) tpp = 1;
+  if (tpp > 64) tpp = 64;
+  if (tpp > tiles) tpp = tiles > 0 ? tiles : 1;
+  return (int)tpp;
+}
+
+int max_partitions(int max_seq_len, int tile, int tpp) {
+  const int tiles = (max_seq_len + tile - 1) / tile;
+  return (tiles + tpp - 1) / tpp;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_err; }
+
+const char* kvq_version(void) { return "kvq 0.1 gfx950"; }
+
+size_t kvq_slot_bytes(const kvq_config* cfg, int32_t is_v) {
+  if (check_config(cfg, true) != KVQ_OK) return 0;
+  return (size_t)kvq::slot_bytes(is_v ? cfg->bits_v : cfg->bits_k, cfg->tile_tokens);
+}
+
+kvq_status kvq_quantize_tiles(const kvq_config* cfg, const kvq_half* x, int32_t n_tokens,
+                              int32_t heads, int32_t bits, uint8_t* codes, float* alpha,
+                              float* tok_scale, float* tok_offset, void* stream) {
+  KVQ_TRY(check_config(cfg, false));
+  KVQ_TRY(check_bits(bits));
+  KVQ_NONNULL(x);
+  KVQ_NONNULL(codes);
+  KVQ_NONNULL(alpha);
+  KVQ_NONNULL(tok_scale);
+  KVQ_NONNULL(tok_offset);
+  if (n_tokens <= 0 || heads <= 0) return fail(KVQ_ERR_ARG, "n_tokens %d and heads %d must be > 0", n_tokens, heads);
+  if ((long)((n_tokens + cfg->tile_tokens - 1) / cfg->tile_tokens) > 2147483647L || heads > 65535)
+    return fail(KVQ_ERR_ARG, "too many tiles or heads for one launch");
+  kvq::QuantArgs a{};
+  a.x = x;
+  a.codes = codes;
+  a.alpha = alpha;
+  a.scale = tok_scale;
+  a.offset = tok_offset;
+  a.n_tokens = n_tokens;
+  a.heads = heads;
+  a.iters = cfg->sinkhorn_iters;
+  return launched(kvq::launch_quantize_dense(a, cfg->tile_tokens, bits, (hipStream_t)stream),
+                  "kvq_quantize_tiles");
+}
+
+kvq_status kvq_dequantize(const kvq_config* cfg, const uint8_t* codes, const float* alpha,
+                          const float* tok_scale, const float* tok_offset, int32_t n_tokens,
+                          int32_t heads, int32_t bits, kvq_half* out, void* stream) {
+  KVQ_TRY(check_config(cfg, false));
+  KVQ_TRY(check_bits(bits));
+  KVQ_NONNULL(codes);
+  KVQ_NONNULL(alpha);
+  KVQ_NONNULL(tok_scale);
+  KVQ_NONNULL(tok_offset);
+  KVQ_NONNULL(out);
+  if (n_tokens <= 0 || heads <= 0) return fail(KVQ_ERR_ARG, "n_tokens %d and heads %d must be > 0", n_tokens, heads);
+  kvq::DequantArgs a{codes, alpha, tok_scale, tok_offset, n_tokens, heads, out};
+  return launched(kvq::launch_dequantize(a, cfg->tile_tokens, bits, (hipStream_t)stream), "kvq_dequantize");
+}
+
+kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t max_seq_len, int32_t kv_heads,
+                                 const int32_t* block_table, int32_t max_blocks, void* pool_k,
+                                 void* pool_v, kvq_half* staging_k, kvq_half* staging_v,
+                                 void* stream) {
+  KVQ_TRY(check_config(cfg, true));
+  KVQ_NONNULL(k);
+  KVQ_NONNULL(v);
+  KVQ_NONNULL(cu_seqlens);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  if ((staging_k == nullptr) != (staging_v == nullptr))
+    return fail(KVQ_ERR_ARG, "staging_k and staging_v must both be set or both be NULL");
+  if (num_seqs <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (2 * kv_heads > 65535 || num_seqs > 65535) return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  const int tile = cfg->tile_tokens;
+  const long need_blocks = (long)((max_seq_len + tile - 1) / tile) * (tile / kvq::kPage);
+  if (need_blocks > max_blocks)
+    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens in whole tiles (%ld pages)", max_blocks,
+                max_seq_len, need_blocks);
+  kvq::QuantArgs a{};
+  a.src[0] = k;
+  a.src[1] = v;
+  a.pool[0] = (uint8_t*)pool_k;
+  a.pool[1] = (uint8_t*)pool_v;
+  a.staging[0] = staging_k;
+  a.staging[1] = staging_v;
+  a.cu_seqlens = cu_seqlens;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.kv_heads = kv_heads;
+  a.iters = cfg->sinkhorn_iters;
+  return launched(kvq::launch_quantize_paged(a, tile, cfg->bits_k, cfg->bits_v, num_seqs, max_seq_len,
+                                             (hipStream_t)stream),
+                  "kvq_quantize_to_pages");
+}
+
+kvq_status kvq_append_and_requant(const kvq_config* cfg, const kvq_half* k_new,
+                                  const kvq_half* v_new, const int32_t* seq_lens_before,
+                                  int32_t num_seqs, int32_t kv_heads, kvq_half* staging_k,
+                                  kvq_half* staging_v, const int32_t* block_table,
+                                  int32_t max_blocks, void* pool_k, void* pool_v, void* stream) {
+  KVQ_TRY(check_config(cfg, true));
+  KVQ_NONNULL(k_new);
+  KVQ_NONNULL(v_new);
+  KVQ_NONNULL(seq_lens_before);
+  KVQ_NONNULL(staging_k);
+  KVQ_NONNULL(staging_v);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  if (num_seqs <= 0 || kv_heads <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, kv_heads and max_blocks must be > 0");
+  if (kv_heads > 65535 || num_seqs > 65535) return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  if (max_blocks < cfg->tile_tokens / kvq::kPage)
+    return fail(KVQ_ERR_ARG, "max_blocks %d is smaller than one tile", max_blocks);
+  kvq::QuantArgs a{};
+  a.src[0] = k_new;
+  a.src[1] = v_new;
+  a.pool[0] = (uint8_t*)pool_k;
+  a.pool[1] = (uint8_t*)pool_v;
+  a.staging[0] = staging_k;
+  a.staging[1] = staging_v;
+  a.lens_before = seq_lens_before;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.kv_heads = kv_heads;
+  a.iters = cfg->sinkhorn_iters;
+  return launched(kvq::launch_append(a, cfg->tile_tokens, cfg->bits_k, cfg->bits_v, num_seqs,
+                                     (hipStream_t)stream),
+                  "kvq_append_and_requant");
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t q_heads,
+                                  int32_t kv_heads, int32_t max_seq_len) {
+  if (check_config(cfg, true) != KVQ_OK) return 0;
+  if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0) return 0;
+  const int tpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, cfg->tile_tokens);
+  const int parts = max_partitions(max_seq_len, cfg->tile_tokens, tpp);
+  return (size_t)num_seqs * q_heads * parts * (kvq::kHeadDim + 2) * sizeof(float);
+}
+
+kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs,
+                                 int32_t q_heads, int32_t kv_heads, const int32_t* block_table,
+                                 int32_t max_blocks, const int32_t* seq_lens,
+                                 int32_t max_seq_len, const void* pool_k, const void* pool_v,
+                                 float sm_scale, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  KVQ_TRY(check_config(cfg, true));
+  KVQ_NONNULL(q);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(seq_lens);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  KVQ_NONNULL(out);
+  KVQ_NONNULL(workspace);
+  if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, q_heads, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (q_heads % kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "q_heads %d is not a multiple of kv_heads %d", q_heads, kv_heads);
+  const int group = q_heads / kv_heads;
+  if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d larger than 16", group);
+  if (kv_heads > 65535 || num_seqs > 65535 || (long)num_seqs * q_heads > 2147483647L)
+    return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  const int tile = cfg->tile_tokens;
+  const long need_blocks = (long)((max_seq_len + tile - 1) / tile) * (tile / kvq::kPage);
+  if (need_blocks > max_blocks)
+    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens in whole tiles", max_blocks, max_seq_len);
+  const size_t need = kvq_decode_workspace_bytes(cfg, num_seqs, q_heads, kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const int tpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, tile);
+  const int parts = max_partitions(max_seq_len, tile, tpp);
+  kvq::DecodeArgs a{};
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.pool_k = (const uint8_t*)pool_k;
+  a.pool_v = (const uint8_t*)pool_v;
+  a.out = out;
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = (float*)workspace + (size_t)num_seqs * q_heads * parts * kvq::kHeadDim;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks;
+  a.tiles_per_part = tpp;
+  a.max_parts = parts;
+  a.max_tiles = (max_seq_len + tile - 1) / tile;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  return launched(kvq::launch_decode(a, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
+                  "kvq_paged_decode_attn");
+}
+
+kvq_status kvq_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream) {
+  KVQ_NONNULL(src);
+  KVQ_NONNULL(dst);
+  if (bytes == 0 || bytes % 16 != 0) return fail(KVQ_ERR_ARG, "bytes must be a positive multiple of 16");
+  return launched(kvq::launch_copy_probe(src, dst, bytes, (hipStream_t)stream), "kvq_bandwidth_probe");
+}
+
+}  // extern "C"

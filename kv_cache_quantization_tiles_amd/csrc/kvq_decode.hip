@@ -1,0 +1,428 @@
+// Paged decode attention that reads the quantized pages directly, for gfx950.
+//
+// The attention backend reads compressed KV pages as they are stored, without
+// re-materializing fp16 K/V (aitrends.kr article 74976, TL;DR and the glossary
+// entries on KV compression and the attention backend).
+//
+// Algebra (H = orthonormal Sylvester Hadamard, symmetric, H H = I):
+//   key t restored:    x_t = H r_t,  r_tc = alpha_c (S_t k_tc + O_t)
+//   score:             q . x_t = (H q) . r_t
+//                          = S_t sum_c qt_c k_tc + O_t sum_c qt_c,  qt = (H q) * alpha_K
+//   value output:      sum_t p_t x_t = H sum_t p_t r_t, with
+//                      sum_t p_t r_tc = alpha_c (sum_t p_t S_t k_tc + sum_t p_t O_t)
+// so the inverse rotation and the channel factors act on the query (once per
+// tile) and on the accumulated output (once per sequence and head), never on
+// the cached tokens.
+//
+// Work split: one wave per (sequence, kv head, partition of tiles).  The
+// group of G query heads sharing the kv head is padded to 16 and both
+// contractions run on v_mfma_f32_16x16x32_f16:
+//   QK:  S^T[t][g] = sum_c K[t][c] W[c][g]: A = 16 tokens of codes (each code
+//        k as the exact fp16 1 + k/64), B = qt split into fp16 hi + lo.
+//   PV:  O^T[c][g] = sum_t V[t][c] P[t][g]: A = codes of 2 pages (32 tokens),
+//        B = p_t S_t split into fp16 hi + lo.
+// The QK output layout (lane = query head, 4 tokens per lane) is exactly the
+// B layout PV needs, so no shuffle sits between the two.  Codes unpack with
+// two integer ops per pair of codes (shift, and-or) and no conversion.
+// Online softmax runs per tile; partitions are merged by a second kernel that
+// also applies the final Hadamard.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr unsigned kOne = 0x3C003C00u;  // fp16 1.0 in both halves
+
+// Pair of codes from nibble/field position x of both 16-bit halves, moved to
+// mantissa bits 4.. so that the fp16 value is 1 + code/64.
+template <int BITS, int X>
+__device__ __forceinline__ unsigned code_pair(unsigned w) {
+  constexpr unsigned mask = (BITS == 4) ? 0x00F000F0u : 0x00300030u;
+  constexpr int shift = 4 - BITS * X;  // > 0: left, < 0: right
+  const unsigned s = (shift >= 0) ? (w << (shift >= 0 ? shift : 0)) : (w >> (shift < 0 ? -shift : 0));
+  return (s & mask) | kOne;
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(unsigned a, unsigned b, unsigned c, unsigned d) {
+  u32x4 v{a, b, c, d};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (unsigned)__builtin_bit_cast(uint16_t, a) | ((unsigned)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// hi/lo fp16 split of two fp32 values, returned as (hi pair, lo pair).
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+  const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+  hi = (unsigned)__builtin_bit_cast(uint16_t, h0) | ((unsigned)__builtin_bit_cast(uint16_t, h1) << 16);
+  lo = (unsigned)__builtin_bit_cast(uint16_t, l0) | ((unsigned)__builtin_bit_cast(uint16_t, l1) << 16);
+}
+
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
+
+__device__ __forceinline__ float group_max(float v) {  // over the 4 lanes l, l^16, l^32, l^48
+  v = fmaxf(v, lane_xor<16>(v));
+  return fmaxf(v, xor32(v));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  v += lane_xor<16>(v);
+  return v + xor32(v);
+}
+
+// Channel of A-operand slot (chunk ch, lane group grp, slot j) for K codes.
+template <int BITS>
+__device__ __forceinline__ int k_channel(int ch, int grp, int j) {
+  const int m = j >> 1, hi = j & 1;
+  if (BITS == 4) return 32 * grp + 8 * ch + m + 4 * hi;
+  return 32 * grp + 16 * (ch >> 1) + 4 * (ch & 1) + m + 8 * hi;
+}
+
+template <int T, int BK, int BV>
+__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs A) {
+  constexpr int NP = T / kPage;                 // pages per tile
+  constexpr int SLOT_K = slot_bytes(BK, T), SLOT_V = slot_bytes(BV, T);
+  constexpr int CODE_K = slot_code_bytes(BK), CODE_V = slot_code_bytes(BV);
+  constexpr int AL = slot_alpha_len(T);
+
+  const int lane = threadIdx.x;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const int G = A.group;
+  const int L = A.seq_lens[seq];
+  const int ntiles = min((L + T - 1) / T, A.max_tiles);
+  const int tile_begin = part * A.tiles_per_part;
+  const int tile_end = min(ntiles, tile_begin + A.tiles_per_part);
+  if (tile_begin >= tile_end) return;
+  const int H = A.kv_heads;
+  const int32_t* pages = A.block_table + (size_t)seq * A.max_blocks;
+
+  // ------------------------------------------------ H q for this lane's head and channels
+  // lane (g = n16, grp) keeps (H q_g)[32 grp + i], i < 32, orthonormal.
+  float hq[32];
+  const bool real = n16 < G;
+  {
+    const uint16_t* qrow = A.q + ((size_t)seq * A.q_heads + kvh * G + (real ? n16 : 0)) * kHeadDim + 32 * grp;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      u32x4 w = real ? *reinterpret_cast<const u32x4*>(qrow + 8 * v) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hq[8 * v + 2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFF));
+        hq[8 * v + 2 * i + 1] = half_bits_to_float((uint16_t)(w[i] >> 16));
+      }
+    }
+#pragma unroll
+    for (int bit = 1; bit < 32; bit <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i & bit) continue;
+        const float lo = hq[i], hi = hq[i | bit];
+        hq[i] = lo + hi;
+        hq[i | bit] = lo - hi;
+      }
+    const float s16 = (grp & 1) ? -1.f : 1.f, s32 = (grp & 2) ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) hq[i] = __builtin_fmaf(hq[i], s16, lane_xor<16>(hq[i]));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) hq[i] = __builtin_fmaf(hq[i], s32, xor32(hq[i])) * kInvSqrtD;
+  }
+
+  const float c0 = A.sm_scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[8][4];  // [block i][r]: channel 32 grp + 8 r + i, head g = n16
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    const int32_t* tp = pages + tile * NP;
+    // -------------------------------------------- query fold: qt = (H q) * alpha_K
+    float qt[32];
+    {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int c = 32 * grp + 4 * v;
+        const uint8_t* slot = A.pool_k + ((size_t)tp[c / AL] * H + kvh) * SLOT_K;
+        const f32x4 al = *reinterpret_cast<const f32x4*>(slot + CODE_K + 8 * kPage + 4 * (c % AL));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qt[4 * v + e] = hq[4 * v + e] * al[e];
+      }
+    }
+    float qsum = 0.f, qmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) { qsum += qt[i]; qmax = fmaxf(qmax, fabsf(qt[i])); }
+    qsum = group_sum(qsum);
+    // a power-of-two scale keeps the fp16 split of qt in range
+    qmax = fmaxf(qmax, lane_xor<1>(qmax));
+    qmax = fmaxf(qmax, lane_xor<2>(qmax));
+    qmax = fmaxf(qmax, lane_xor<4>(qmax));
+    qmax = fmaxf(qmax, lane_xor<8>(qmax));
+    qmax = group_max(qmax);
+    int e = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;  // floor(log2 qmax)
+    e = min(max(e, -100), 100);
+    const float qscale = __uint_as_float((unsigned)(127 + 14 - e) << 23);   // 2^(14-e)
+    const float qunscale = __uint_as_float((unsigned)(127 - 14 + e) << 23); // 2^(e-14)
+    f16x8 bq_hi[4], bq_lo[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      unsigned hi[4], lo[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i0 = k_channel<BK>(ch, grp, 2 * m) - 32 * grp;
+        const int i1 = k_channel<BK>(ch, grp, 2 * m + 1) - 32 * grp;
+        split_pair(qt[i0] * qscale, qt[i1] * qscale, hi[m], lo[m]);
+      }
+      bq_hi[ch] = as_f16x8(hi[0], hi[1], hi[2], hi[3]);
+      bq_lo[ch] = as_f16x8(lo[0], lo[1], lo[2], lo[3]);
+    }
+
+    // -------------------------------------------- scores of the tile's pages
+    float s[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint8_t* slot = A.pool_k + ((size_t)tp[p] * H + kvh) * SLOT_K;
+      unsigned w[4];
+      if (BK == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(slot + 16 * lane);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(slot + 8 * lane);
+        w[0] = v[0]; w[1] = v[1]; w[2] = 0; w[3] = 0;
+      }
+      f32x4 d{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        f16x8 a;
+        if (BK == 4) {
+          a = as_f16x8(code_pair<4, 0>(w[ch]), code_pair<4, 1>(w[ch]), code_pair<4, 2>(w[ch]),
+                       code_pair<4, 3>(w[ch]));
+        } else {
+          const unsigned x = w[ch >> 1];
+          if (ch & 1)
+            a = as_f16x8(code_pair<2, 4>(x), code_pair<2, 5>(x), code_pair<2, 6>(x), code_pair<2, 7>(x));
+          else
+            a = as_f16x8(code_pair<2, 0>(x), code_pair<2, 1>(x), code_pair<2, 2>(x), code_pair<2, 3>(x));
+        }
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_hi[ch], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_lo[ch], d, 0, 0, 0);
+      }
+      const f32x4 S = *reinterpret_cast<const f32x4*>(slot + CODE_K + 16 * grp);
+      const f32x4 O = *reinterpret_cast<const f32x4*>(slot + CODE_K + 4 * kPage + 16 * grp);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // score = S (sum qt k) + O sum qt, with sum qt k = 64 (D - sum qt)
+        const float dk = d[r] * qunscale;
+        const float sc = c0 * __builtin_fmaf(64.f * S[r], dk - qsum, O[r] * qsum);
+        const int t = tile * T + p * kPage + 4 * grp + r;
+        s[p][r] = (t < L) ? sc : -INFINITY;
+      }
+    }
+
+    // -------------------------------------------- online softmax
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[p][r]);
+    tmax = group_max(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float corr = exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[p][r] = exp2f(s[p][r] - m_new);
+        psum += s[p][r];
+      }
+    l_run = l_run * corr + psum;
+
+    // -------------------------------------------- values of the tile's pages
+    float vacc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vacc[i][r] = 0.f;
+    float sp = 0.f, spo = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NP; pp += 2) {
+      unsigned bh[4], bl[4];
+      unsigned vw[2][4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint8_t* slot = A.pool_v + ((size_t)tp[pp + h2] * H + kvh) * SLOT_V;
+        const f32x4 S = *reinterpret_cast<const f32x4*>(slot + CODE_V + 16 * grp);
+        const f32x4 O = *reinterpret_cast<const f32x4*>(slot + CODE_V + 4 * kPage + 16 * grp);
+        float pw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pw[r] = s[pp + h2][r] * S[r];
+          sp += pw[r];
+          spo = __builtin_fmaf(s[pp + h2][r], O[r], spo);
+        }
+        split_pair(pw[0], pw[1], bh[2 * h2], bl[2 * h2]);
+        split_pair(pw[2], pw[3], bh[2 * h2 + 1], bl[2 * h2 + 1]);
+        if (BV == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(slot + 16 * lane);
+          vw[h2][0] = v[0]; vw[h2][1] = v[1]; vw[h2][2] = v[2]; vw[h2][3] = v[3];
+        } else {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(slot + 8 * lane);
+          vw[h2][0] = v[0]; vw[h2][1] = v[1]; vw[h2][2] = 0; vw[h2][3] = 0;
+        }
+      }
+      const f16x8 ph = as_f16x8(bh[0], bh[1], bh[2], bh[3]);
+      const f16x8 pl = as_f16x8(bl[0], bl[1], bl[2], bl[3]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        unsigned u[4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          if (BV == 4) {
+            const unsigned x = vw[h2][i >> 1];
+            if (i & 1) { u[2 * h2] = code_pair<4, 2>(x); u[2 * h2 + 1] = code_pair<4, 3>(x); }
+            else { u[2 * h2] = code_pair<4, 0>(x); u[2 * h2 + 1] = code_pair<4, 1>(x); }
+          } else {
+            const unsigned x = vw[h2][i >> 2];
+            switch (i & 3) {
+              case 0: u[2 * h2] = code_pair<2, 0>(x); u[2 * h2 + 1] = code_pair<2, 1>(x); break;
+              case 1: u[2 * h2] = code_pair<2, 2>(x); u[2 * h2 + 1] = code_pair<2, 3>(x); break;
+              case 2: u[2 * h2] = code_pair<2, 4>(x); u[2 * h2 + 1] = code_pair<2, 5>(x); break;
+              default: u[2 * h2] = code_pair<2, 6>(x); u[2 * h2 + 1] = code_pair<2, 7>(x); break;
+            }
+          }
+        }
+        const f16x8 a = as_f16x8(u[0], u[1], u[2], u[3]);
+        f32x4 d{vacc[i][0], vacc[i][1], vacc[i][2], vacc[i][3]};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pl, d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vacc[i][r] = d[r];
+      }
+    }
+    sp = group_sum(sp);
+    spo = group_sum(spo);
+
+    // -------------------------------------------- fold the tile: alpha_V (64 (D - sp) + spo)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 32 * grp + 8 * r;
+      const uint8_t* slot = A.pool_v + ((size_t)tp[c / AL] * H + kvh) * SLOT_V + CODE_V + 8 * kPage;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(slot + 4 * (c % AL));
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(slot + 4 * (c % AL) + 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float al = (i < 4) ? a0[i] : a1[i - 4];
+        const float val = __builtin_fmaf(64.f, vacc[i][r] - sp, spo);
+        acc[i][r] = __builtin_fmaf(acc[i][r], corr, al * val);
+      }
+    }
+  }
+
+  // ------------------------------------------------ partial results
+  l_run = group_sum(l_run);
+  if (!real) return;
+  const int hq_idx = kvh * G + n16;
+  const size_t pidx = ((size_t)seq * A.q_heads + hq_idx) * A.max_parts + part;
+  float* dst = A.ws_acc + pidx * kHeadDim + 32 * grp;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    *reinterpret_cast<f32x4*>(dst + 8 * r) = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+    *reinterpret_cast<f32x4*>(dst + 8 * r + 4) = f32x4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+  }
+  if (grp == 0) {
+    A.ws_ml[2 * pidx] = m_run;
+    A.ws_ml[2 * pidx + 1] = l_run;
+  }
+}
+
+// Merge the partitions of one (sequence, query head) and rotate back:
+// out = H (sum_p w_p acc_p) / (sum_p w_p l_p), w_p = 2^(m_p - max m).
+template <int T>
+__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
+  const int lane = threadIdx.x;
+  const int seq = blockIdx.x / A.q_heads;
+  const int L = A.seq_lens[seq];
+  const int ntiles = min((L + T - 1) / T, A.max_tiles);
+  const int nparts = (ntiles + A.tiles_per_part - 1) / A.tiles_per_part;
+  const size_t base = (size_t)blockIdx.x * A.max_parts;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, A.ws_ml[2 * (base + p)]);
+  float x0 = 0.f, x1 = 0.f, den = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = exp2f(A.ws_ml[2 * (base + p)] - M);
+    den = __builtin_fmaf(w, A.ws_ml[2 * (base + p) + 1], den);
+    const float* src = A.ws_acc + (base + p) * kHeadDim;
+    x0 = __builtin_fmaf(w, src[lane], x0);
+    x1 = __builtin_fmaf(w, src[lane + 64], x1);
+  }
+  const float inv = kInvSqrtD / den;
+  // channels lane (bit 6 = 0) and lane + 64 (bit 6 = 1)
+  float y0 = x0 + x1, y1 = x0 - x1;
+  auto stage = [&](float& v, auto xorer, int bit) {
+    const float sg = (lane & bit) ? -1.f : 1.f;
+    v = __builtin_fmaf(v, sg, xorer(v));
+  };
+  stage(y0, [](float v) { return lane_xor<1>(v); }, 1);
+  stage(y1, [](float v) { return lane_xor<1>(v); }, 1);
+  stage(y0, [](float v) { return lane_xor<2>(v); }, 2);
+  stage(y1, [](float v) { return lane_xor<2>(v); }, 2);
+  stage(y0, [](float v) { return lane_xor<4>(v); }, 4);
+  stage(y1, [](float v) { return lane_xor<4>(v); }, 4);
+  stage(y0, [](float v) { return lane_xor<8>(v); }, 8);
+  stage(y1, [](float v) { return lane_xor<8>(v); }, 8);
+  stage(y0, [](float v) { return lane_xor<16>(v); }, 16);
+  stage(y1, [](float v) { return lane_xor<16>(v); }, 16);
+  stage(y0, [](float v) { return xor32(v); }, 32);
+  stage(y1, [](float v) { return xor32(v); }, 32);
+  float* o = A.out + (size_t)blockIdx.x * kHeadDim;
+  o[lane] = y0 * inv;
+  o[lane + 64] = y1 * inv;
+}
+
+template <typename F>
+hipError_t by_tile(int tile, F&& f) {
+  switch (tile) {
+    case 32: return f(std::integral_constant<int, 32>{});
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+  }
+  return hipErrorInvalidValue;
+}
+template <typename F>
+hipError_t by_bits(int bits, F&& f) {
+  switch (bits) {
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_bits(bits_k, [&](auto BK) {
+      return by_bits(bits_v, [&](auto BV) {
+        dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV()>), grid, dim3(64), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((combine_kernel<T()>), dim3(a.num_seqs * a.q_heads), dim3(64), 0, s, a);
+        return hipGetLastError();
+      });
+    });
+  });
+}
+
+}  // namespace kvq

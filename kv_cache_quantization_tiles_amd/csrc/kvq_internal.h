@@ -1,0 +1,107 @@
+// Internal declarations shared by the HIP translation units of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+// A channel (token) whose spread is at most 1e-2 of its RMS keeps factor 1:
+// var > kGuard2 * meansq  <=>  std > 1e-2 * rms.
+constexpr float kGuard2 = 1e-4f;
+constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
+
+__host__ __device__ constexpr int slot_code_bytes(int bits) { return kPage * kHeadDim * bits / 8; }
+__host__ __device__ constexpr int slot_alpha_len(int tile) { return kPage * kHeadDim / tile; }
+__host__ __device__ constexpr int slot_bytes(int bits, int tile) {
+  return slot_code_bytes(bits) + 8 * kPage + 4 * slot_alpha_len(tile);
+}
+
+// Arguments of the tile-quantizer kernels (dense, paged prefill, append).
+struct QuantArgs {
+  // dense layout
+  const uint16_t* x;
+  uint8_t* codes;
+  float* alpha;
+  float* scale;
+  float* offset;
+  int n_tokens;
+  int heads;
+  // paged layouts: index 0 = K, 1 = V
+  const uint16_t* src[2];     // prefill rows [total][Hkv][D] or new rows [S][Hkv][D]
+  uint8_t* pool[2];
+  uint16_t* staging[2];       // [S][T][Hkv][D] or null
+  const int32_t* cu_seqlens;  // prefill
+  const int32_t* lens_before; // append
+  const int32_t* block_table;
+  int max_blocks;
+  int kv_heads;
+  int iters;
+};
+
+struct DequantArgs {
+  const uint8_t* codes;
+  const float* alpha;
+  const float* scale;
+  const float* offset;
+  int n_tokens;
+  int heads;
+  uint16_t* out;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;          // [S][Hq][D]
+  const int32_t* block_table; // [S][max_blocks]
+  const int32_t* seq_lens;    // [S]
+  const uint8_t* pool_k;
+  const uint8_t* pool_v;
+  float* out;                 // [S][Hq][D]
+  float* ws_acc;              // [S][Hq][P][D]
+  float* ws_ml;               // [S][Hq][P][2]
+  int num_seqs;
+  int q_heads;
+  int kv_heads;
+  int group;
+  int max_blocks;
+  int tiles_per_part;
+  int max_parts;
+  int max_tiles;               // ceil(max_seq_len / T): no tile past it is read
+  float sm_scale_log2;        // sm_scale * log2(e)
+};
+
+hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s);
+hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v,
+                                 int num_seqs, int max_seq_len, hipStream_t s);
+hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
+                         hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
+hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+
+// Value of lane (lane ^ M) for M in {1, 2, 4, 8, 16} (ds_swizzle bit mode,
+// within each group of 32 lanes).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16, "xor within 32 lanes");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  _Float16 f;
+  __builtin_memcpy(&f, &h, 2);
+  return (float)f;
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float x) {
+  _Float16 f = (_Float16)x;  // round to nearest even
+  uint16_t h;
+  __builtin_memcpy(&h, &f, 2);
+  return h;
+}
+
+}  // namespace kvq

@@ -1,0 +1,644 @@
+// Tile quantizer kernels for gfx950: Hadamard rotation along channels, then
+// Sinkhorn-like alternating channel/token variance normalization, then
+// per-token asymmetric round-to-nearest to packed 2- or 4-bit codes.
+//
+// Method: page "Huawei's KVarN boosts vLLM KV-cache capacity by 5x without
+// accuracy loss" (axbrief.com), section "기존 방식과 달라진 지점" (the
+// four-step tile quantizer); restore: page "화웨이가 공개한 KVarN" (ttj.kr),
+// section "양자화로 캐시를 다이어트시킨다".
+//
+// One workgroup quantizes one tile of T tokens x 128 channels with 2T
+// threads.  Thread (tq, cg) holds the 4 tokens 4tq..4tq+3 and the 16
+// channels 8cg+j and 64+8cg+j (j < 8) in registers for the whole kernel:
+//   * the fp16 rows are read once (two 16-byte loads per token, the 8 cg
+//     threads of a token covering its 256-byte row);
+//   * the Hadamard butterfly runs 4 stages in registers (channel bits 0,1,2,6)
+//     and 3 stages across the 8 cg lanes with ds_swizzle (channel bits 3,4,5);
+//     it is left unnormalized and the 1/sqrt(128) is folded into the factors;
+//   * the normalization never rewrites the tile: with weights b = 1/beta and
+//     a = 1/alpha, the channel step needs the spread over t of u = b_t R_tc
+//     and the token step that over c of u = a_c R_tc.  Each is one pass of
+//     d = u - ref (ref: the first token's, resp. channel 0's, value of u),
+//     sum d and sum d^2 (three VALU ops per element); the shift keeps
+//     E[d^2] - E[d]^2 accurate when a mean dwarfs the spread.  Partial sums
+//     go through LDS and one thread per channel (token) finalizes the
+//     variance, the guard and the reciprocal std;
+//   * the last token step is skipped: its factor cancels exactly in the
+//     stored scale, offset and codes (rounding is per token row);
+//   * codes: z = R * a, per-row min/max through LDS, v = (z - min) / step,
+//     round half to even, packed and stored straight into the output layout.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+enum Mode { kDense = 0, kPaged = 1, kAppend = 2 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void unpack8(u32x4 w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
+    out[2 * i + 1] = half_bits_to_float((uint16_t)(w[i] >> 16));
+  }
+}
+
+// Shared-memory footprint of one workgroup (floats).
+template <int T>
+struct Smem {
+  float red[2][T / 4][kHeadDim];  // channel partials; token partials alias it
+  float a[kHeadDim];              // 1/alpha in unnormalized units
+  float alpha[kHeadDim];          // channel factors (normalized units)
+  float b[T];                     // 1/beta
+  float ref_c[kHeadDim];          // R of the tile's first token (channel-step shift)
+  float ref_t[T];                 // R of channel 0 of each token (token-step shift)
+  float inv[T];                   // 1/step per row
+  float nmi[T];                   // -min/step per row
+};
+
+template <int T, int BITS, bool VLAYOUT, int MODE>
+__device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& sm, int role,
+                                                   int head, int seq, int tile_idx) {
+  constexpr int NT = 2 * T;
+  constexpr float LEVELS = (float)((1 << BITS) - 1);
+  const int tid = threadIdx.x;
+  const int cg = tid & 7;
+  const int tq = tid >> 3;
+
+  // ---------------------------------------------------------------- rows of this tile
+  const int t0 = tile_idx * T;
+  int n_valid;
+  const uint16_t* rows_base = nullptr;  // rows t < n_valid at rows_base + t * row_stride
+  size_t row_stride = 0;
+  int r_new = -1;                       // append: the row taken from the new token
+  const int H = (MODE == kDense) ? A.heads : A.kv_heads;
+  if (MODE == kDense) {
+    n_valid = min(T, A.n_tokens - t0);
+    rows_base = A.x + ((size_t)t0 * H + head) * kHeadDim;
+    row_stride = (size_t)H * kHeadDim;
+  } else if (MODE == kPaged) {
+    const int a0 = A.cu_seqlens[seq];
+    const int len = A.cu_seqlens[seq + 1] - a0;
+    n_valid = min(T, len - t0);
+    rows_base = A.src[role] + ((size_t)(a0 + t0) * H + head) * kHeadDim;
+    row_stride = (size_t)H * kHeadDim;
+  } else {
+    const int pos = A.lens_before[seq];
+    r_new = pos % T;
+    n_valid = r_new + 1;
+    rows_base = A.staging[role] + ((size_t)seq * T * H + head) * kHeadDim;
+    row_stride = (size_t)H * kHeadDim;
+  }
+
+  // ---------------------------------------------------------------- load fp16 rows
+  u32x4 raw[4][2];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 4 * tq + r;
+    if (t < n_valid) {
+      const uint16_t* row = rows_base + (size_t)t * row_stride;
+      if (MODE == kAppend && t == r_new)
+        row = A.src[role] + ((size_t)seq * H + head) * kHeadDim;
+      raw[r][0] = *reinterpret_cast<const u32x4*>(row + 8 * cg);
+      raw[r][1] = *reinterpret_cast<const u32x4*>(row + 64 + 8 * cg);
+    } else {
+      raw[r][0] = u32x4{0, 0, 0, 0};
+      raw[r][1] = u32x4{0, 0, 0, 0};
+    }
+  }
+  // Keep the fp16 rows of a partial tile for later appends.
+  if (MODE != kDense && A.staging[role] != nullptr) {
+    uint16_t* stg = A.staging[role] + ((size_t)seq * T * H + head) * kHeadDim;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tq + r;
+      const bool write = (MODE == kPaged) ? (n_valid < T && t < n_valid) : (t == r_new);
+      if (write) {
+        *reinterpret_cast<u32x4*>(stg + (size_t)t * row_stride + 8 * cg) = raw[r][0];
+        *reinterpret_cast<u32x4*>(stg + (size_t)t * row_stride + 64 + 8 * cg) = raw[r][1];
+      }
+    }
+  }
+
+  float R[4][16];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    unpack8(raw[r][0], &R[r][0]);
+    unpack8(raw[r][1], &R[r][8]);
+  }
+
+  // ---------------------------------------------------------------- Hadamard (unnormalized)
+  // register index k = 8*half + j  <->  channel 64*half + 8*cg + j
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int bit = 1; bit < 16; bit <<= 1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k & bit) continue;
+        const float lo = R[r][k], hi = R[r][k | bit];
+        R[r][k] = lo + hi;
+        R[r][k | bit] = lo - hi;
+      }
+    }
+  }
+  {
+    const float s1 = (cg & 1) ? -1.f : 1.f;
+    const float s2 = (cg & 2) ? -1.f : 1.f;
+    const float s4 = (cg & 4) ? -1.f : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], s1, lane_xor<1>(R[r][k]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], s2, lane_xor<2>(R[r][k]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], s4, lane_xor<4>(R[r][k]));
+  }
+
+  // ---------------------------------------------------------------- normalization
+  // Sums are taken over values shifted by a reference (channel step: the
+  // tile's first token; token step: the token's channel 0), so that
+  // E[d^2] - E[d]^2 does not cancel when a mean dwarfs the spread.
+  if (tq == 0) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm.ref_c[64 * half + 8 * cg + j] = R[0][8 * half + j];
+  }
+  if (cg == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.ref_t[4 * tq + r] = R[r][0];
+  }
+  for (int c = tid; c < kHeadDim; c += NT) {
+    sm.a[c] = kInvSqrtD;
+    sm.alpha[c] = 1.0f;
+  }
+  if (tid < T) sm.b[tid] = 1.0f;
+  __syncthreads();
+  float a[16], b[4], refc[16], reft[4];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int c0 = 64 * half + 8 * cg;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.ref_c[c0]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.ref_c[c0 + 4]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { refc[8 * half + i] = lo[i]; refc[8 * half + 4 + i] = hi[i]; }
+  }
+  {
+    const f32x4 rt = *reinterpret_cast<const f32x4*>(&sm.ref_t[4 * tq]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) reft[r] = rt[r];
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a[k] = kInvSqrtD;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) b[r] = 1.0f;
+  const float inv_n = 1.0f / (float)n_valid;
+  const int iters = A.iters;
+  float b0 = 1.0f;
+
+  for (int it = 0; it < iters; ++it) {
+    // channel step: spread over the tile's valid tokens of u = b_t R_tc
+    {
+      float s1[16], s2[16], kc[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) { s1[k] = 0.f; s2[k] = 0.f; kc[k] = b0 * refc[k]; }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * tq + r < n_valid) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const float d = __builtin_fmaf(b[r], R[r][k], -kc[k]);
+            s1[k] += d;
+            s2[k] = __builtin_fmaf(d, d, s2[k]);
+          }
+        }
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int c0 = 64 * half + 8 * cg;
+        *reinterpret_cast<f32x4*>(&sm.red[0][tq][c0]) =
+            f32x4{s1[8 * half], s1[8 * half + 1], s1[8 * half + 2], s1[8 * half + 3]};
+        *reinterpret_cast<f32x4*>(&sm.red[0][tq][c0 + 4]) =
+            f32x4{s1[8 * half + 4], s1[8 * half + 5], s1[8 * half + 6], s1[8 * half + 7]};
+        *reinterpret_cast<f32x4*>(&sm.red[1][tq][c0]) =
+            f32x4{s2[8 * half], s2[8 * half + 1], s2[8 * half + 2], s2[8 * half + 3]};
+        *reinterpret_cast<f32x4*>(&sm.red[1][tq][c0 + 4]) =
+            f32x4{s2[8 * half + 4], s2[8 * half + 5], s2[8 * half + 6], s2[8 * half + 7]};
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < kHeadDim; c += NT) {
+      float S1 = 0.f, S2 = 0.f;
+#pragma unroll
+      for (int g = 0; g < T / 4; ++g) {
+        S1 += sm.red[0][g][c];
+        S2 += sm.red[1][g][c];
+      }
+      const float m = S1 * inv_n;                         // mean of the shifted values
+      const float var = fmaxf(__builtin_fmaf(-m, m, S2 * inv_n), 0.f);
+      const float mu = __builtin_fmaf(b0, sm.ref_c[c], m);  // mean of u
+      const float ms = __builtin_fmaf(mu, mu, var);           // mean square of u
+      if (var > kGuard2 * ms) {
+        sm.a[c] = __builtin_amdgcn_rsqf(var);
+        sm.alpha[c] = __builtin_sqrtf(var * (1.0f / kHeadDim));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c0 = 64 * half + 8 * cg;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.a[c0]);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.a[c0 + 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[8 * half + i] = lo[i]; a[8 * half + 4 + i] = hi[i]; }
+    }
+    if (it + 1 == iters) break;  // the final token step cancels in every stored value
+
+    // token step: spread over the 128 channels of u = a_c R_tc
+    const float a0 = sm.a[0];
+    {
+      float t1[4], t2[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float kt = a0 * reft[r];
+        float x1 = 0.f, x2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float d = __builtin_fmaf(a[k], R[r][k], -kt);
+          x1 += d;
+          x2 = __builtin_fmaf(d, d, x2);
+        }
+        t1[r] = x1;
+        t2[r] = x2;
+      }
+      float* tr = &sm.red[0][0][0];  // [2][8][T] view
+      *reinterpret_cast<f32x4*>(&tr[(0 * 8 + cg) * T + 4 * tq]) = f32x4{t1[0], t1[1], t1[2], t1[3]};
+      *reinterpret_cast<f32x4*>(&tr[(1 * 8 + cg) * T + 4 * tq]) = f32x4{t2[0], t2[1], t2[2], t2[3]};
+    }
+    __syncthreads();
+    if (tid < T) {
+      const float* tr = &sm.red[0][0][0];
+      float T1 = 0.f, T2 = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        T1 += tr[(0 * 8 + g) * T + tid];
+        T2 += tr[(1 * 8 + g) * T + tid];
+      }
+      const float m = T1 * (1.0f / kHeadDim);
+      const float var = fmaxf(__builtin_fmaf(-m, m, T2 * (1.0f / kHeadDim)), 0.f);
+      const float mu = __builtin_fmaf(a0, sm.ref_t[tid], m);
+      const float ms = __builtin_fmaf(mu, mu, var);
+      if (var > kGuard2 * ms) sm.b[tid] = __builtin_amdgcn_rsqf(var);
+    }
+    __syncthreads();
+    {
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(&sm.b[4 * tq]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[r] = bb[r];
+      b0 = sm.b[0];
+    }
+  }
+
+  // ---------------------------------------------------------------- rounding
+  float zmin[4], zmax[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float mn = 3.4e38f, mx = -3.4e38f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      R[r][k] *= a[k];
+      mn = fminf(mn, R[r][k]);
+      mx = fmaxf(mx, R[r][k]);
+    }
+    zmin[r] = mn;
+    zmax[r] = mx;
+  }
+  {
+    float* tr = &sm.red[0][0][0];
+    *reinterpret_cast<f32x4*>(&tr[(0 * 8 + cg) * T + 4 * tq]) = f32x4{zmin[0], zmin[1], zmin[2], zmin[3]};
+    *reinterpret_cast<f32x4*>(&tr[(1 * 8 + cg) * T + 4 * tq]) = f32x4{zmax[0], zmax[1], zmax[2], zmax[3]};
+  }
+  __syncthreads();
+
+  // Output addressing (paged): the tile's pages.
+  uint8_t* pool = nullptr;
+  const int32_t* pages = nullptr;
+  constexpr int SLOT = slot_bytes(BITS, T);
+  constexpr int CODE_BYTES = slot_code_bytes(BITS);
+  if (MODE != kDense) {
+    pool = A.pool[role];
+    pages = A.block_table + (size_t)seq * A.max_blocks + (t0 / kPage);
+  }
+  auto slot_ptr = [&](int page_in_tile) -> uint8_t* {
+    const int page = pages[page_in_tile];
+    return pool + ((size_t)page * H + head) * SLOT;
+  };
+
+  if (tid < T) {
+    const float* tr = &sm.red[0][0][0];
+    float mn = tr[(0 * 8) * T + tid], mx = tr[(1 * 8) * T + tid];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) {
+      mn = fminf(mn, tr[(0 * 8 + g) * T + tid]);
+      mx = fmaxf(mx, tr[(1 * 8 + g) * T + tid]);
+    }
+    float step = 0.f, off = 0.f, inv = 0.f, nmi = 0.f;
+    if (tid < n_valid) {
+      const float range = mx - mn;
+      step = range * (1.0f / LEVELS);
+      off = mn;
+      if (range > 0.f) {
+        inv = LEVELS * __builtin_amdgcn_rcpf(range);
+        nmi = -mn * inv;
+      }
+    }
+    sm.inv[tid] = inv;
+    sm.nmi[tid] = nmi;
+    if (MODE == kDense) {
+      if (tid < n_valid) {
+        A.scale[(size_t)(t0 + tid) * H + head] = step;
+        A.offset[(size_t)(t0 + tid) * H + head] = off;
+      }
+    } else {
+      uint8_t* slot = slot_ptr(tid / kPage);
+      reinterpret_cast<float*>(slot + CODE_BYTES)[tid % kPage] = step;
+      reinterpret_cast<float*>(slot + CODE_BYTES + 4 * kPage)[tid % kPage] = off;
+    }
+  }
+  for (int c = tid; c < kHeadDim; c += NT) {
+    const float al = sm.alpha[c];
+    if (MODE == kDense) {
+      A.alpha[((size_t)tile_idx * H + head) * kHeadDim + c] = al;
+    } else {
+      constexpr int AL = slot_alpha_len(T);
+      uint8_t* slot = slot_ptr(c / AL);
+      reinterpret_cast<float*>(slot + CODE_BYTES + 8 * kPage)[c % AL] = al;
+    }
+  }
+  __syncthreads();
+
+  // codes, packed
+  unsigned code[4][16];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float inv = sm.inv[4 * tq + r], nmi = sm.nmi[4 * tq + r];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float v = __builtin_fmaf(R[r][k], inv, nmi);
+      // adding 1.5*2^23 rounds to the nearest integer (ties to even) and leaves
+      // it in the low mantissa bits; 0 <= v <= LEVELS up to rounding.
+      code[r][k] = __float_as_uint(v + 12582912.0f) & ((1u << BITS) - 1u);
+    }
+  }
+
+  if (MODE == kDense) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tq + r;
+      if (t >= n_valid) continue;
+      uint8_t* row = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        unsigned w = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w |= code[r][8 * half + j] << (BITS * j);
+        if (BITS == 4) *reinterpret_cast<uint32_t*>(row + BITS * (8 * half + cg)) = w;
+        else *reinterpret_cast<uint16_t*>(row + BITS * (8 * half + cg)) = (uint16_t)w;
+      }
+    }
+  } else if (!VLAYOUT) {
+    // K slot: 4 blocks of 32 channels, token after token, natural packing.
+    constexpr int CB = 4 * BITS;  // bytes per token per block
+    uint8_t* slot = slot_ptr((4 * tq) / kPage);
+    const int tp0 = (4 * tq) % kPage;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        unsigned w = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w |= code[r][8 * half + j] << (BITS * j);
+        const int blk = 2 * half + (cg >> 2);
+        uint8_t* dst = slot + blk * (kPage * CB) + (tp0 + r) * CB + BITS * (cg & 3);
+        if (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = w;
+        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+      }
+    }
+  } else {
+    // V slot: quads of 4 tokens, groups of 8 channels, fields 2j + (r>>1) + (F/2)(r&1).
+    uint8_t* slot = slot_ptr((4 * tq) / kPage);
+    const int quad = tq % (kPage / 4);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int grp = 8 * half + cg;
+      uint8_t* dst = slot + quad * (16 * BITS * 4) + grp * (4 * BITS);
+      if (BITS == 4) {
+        u32x4 words;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          unsigned x = 0;
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x |= code[r][8 * half + 2 * w + p] << (4 * (2 * p + (r >> 1) + 4 * (r & 1)));
+          words[w] = x;
+        }
+        *reinterpret_cast<u32x4*>(dst) = words;
+      } else {
+        u32x2 words;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          unsigned x = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x |= code[r][8 * half + 4 * w + j] << (2 * (2 * j + (r >> 1) + 8 * (r & 1)));
+          words[w] = x;
+        }
+        *reinterpret_cast<u32x2*>(dst) = words;
+      }
+    }
+  }
+}
+
+template <int T, int BITS>
+__global__ __launch_bounds__(2 * T) void quantize_dense_kernel(QuantArgs A) {
+  __shared__ Smem<T> sm;
+  quantize_tile_body<T, BITS, false, kDense>(A, sm, 0, blockIdx.y, 0, blockIdx.x);
+}
+
+// grid: x = tile index in the sequence, y = head + Hkv * role (0 K, 1 V), z = sequence
+template <int T, int BK, int BV>
+__global__ __launch_bounds__(2 * T) void quantize_paged_kernel(QuantArgs A) {
+  __shared__ Smem<T> sm;
+  const int seq = blockIdx.z;
+  const int len = A.cu_seqlens[seq + 1] - A.cu_seqlens[seq];
+  if ((int)blockIdx.x * T >= len) return;
+  const int role = blockIdx.y / A.kv_heads;
+  const int head = blockIdx.y % A.kv_heads;
+  if (role == 0) quantize_tile_body<T, BK, false, kPaged>(A, sm, 0, head, seq, blockIdx.x);
+  else quantize_tile_body<T, BV, true, kPaged>(A, sm, 1, head, seq, blockIdx.x);
+}
+
+// grid: x = head, y = role, z = sequence
+template <int T, int BK, int BV>
+__global__ __launch_bounds__(2 * T) void append_kernel(QuantArgs A) {
+  __shared__ Smem<T> sm;
+  const int seq = blockIdx.z;
+  const int tile_idx = A.lens_before[seq] / T;
+  if ((tile_idx + 1) * (T / kPage) > A.max_blocks) return;  // no page for this tile
+  if (blockIdx.y == 0) quantize_tile_body<T, BK, false, kAppend>(A, sm, 0, blockIdx.x, seq, tile_idx);
+  else quantize_tile_body<T, BV, true, kAppend>(A, sm, 1, blockIdx.x, seq, tile_idx);
+}
+
+// ---------------------------------------------------------------- dequantize (dense)
+// 128 threads = 16 rows (token, head) x 8 channel groups; same register
+// layout and butterfly as the quantizer.
+template <int T, int BITS>
+__global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
+  const int tid = threadIdx.x;
+  const int cg = tid & 7;
+  const long row = (long)blockIdx.x * 16 + (tid >> 3);
+  const long nrows = (long)A.n_tokens * A.heads;
+  const bool valid = row < nrows;
+  const long rr = valid ? row : 0;
+  const int t = (int)(rr / A.heads), h = (int)(rr % A.heads);
+  const uint8_t* crow = A.codes + rr * (kHeadDim * BITS / 8);
+  const float* al = A.alpha + ((size_t)(t / T) * A.heads + h) * kHeadDim;
+  const float S = A.scale[rr], O = A.offset[rr];
+  float x[16];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    unsigned w = (BITS == 4) ? *reinterpret_cast<const uint32_t*>(crow + BITS * (8 * half + cg))
+                             : *reinterpret_cast<const uint16_t*>(crow + BITS * (8 * half + cg));
+    const int c0 = 64 * half + 8 * cg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float q = (float)((w >> (BITS * j)) & ((1u << BITS) - 1u));
+      x[8 * half + j] = al[c0 + j] * __builtin_fmaf(S, q, O);
+    }
+  }
+#pragma unroll
+  for (int bit = 1; bit < 16; bit <<= 1)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k & bit) continue;
+      const float lo = x[k], hi = x[k | bit];
+      x[k] = lo + hi;
+      x[k | bit] = lo - hi;
+    }
+  const float s1 = (cg & 1) ? -1.f : 1.f, s2 = (cg & 2) ? -1.f : 1.f, s4 = (cg & 4) ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s1, lane_xor<1>(x[k]));
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s2, lane_xor<2>(x[k]));
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s4, lane_xor<4>(x[k]));
+  if (!valid) return;
+  uint16_t* orow = A.out + rr * kHeadDim;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (unsigned)float_to_half_bits(x[8 * half + 2 * i] * kInvSqrtD) |
+             ((unsigned)float_to_half_bits(x[8 * half + 2 * i + 1] * kInvSqrtD) << 16);
+    *reinterpret_cast<u32x4*>(orow + 64 * half + 8 * cg) = w;
+  }
+}
+
+// ---------------------------------------------------------------- bandwidth probe
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, size_t n) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (; i < n; i += stride) dst[i] = __builtin_nontemporal_load(&src[i]);
+}
+
+template <typename F>
+hipError_t by_tile(int tile, F&& f) {
+  switch (tile) {
+    case 32: return f(std::integral_constant<int, 32>{});
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename F>
+hipError_t by_bits(int bits, F&& f) {
+  switch (bits) {
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_bits(bits, [&](auto B) {
+      dim3 grid((a.n_tokens + T() - 1) / T(), a.heads);
+      hipLaunchKernelGGL((quantize_dense_kernel<T(), B()>), grid, dim3(2 * T()), 0, s, a);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v,
+                                 int num_seqs, int max_seq_len, hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_bits(bits_k, [&](auto BK) {
+      return by_bits(bits_v, [&](auto BV) {
+        dim3 grid((max_seq_len + T() - 1) / T(), 2 * a.kv_heads, num_seqs);
+        hipLaunchKernelGGL((quantize_paged_kernel<T(), BK(), BV()>), grid, dim3(2 * T()), 0, s, a);
+        return hipGetLastError();
+      });
+    });
+  });
+}
+
+hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
+                         hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_bits(bits_k, [&](auto BK) {
+      return by_bits(bits_v, [&](auto BV) {
+        dim3 grid(a.kv_heads, 2, num_seqs);
+        hipLaunchKernelGGL((append_kernel<T(), BK(), BV()>), grid, dim3(2 * T()), 0, s, a);
+        return hipGetLastError();
+      });
+    });
+  });
+}
+
+hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_bits(bits, [&](auto B) {
+      const long rows = (long)a.n_tokens * a.heads;
+      dim3 grid((unsigned)((rows + 15) / 16));
+      hipLaunchKernelGGL((dequantize_kernel<T(), B()>), grid, dim3(128), 0, s, a);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  hipLaunchKernelGGL(copy_kernel, dim3(256 * 16), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

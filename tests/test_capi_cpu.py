@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every function its header declares, and
+rejects bad arguments on the host before touching a GPU (no kernel runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as orc
+from kv_cache_quantization_tiles_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libkvq.so is not built: run __graft_entry__.build()")
+    return L.load()
+
+
+def test_exports_every_declared_function(lib):
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    assert set(declared) == set(L.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_slot_sizes_match_oracle_layout(lib):
+    assert "gfx950" in L.kvq_version()
+    for tile in (32, 64, 128):
+        for bk in (2, 4):
+            for bv in (2, 4):
+                cfg = L.config(tile, bk, bv, 3)
+                assert L.kvq_slot_bytes(cfg, False) == orc.slot_bytes(bk, tile)
+                assert L.kvq_slot_bytes(cfg, True) == orc.slot_bytes(bv, tile)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, L.KVQ_ERR_UNSUPPORTED), ("page_tokens", 32, L.KVQ_ERR_UNSUPPORTED),
+    ("tile_tokens", 48, L.KVQ_ERR_UNSUPPORTED), ("bits_k", 3, L.KVQ_ERR_UNSUPPORTED),
+    ("bits_v", 8, L.KVQ_ERR_UNSUPPORTED), ("sinkhorn_iters", -1, L.KVQ_ERR_UNSUPPORTED),
+    ("sinkhorn_iters", 17, L.KVQ_ERR_UNSUPPORTED)])
+def test_bad_config_rejected(lib, field, value, status):
+    cfg = L.config(64, 4, 4, 3)
+    setattr(cfg, field, value)
+    st = lib.kvq_quantize_to_pages(ctypes.byref(cfg), 16, 16, 16, 1, 64, 1, 16, 4, 16, 16, None, None, None)
+    assert st == status
+    assert L.kvq_last_error()
+    assert L.kvq_slot_bytes(cfg, False) == 0
+
+
+def test_null_and_size_errors(lib):
+    cfg = ctypes.byref(L.config(64, 4, 4, 3))
+    assert lib.kvq_quantize_tiles(None, 16, 1, 1, 4, 16, 16, 16, 16, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_quantize_tiles(cfg, None, 1, 1, 4, 16, 16, 16, 16, None) == L.KVQ_ERR_ARG
+    assert "x is NULL" in L.kvq_last_error()
+    assert lib.kvq_quantize_tiles(cfg, 16, 0, 1, 4, 16, 16, 16, 16, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_quantize_tiles(cfg, 16, 8, 1, 3, 16, 16, 16, 16, None) == L.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_dequantize(cfg, 16, 16, 16, None, 8, 1, 4, 16, None) == L.KVQ_ERR_ARG
+    # staging must be both or neither
+    assert lib.kvq_quantize_to_pages(cfg, 16, 16, 16, 1, 64, 1, 16, 4, 16, 16, 16, None, None) == L.KVQ_ERR_ARG
+    # block table too narrow for whole tiles of max_seq_len
+    assert lib.kvq_quantize_to_pages(cfg, 16, 16, 16, 1, 65, 1, 16, 4, 16, 16, None, None, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_append_and_requant(cfg, 16, 16, 16, 1, 1, None, 16, 16, 4, 16, 16, None) == L.KVQ_ERR_ARG
+
+
+def test_decode_validation(lib):
+    cfg = L.config(64, 4, 4, 3)
+    need = L.kvq_decode_workspace_bytes(cfg, 4, 32, 8, 16385)
+    assert need > 0 and need % (130 * 4) == 0
+    c = ctypes.byref(cfg)
+    # q_heads not a multiple of kv_heads
+    assert lib.kvq_paged_decode_attn(c, 16, 4, 30, 8, 16, 1028, 16, 16385, 16, 16, 0.1, 16, 16, need,
+                                     None) == L.KVQ_ERR_ARG
+    # group larger than 16
+    assert lib.kvq_paged_decode_attn(c, 16, 4, 64, 2, 16, 1028, 16, 16385, 16, 16, 0.1, 16, 16, 1 << 30,
+                                     None) == L.KVQ_ERR_UNSUPPORTED
+    # workspace too small
+    assert lib.kvq_paged_decode_attn(c, 16, 4, 32, 8, 16, 1028, 16, 16385, 16, 16, 0.1, 16, 16, need - 1,
+                                     None) == L.KVQ_ERR_WORKSPACE
+    assert "needed" in L.kvq_last_error()
+    assert lib.kvq_bandwidth_probe(16, 16, 15, None) == L.KVQ_ERR_ARG

@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle, on the
+same seeded inputs.  Rules in tests/parity_util.py."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from kv_cache_quantization_tiles_amd import api, inputs
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api._lib.load()
+
+
+def _report(what, counts):
+    n, win, mism = counts
+    print(f"[codes] {what}: {n} elements, {win} in window ({100.0 * win / max(n, 1):.3f}%), "
+          f"{mism} mismatches", flush=True)
+
+
+def _x(n, heads, recipe=2, role="K", seed=0):
+    base = inputs.workload(recipe)
+    wl = dataclasses.replace(base, seq_lens=(n,), hkv=heads, hq=heads * base.group,
+                             index=base.index * 100 + seed)
+    return inputs.gen_kv(wl, role)
+
+
+DENSE_CASES = [
+    # (tile, bits, iters, n_tokens, heads, recipe)
+    (64, 4, 3, 1024, 1, 1),     # the single-head 1K correctness workload (K)
+    (64, 4, 3, 1000, 2, 2),     # ragged tail, 2 heads, 2% outliers x10-50
+    (32, 2, 5, 77, 3, 5),       # heavy-tailed K, 5 iterations
+    (128, 4, 0, 300, 1, 2),     # no normalization
+    (128, 2, 1, 129, 1, 2),     # one-row last tile
+    (64, 4, 3, 1, 1, 2),        # a single token
+    (32, 4, 3, 33, 2, 1),
+]
+
+
+@pytest.mark.parametrize("tile,bits,iters,n,heads,recipe", DENSE_CASES)
+def test_dense_quantize_and_dequantize(tile, bits, iters, n, heads, recipe):
+    x = _x(n, heads, recipe)
+    cfg = api.config(tile, bits, bits, iters)
+    q = api.quantize_tiles(torch.from_numpy(x).cuda(), cfg, bits)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in q.items()}
+    ref = orc.quantize_dense(x, tile, bits, iters)
+    codes = orc.unpack_natural(got["codes"], bits)
+    _report(f"dense T{tile} b{bits} it{iters} n{n} h{heads}",
+            pu.compare_codes(codes, ref["codes_raw"], ref["pre"], "dense"))
+    pu.assert_rel(got["alpha"], ref["alpha"], pu.META_RTOL, "alpha")
+    pu.assert_rel(got["scale"], ref["scale"], pu.META_RTOL, "scale")
+    pu.assert_rel(got["offset"], ref["offset"], pu.META_RTOL, "offset")
+    # restore: GPU dequantize of the GPU codes vs the oracle restoring the same codes
+    deq = api.dequantize(q, cfg, bits).cpu().numpy().astype(np.float64)
+    ref_deq = orc.dequantize_dense(got["codes"], got["alpha"], got["scale"], got["offset"], tile, bits)
+    pu.assert_dequant(deq, ref_deq, "dequantize")
+    # and the round trip stays within the rounding bound of the method
+    err = np.linalg.norm(deq - x.astype(np.float64), axis=-1)
+    bound = got["scale"] / 2 * np.linalg.norm(got["alpha"], axis=-1)[np.arange(n) // tile]
+    assert np.all(err <= bound * 1.01 + 2e-3 * np.linalg.norm(x.astype(np.float64), axis=-1))
+
+
+def test_dense_quantize_is_deterministic():
+    x = torch.from_numpy(_x(4096, 4, 2)).cuda()
+    cfg = api.config(64, 4, 4, 3)
+    a = api.quantize_tiles(x, cfg, 4)
+    b = api.quantize_tiles(x, cfg, 4)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def _paged_workload(recipe, lens, hkv, hq, tile, bits_k, bits_v, iters, decode_steps=4):
+    base = inputs.workload(recipe)
+    return dataclasses.replace(base, seq_lens=tuple(lens), hkv=hkv, hq=hq, tile_tokens=tile,
+                               bits_k=bits_k, bits_v=bits_v, iters=iters, decode_steps=decode_steps)
+
+
+PAGED_CASES = [
+    # (recipe, lens, hkv, hq, tile, bits_k, bits_v, iters)
+    (1, (1024,), 1, 8, 64, 4, 4, 3),
+    (2, (200, 131, 64, 17), 2, 8, 64, 4, 4, 3),
+    (5, (300, 97, 33), 2, 16, 32, 4, 2, 5),
+    (2, (260, 128), 1, 4, 128, 2, 2, 3),
+]
+
+
+def _gpu_prefill(wl, shuffled=True):
+    k = inputs.gen_kv(wl, "K")
+    v = inputs.gen_kv(wl, "V")
+    table, npages = (inputs.block_table if shuffled else inputs.identity_block_table)(wl)
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+    cu = torch.from_numpy(wl.cu_seqlens()).cuda()
+    cache.quantize_prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), cu, max(wl.seq_lens))
+    torch.cuda.synchronize()
+    return k, v, table, npages, cache
+
+
+def _compare_pools(wl, table, lens, gpu_pk, gpu_pv, ref_pk, ref_pv, pre, what):
+    tot = [0, 0, 0]
+    for s in range(wl.num_seqs):
+        for h in range(wl.hkv):
+            for role, bits, gp, rp in (("K", wl.bits_k, gpu_pk, ref_pk), ("V", wl.bits_v, gpu_pv, ref_pv)):
+                _, gc, ga, gs, go = orc.read_sequence(gp, table[s], int(lens[s]), h, role, bits, wl.tile_tokens)
+                _, rc, ra, rs, ro = orc.read_sequence(rp, table[s], int(lens[s]), h, role, bits, wl.tile_tokens)
+                c = pu.compare_codes(gc, rc, pre[(s, h, role)], f"{what} s{s} h{h} {role}")
+                tot = [a + b for a, b in zip(tot, c)]
+                t = wl.tile_tokens
+                for j in range(ga.shape[0]):
+                    sl = slice(j * t, min(int(lens[s]), (j + 1) * t))
+                    pu.check_tile_metadata(rc[sl], ga[j], gs[sl], go[sl], ra[j], rs[sl], ro[sl],
+                                           orc.dequantize_tile, f"{what} s{s} h{h} {role} tile{j}")
+    _report(what, tot)
+    # every byte past the sequences' ends inside their last tiles is zero-filled as the
+    # layout says, so whole slots agree apart from codes in the window
+    return tot
+
+
+@pytest.mark.parametrize("case", PAGED_CASES)
+def test_paged_prefill_parity(case):
+    recipe, lens, hkv, hq, tile, bk, bv, iters = case
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    ref_pk = orc.new_pool(npages, hkv, bk, tile)
+    ref_pv = orc.new_pool(npages, hkv, bv, tile)
+    stg_k = np.zeros((wl.num_seqs, tile, hkv, 128), np.float16)
+    stg_v = np.zeros_like(stg_k)
+    pre = orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, tile, bk, bv, iters, ref_pk, ref_pv, stg_k, stg_v)
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    _compare_pools(wl, table, wl.seq_lens, gpk, gpv, ref_pk, ref_pv, pre, f"prefill {case}")
+    # staging holds the fp16 tail rows of partial tiles
+    gsk, gsv = cache.staging_k.cpu().numpy(), cache.staging_v.cpu().numpy()
+    for s, n in enumerate(wl.seq_lens):
+        tail = n % tile
+        np.testing.assert_array_equal(gsk[s, :tail], stg_k[s, :tail])
+        np.testing.assert_array_equal(gsv[s, :tail], stg_v[s, :tail])
+
+
+@pytest.mark.parametrize("case", [PAGED_CASES[1], PAGED_CASES[2], PAGED_CASES[3]])
+def test_append_and_requant_parity(case):
+    recipe, lens, hkv, hq, tile, bk, bv, iters = case
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters, decode_steps=tile + 3)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    ref_pk = orc.new_pool(npages, hkv, bk, tile)
+    ref_pv = orc.new_pool(npages, hkv, bv, tile)
+    stg_k = np.zeros((wl.num_seqs, tile, hkv, 128), np.float16)
+    stg_v = np.zeros_like(stg_k)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, tile, bk, bv, iters, ref_pk, ref_pv, stg_k, stg_v)
+    lens_now = np.array(wl.seq_lens, np.int32)
+    prefill_k, prefill_v = cache.pool_k.clone(), cache.pool_v.clone()
+    steps = [0, 1, 2, tile - 1, tile, tile + 2]   # crosses a tile boundary for every sequence
+    for step in range(max(steps) + 1):
+        kn = inputs.gen_decode_kv(wl, "K", step)
+        vn = inputs.gen_decode_kv(wl, "V", step)
+        cache.append(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens_now).cuda())
+        pre = orc.append_and_requant(kn, vn, lens_now, table, tile, bk, bv, iters, ref_pk, ref_pv, stg_k, stg_v)
+        lens_now = lens_now + 1
+        if step not in steps:
+            continue
+        torch.cuda.synchronize()
+        gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+        for s in range(wl.num_seqs):
+            n = int(lens_now[s])
+            t0 = ((n - 1) // tile) * tile          # first row of the re-quantized tile
+            for h in range(hkv):
+                for role, bits, gp, rp in (("K", bk, gpk, ref_pk), ("V", bv, gpv, ref_pv)):
+                    _, gc, ga, gs, go = orc.read_sequence(gp, table[s], n, h, role, bits, tile)
+                    _, rc, ra, rs, ro = orc.read_sequence(rp, table[s], n, h, role, bits, tile)
+                    pu.compare_codes(gc[t0:], rc[t0:], pre[(s, h, role)], f"append step{step} s{s} h{h} {role}")
+                    j = t0 // tile
+                    pu.check_tile_metadata(rc[t0:], ga[j], gs[t0:], go[t0:], ra[j], rs[t0:], ro[t0:],
+                                           orc.dequantize_tile, f"append step{step} s{s} h{h} {role}")
+            # pages of tiles the prefill completed are untouched by the appends
+            first_new_tile = wl.seq_lens[s] // tile
+            done = table[s, :first_new_tile * (tile // 16)]
+            assert torch.equal(cache.pool_k[done], prefill_k[done])
+            assert torch.equal(cache.pool_v[done], prefill_v[done])
+            r = int(lens_now[s] % tile) or tile
+            np.testing.assert_array_equal(cache.staging_k[s, :r].cpu().numpy(), stg_k[s, :r])
+            np.testing.assert_array_equal(cache.staging_v[s, :r].cpu().numpy(), stg_v[s, :r])
+
+
+DECODE_CASES = [
+    # (recipe, lens, hkv, hq, tile, bits_k, bits_v, iters)
+    (1, (1024,), 1, 8, 64, 4, 4, 3),                 # single-head 1K workload, G = 8
+    (2, (700, 513, 64, 1), 2, 8, 64, 4, 4, 3),       # G = 4, ragged, a 1-token sequence
+    (5, (611, 200, 33, 96, 1000, 17), 2, 16, 32, 4, 2, 5),  # G = 8, K4/V2, tile 32
+    (2, (900, 129), 2, 8, 128, 2, 2, 3),             # 2-bit, tile 128
+    (2, (300,), 1, 1, 64, 4, 4, 3),                  # G = 1 (padded)
+    (2, (257, 40), 1, 16, 64, 4, 2, 3),              # G = 16
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_paged_decode_parity(case):
+    recipe, lens, hkv, hq, tile, bk, bv, iters = case
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    q = inputs.gen_q(wl)
+    seq_lens = np.array(wl.seq_lens, np.int32)
+    out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(seq_lens).cuda(), max(lens))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    ref = orc.paged_decode_attn(q, table, seq_lens, gpk, gpv, tile, bk, bv)
+    err = pu.assert_attn(got, ref, f"decode {case}")
+    # informative: against the oracle's own pages (quantization error included)
+    ref_pk = orc.new_pool(npages, hkv, bk, tile)
+    ref_pv = orc.new_pool(npages, hkv, bv, tile)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, tile, bk, bv, iters, ref_pk, ref_pv)
+    e2e = np.abs(got - orc.paged_decode_attn(q, table, seq_lens, ref_pk, ref_pv, tile, bk, bv)).max()
+    print(f"[attn] {case}: max abs err vs oracle on GPU pages {err:.2e}; vs oracle pages {e2e:.2e}", flush=True)
+
+
+def test_decode_page_order_and_determinism():
+    case = DECODE_CASES[1]
+    recipe, lens, hkv, hq, tile, bk, bv, iters = case
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    q = torch.from_numpy(inputs.gen_q(wl)).cuda()
+    sl = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    outs = []
+    for shuffled in (True, False, True):
+        _, _, _, _, cache = _gpu_prefill(wl, shuffled)
+        outs.append(cache.decode(q, sl, max(lens)))
+    assert torch.equal(outs[0], outs[2])
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_append_then_decode_matches_oracle():
+    # a decode step as the bench runs it: append one token, attend over all of them
+    wl = _paged_workload(2, (511, 64, 300), 2, 8, 64, 4, 4, 3)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    lens = np.array(wl.seq_lens, np.int32)
+    kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
+    cache.append(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens).cuda())
+    q = inputs.gen_q(wl, step=0)
+    out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(lens + 1).cuda(), int(lens.max()) + 1)
+    torch.cuda.synchronize()
+    ref = orc.paged_decode_attn(q, table, lens + 1, cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy(),
+                                64, 4, 4)
+    pu.assert_attn(out.cpu().numpy(), ref, "append+decode")
