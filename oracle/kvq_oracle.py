@@ -315,29 +315,39 @@ def _v_field(bits: int, c: int, r: int):
     return m * 4 * bits + 4 * w, field
 
 
+_V_MAPS = {}
+
+
+def _v_map(bits: int):
+    """For every (token, channel) of a page: index of its 32-bit word in the
+    V-slot code area and the bit shift of its field (from _v_field)."""
+    if bits not in _V_MAPS:
+        quad_bytes = 4 * HEAD_DIM * bits // 8
+        word = np.zeros((PAGE_TOKENS, HEAD_DIM), np.int64)
+        shift = np.zeros((PAGE_TOKENS, HEAD_DIM), np.int64)
+        for t in range(PAGE_TOKENS):
+            q, r = divmod(t, 4)
+            for c in range(HEAD_DIM):
+                off, field = _v_field(bits, c, r)
+                word[t, c] = (q * quad_bytes + off) // 4
+                shift[t, c] = bits * field
+        _V_MAPS[bits] = (word, shift)
+    return _V_MAPS[bits]
+
+
 def v_codes_to_bytes(codes: np.ndarray, bits: int) -> np.ndarray:
     """codes uint8 [16, 128] -> V-slot code bytes."""
-    quad_bytes = 4 * HEAD_DIM * bits // 8
+    word, shift = _v_map(bits)
     words = np.zeros(PAGE_TOKENS * HEAD_DIM * bits // 32, np.uint64)
-    for t in range(PAGE_TOKENS):
-        q, r = divmod(t, 4)
-        for c in range(HEAD_DIM):
-            off, field = _v_field(bits, c, r)
-            wi = (q * quad_bytes + off) // 4
-            words[wi] |= np.uint64(int(codes[t, c]) & ((1 << bits) - 1)) << np.uint64(bits * field)
+    vals = (np.asarray(codes, np.uint64) & np.uint64((1 << bits) - 1)) << shift.astype(np.uint64)
+    np.bitwise_or.at(words, word.ravel(), vals.ravel())
     return words.astype("<u4").view(np.uint8).copy()
 
 
 def bytes_to_v_codes(raw: np.ndarray, bits: int) -> np.ndarray:
-    quad_bytes = 4 * HEAD_DIM * bits // 8
-    words = np.ascontiguousarray(raw).view("<u4")
-    codes = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
-    for t in range(PAGE_TOKENS):
-        q, r = divmod(t, 4)
-        for c in range(HEAD_DIM):
-            off, field = _v_field(bits, c, r)
-            codes[t, c] = (int(words[(q * quad_bytes + off) // 4]) >> (bits * field)) & ((1 << bits) - 1)
-    return codes
+    word, shift = _v_map(bits)
+    words = np.ascontiguousarray(raw).view("<u4").astype(np.int64)
+    return ((words[word] >> shift) & ((1 << bits) - 1)).astype(np.uint8)
 
 
 def new_pool(num_pages: int, kv_heads: int, bits: int, tile_tokens: int) -> np.ndarray:
