@@ -58,14 +58,16 @@ kvq_status launched(hipError_t e, const char* what) {
 #define KVQ_NONNULL(p) \
   if ((p) == nullptr) return fail(KVQ_ERR_ARG, "%s is NULL", #p)
 
-// Split of the context into partitions of tiles for the decode kernel: enough
-// waves to cover 256 CUs several times over, at least one tile each.
+// Split of the context into partitions of tiles for the decode kernel (one
+// workgroup of 4 waves each): about two workgroups per CU over the whole grid,
+// 4..64 tiles per partition, and at most 1024 partitions per sequence.
 int tiles_per_partition(int num_seqs, int kv_heads, int max_seq_len, int tile) {
   const long tiles = (long)((max_seq_len + tile - 1) / tile);
   const long total = tiles * num_seqs * kv_heads;
-  long tpp = (total + 2047) / 2048;
-  if (tpp < 1) tpp = 1;
+  long tpp = (total + 511) / 512;
+  if (tpp < 4) tpp = 4;
   if (tpp > 64) tpp = 64;
+  if (tpp < (tiles + 1023) / 1024) tpp = (tiles + 1023) / 1024;
   if (tpp > tiles) tpp = tiles > 0 ? tiles : 1;
   return (int)tpp;
 }

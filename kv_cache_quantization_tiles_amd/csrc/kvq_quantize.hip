@@ -38,26 +38,46 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void unpack8(u32x4 w, float* out) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
-    out[2 * i + 1] = half_bits_to_float((uint16_t)(w[i] >> 16));
-  }
+// fp16 pair (low, high half of w) -> fp32 (low + high, low - high): the
+// conversion rides on the first butterfly stage (fma with fp16 operands).
+__device__ __forceinline__ void first_stage(unsigned w, float& y0, float& y1) {
+  _Float16 lo, hi;
+  const uint16_t l16 = (uint16_t)(w & 0xFFFFu), h16 = (uint16_t)(w >> 16);
+  __builtin_memcpy(&lo, &l16, 2);
+  __builtin_memcpy(&hi, &h16, 2);
+  y0 = __builtin_fmaf((float)lo, 1.0f, (float)hi);
+  y1 = __builtin_fmaf((float)lo, 1.0f, -(float)hi);
 }
 
-// Shared-memory footprint of one workgroup (floats).
+// Shared memory of one workgroup.
 template <int T>
-struct Smem {
-  float red[2][T / 4][kHeadDim];  // channel partials; token partials alias it
+struct alignas(16) Smem {
+  float red[2][T / 4][kHeadDim];  // channel partials; token partials and row min/max alias it
   float a[kHeadDim];              // 1/alpha in unnormalized units
   float alpha[kHeadDim];          // channel factors (normalized units)
-  float b[T];                     // 1/beta
   float ref_c[kHeadDim];          // R of the tile's first token (channel-step shift)
+  float b[T];                     // 1/beta
   float ref_t[T];                 // R of channel 0 of each token (token-step shift)
-  float inv[T];                   // 1/step per row
-  float nmi[T];                   // -min/step per row
+  float inv[T];                   // levels / range per row (0 for empty rows)
+  float nmi[T];                   // -min * inv per row
 };
+
+// Packs 8 codes (values v[idx[i]] rounded to nearest even by v_cvt_pk_u8_f32)
+// into one 32-bit word whose field f (bits [BITS*f, BITS*(f+1))) takes the
+// code listed at position f of `order`.
+template <int BITS, int N>
+__device__ __forceinline__ unsigned pack_fields(const float (&v)[N]) {
+  constexpr int PER = 8 / BITS;  // fields per byte
+  unsigned acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = 0u;
+#pragma unroll
+  for (int f = 0; f < N; ++f) acc[f % PER] = __builtin_amdgcn_cvt_pk_u8_f32(v[f], f / PER, acc[f % PER]);
+  unsigned w = acc[0];
+#pragma unroll
+  for (int p = 1; p < PER; ++p) w |= acc[p] << (BITS * p);
+  return w;
+}
 
 template <int T, int BITS, bool VLAYOUT, int MODE>
 __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& sm, int role,
@@ -71,43 +91,35 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
   // ---------------------------------------------------------------- rows of this tile
   const int t0 = tile_idx * T;
   int n_valid;
-  const uint16_t* rows_base = nullptr;  // rows t < n_valid at rows_base + t * row_stride
-  size_t row_stride = 0;
+  const uint16_t* rows_base = nullptr;  // row t at rows_base + t * row_stride
   int r_new = -1;                       // append: the row taken from the new token
   const int H = (MODE == kDense) ? A.heads : A.kv_heads;
+  const size_t row_stride = (size_t)H * kHeadDim;
   if (MODE == kDense) {
     n_valid = min(T, A.n_tokens - t0);
     rows_base = A.x + ((size_t)t0 * H + head) * kHeadDim;
-    row_stride = (size_t)H * kHeadDim;
   } else if (MODE == kPaged) {
     const int a0 = A.cu_seqlens[seq];
-    const int len = A.cu_seqlens[seq + 1] - a0;
-    n_valid = min(T, len - t0);
+    n_valid = min(T, A.cu_seqlens[seq + 1] - a0 - t0);
     rows_base = A.src[role] + ((size_t)(a0 + t0) * H + head) * kHeadDim;
-    row_stride = (size_t)H * kHeadDim;
   } else {
-    const int pos = A.lens_before[seq];
-    r_new = pos % T;
+    r_new = A.lens_before[seq] % T;
     n_valid = r_new + 1;
     rows_base = A.staging[role] + ((size_t)seq * T * H + head) * kHeadDim;
-    row_stride = (size_t)H * kHeadDim;
   }
 
   // ---------------------------------------------------------------- load fp16 rows
+  // Rows past the tile's end load row 0 again: their values are then exact
+  // copies of row 0, which the statistics below exclude exactly.
   u32x4 raw[4][2];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 4 * tq + r;
-    if (t < n_valid) {
-      const uint16_t* row = rows_base + (size_t)t * row_stride;
-      if (MODE == kAppend && t == r_new)
-        row = A.src[role] + ((size_t)seq * H + head) * kHeadDim;
-      raw[r][0] = *reinterpret_cast<const u32x4*>(row + 8 * cg);
-      raw[r][1] = *reinterpret_cast<const u32x4*>(row + 64 + 8 * cg);
-    } else {
-      raw[r][0] = u32x4{0, 0, 0, 0};
-      raw[r][1] = u32x4{0, 0, 0, 0};
-    }
+    const int src_t = (t < n_valid) ? t : 0;
+    const uint16_t* row = rows_base + (size_t)src_t * row_stride;
+    if (MODE == kAppend && src_t == r_new) row = A.src[role] + ((size_t)seq * H + head) * kHeadDim;
+    raw[r][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 8 * cg));
+    raw[r][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 64 + 8 * cg));
   }
   // Keep the fp16 rows of a partial tile for later appends.
   if (MODE != kDense && A.staging[role] != nullptr) {
@@ -123,19 +135,19 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     }
   }
 
-  float R[4][16];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    unpack8(raw[r][0], &R[r][0]);
-    unpack8(raw[r][1], &R[r][8]);
-  }
-
   // ---------------------------------------------------------------- Hadamard (unnormalized)
   // register index k = 8*half + j  <->  channel 64*half + 8*cg + j
+  float R[4][16];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) first_stage(raw[r][half][i], R[r][8 * half + 2 * i], R[r][8 * half + 2 * i + 1]);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
 #pragma unroll
-    for (int bit = 1; bit < 16; bit <<= 1) {
+    for (int bit = 2; bit < 16; bit <<= 1) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         if (k & bit) continue;
@@ -164,19 +176,20 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
   }
 
   // ---------------------------------------------------------------- normalization
-  // Sums are taken over values shifted by a reference (channel step: the
-  // tile's first token; token step: the token's channel 0), so that
+  // Spread sums are taken over values shifted by a reference (channel step:
+  // the tile's first token; token step: the token's channel 0), so that
   // E[d^2] - E[d]^2 does not cancel when a mean dwarfs the spread.
   if (tq == 0) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sm.ref_c[64 * half + 8 * cg + j] = R[0][8 * half + j];
+    for (int half = 0; half < 2; ++half) {
+      *reinterpret_cast<f32x4*>(&sm.ref_c[64 * half + 8 * cg]) =
+          f32x4{R[0][8 * half], R[0][8 * half + 1], R[0][8 * half + 2], R[0][8 * half + 3]};
+      *reinterpret_cast<f32x4*>(&sm.ref_c[64 * half + 8 * cg + 4]) =
+          f32x4{R[0][8 * half + 4], R[0][8 * half + 5], R[0][8 * half + 6], R[0][8 * half + 7]};
+    }
   }
-  if (cg == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.ref_t[4 * tq + r] = R[r][0];
-  }
+  if (cg == 0)
+    *reinterpret_cast<f32x4*>(&sm.ref_t[4 * tq]) = f32x4{R[0][0], R[1][0], R[2][0], R[3][0]};
   for (int c = tid; c < kHeadDim; c += NT) {
     sm.a[c] = kInvSqrtD;
     sm.alpha[c] = 1.0f;
@@ -186,9 +199,8 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
   float a[16], b[4], refc[16], reft[4];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int c0 = 64 * half + 8 * cg;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.ref_c[c0]);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.ref_c[c0 + 4]);
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.ref_c[64 * half + 8 * cg]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.ref_c[64 * half + 8 * cg + 4]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { refc[8 * half + i] = lo[i]; refc[8 * half + 4 + i] = hi[i]; }
   }
@@ -202,6 +214,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
 #pragma unroll
   for (int r = 0; r < 4; ++r) b[r] = 1.0f;
   const float inv_n = 1.0f / (float)n_valid;
+  const float n_copies = (float)(T - n_valid);  // rows that are copies of row 0
   const int iters = A.iters;
   float b0 = 1.0f;
 
@@ -210,16 +223,20 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     {
       float s1[16], s2[16], kc[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) { s1[k] = 0.f; s2[k] = 0.f; kc[k] = b0 * refc[k]; }
+      for (int k = 0; k < 16; ++k) kc[k] = b0 * refc[k];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (4 * tq + r < n_valid) {
+      for (int k = 0; k < 16; ++k) {
+        const float d = __builtin_fmaf(b[0], R[0][k], -kc[k]);
+        s1[k] = d;
+        s2[k] = d * d;
+      }
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const float d = __builtin_fmaf(b[r], R[r][k], -kc[k]);
-            s1[k] += d;
-            s2[k] = __builtin_fmaf(d, d, s2[k]);
-          }
+      for (int r = 1; r < 4; ++r) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float d = __builtin_fmaf(b[r], R[r][k], -kc[k]);
+          s1[k] += d;
+          s2[k] = __builtin_fmaf(d, d, s2[k]);
         }
       }
 #pragma unroll
@@ -243,10 +260,17 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         S1 += sm.red[0][g][c];
         S2 += sm.red[1][g][c];
       }
-      const float m = S1 * inv_n;                         // mean of the shifted values
+      // copies of row 0 each added row 0's own shifted value rho (the fma
+      // residual of the shift); take them out
+      const float rc = sm.ref_c[c];
+      const float kcc = b0 * rc;
+      const float rho = __builtin_fmaf(b0, rc, -kcc);
+      S1 = __builtin_fmaf(-n_copies, rho, S1);
+      S2 = __builtin_fmaf(-n_copies, rho * rho, S2);
+      const float m = S1 * inv_n;                                   // mean of the shifted values
       const float var = fmaxf(__builtin_fmaf(-m, m, S2 * inv_n), 0.f);
-      const float mu = __builtin_fmaf(b0, sm.ref_c[c], m);  // mean of u
-      const float ms = __builtin_fmaf(mu, mu, var);           // mean square of u
+      const float mu = m + kcc;                                     // mean of u
+      const float ms = __builtin_fmaf(mu, mu, var);                 // mean square of u
       if (var > kGuard2 * ms) {
         sm.a[c] = __builtin_amdgcn_rsqf(var);
         sm.alpha[c] = __builtin_sqrtf(var * (1.0f / kHeadDim));
@@ -255,9 +279,8 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     __syncthreads();
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int c0 = 64 * half + 8 * cg;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.a[c0]);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.a[c0 + 4]);
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.a[64 * half + 8 * cg]);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.a[64 * half + 8 * cg + 4]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) { a[8 * half + i] = lo[i]; a[8 * half + 4 + i] = hi[i]; }
     }
@@ -270,9 +293,14 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float kt = a0 * reft[r];
-        float x1 = 0.f, x2 = 0.f;
+        float x1, x2;
+        {
+          const float d = __builtin_fmaf(a[0], R[r][0], -kt);
+          x1 = d;
+          x2 = d * d;
+        }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 1; k < 16; ++k) {
           const float d = __builtin_fmaf(a[k], R[r][k], -kt);
           x1 += d;
           x2 = __builtin_fmaf(d, d, x2);
@@ -301,10 +329,10 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     }
     __syncthreads();
     {
+      b0 = sm.b[0];
       const f32x4 bb = *reinterpret_cast<const f32x4*>(&sm.b[4 * tq]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) b[r] = bb[r];
-      b0 = sm.b[0];
+      for (int r = 0; r < 4; ++r) b[r] = (4 * tq + r < n_valid) ? bb[r] : b0;  // copies weigh as row 0
     }
   }
 
@@ -312,12 +340,13 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
   float zmin[4], zmax[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float mn = 3.4e38f, mx = -3.4e38f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      R[r][k] *= a[k];
-      mn = fminf(mn, R[r][k]);
-      mx = fmaxf(mx, R[r][k]);
+    for (int k = 0; k < 16; ++k) R[r][k] *= a[k];
+    float mn = fminf(R[r][0], R[r][1]), mx = fmaxf(R[r][0], R[r][1]);
+#pragma unroll
+    for (int k = 2; k < 16; k += 2) {
+      mn = fminf(mn, fminf(R[r][k], R[r][k + 1]));
+      mx = fmaxf(mx, fmaxf(R[r][k], R[r][k + 1]));
     }
     zmin[r] = mn;
     zmax[r] = mx;
@@ -339,8 +368,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     pages = A.block_table + (size_t)seq * A.max_blocks + (t0 / kPage);
   }
   auto slot_ptr = [&](int page_in_tile) -> uint8_t* {
-    const int page = pages[page_in_tile];
-    return pool + ((size_t)page * H + head) * SLOT;
+    return pool + ((size_t)pages[page_in_tile] * H + head) * SLOT;
   };
 
   if (tid < T) {
@@ -380,107 +408,89 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
       A.alpha[((size_t)tile_idx * H + head) * kHeadDim + c] = al;
     } else {
       constexpr int AL = slot_alpha_len(T);
-      uint8_t* slot = slot_ptr(c / AL);
-      reinterpret_cast<float*>(slot + CODE_BYTES + 8 * kPage)[c % AL] = al;
+      reinterpret_cast<float*>(slot_ptr(c / AL) + CODE_BYTES + 8 * kPage)[c % AL] = al;
     }
   }
   __syncthreads();
 
-  // codes, packed
-  unsigned code[4][16];
+  // values before rounding: v = (z - min) * levels / range, in [0, levels]
+  {
+    const f32x4 iv = *reinterpret_cast<const f32x4*>(&sm.inv[4 * tq]);
+    const f32x4 nm = *reinterpret_cast<const f32x4*>(&sm.nmi[4 * tq]);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float inv = sm.inv[4 * tq + r], nmi = sm.nmi[4 * tq + r];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float v = __builtin_fmaf(R[r][k], inv, nmi);
-      // adding 1.5*2^23 rounds to the nearest integer (ties to even) and leaves
-      // it in the low mantissa bits; 0 <= v <= LEVELS up to rounding.
-      code[r][k] = __float_as_uint(v + 12582912.0f) & ((1u << BITS) - 1u);
-    }
+      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], iv[r], nm[r]);
   }
 
-  if (MODE == kDense) {
+  if (MODE == kDense || !VLAYOUT) {
+    // natural packing, 8 channels of one token per 8*BITS bits
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * tq + r;
-      if (t >= n_valid) continue;
-      uint8_t* row = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8);
+      if (MODE == kDense && t >= n_valid) continue;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        unsigned w = 0;
+        float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w |= code[r][8 * half + j] << (BITS * j);
-        if (BITS == 4) *reinterpret_cast<uint32_t*>(row + BITS * (8 * half + cg)) = w;
-        else *reinterpret_cast<uint16_t*>(row + BITS * (8 * half + cg)) = (uint16_t)w;
-      }
-    }
-  } else if (!VLAYOUT) {
-    // K slot: 4 blocks of 32 channels, token after token, natural packing.
-    constexpr int CB = 4 * BITS;  // bytes per token per block
-    uint8_t* slot = slot_ptr((4 * tq) / kPage);
-    const int tp0 = (4 * tq) % kPage;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        unsigned w = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w |= code[r][8 * half + j] << (BITS * j);
-        const int blk = 2 * half + (cg >> 2);
-        uint8_t* dst = slot + blk * (kPage * CB) + (tp0 + r) * CB + BITS * (cg & 3);
-        if (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = w;
-        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+        for (int j = 0; j < 8; ++j) v[j] = R[r][8 * half + j];
+        unsigned w;
+        if (BITS == 4) {
+          // fields in order 0..7; bytes take fields (0,1), (2,3), ...
+          float o[8] = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+          w = pack_fields<4>(o);
+        } else {
+          w = pack_fields<2>(v);
+        }
+        if (MODE == kDense) {
+          uint8_t* row = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8);
+          if (BITS == 4) *reinterpret_cast<uint32_t*>(row + BITS * (8 * half + cg)) = w;
+          else *reinterpret_cast<uint16_t*>(row + BITS * (8 * half + cg)) = (uint16_t)w;
+        } else {
+          // K slot: 4 blocks of 32 channels, token after token
+          constexpr int CB = 4 * BITS;  // bytes per token per block
+          uint8_t* dst = slot_ptr((4 * tq) / kPage) + (2 * half + (cg >> 2)) * (kPage * CB) +
+                         ((4 * tq) % kPage + r) * CB + BITS * (cg & 3);
+          if (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = w;
+          else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+        }
       }
     }
   } else {
-    // V slot: quads of 4 tokens, groups of 8 channels, fields 2j + (r>>1) + (F/2)(r&1).
+    // V slot: quads of 4 tokens, groups of 8 channels; word w holds channels
+    // j < F/4 of the group's word, field 2j + (r>>1) + (F/2)(r&1).
+    constexpr int F = 32 / BITS;
     uint8_t* slot = slot_ptr((4 * tq) / kPage);
     const int quad = tq % (kPage / 4);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int grp = 8 * half + cg;
-      uint8_t* dst = slot + quad * (16 * BITS * 4) + grp * (4 * BITS);
-      if (BITS == 4) {
-        u32x4 words;
+      uint8_t* dst = slot + quad * (16 * BITS * 4) + (8 * half + cg) * (4 * BITS);
+      unsigned words[BITS];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          unsigned x = 0;
+      for (int w = 0; w < BITS; ++w) {
+        float o[F];
 #pragma unroll
-          for (int p = 0; p < 2; ++p)
+        for (int j = 0; j < F / 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              x |= code[r][8 * half + 2 * w + p] << (4 * (2 * p + (r >> 1) + 4 * (r & 1)));
-          words[w] = x;
-        }
-        *reinterpret_cast<u32x4*>(dst) = words;
-      } else {
-        u32x2 words;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          unsigned x = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              x |= code[r][8 * half + 4 * w + j] << (2 * (2 * j + (r >> 1) + 8 * (r & 1)));
-          words[w] = x;
-        }
-        *reinterpret_cast<u32x2*>(dst) = words;
+          for (int r = 0; r < 4; ++r)
+            o[2 * j + (r >> 1) + (F / 2) * (r & 1)] = R[r][8 * half + (F / 4) * w + j];
+        words[w] = pack_fields<BITS>(o);
       }
+      if (BITS == 4) *reinterpret_cast<u32x4*>(dst) = u32x4{words[0], words[1], words[2], words[3]};
+      else *reinterpret_cast<u32x2*>(dst) = u32x2{words[0], words[1]};
     }
   }
 }
 
 template <int T, int BITS>
-__global__ __launch_bounds__(2 * T) void quantize_dense_kernel(QuantArgs A) {
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(3))) void quantize_dense_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
   quantize_tile_body<T, BITS, false, kDense>(A, sm, 0, blockIdx.y, 0, blockIdx.x);
 }
 
 // grid: x = tile index in the sequence, y = head + Hkv * role (0 K, 1 V), z = sequence
 template <int T, int BK, int BV>
-__global__ __launch_bounds__(2 * T) void quantize_paged_kernel(QuantArgs A) {
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(3))) void quantize_paged_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
   const int seq = blockIdx.z;
   const int len = A.cu_seqlens[seq + 1] - A.cu_seqlens[seq];
@@ -493,7 +503,7 @@ __global__ __launch_bounds__(2 * T) void quantize_paged_kernel(QuantArgs A) {
 
 // grid: x = head, y = role, z = sequence
 template <int T, int BK, int BV>
-__global__ __launch_bounds__(2 * T) void append_kernel(QuantArgs A) {
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(3))) void append_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
   const int seq = blockIdx.z;
   const int tile_idx = A.lens_before[seq] / T;
