@@ -30,7 +30,36 @@ sys.path.insert(0, ROOT)
 from kv_cache_quantization_tiles_amd import inputs  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+# Non-packed fp32 VALU issue peak of MI355X: 256 CUs x 64 lanes x 2.4 GHz
+# (packed fp32 is kept out of the generated code).
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 D = 128
+
+
+def quantize_valu_ops_per_element(iters: int) -> int:
+    """Algorithmic VALU lane-ops per element of the quantizer: fp16->fp32 (1),
+    the 7-stage butterfly (7), 3 per normalization half-step (shifted value,
+    sum, sum of squares) over 2*iters-1 half-steps (the last token step
+    cancels), and rounding (scale, min/max, affine map, convert: 4)."""
+    return 1 + 7 + 3 * max(2 * iters - 1, 0) + 4
+
+
+def measured_traffic(kernel_source: str, profile: str):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    measurement, if it was taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "kv_cache_quantization_tiles_amd", "csrc", kernel_source)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return {"read_bytes": rec["read_bytes"], "write_bytes": rec["write_bytes"],
+            "total_bytes": rec["read_bytes"] + rec["write_bytes"], "source": "profiles/" + profile}
 
 
 # ----------------------------------------------------------------------------- byte model
@@ -223,6 +252,8 @@ def main():
     dbytes = decode_bytes(wl, [l + 1 for l in wl.seq_lens])
     q_ms, a_ms, d_ms = float(np.mean(tq)), float(np.mean(ta)), float(np.mean(td))
     q_gbps = qbytes / (q_ms * 1e-3) / 1e9
+    n_elem = 2 * ntok_heads * D
+    q_tops = n_elem * quantize_valu_ops_per_element(wl.iters) / (q_ms * 1e-3) / 1e12
     d_gbps_cold = dbytes / (td_cold * 1e-3) / 1e9
     value = (qbytes + abytes + dbytes) / (ms_step * 1e-3) / 1e9
     rec = {
@@ -245,9 +276,12 @@ def main():
         "decode_tok_per_s": round(wl.num_seqs / ((a_ms + d_ms) * 1e-3), 1),
         "decode_attn_only_tok_per_s": round(wl.num_seqs / (td_cold * 1e-3), 1),
         "copy_probe_GBps": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "kernel": "quantize_paged_kernel",
-                     "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(q_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "roofline": {"bound": "alu", "kernel": "quantize_paged_kernel",
+                     "achieved": round(q_tops, 3), "peak": round(VALU_PEAK_TOPS, 3), "unit": "Tlane-op/s",
+                     "frac": round(q_tops / VALU_PEAK_TOPS, 4),
+                     "ops_per_element": quantize_valu_ops_per_element(wl.iters),
+                     "hbm_GBps": round(q_gbps, 1), "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("kvq_quantize.hip", f"traffic-quantize_paged_kernel-{wl.name}.json")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -503,3 +503,92 @@ def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, b
             for h in range(kh * g, (kh + 1) * g):
                 out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Baselines for the long-context comparison: the same paged decode attention on
+# fp16 pages and on fp8 (OCP E4M3) pages with one scale per tensor, the two
+# modes the aitrends.kr page (article 74976, TL;DR) runs beside its compressed
+# cache.  Layouts (per page, per kv head): K page [16 tokens][128 channels],
+# V page [128 channels][16 tokens] (channel-major, as paged attention usually
+# keeps V).  Rows past the sequence's end are 0.
+# ----------------------------------------------------------------------------
+
+def fp8_encode(x: np.ndarray, scale: float) -> np.ndarray:
+    """x / scale rounded to OCP E4M3 (nearest, ties to even) by torch's CPU
+    float8_e4m3fn conversion; returns the code bytes."""
+    import torch
+    t = torch.from_numpy(np.asarray(x, np.float32) / np.float32(scale))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_decode(b: np.ndarray, scale: float) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.double().numpy() * float(scale)
+
+
+def fp8_scale(x: np.ndarray) -> float:
+    """Per-tensor scale amax / 448 (448 = largest finite E4M3 value)."""
+    amax = float(np.max(np.abs(np.asarray(x, np.float32))))
+    return amax / 448.0 if amax > 0 else 1.0
+
+
+def new_baseline_pool(num_pages: int, kv_heads: int, fp8: bool) -> np.ndarray:
+    return np.zeros((num_pages, kv_heads, PAGE_TOKENS * HEAD_DIM), np.uint8 if fp8 else np.float16)
+
+
+def fill_pages_baseline(k, v, cu_seqlens, table, pool_k, pool_v, fp8=False, k_scale=1.0, v_scale=1.0):
+    """Write a prefill into fp16 or fp8 page pools (in place)."""
+    heads = k.shape[1]
+    for s in range(len(cu_seqlens) - 1):
+        a0, a1 = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        n = a1 - a0
+        for j in range((n + PAGE_TOKENS - 1) // PAGE_TOKENS):
+            page = int(table[s][j])
+            rows = slice(a0 + j * PAGE_TOKENS, min(a1, a0 + (j + 1) * PAGE_TOKENS))
+            for h in range(heads):
+                kp = np.zeros((PAGE_TOKENS, HEAD_DIM), np.float16)
+                vp = np.zeros((PAGE_TOKENS, HEAD_DIM), np.float16)
+                m = rows.stop - rows.start
+                kp[:m] = k[rows, h]
+                vp[:m] = v[rows, h]
+                vt = np.ascontiguousarray(vp.T)           # [channel][token]
+                if fp8:
+                    kb = fp8_encode(kp, k_scale)
+                    vb = fp8_encode(vt, v_scale)
+                    kb[m:] = 0
+                    vb[:, m:] = 0
+                    pool_k[page, h] = kb.reshape(-1)
+                    pool_v[page, h] = vb.reshape(-1)
+                else:
+                    pool_k[page, h] = kp.reshape(-1)
+                    pool_v[page, h] = vt.reshape(-1)
+
+
+def read_baseline_sequence(pool, table_row, seq_len, head, role, fp8=False, scale=1.0):
+    """Restored tokens float64 [L, 128] of one (sequence, kv head)."""
+    out = np.zeros((seq_len, HEAD_DIM))
+    for j in range((seq_len + PAGE_TOKENS - 1) // PAGE_TOKENS):
+        raw = pool[int(table_row[j]), head]
+        raw = raw.reshape(PAGE_TOKENS, HEAD_DIM) if role == "K" else raw.reshape(HEAD_DIM, PAGE_TOKENS).T
+        vals = fp8_decode(raw, scale) if fp8 else raw.astype(np.float64)
+        m = min(PAGE_TOKENS, seq_len - j * PAGE_TOKENS)
+        out[j * PAGE_TOKENS:j * PAGE_TOKENS + m] = vals[:m]
+    return out
+
+
+def paged_decode_attn_baseline(q, table, seq_lens, pool_k, pool_v, fp8=False, k_scale=1.0, v_scale=1.0,
+                               sm_scale=None):
+    s_n, hq, d = q.shape
+    hkv = pool_k.shape[1]
+    g = hq // hkv
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+    out = np.zeros((s_n, hq, d))
+    for s in range(s_n):
+        for kh in range(hkv):
+            kx = read_baseline_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", fp8, k_scale)
+            vx = read_baseline_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", fp8, v_scale)
+            for h in range(kh * g, (kh + 1) * g):
+                out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
+    return out

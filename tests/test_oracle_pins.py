@@ -400,3 +400,43 @@ def test_paged_attention_equals_brute_force_with_gqa_and_ignores_page_order():
     vt = torch.tensor(vx).permute(1, 0, 2).repeat_interleave(4, dim=0)
     ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0].numpy()
     np.testing.assert_allclose(out[0], ref, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- fp16 / fp8 baselines
+
+def test_fp8_encoding_hand_values():
+    # OCP E4M3: bias 7, 3 mantissa bits, max 448 = 0x7E; 1.0 = 0x38; 0.5 = 0x30;
+    # -2.0 = 0xC0; 1.0625 lies halfway between 1.0 and 1.125 -> ties to even -> 1.0;
+    # 1.1875 halfway between 1.125 and 1.25 -> 1.25 (even mantissa 010).
+    x = np.array([1.0, 0.5, -2.0, 448.0, 1.0625, 1.1875, 0.0], np.float32)
+    np.testing.assert_array_equal(orc.fp8_encode(x, 1.0), [0x38, 0x30, 0xC0, 0x7E, 0x38, 0x3A, 0x00])
+    np.testing.assert_array_equal(orc.fp8_decode(np.array([0x38, 0x30, 0xC0, 0x7E, 0x3A]), 2.0),
+                                  [2.0, 1.0, -4.0, 896.0, 2.5])
+
+
+def test_baseline_pages_round_trip_and_attention():
+    import dataclasses
+    wl = dataclasses.replace(inputs.workload(2), seq_lens=(70, 33), hkv=2, hq=8, tile_tokens=64)
+    k, v = inputs.gen_kv(wl, "K"), inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    cu = wl.cu_seqlens()
+    for fp8 in (False, True):
+        pk = orc.new_baseline_pool(npages, 2, fp8)
+        pv = orc.new_baseline_pool(npages, 2, fp8)
+        ks, vs = (orc.fp8_scale(k), orc.fp8_scale(v)) if fp8 else (1.0, 1.0)
+        orc.fill_pages_baseline(k, v, cu, table, pk, pv, fp8, ks, vs)
+        kx = orc.read_baseline_sequence(pk, table[0], 70, 1, "K", fp8, ks)
+        vx = orc.read_baseline_sequence(pv, table[0], 70, 1, "V", fp8, vs)
+        if fp8:
+            np.testing.assert_allclose(kx, k[:70, 1], rtol=2 ** -4, atol=ks * 2 ** -9)
+            np.testing.assert_allclose(vx, v[:70, 1], rtol=2 ** -4, atol=vs * 2 ** -9)
+        else:
+            np.testing.assert_array_equal(kx, k[:70, 1])
+            np.testing.assert_array_equal(vx, v[:70, 1])
+        q = inputs.gen_q(wl)
+        out = orc.paged_decode_attn_baseline(q, table, np.array(wl.seq_lens), pk, pv, fp8, ks, vs)
+        qt = torch.tensor(q[1].astype(np.float64))[:, None, :]
+        kt = torch.tensor(orc.read_baseline_sequence(pk, table[1], 33, 0, "K", fp8, ks))[None].expand(4, -1, -1)
+        vt = torch.tensor(orc.read_baseline_sequence(pv, table[1], 33, 0, "V", fp8, vs))[None].expand(4, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt[:4], kt, vt)[:, 0].numpy()
+        np.testing.assert_allclose(out[1, :4], ref, rtol=1e-10, atol=1e-12)
