@@ -187,8 +187,11 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32
  * quantized pages (no fp16 K/V is rebuilt).
  *   q            fp16 [num_seqs][q_heads][128]; query head h reads kv head
  *                h / (q_heads / kv_heads).
- *   seq_lens     int32 [num_seqs], device: tokens to attend (newest included).
- *   max_seq_len  host upper bound of seq_lens (sizes the grid).
+ *   seq_lens     int32 [num_seqs], device: tokens to attend (newest included);
+ *                a sequence of length 0 gets a zero output row.
+ *   max_seq_len  host upper bound of seq_lens (sizes the grid); every
+ *                seq_lens entry must be <= max_seq_len (not checked: the
+ *                lengths live on the device).
  *   sm_scale     softmax scale (1/sqrt(128) for standard attention).
  *   out          float32 [num_seqs][q_heads][128]:
  *                softmax(sm_scale * q.K^T) V over the restored tokens,
@@ -205,6 +208,51 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
                                  int32_t max_seq_len, const void* pool_k, const void* pool_v,
                                  float sm_scale, float* out, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Baselines (fp16 and fp8 paged KV without the quantizer), for comparing the
+ * quantized read path with the two modes the aitrends.kr page (article
+ * 74976, TL;DR) runs on the same workload.  Page layout per (page, kv head):
+ * K [16 tokens][128 channels], V [128 channels][16 tokens] (channel-major),
+ * elements fp16 or OCP E4M3 bytes (value = byte decoded times the tensor's
+ * scale; the fill rounds x / scale to nearest, ties to even).  A pool is
+ * [num_pages][kv_heads][16*128] elements; rows past a sequence's end are 0.
+ * Block tables as for the quantized pools (one page per 16 tokens).
+ */
+size_t kvq_baseline_page_bytes(int32_t fp8); /* 4096 (fp16) or 2048 (fp8) */
+
+/* Write a prefill (k, v fp16 [total][kv_heads][128], packed by cu_seqlens)
+ * into fp16 pools.  Errors as kvq_quantize_to_pages. */
+kvq_status kvq_fill_pages_fp16(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seq_len,
+                               int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,
+                               void* pool_k, void* pool_v, void* stream);
+
+/* Same into E4M3 pools with per-tensor scales k_scale, v_scale > 0
+ * (KVQ_ERR_ARG otherwise). */
+kvq_status kvq_fill_pages_fp8(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seq_len,
+                              int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,
+                              void* pool_k, void* pool_v, float k_scale, float v_scale, void* stream);
+
+/* Workspace bytes of the two baseline decode functions. */
+size_t kvq_baseline_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t q_heads,
+                                    int32_t kv_heads, int32_t max_seq_len);
+
+/* One decode step of softmax(sm_scale q.K^T) V over fp16 (resp. E4M3) pages;
+ * arguments, output and errors as kvq_paged_decode_attn (only head_dim and
+ * page_tokens of cfg are used). */
+kvq_status kvq_paged_decode_attn_fp16(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs,
+                                      int32_t q_heads, int32_t kv_heads, const int32_t* block_table,
+                                      int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                                      const void* pool_k, const void* pool_v, float sm_scale, float* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+kvq_status kvq_paged_decode_attn_fp8(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs,
+                                     int32_t q_heads, int32_t kv_heads, const int32_t* block_table,
+                                     int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                                     const void* pool_k, const void* pool_v, float k_scale, float v_scale,
+                                     float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * kvq_bandwidth_probe - measurement helper, not part of the method: copies

@@ -18,7 +18,9 @@ KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP, KVQ_ERR_WORKSPACE = 0, -1
 EXPORTED = (
     "kvq_last_error", "kvq_version", "kvq_slot_bytes", "kvq_quantize_tiles", "kvq_dequantize",
     "kvq_quantize_to_pages", "kvq_append_and_requant", "kvq_decode_workspace_bytes",
-    "kvq_paged_decode_attn", "kvq_bandwidth_probe",
+    "kvq_paged_decode_attn", "kvq_bandwidth_probe", "kvq_baseline_page_bytes", "kvq_fill_pages_fp16",
+    "kvq_fill_pages_fp8", "kvq_baseline_workspace_bytes", "kvq_paged_decode_attn_fp16",
+    "kvq_paged_decode_attn_fp8",
 )
 
 
@@ -66,8 +68,21 @@ def load():
     lib.kvq_paged_decode_attn.argtypes = [_CFG, _P, _I, _I, _I, _P, _I, _P, _I, _P, _P,
                                           ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
     lib.kvq_bandwidth_probe.argtypes = [_P, _P, ctypes.c_size_t, _P]
+    _F = ctypes.c_float
+    lib.kvq_baseline_page_bytes.argtypes = [_I]
+    lib.kvq_baseline_page_bytes.restype = ctypes.c_size_t
+    lib.kvq_fill_pages_fp16.argtypes = [_CFG, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P]
+    lib.kvq_fill_pages_fp8.argtypes = [_CFG, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _F, _F, _P]
+    lib.kvq_baseline_workspace_bytes.argtypes = [_CFG, _I, _I, _I, _I]
+    lib.kvq_baseline_workspace_bytes.restype = ctypes.c_size_t
+    lib.kvq_paged_decode_attn_fp16.argtypes = [_CFG, _P, _I, _I, _I, _P, _I, _P, _I, _P, _P, _F, _P, _P,
+                                               ctypes.c_size_t, _P]
+    lib.kvq_paged_decode_attn_fp8.argtypes = [_CFG, _P, _I, _I, _I, _P, _I, _P, _I, _P, _P, _F, _F, _F, _P,
+                                              _P, ctypes.c_size_t, _P]
     for name in ("kvq_quantize_tiles", "kvq_dequantize", "kvq_quantize_to_pages",
-                 "kvq_append_and_requant", "kvq_paged_decode_attn", "kvq_bandwidth_probe"):
+                 "kvq_append_and_requant", "kvq_paged_decode_attn", "kvq_bandwidth_probe",
+                 "kvq_fill_pages_fp16", "kvq_fill_pages_fp8", "kvq_paged_decode_attn_fp16",
+                 "kvq_paged_decode_attn_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -147,3 +162,45 @@ def kvq_paged_decode_attn(cfg, q, num_seqs, q_heads, kv_heads, block_table, max_
 
 def kvq_bandwidth_probe(src, dst, nbytes, stream=None):
     _check(load().kvq_bandwidth_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def kvq_baseline_page_bytes(fp8: bool) -> int:
+    return int(load().kvq_baseline_page_bytes(int(fp8)))
+
+
+def kvq_fill_pages_fp16(cfg, k, v, cu_seqlens, num_seqs, max_seq_len, kv_heads, block_table, max_blocks,
+                        pool_k, pool_v, stream=None):
+    _check(load().kvq_fill_pages_fp16(ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs,
+                                      max_seq_len, kv_heads, _ptr(block_table), max_blocks, _ptr(pool_k),
+                                      _ptr(pool_v), _stream(stream)))
+
+
+def kvq_fill_pages_fp8(cfg, k, v, cu_seqlens, num_seqs, max_seq_len, kv_heads, block_table, max_blocks,
+                       pool_k, pool_v, k_scale, v_scale, stream=None):
+    _check(load().kvq_fill_pages_fp8(ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs,
+                                     max_seq_len, kv_heads, _ptr(block_table), max_blocks, _ptr(pool_k),
+                                     _ptr(pool_v), float(k_scale), float(v_scale), _stream(stream)))
+
+
+def kvq_baseline_workspace_bytes(cfg, num_seqs, q_heads, kv_heads, max_seq_len) -> int:
+    return int(load().kvq_baseline_workspace_bytes(ctypes.byref(cfg), num_seqs, q_heads, kv_heads,
+                                                   max_seq_len))
+
+
+def kvq_paged_decode_attn_fp16(cfg, q, num_seqs, q_heads, kv_heads, block_table, max_blocks, seq_lens,
+                               max_seq_len, pool_k, pool_v, sm_scale, out, workspace, workspace_bytes,
+                               stream=None):
+    _check(load().kvq_paged_decode_attn_fp16(ctypes.byref(cfg), _ptr(q), num_seqs, q_heads, kv_heads,
+                                             _ptr(block_table), max_blocks, _ptr(seq_lens), max_seq_len,
+                                             _ptr(pool_k), _ptr(pool_v), float(sm_scale), _ptr(out),
+                                             _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kvq_paged_decode_attn_fp8(cfg, q, num_seqs, q_heads, kv_heads, block_table, max_blocks, seq_lens,
+                              max_seq_len, pool_k, pool_v, k_scale, v_scale, sm_scale, out, workspace,
+                              workspace_bytes, stream=None):
+    _check(load().kvq_paged_decode_attn_fp8(ctypes.byref(cfg), _ptr(q), num_seqs, q_heads, kv_heads,
+                                            _ptr(block_table), max_blocks, _ptr(seq_lens), max_seq_len,
+                                            _ptr(pool_k), _ptr(pool_v), float(k_scale), float(v_scale),
+                                            float(sm_scale), _ptr(out), _ptr(workspace), workspace_bytes,
+                                            _stream(stream)))

@@ -11,8 +11,10 @@ import math
 import torch
 
 from . import _lib
-from ._lib import (config, kvq_append_and_requant, kvq_decode_workspace_bytes,  # noqa: F401
-                   kvq_dequantize, kvq_paged_decode_attn, kvq_quantize_tiles,
+from ._lib import (config, kvq_append_and_requant, kvq_baseline_page_bytes,  # noqa: F401
+                   kvq_baseline_workspace_bytes, kvq_decode_workspace_bytes, kvq_dequantize,
+                   kvq_fill_pages_fp8, kvq_fill_pages_fp16, kvq_paged_decode_attn,
+                   kvq_paged_decode_attn_fp8, kvq_paged_decode_attn_fp16, kvq_quantize_tiles,
                    kvq_quantize_to_pages, kvq_slot_bytes)
 
 HEAD_DIM = 128
@@ -92,4 +94,51 @@ class PagedCache:
         kvq_paged_decode_attn(self.cfg, q.contiguous(), s, hq, self.kv_heads, self.block_table,
                               self.max_blocks, seq_lens, int(max_seq_len), self.pool_k, self.pool_v, sm,
                               out, workspace, workspace.numel())
+        return out
+
+
+class BaselineCache:
+    """fp16 or fp8 (E4M3, one scale per tensor) page pools of one layer, the
+    uncompressed and 8-bit modes the quantized cache is compared with."""
+
+    def __init__(self, num_pages: int, kv_heads: int, block_table: torch.Tensor, num_seqs: int,
+                 fp8: bool = False, k_scale: float = 1.0, v_scale: float = 1.0, device="cuda"):
+        self.cfg = config()
+        self.fp8 = fp8
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.kv_heads = kv_heads
+        self.num_seqs = num_seqs
+        self.block_table = block_table.to(device=device, dtype=torch.int32).contiguous()
+        self.max_blocks = self.block_table.shape[1]
+        dt = torch.uint8 if fp8 else torch.float16
+        self.pool_k = torch.zeros((num_pages, kv_heads, PAGE_TOKENS * HEAD_DIM), dtype=dt, device=device)
+        self.pool_v = torch.zeros_like(self.pool_k)
+
+    def fill(self, k, v, cu_seqlens, max_seq_len):
+        _require_cuda(k, v, cu_seqlens)
+        args = (self.cfg, k.contiguous(), v.contiguous(), cu_seqlens, self.num_seqs, int(max_seq_len),
+                self.kv_heads, self.block_table, self.max_blocks, self.pool_k, self.pool_v)
+        if self.fp8:
+            kvq_fill_pages_fp8(*args, self.k_scale, self.v_scale)
+        else:
+            kvq_fill_pages_fp16(*args)
+
+    def workspace(self, q_heads, max_seq_len):
+        nbytes = kvq_baseline_workspace_bytes(self.cfg, self.num_seqs, q_heads, self.kv_heads, int(max_seq_len))
+        return torch.empty(max(nbytes, 4), dtype=torch.uint8, device=self.pool_k.device)
+
+    def decode(self, q, seq_lens, max_seq_len, out=None, workspace=None, sm_scale=None):
+        _require_cuda(q, seq_lens)
+        s, hq, d = q.shape
+        if out is None:
+            out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(hq, max_seq_len)
+        sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        args = (self.cfg, q.contiguous(), s, hq, self.kv_heads, self.block_table, self.max_blocks, seq_lens,
+                int(max_seq_len), self.pool_k, self.pool_v)
+        if self.fp8:
+            kvq_paged_decode_attn_fp8(*args, self.k_scale, self.v_scale, sm, out, workspace, workspace.numel())
+        else:
+            kvq_paged_decode_attn_fp16(*args, sm, out, workspace, workspace.numel())
         return out

@@ -67,7 +67,7 @@ int tiles_per_partition(int num_seqs, int kv_heads, int max_seq_len, int tile) {
   long tpp = (total + 511) / 512;
   if (tpp < 4) tpp = 4;
   if (tpp > 64) tpp = 64;
-  if (tpp < (tiles + 1023) / 1024) tpp = (tiles + 1023) / 1024;
+  if (tpp < (tiles + 1023) / 1024) tpp = (tiles + 1023) / 1024;  // > 64 only past 65536 tiles
   if (tpp > tiles) tpp = tiles > 0 ? tiles : 1;
   return (int)tpp;
 }
@@ -247,6 +247,8 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
     return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const int tpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, tile);
   const int parts = max_partitions(max_seq_len, tile, tpp);
+  if (tpp > 64 || parts > 1024)
+    return fail(KVQ_ERR_UNSUPPORTED, "max_seq_len %d is beyond 65536 tiles", max_seq_len);
   kvq::DecodeArgs a{};
   a.q = q;
   a.block_table = block_table;
@@ -265,8 +267,135 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
   a.max_parts = parts;
   a.max_tiles = (max_seq_len + tile - 1) / tile;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.unit_tokens = tile;
+  a.out_scale = 1.0f;
   return launched(kvq::launch_decode(a, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
                   "kvq_paged_decode_attn");
+}
+
+size_t kvq_baseline_page_bytes(int32_t fp8) { return (size_t)kvq::kPage * kvq::kHeadDim * (fp8 ? 1 : 2); }
+
+static kvq_status fill_baseline(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
+                                const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seq_len,
+                                int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,
+                                void* pool_k, void* pool_v, bool fp8, float k_scale, float v_scale,
+                                void* stream, const char* what) {
+  KVQ_TRY(check_config(cfg, false));
+  KVQ_NONNULL(k);
+  KVQ_NONNULL(v);
+  KVQ_NONNULL(cu_seqlens);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  if (num_seqs <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (kv_heads > 65535 || num_seqs > 65535) return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  if ((max_seq_len + kvq::kPage - 1) / kvq::kPage > max_blocks)
+    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens", max_blocks, max_seq_len);
+  if (fp8 && !(k_scale > 0.f && v_scale > 0.f)) return fail(KVQ_ERR_ARG, "fp8 scales must be > 0");
+  kvq::BaseFillArgs a{k, v, cu_seqlens, block_table, max_blocks, kv_heads, (uint8_t*)pool_k, (uint8_t*)pool_v,
+                      k_scale, v_scale};
+  return launched(kvq::launch_fill_baseline(a, fp8, num_seqs, max_seq_len, (hipStream_t)stream), what);
+}
+
+kvq_status kvq_fill_pages_fp16(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seq_len,
+                               int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,
+                               void* pool_k, void* pool_v, void* stream) {
+  return fill_baseline(cfg, k, v, cu_seqlens, num_seqs, max_seq_len, kv_heads, block_table, max_blocks,
+                       pool_k, pool_v, false, 1.f, 1.f, stream, "kvq_fill_pages_fp16");
+}
+
+kvq_status kvq_fill_pages_fp8(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seq_len,
+                              int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,
+                              void* pool_k, void* pool_v, float k_scale, float v_scale, void* stream) {
+  return fill_baseline(cfg, k, v, cu_seqlens, num_seqs, max_seq_len, kv_heads, block_table, max_blocks,
+                       pool_k, pool_v, true, k_scale, v_scale, stream, "kvq_fill_pages_fp8");
+}
+
+size_t kvq_baseline_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t q_heads,
+                                    int32_t kv_heads, int32_t max_seq_len) {
+  if (check_config(cfg, false) != KVQ_OK) return 0;
+  if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0) return 0;
+  const int tpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, 64);
+  const int parts = max_partitions(max_seq_len, 64, tpp);
+  return (size_t)num_seqs * q_heads * parts * (kvq::kHeadDim + 2) * sizeof(float);
+}
+
+static kvq_status decode_baseline(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs, int32_t q_heads,
+                                  int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* seq_lens, int32_t max_seq_len, const void* pool_k,
+                                  const void* pool_v, float sm_scale, bool fp8, float k_scale, float v_scale,
+                                  float* out, void* workspace, size_t workspace_bytes, void* stream,
+                                  const char* what) {
+  KVQ_TRY(check_config(cfg, false));
+  KVQ_NONNULL(q);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(seq_lens);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  KVQ_NONNULL(out);
+  KVQ_NONNULL(workspace);
+  if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, q_heads, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (q_heads % kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "q_heads %d is not a multiple of kv_heads %d", q_heads, kv_heads);
+  const int group = q_heads / kv_heads;
+  if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d larger than 16", group);
+  if (kv_heads > 65535 || num_seqs > 65535) return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  if ((max_seq_len + kvq::kPage - 1) / kvq::kPage > max_blocks)
+    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens", max_blocks, max_seq_len);
+  if (fp8 && !(k_scale > 0.f && v_scale > 0.f)) return fail(KVQ_ERR_ARG, "fp8 scales must be > 0");
+  const size_t need = kvq_baseline_workspace_bytes(cfg, num_seqs, q_heads, kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const int tpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, 64);
+  const int parts = max_partitions(max_seq_len, 64, tpp);
+  if (tpp > 64 || parts > 1024)
+    return fail(KVQ_ERR_UNSUPPORTED, "max_seq_len %d is beyond 65536 blocks of 64 tokens", max_seq_len);
+  kvq::DecodeArgs a{};
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.pool_k = (const uint8_t*)pool_k;
+  a.pool_v = (const uint8_t*)pool_v;
+  a.out = out;
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = (float*)workspace + (size_t)num_seqs * q_heads * parts * kvq::kHeadDim;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks;
+  a.tiles_per_part = tpp;
+  a.max_parts = parts;
+  a.max_tiles = (max_seq_len + 63) / 64;
+  a.sm_scale_log2 = sm_scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;
+  a.unit_tokens = 64;
+  a.out_scale = fp8 ? v_scale : 1.f;
+  return launched(kvq::launch_decode_baseline(a, fp8, (hipStream_t)stream), what);
+}
+
+kvq_status kvq_paged_decode_attn_fp16(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs,
+                                      int32_t q_heads, int32_t kv_heads, const int32_t* block_table,
+                                      int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                                      const void* pool_k, const void* pool_v, float sm_scale, float* out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_baseline(cfg, q, num_seqs, q_heads, kv_heads, block_table, max_blocks, seq_lens, max_seq_len,
+                         pool_k, pool_v, sm_scale, false, 1.f, 1.f, out, workspace, workspace_bytes, stream,
+                         "kvq_paged_decode_attn_fp16");
+}
+
+kvq_status kvq_paged_decode_attn_fp8(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs,
+                                     int32_t q_heads, int32_t kv_heads, const int32_t* block_table,
+                                     int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                                     const void* pool_k, const void* pool_v, float k_scale, float v_scale,
+                                     float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return decode_baseline(cfg, q, num_seqs, q_heads, kv_heads, block_table, max_blocks, seq_lens, max_seq_len,
+                         pool_k, pool_v, sm_scale, true, k_scale, v_scale, out, workspace, workspace_bytes,
+                         stream, "kvq_paged_decode_attn_fp8");
 }
 
 kvq_status kvq_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream) {

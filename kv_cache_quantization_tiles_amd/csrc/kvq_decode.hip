@@ -71,14 +71,30 @@ __device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, uns
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
-__device__ __forceinline__ float group_max(float v) {  // over the 4 lanes l, l^16, l^32, l^48
-  v = fmaxf(v, lane_xor<16>(v));
-  return fmaxf(v, xor32(v));
+// v_permlane16_swap / v_permlane32_swap with both operands a copy of v return
+// a pair whose two members are v and the value of lane l^16 (resp. l^32) in
+// some order, so a symmetric op over the pair reduces over that lane pair in
+// the VALU (no LDS round trip).
+__device__ __forceinline__ float sum16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
 }
-__device__ __forceinline__ float group_sum(float v) {
-  v += lane_xor<16>(v);
-  return v + xor32(v);
+__device__ __forceinline__ float sum32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
 }
+__device__ __forceinline__ float max16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+__device__ __forceinline__ float max32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+}
+
+// Reductions over the 4 lanes l, l^16, l^32, l^48 (one query head's lanes).
+__device__ __forceinline__ float group_max(float v) { return max32(max16(v)); }
+__device__ __forceinline__ float group_sum(float v) { return sum32(sum16(v)); }
 
 // Channel of A-operand slot (chunk ch, lane group grp, slot j) for K codes.
 template <int BITS>
@@ -101,8 +117,11 @@ struct TileMeta {
   static constexpr int PER_LANE = (PIECES + 63) / 64;
 };
 
+constexpr int kMaxTilesPerPart = 64;
+
 template <int T>
 struct alignas(16) DecodeSmem {
+  int32_t pages[kMaxTilesPerPart * (T / kPage)];  // the partition's page ids
   union {
     struct {
       float hq[16][kHeadDim];                                  // H q of the group, orthonormal
@@ -121,16 +140,14 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, lane_xor<2>(v));
   v = fmaxf(v, lane_xor<4>(v));
   v = fmaxf(v, lane_xor<8>(v));
-  v = fmaxf(v, lane_xor<16>(v));
-  return fmaxf(v, xor32(v));
+  return group_max(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
   v += lane_xor<1>(v);
   v += lane_xor<2>(v);
   v += lane_xor<4>(v);
   v += lane_xor<8>(v);
-  v += lane_xor<16>(v);
-  return v + xor32(v);
+  return group_sum(v);
 }
 
 // One workgroup of 4 waves per (partition of tiles, kv head, sequence); wave
@@ -161,13 +178,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   const int tile_end = min(ntiles, tile_begin + A.tiles_per_part);
   if (tile_begin >= tile_end) return;  // uniform over the workgroup
   const int H = A.kv_heads;
-  const int32_t* pages = A.block_table + (size_t)seq * A.max_blocks;
   const bool real = n16 < G;
+  // the partition's page ids, staged once in LDS (a scalar load per tile would
+  // make every later LDS wait also wait for global memory)
+  {
+    const int32_t* row = A.block_table + (size_t)seq * A.max_blocks + tile_begin * NP;
+    const int n = (tile_end - tile_begin) * NP;
+    for (int i = threadIdx.x; i < n; i += 64 * kWaves) sm.pages[i] = row[i];
+  }
+  __syncthreads();
 
   // ------------------------------------------------ prefetch of one tile
   u32x4 ck[NP], cv[NP], mpre[TM::PER_LANE];
   auto issue = [&](int tl) {
-    const int32_t* tp = pages + tl * NP;
+    const int32_t* tp = sm.pages + (tl - tile_begin) * NP;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const size_t pg = (size_t)tp[p] * H + kvh;
@@ -290,30 +314,39 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     const float sB = c0 * qsum;
 
     // -------------------------------------------- scores of the tile's pages
-    float s[NP][4];
+    // chunk-major order: the NP pages' accumulation chains interleave
+    f32x4 d[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      f32x4 d{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < NP; ++p) d[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
+    for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
         f16x8 a;
         if (BK == 4) {
           const unsigned x = kc[p][ch];
-          a = as_f16x8(code_pair<4, 0>(x, m4, one), code_pair<4, 1>(x, m4, one), code_pair<4, 2>(x, m4, one), code_pair<4, 3>(x, m4, one));
+          a = as_f16x8(code_pair<4, 0>(x, m4, one), code_pair<4, 1>(x, m4, one), code_pair<4, 2>(x, m4, one),
+                       code_pair<4, 3>(x, m4, one));
         } else {
           const unsigned x = kc[p][ch >> 1];
           if (ch & 1)
-            a = as_f16x8(code_pair<2, 4>(x, m2, one), code_pair<2, 5>(x, m2, one), code_pair<2, 6>(x, m2, one), code_pair<2, 7>(x, m2, one));
+            a = as_f16x8(code_pair<2, 4>(x, m2, one), code_pair<2, 5>(x, m2, one), code_pair<2, 6>(x, m2, one),
+                         code_pair<2, 7>(x, m2, one));
           else
-            a = as_f16x8(code_pair<2, 0>(x, m2, one), code_pair<2, 1>(x, m2, one), code_pair<2, 2>(x, m2, one), code_pair<2, 3>(x, m2, one));
+            a = as_f16x8(code_pair<2, 0>(x, m2, one), code_pair<2, 1>(x, m2, one), code_pair<2, 2>(x, m2, one),
+                         code_pair<2, 3>(x, m2, one));
         }
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_hi[ch], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_lo[ch], d, 0, 0, 0);
+        d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_hi[ch], d[p], 0, 0, 0);
+        d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_lo[ch], d[p], 0, 0, 0);
       }
+    }
+    float s[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
       const f32x4 S = *reinterpret_cast<const f32x4*>(mK + p * META + 16 * grp);
       const f32x4 O = *reinterpret_cast<const f32x4*>(mK + p * META + 4 * kPage + 16 * grp);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[p][r] = __builtin_fmaf(sA * S[r], d[r], sB * __builtin_fmaf(-64.f, S[r], O[r]));
+      for (int r = 0; r < 4; ++r) s[p][r] = __builtin_fmaf(sA * S[r], d[p][r], sB * __builtin_fmaf(-64.f, S[r], O[r]));
     }
     if (tile == ntiles - 1 && (L % T) != 0) {
 #pragma unroll
@@ -461,14 +494,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   }
 }
 
-// Merge the partitions of one (sequence, query head) and rotate back:
-// out = H (sum_p w_p acc_p) / (sum_p w_p l_p), w_p = 2^(m_p - max m).
-template <int T>
+// Merge the partitions of one (sequence, query head):
+// out = s H (sum_p w_p acc_p) / (sum_p w_p l_p), w_p = 2^(m_p - max m), with
+// the Hadamard H applied for pages quantized in the rotated basis (ROT) and
+// s = A.out_scale.
+template <bool ROT>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
   __shared__ float wts[1024];
   const int lane = threadIdx.x;
   const int seq = blockIdx.x / A.q_heads;
   const int L = A.seq_lens[seq];
+  const int T = A.unit_tokens;
   const int ntiles = min((L + T - 1) / T, A.max_tiles);
   const int nparts = min((ntiles + A.tiles_per_part - 1) / A.tiles_per_part, A.max_parts);
   const size_t base = (size_t)blockIdx.x * A.max_parts;
@@ -500,7 +536,14 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
     x0 = __builtin_fmaf(wts[p], src[p * kHeadDim + lane], x0);
     x1 = __builtin_fmaf(wts[p], src[p * kHeadDim + lane + 64], x1);
   }
-  const float inv = kInvSqrtD / den;
+  float* o = A.out + (size_t)blockIdx.x * kHeadDim;
+  if (!ROT) {
+    const float inv = den > 0.f ? A.out_scale / den : 0.f;   // an empty sequence gives zeros
+    o[lane] = x0 * inv;
+    o[lane + 64] = x1 * inv;
+    return;
+  }
+  const float inv = den > 0.f ? A.out_scale * kInvSqrtD / den : 0.f;
   // channels lane (bit 6 = 0) and lane + 64 (bit 6 = 1)
   float y0 = x0 + x1, y1 = x0 - x1;
   auto stage = [&](float& v, float partner, int bit) {
@@ -512,7 +555,6 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
   stage(y0, lane_xor<8>(y0), 8);   stage(y1, lane_xor<8>(y1), 8);
   stage(y0, lane_xor<16>(y0), 16); stage(y1, lane_xor<16>(y1), 16);
   stage(y0, xor32(y0), 32);        stage(y1, xor32(y1), 32);
-  float* o = A.out + (size_t)blockIdx.x * kHeadDim;
   o[lane] = y0 * inv;
   o[lane + 64] = y1 * inv;
 }
@@ -537,6 +579,14 @@ hipError_t by_bits(int bits, F&& f) {
 
 }  // namespace
 
+hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s) {
+  DecodeArgs b = a;
+  b.unit_tokens = unit_tokens;
+  if (rotate) hipLaunchKernelGGL(combine_kernel<true>, dim3(a.num_seqs * a.q_heads), dim3(64), 0, s, b);
+  else hipLaunchKernelGGL(combine_kernel<false>, dim3(a.num_seqs * a.q_heads), dim3(64), 0, s, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
     return by_bits(bits_k, [&](auto BK) {
@@ -545,8 +595,7 @@ hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, 
         hipLaunchKernelGGL((decode_kernel<T(), BK(), BV()>), grid, dim3(64 * kWaves), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((combine_kernel<T()>), dim3(a.num_seqs * a.q_heads), dim3(64), 0, s, a);
-        return hipGetLastError();
+        return launch_combine(a, T(), true, s);
       });
     });
   });

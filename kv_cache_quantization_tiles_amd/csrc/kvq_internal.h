@@ -69,7 +69,22 @@ struct DecodeArgs {
   int tiles_per_part;
   int max_parts;
   int max_tiles;               // ceil(max_seq_len / T): no tile past it is read
-  float sm_scale_log2;        // sm_scale * log2(e)
+  float sm_scale_log2;        // sm_scale * log2(e) (times the K scale for fp8 pages)
+  int unit_tokens;            // tokens per partition unit (tile, or 64 for the baselines)
+  float out_scale;            // output multiplier (the V scale for fp8 pages, else 1)
+};
+
+struct BaseFillArgs {
+  const uint16_t* k;          // [total][Hkv][D] fp16
+  const uint16_t* v;
+  const int32_t* cu_seqlens;
+  const int32_t* block_table;
+  int max_blocks;
+  int kv_heads;
+  uint8_t* pool_k;            // [pages][Hkv][16][D] fp16 or E4M3
+  uint8_t* pool_v;            // [pages][Hkv][D][16]
+  float k_scale;
+  float v_scale;
 };
 
 hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s);
@@ -80,6 +95,9 @@ hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, i
 hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s);
+hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, int max_seq_len, hipStream_t s);
+hipError_t launch_decode_baseline(const DecodeArgs& a, bool fp8, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -88,3 +88,25 @@ def test_decode_validation(lib):
                                      None) == L.KVQ_ERR_WORKSPACE
     assert "needed" in L.kvq_last_error()
     assert lib.kvq_bandwidth_probe(16, 16, 15, None) == L.KVQ_ERR_ARG
+
+
+def test_baseline_validation(lib):
+    cfg = L.config()
+    c = ctypes.byref(cfg)
+    assert L.kvq_baseline_page_bytes(False) == 16 * 128 * 2
+    assert L.kvq_baseline_page_bytes(True) == 16 * 128
+    need = L.kvq_baseline_workspace_bytes(cfg, 4, 32, 8, 16385)
+    assert need > 0 and need % (130 * 4) == 0
+    assert L.kvq_baseline_workspace_bytes(cfg, 0, 32, 8, 16385) == 0
+    # fp8 scales must be positive
+    assert lib.kvq_fill_pages_fp8(c, 16, 16, 16, 1, 64, 1, 16, 4, 16, 16, 0.0, 1.0, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_paged_decode_attn_fp8(c, 16, 4, 32, 8, 16, 1028, 16, 16385, 16, 16, 1.0, -1.0, 0.1, 16, 16,
+                                         need, None) == L.KVQ_ERR_ARG
+    # block table too narrow, NULL pool
+    assert lib.kvq_fill_pages_fp16(c, 16, 16, 16, 1, 65, 1, 16, 4, 16, 16, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_fill_pages_fp16(c, 16, 16, 16, 1, 64, 1, 16, 4, None, 16, None) == L.KVQ_ERR_ARG
+    # workspace too small, group too large
+    assert lib.kvq_paged_decode_attn_fp16(c, 16, 4, 32, 8, 16, 1028, 16, 16385, 16, 16, 0.1, 16, 16, need - 1,
+                                          None) == L.KVQ_ERR_WORKSPACE
+    assert lib.kvq_paged_decode_attn_fp16(c, 16, 4, 64, 2, 16, 1028, 16, 16385, 16, 16, 0.1, 16, 16, 1 << 30,
+                                          None) == L.KVQ_ERR_UNSUPPORTED

@@ -249,3 +249,65 @@ def test_append_then_decode_matches_oracle():
     ref = orc.paged_decode_attn(q, table, lens + 1, cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy(),
                                 64, 4, 4)
     pu.assert_attn(out.cpu().numpy(), ref, "append+decode")
+
+
+BASELINE_CASES = [
+    # (recipe, lens, hkv, hq)
+    (1, (1024,), 1, 8),
+    (2, (700, 513, 64, 1), 2, 8),
+    (5, (611, 200, 33, 96, 1000, 17), 2, 16),
+    (2, (300,), 1, 1),
+    (2, (257, 40), 1, 16),
+    (2, (5000, 37), 2, 8),      # several partitions per sequence
+]
+
+
+def _baseline_prefill(wl, fp8):
+    k = inputs.gen_kv(wl, "K")
+    v = inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    ks, vs = (orc.fp8_scale(k), orc.fp8_scale(v)) if fp8 else (1.0, 1.0)
+    cache = api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs, fp8, ks, vs)
+    cache.fill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+               torch.from_numpy(wl.cu_seqlens()).cuda(), max(wl.seq_lens))
+    torch.cuda.synchronize()
+    return k, v, table, npages, ks, vs, cache
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["fp16", "fp8"])
+@pytest.mark.parametrize("case", BASELINE_CASES)
+def test_baseline_fill_and_decode_parity(case, fp8):
+    recipe, lens, hkv, hq = case
+    wl = _paged_workload(recipe, lens, hkv, hq, 64, 4, 4, 3)
+    k, v, table, npages, ks, vs, cache = _baseline_prefill(wl, fp8)
+    # the pages: byte-exact, unused pages and rows past the ends included
+    ref_pk = orc.new_baseline_pool(npages, hkv, fp8)
+    ref_pv = orc.new_baseline_pool(npages, hkv, fp8)
+    orc.fill_pages_baseline(k, v, wl.cu_seqlens(), table, ref_pk, ref_pv, fp8, ks, vs)
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    np.testing.assert_array_equal(gpk.view(np.uint8), ref_pk.view(np.uint8))
+    np.testing.assert_array_equal(gpv.view(np.uint8), ref_pv.view(np.uint8))
+    # one decode step over them
+    q = inputs.gen_q(wl)
+    seq_lens = np.array(wl.seq_lens, np.int32)
+    out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(seq_lens).cuda(), max(lens))
+    torch.cuda.synchronize()
+    ref = orc.paged_decode_attn_baseline(q, table, seq_lens, ref_pk, ref_pv, fp8, ks, vs)
+    err = pu.assert_attn(out.cpu().numpy(), ref, f"baseline {'fp8' if fp8 else 'fp16'} {case}")
+    print(f"[attn] baseline {'fp8' if fp8 else 'fp16'} {case}: max abs err {err:.2e}", flush=True)
+
+
+def test_baseline_decode_is_deterministic_and_order_free():
+    wl = _paged_workload(2, (700, 513, 64, 1), 2, 8, 64, 4, 4, 3)
+    q = torch.from_numpy(inputs.gen_q(wl)).cuda()
+    sl = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    k = torch.from_numpy(inputs.gen_kv(wl, "K")).cuda()
+    v = torch.from_numpy(inputs.gen_kv(wl, "V")).cuda()
+    cu = torch.from_numpy(wl.cu_seqlens()).cuda()
+    outs = []
+    for tab in (inputs.block_table, inputs.identity_block_table, inputs.block_table):
+        table, npages = tab(wl)
+        cache = api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+        cache.fill(k, v, cu, max(wl.seq_lens))
+        outs.append(cache.decode(q, sl, max(wl.seq_lens)))
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
