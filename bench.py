@@ -152,6 +152,81 @@ def cpu_baseline(wl, max_seqs: int):
             "machine_cores": os.cpu_count()}
 
 
+# ----------------------------------------------------------------------------- long-context comparison
+def long_context_leg(n_iter: int = 10):
+    """One layer of the 36-layer, 6 x 128K Qwen3-4B-shaped workload (8 kv /
+    32 query heads, tile 128): the decode-attention step on fp16 pages, fp8
+    (E4M3, per-tensor scale) pages, and 4-bit and 2-bit quantized pages, all
+    filled from the same inputs.  Attention only (no append), context 131072,
+    pages far larger than the 256 MB last-level cache, so every call streams
+    from HBM.  tok/s is for all 36 layers (36 such steps per token)."""
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+
+    wl = inputs.workload(4)
+    dev = torch.device("cuda:0")
+    table, npages = inputs.block_table(wl, capacity_tokens=max(wl.seq_lens))
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    max_len = max(wl.seq_lens)
+    cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+    q = torch.from_numpy(inputs.gen_q(wl)).to(dev)
+    out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+    k = inputs.gen_kv_device(wl, "K", device=dev)
+    v = inputs.gen_kv_device(wl, "V", device=dev)
+    token_heads = wl.total_tokens * wl.hkv
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    modes = {}
+    for name in ("fp16", "fp8", "kvq4", "kvq2"):
+        if name in ("fp16", "fp8"):
+            fp8 = name == "fp8"
+            ks = float(k.abs().max()) / 448.0 if fp8 else 1.0
+            vs = float(v.abs().max()) / 448.0 if fp8 else 1.0
+            cache = api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs, fp8, ks, vs)
+            fill_ms = timed(lambda: cache.fill(k, v, cu, max_len), 3)
+            per_token_head = 2 * 128 * (1 if fp8 else 2)
+            fill_bytes = token_heads * (2 * 2 * D + per_token_head)
+        else:
+            bits = 4 if name == "kvq4" else 2
+            cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
+            cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+            fill_ms = timed(lambda: cache.quantize_prefill(k, v, cu, max_len), 3)
+            per_token_head = 2 * slot_bytes_per_token(bits, wl.tile_tokens)
+            fill_bytes = 2 * quantize_bytes(token_heads, bits, wl.tile_tokens)
+        ws = cache.workspace(wl.hq, max_len)
+        dec_ms = timed(lambda: cache.decode(q, lens, max_len, out=out, workspace=ws), n_iter)
+        dbytes = token_heads * per_token_head
+        modes[name] = {"decode_attn_ms": round(dec_ms, 4),
+                       "decode_GBps": round(dbytes / (dec_ms * 1e-3) / 1e9, 1),
+                       "decode_hbm_frac": round(dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "kv_bytes_per_layer_GB": round(dbytes / 1e9, 3),
+                       "tok_per_s_36_layers_attn_only": round(wl.num_seqs / (wl.layers * dec_ms * 1e-3), 1),
+                       "fill_ms": round(fill_ms, 3),
+                       "fill_GBps": round(fill_bytes / (fill_ms * 1e-3) / 1e9, 1)}
+        del cache, ws
+        torch.cuda.empty_cache()
+    del k, v
+    torch.cuda.empty_cache()
+    base = modes["fp16"]["decode_attn_ms"]
+    for m in modes.values():
+        m["speedup_vs_fp16"] = round(base / m["decode_attn_ms"], 3)
+    return {"workload": f"{wl.name}, one layer of {wl.layers}", "num_seqs": wl.num_seqs, "context": max_len,
+            "kv_heads": wl.hkv, "q_heads": wl.hq, "tile_tokens": wl.tile_tokens, "iters": n_iter,
+            "modes": modes,
+            "pages_context": "A100-80GB, whole Qwen3-4B at 128K: 66.6 / 105.0 / 140.9 tok/s for "
+                             "fp16 / fp8 / compressed KV (other hardware, end-to-end; context only)"}
+
+
 # ----------------------------------------------------------------------------- GPU leg
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -159,8 +234,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--cpu-seqs", type=int, default=1, help="sequences in the CPU-oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the fp16 / fp8 / 4-bit / 2-bit comparison at 6 x 128K")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards "
@@ -284,6 +361,9 @@ def main():
                      "traffic": measured_traffic("kvq_quantize.hip", f"traffic-quantize_paged_kernel-{wl.name}.json")},
         "cpu_baseline": cpu,
     }
+    del caches, ks, vs, src, dst
+    torch.cuda.empty_cache()
+    rec["long_context"] = None if args.no_long_context else long_context_leg()
     print(json.dumps(rec), flush=True)
 
 

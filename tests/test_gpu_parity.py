@@ -311,3 +311,111 @@ def test_baseline_decode_is_deterministic_and_order_free():
         cache.fill(k, v, cu, max(wl.seq_lens))
         outs.append(cache.decode(q, sl, max(wl.seq_lens)))
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+# ----------------------------------------------------------------------------- full sizes, sampled
+def _sampled_tile_checks(wl, k, v, table, gpk, gpv, rng, n_samples, what):
+    """Complete prefill tiles drawn at random: GPU slots vs the oracle on that tile alone."""
+    cu = wl.cu_seqlens()
+    t = wl.tile_tokens
+    ppt = t // 16
+    tot = [0, 0, 0]
+    for _ in range(n_samples):
+        s = int(rng.integers(wl.num_seqs))
+        h = int(rng.integers(wl.hkv))
+        role = ("K", "V")[int(rng.integers(2))]
+        j = int(rng.integers(wl.seq_lens[s] // t))
+        x = (k if role == "K" else v)[cu[s] + j * t:cu[s] + (j + 1) * t, h]
+        bits = wl.bits_k if role == "K" else wl.bits_v
+        ref = orc.quantize_tile(x, bits, wl.iters)
+        gp = gpk if role == "K" else gpv
+        _, gc, ga, gs, go = orc.read_sequence(gp, table[s, j * ppt:(j + 1) * ppt], t, h, role, bits, t)
+        c = pu.compare_codes(gc, ref.codes, ref.pre, f"{what} s{s} h{h} {role} tile{j}")
+        tot = [a + b for a, b in zip(tot, c)]
+        pu.check_tile_metadata(ref.codes, ga[0], gs, go, ref.alpha, ref.scale, ref.offset, orc.dequantize_tile,
+                               f"{what} s{s} h{h} {role} tile{j}")
+    _report(f"{what} sampled tiles", tot)
+
+
+def _sampled_decode_checks(wl, q, table, lens, gpk, gpv, got, pairs, what):
+    g = wl.group
+    for s, kh in pairs:
+        ref = orc.paged_decode_attn(q[s:s + 1, kh * g:(kh + 1) * g], table[s:s + 1], lens[s:s + 1],
+                                    gpk[:, kh:kh + 1], gpv[:, kh:kh + 1], wl.tile_tokens, wl.bits_k, wl.bits_v)
+        err = pu.assert_attn(got[s, kh * g:(kh + 1) * g], ref[0], f"{what} s{s} kv head {kh}")
+        print(f"[attn] {what} s{s} kv head {kh} (L={int(lens[s])}): max abs err {err:.2e}", flush=True)
+
+
+def test_full_size_qwen3_4b_layer_4x16k_sampled():
+    """The 4 x 16K, 8/32-head layer in the launch configuration the bench times:
+    quantize every page, append one token, one decode step; tiles, appended
+    rows and attention outputs sampled against the oracle."""
+    wl = inputs.workload(2)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    lens = np.array(wl.seq_lens, np.int32)
+    kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
+    cache.append(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens).cuda())
+    q = inputs.gen_q(wl)
+    out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(lens + 1).cuda(), int(lens.max()) + 1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    rng = np.random.default_rng(42)
+    _sampled_tile_checks(wl, k, v, table, gpk, gpv, rng, 32, "4x16k")
+    # the appended token opens tile 256 of every sequence: a one-row tile
+    t = wl.tile_tokens
+    for s in range(wl.num_seqs):
+        j = int(lens[s]) // t
+        for h in range(wl.hkv):
+            for role, new, gp, bits in (("K", kn, gpk, wl.bits_k), ("V", vn, gpv, wl.bits_v)):
+                ref = orc.quantize_tile(new[s, h][None], bits, wl.iters)
+                _, gc, ga, gs, go = orc.read_sequence(gp, table[s, j * 4:(j + 1) * 4], 1, h, role, bits, t)
+                pu.compare_codes(gc, ref.codes, ref.pre, f"append s{s} h{h} {role}")
+                pu.check_tile_metadata(ref.codes, ga[0], gs, go, ref.alpha, ref.scale, ref.offset,
+                                       orc.dequantize_tile, f"append s{s} h{h} {role}")
+    _sampled_decode_checks(wl, q, table, lens + 1, gpk, gpv, got, [(0, 0), (3, 7), (1, 4)], "4x16k decode")
+    assert np.isfinite(got).all()
+
+
+def test_full_size_qwen3_32b_tp2_burst_sampled():
+    """One GPU's share of the 32 x 16K burst (4 kv heads, 32 query heads):
+    quantize the prefill, then 66 decode steps of append + attend (every
+    sequence crosses a tile boundary); sampled checks at the end."""
+    wl = inputs.workload(3)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    lens = np.array(wl.seq_lens, np.int32)
+    q = None
+    steps = 66
+    d_lens = torch.from_numpy(lens).cuda()
+    for step in range(steps):
+        kn = torch.from_numpy(inputs.gen_decode_kv(wl, "K", step)).cuda()
+        vn = torch.from_numpy(inputs.gen_decode_kv(wl, "V", step)).cuda()
+        cache.append(kn, vn, d_lens)
+        d_lens = d_lens + 1
+        q = inputs.gen_q(wl, step)
+        out = cache.decode(torch.from_numpy(q).cuda(), d_lens, int(lens.max()) + step + 1)
+    torch.cuda.synchronize()
+    lens_now = lens + steps
+    got = out.cpu().numpy()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    rng = np.random.default_rng(43)
+    _sampled_tile_checks(wl, k, v, table, gpk, gpv, rng, 24, "32x16k")
+    # the last (partial) tile of two sequences, rebuilt by the oracle from its fp16 rows
+    t = wl.tile_tokens
+    for s in (0, 31):
+        j = int(lens_now[s] - 1) // t
+        rows = []
+        for pos in range(j * t, int(lens_now[s])):
+            if pos < lens[s]:
+                rows.append(k[wl.cu_seqlens()[s] + pos])
+            else:
+                rows.append(inputs.gen_decode_kv(wl, "K", pos - int(lens[s]))[s])
+        x = np.stack(rows)                                   # [n, hkv, 128]
+        for h in range(wl.hkv):
+            ref = orc.quantize_tile(x[:, h], wl.bits_k, wl.iters)
+            n = x.shape[0]
+            _, gc, ga, gs, go = orc.read_sequence(gpk, table[s, j * 4:(j + 1) * 4], n, h, "K", wl.bits_k, t)
+            pu.compare_codes(gc, ref.codes, ref.pre, f"burst last tile s{s} h{h}")
+            pu.check_tile_metadata(ref.codes, ga[0], gs, go, ref.alpha, ref.scale, ref.offset,
+                                   orc.dequantize_tile, f"burst last tile s{s} h{h}")
+    _sampled_decode_checks(wl, q, table, lens_now, gpk, gpv, got, [(0, 0), (31, 3)], "32x16k decode")
