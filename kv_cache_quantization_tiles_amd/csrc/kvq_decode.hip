@@ -14,59 +14,36 @@
 // tile) and on the accumulated output (once per sequence and head), never on
 // the cached tokens.
 //
-// Work split: one wave per (sequence, kv head, partition of tiles).  The
-// group of G query heads sharing the kv head is padded to 16 and both
-// contractions run on v_mfma_f32_16x16x32_f16:
-//   QK:  S^T[t][g] = sum_c K[t][c] W[c][g]: A = 16 tokens of codes (each code
-//        k as the exact fp16 1 + k/64), B = qt split into fp16 hi + lo.
+// Work split: one workgroup of 4 waves per (sequence, kv head, partition of
+// tiles).  The group of G query heads sharing the kv head is padded to 16
+// MFMA columns and both contractions run on v_mfma_f32_16x16x32_f16:
+//   QK:  S^T[t][g] = sum_c K[t][c] W[c][g]: A = 16 tokens of codes, B = qt
+//        split into fp16 hi + lo (two MFMAs into one accumulator).
 //   PV:  O^T[c][g] = sum_t V[t][c] P[t][g]: A = codes of 2 pages (32 tokens),
 //        B = p_t S_t split into fp16 hi + lo.
-// The QK output layout (lane = query head, 4 tokens per lane) is exactly the
-// B layout PV needs, so no shuffle sits between the two.  Codes unpack with
-// two integer ops per pair of codes (shift, and-or) and no conversion.
-// Online softmax runs per tile; partitions are merged by a second kernel that
-// also applies the final Hadamard.
+// Codes enter the MFMA as fp16 denormals: a field masked in place in its
+// 16-bit half reads as (code * 2^e) * 2^-24, exactly, with e fixed by the
+// field's position; the matching 2^-e rides on the query (K side), on the
+// probabilities (V tokens) or on the output fold (V channels).  Unpacking is
+// one AND per two codes.  The QK output layout (lane = query head, 4 tokens
+// per lane) is exactly the B layout PV needs, so no shuffle sits between the
+// two.  Online softmax runs per tile; partitions are merged by a second
+// kernel that also applies the final Hadamard.
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr unsigned kOne = 0x3C003C00u;  // fp16 1.0 in both halves
-
-// Pair of codes from nibble/field position x of both 16-bit halves, moved to
-// mantissa bits 4.. so that the fp16 value is 1 + code/64.  The mask and the
-// fp16 one are passed in VGPRs so that one v_and_or_b32 does the masking.
-template <int BITS, int X>
-__device__ __forceinline__ unsigned code_pair(unsigned w, unsigned mask, unsigned one) {
-  constexpr int shift = 4 - BITS * X;  // > 0: left, < 0: right
-  const unsigned s = (shift >= 0) ? (w << (shift >= 0 ? shift : 0)) : (w >> (shift < 0 ? -shift : 0));
-  unsigned r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(s), "v"(mask), "v"(one));
-  return r;
-}
 
 __device__ __forceinline__ f16x8 as_f16x8(unsigned a, unsigned b, unsigned c, unsigned d) {
   u32x4 v{a, b, c, d};
   return __builtin_bit_cast(f16x8, v);
-}
-
-__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
-  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (unsigned)__builtin_bit_cast(uint16_t, a) | ((unsigned)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
-// hi/lo fp16 split of two fp32 values, returned as (hi pair, lo pair).
-__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
-  const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-  const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-  hi = (unsigned)__builtin_bit_cast(uint16_t, h0) | ((unsigned)__builtin_bit_cast(uint16_t, h1) << 16);
-  lo = (unsigned)__builtin_bit_cast(uint16_t, l0) | ((unsigned)__builtin_bit_cast(uint16_t, l1) << 16);
 }
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
@@ -96,14 +73,6 @@ __device__ __forceinline__ float max32(float v) {
 __device__ __forceinline__ float group_max(float v) { return max32(max16(v)); }
 __device__ __forceinline__ float group_sum(float v) { return sum32(sum16(v)); }
 
-// Channel of A-operand slot (chunk ch, lane group grp, slot j) for K codes.
-template <int BITS>
-__device__ __forceinline__ int k_channel(int ch, int grp, int j) {
-  const int m = j >> 1, hi = j & 1;
-  if (BITS == 4) return 32 * grp + 8 * ch + m + 4 * hi;
-  return 32 * grp + 16 * (ch >> 1) + 4 * (ch & 1) + m + 8 * hi;
-}
-
 constexpr int kWaves = 4;  // waves per decode workgroup
 
 // Metadata of one tile as staged in LDS: the slots' (scale, offset, alpha
@@ -119,13 +88,35 @@ struct TileMeta {
 
 constexpr int kMaxTilesPerPart = 64;
 
-template <int T>
+// Code fields of one 32-bit word (two 16-bit halves), masked in place so that
+// each half reads as the fp16 denormal m * 2^-24 whose mantissa m is the code
+// times the power of two fixed by the field's bit position (field_weight).
+// Fields in bits 8..15 of a half are taken from y = x >> 8.  One AND per pair
+// of codes, no conversion and no offset term.
+template <int BITS, int X>
+__device__ __forceinline__ unsigned code_field(unsigned x, unsigned y) {
+  if (BITS == 4) {
+    constexpr unsigned m = (X & 1) ? 0x00F000F0u : 0x000F000Fu;
+    return ((X < 2) ? x : y) & m;
+  } else {
+    constexpr unsigned m = 0x00030003u << (2 * (X & 3));
+    return ((X < 4) ? x : y) & m;
+  }
+}
+template <int BITS>
+__host__ __device__ constexpr float field_weight(int x) {
+  return BITS == 4 ? ((x & 1) ? 16.f : 1.f) : (float)(1 << (2 * (x & 3)));
+}
+
+template <int T, int U>
 struct alignas(16) DecodeSmem {
   int32_t pages[kMaxTilesPerPart * (T / kPage)];  // the partition's page ids
   union {
     struct {
-      float hq[16][kHeadDim];                                  // H q of the group, orthonormal
-      uint8_t meta[kWaves][2][TileMeta<T>::BYTES];             // per-wave double buffer
+      float hq[4 * U][kHeadDim];                       // (H q)_c / weight of channel c's K field
+      uint8_t meta[kWaves][2][TileMeta<T>::BYTES];     // per-wave double buffer
+      u32x4 qb[kWaves][2][4 * U][16];                  // per-wave QK B operands [hi/lo][head][unit]
+      float cab[kWaves][4 * U][2];                     // per-wave, per head: score factors
     } loop;
     struct {
       float acc[kWaves][16][kHeadDim];
@@ -150,11 +141,46 @@ __device__ __forceinline__ float wave_sum(float v) {
   return group_sum(v);
 }
 
+// Sum / max over aligned groups of N lanes (N <= 16).
+template <int N>
+__device__ __forceinline__ float span_sum(float v) {
+  if (N > 1) v += lane_xor<1>(v);
+  if (N > 2) v += lane_xor<2>(v);
+  if (N > 4) v += lane_xor<4>(v);
+  if (N > 8) v += lane_xor<8>(v);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float span_max(float v) {
+  if (N > 1) v = fmaxf(v, lane_xor<1>(v));
+  if (N > 2) v = fmaxf(v, lane_xor<2>(v));
+  if (N > 4) v = fmaxf(v, lane_xor<4>(v));
+  if (N > 8) v = fmaxf(v, lane_xor<8>(v));
+  return v;
+}
+
+// fp32 pair -> fp16 pair hi (nearest even) and the fp16 pair lo of what is
+// left (x - hi is exact in fp32; v_fma_mix_f32 reads hi's halves as fp16).
+// hi + lo carries x to ~2^-22 relative, without bias.
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const unsigned hb = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, f16x2));
+  float r0, r1;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(hb), "v"(x0));
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r1) : "v"(hb), "v"(x1));
+  hi = hb;
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, f16x2));
+}
+
 // One workgroup of 4 waves per (partition of tiles, kv head, sequence); wave
 // w takes tiles begin + w, begin + w + 4, ...  Each wave prefetches its next
 // tile's codes (registers) and metadata (registers, then LDS) while it works
 // on the current one; the 4 waves' softmax states are merged in LDS at the end.
-template <int T, int BK, int BV>
+//
+// U = 1, 2, 4 for groups of up to 4, 8, 16 query heads.  Per tile, the query
+// fold qt = (H q) * alpha_K runs in a compact layout (lane = head, 8U
+// channels) and reaches the MFMA B layout through LDS; MFMA column n reads
+// head n mod 4U, so columns past the group repeat real heads and need no mask.
+template <int T, int BK, int BV, int U>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   using TM = TileMeta<T>;
   constexpr int NP = TM::NP;
@@ -162,13 +188,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   constexpr int SLOT_K = slot_bytes(BK, T), SLOT_V = slot_bytes(BV, T);
   constexpr int CODE_K = slot_code_bytes(BK), CODE_V = slot_code_bytes(BV);
   constexpr int AL = slot_alpha_len(T);
-  __shared__ DecodeSmem<T> sm;
+  constexpr int NH = 4 * U;      // heads laid out per kv head
+  constexpr int LPH = 16 / U;    // fold lanes per head
+  // V fields of tokens 2 and 3 of a quad weigh kTok times those of tokens 0, 1:
+  // their probabilities enter the B operand divided by kTok (2^-kL2Tok).
+  constexpr float kTok = (BV == 4) ? 16.f : 4.f;
+  constexpr float kL2Tok = (BV == 4) ? 4.f : 2.f;
+  constexpr float kTwo24 = 16777216.f;
+  __shared__ DecodeSmem<T, U> sm;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
-  // code-unpack constants, kept in VGPRs (see code_pair)
-  unsigned m4 = 0x00F000F0u, m2 = 0x00300030u, one = kOne;
-  asm volatile("" : "+v"(m4), "+v"(m2), "+v"(one));
   const int n16 = lane & 15, grp = lane >> 4;
   const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int G = A.group;
@@ -178,9 +208,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   const int tile_end = min(ntiles, tile_begin + A.tiles_per_part);
   if (tile_begin >= tile_end) return;  // uniform over the workgroup
   const int H = A.kv_heads;
-  const bool real = n16 < G;
-  // the partition's page ids, staged once in LDS (a scalar load per tile would
-  // make every later LDS wait also wait for global memory)
+  const int head = n16 % NH;           // query head of this lane's MFMA column
+  // the partition's page ids, staged once in LDS
   {
     const int32_t* row = A.block_table + (size_t)seq * A.max_blocks + tile_begin * NP;
     const int n = (tile_end - tile_begin) * NP;
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     const int32_t* tp = sm.pages + (tl - tile_begin) * NP;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const size_t pg = (size_t)tp[p] * H + kvh;
+      const size_t pg = (size_t)__builtin_amdgcn_readfirstlane(tp[p]) * H + kvh;
       const uint8_t* sk = A.pool_k + pg * SLOT_K;
       const uint8_t* sv = A.pool_v + pg * SLOT_V;
       if (BK == 4) ck[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sk + 16 * lane));
@@ -219,7 +248,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   if (tile < tile_end) issue(tile);
 
   // ------------------------------------------------ H q of the group (wave 0), to LDS
+  // stored divided by the weight of channel c's K code field (a power of two)
   if (wave == 0) {
+    const bool real = n16 < G;
     float hq[32];
     const uint16_t* qrow = A.q + ((size_t)seq * A.q_heads + kvh * G + (real ? n16 : 0)) * kHeadDim + 32 * grp;
 #pragma unroll
@@ -244,17 +275,25 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) hq[i] = __builtin_fmaf(hq[i], s16, lane_xor<16>(hq[i]));
 #pragma unroll
-    for (int i = 0; i < 32; ++i) hq[i] = __builtin_fmaf(hq[i], s32, xor32(hq[i])) * kInvSqrtD;
+    for (int i = 0; i < 32; ++i) hq[i] = __builtin_fmaf(hq[i], s32, xor32(hq[i]));
+    if (n16 < NH) {
 #pragma unroll
-    for (int v = 0; v < 8; ++v)
-      *reinterpret_cast<f32x4*>(&sm.loop.hq[n16][32 * grp + 4 * v]) =
-          f32x4{hq[4 * v], hq[4 * v + 1], hq[4 * v + 2], hq[4 * v + 3]};
+      for (int v = 0; v < 8; ++v) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = hq[4 * v + e] * (kInvSqrtD / field_weight<BK>(e));
+        *reinterpret_cast<f32x4*>(&sm.loop.hq[n16][32 * grp + 4 * v]) = x;
+      }
+    }
   }
   __syncthreads();
 
   const float c0 = A.sm_scale_log2;
+  // fold layout: lane -> head fh, units fu0 .. fu0 + U - 1 (unit = chunk + 4 lane group)
+  const int fh = lane / LPH;
+  const int fu0 = (lane % LPH) * U;
   float m_run = -INFINITY, l_run = 0.f;
-  float acc[8][4];  // [block i][r]: channel 32 grp + 8 r + i, query head g = n16
+  float acc[8][4];  // [block i][r]: channel 32 grp + 8 r + i, query head of column n16
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -276,42 +315,71 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     const uint8_t* mK = mb;              // page p: S at +0, O at +64, alpha slice at +128
     const uint8_t* mV = mb + NP * META;
 
-    // -------------------------------------------- query fold: qt = (H q) * alpha_K
-    float qt[32];
-    float qsum = 0.f, qmax = 0.f;
+    // -------------------------------------------- query fold: qt = (H q) * alpha_K (compact)
+    {
+      constexpr int D1 = (BK == 4) ? 4 : 8;   // slot j -> channel cb + (j >> 1) + D1 (j & 1)
+      float qv[U][8];
+      float qsum = 0.f, qmax = 0.f;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int c = 32 * grp + 4 * v;
-      const f32x4 h4 = *reinterpret_cast<const f32x4*>(&sm.loop.hq[n16][c]);
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(mK + (c / AL) * META + 8 * kPage + 4 * (c % AL));
+      for (int u = 0; u < U; ++u) {
+        const int unit = fu0 + u, ch = unit & 3, g4 = unit >> 2;
+        const int cb = (BK == 4) ? 32 * g4 + 8 * ch : 32 * g4 + 16 * (ch >> 1) + 4 * (ch & 1);
+        const f32x4 h0 = *reinterpret_cast<const f32x4*>(&sm.loop.hq[fh][cb]);
+        const f32x4 h1 = *reinterpret_cast<const f32x4*>(&sm.loop.hq[fh][cb + D1]);
+        const uint8_t* ap = mK + (cb / AL) * META + 8 * kPage + 4 * (cb % AL);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 4 * D1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qt[4 * v + e] = h4[e] * a4[e];
-        qsum += qt[4 * v + e];
-        qmax = fmaxf(qmax, fabsf(qt[4 * v + e]));
+        for (int j = 0; j < 8; ++j) {
+          const float x = (j & 1) ? h1[j >> 1] * a1[j >> 1] : h0[j >> 1] * a0[j >> 1];
+          qv[u][j] = x;
+          qmax = fmaxf(qmax, fabsf(x));
+        }
+      }
+      qmax = span_max<LPH>(qmax);
+      // a power-of-two scale per head keeps the fp16 split in range
+      int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
+      ex = min(max(ex, -100), 100);
+      const float qscale = __uint_as_float((unsigned)(127 + 14 - ex) << 23);    // 2^(14-ex)
+      const float qunscale = __uint_as_float((unsigned)(127 - 14 + ex) << 23);  // 2^(ex-14)
+      // The offset term uses the sum of the query exactly as the MFMA sees it
+      // (hi + lo), so that the split's rounding enters every score as
+      // sum_c err_c (S k_c + O), proportional to the restored key, instead of
+      // leaving S sum_c err_c k_c against O sum_c qt_c uncancelled.
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        u32x4 hi, lo;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          unsigned h, l;
+          split_pair(qv[u][2 * m] * qscale, qv[u][2 * m + 1] * qscale, h, l);
+          hi[m] = h;
+          lo[m] = l;
+          const f16x2 hh = __builtin_bit_cast(f16x2, h), ll = __builtin_bit_cast(f16x2, l);
+          const float w = field_weight<BK>(m);   // slots 2m, 2m + 1 share field m
+          qsum = __builtin_fmaf((float)hh[0], w, qsum);
+          qsum = __builtin_fmaf((float)ll[0], w, qsum);
+          qsum = __builtin_fmaf((float)hh[1], w, qsum);
+          qsum = __builtin_fmaf((float)ll[1], w, qsum);
+        }
+        sm.loop.qb[wave][0][fh][fu0 + u] = hi;
+        sm.loop.qb[wave][1][fh][fu0 + u] = lo;
+      }
+      qsum = span_sum<LPH>(qsum) * qunscale;
+      if ((lane % LPH) == 0) {
+        sm.loop.cab[wave][fh][0] = c0 * kTwo24 * qunscale;  // score = S D cab0 + O cab1
+        sm.loop.cab[wave][fh][1] = c0 * qsum;
       }
     }
-    qsum = group_sum(qsum);
-    qmax = group_max(qmax);
-    // a power-of-two scale per query head keeps the fp16 split of qt in range
-    int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
-    ex = min(max(ex, -100), 100);
-    const float qscale = __uint_as_float((unsigned)(127 + 14 - ex) << 23);    // 2^(14-ex)
-    const float qunscale = __uint_as_float((unsigned)(127 - 14 + ex) << 23);  // 2^(ex-14)
+    asm volatile("" ::: "memory");  // the reads below see this wave's writes (LDS keeps order)
     f16x8 bq_hi[4], bq_lo[4];
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
-      unsigned hi[4], lo[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i0 = k_channel<BK>(ch, 0, 2 * m), i1 = k_channel<BK>(ch, 0, 2 * m + 1);
-        split_pair(qt[i0] * qscale, qt[i1] * qscale, hi[m], lo[m]);
-      }
-      bq_hi[ch] = as_f16x8(hi[0], hi[1], hi[2], hi[3]);
-      bq_lo[ch] = as_f16x8(lo[0], lo[1], lo[2], lo[3]);
+      bq_hi[ch] = __builtin_bit_cast(f16x8, sm.loop.qb[wave][0][head][ch + 4 * grp]);
+      bq_lo[ch] = __builtin_bit_cast(f16x8, sm.loop.qb[wave][1][head][ch + 4 * grp]);
     }
-    const float sA = c0 * 64.f * qunscale;   // score = sA S (D) + c0 qsum (O - 64 S)
-    const float sB = c0 * qsum;
+    const float sA = sm.loop.cab[wave][head][0];
+    const float sB = sm.loop.cab[wave][head][1];
 
     // -------------------------------------------- scores of the tile's pages
     // chunk-major order: the NP pages' accumulation chains interleave
@@ -324,17 +392,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
       for (int p = 0; p < NP; ++p) {
         f16x8 a;
         if (BK == 4) {
-          const unsigned x = kc[p][ch];
-          a = as_f16x8(code_pair<4, 0>(x, m4, one), code_pair<4, 1>(x, m4, one), code_pair<4, 2>(x, m4, one),
-                       code_pair<4, 3>(x, m4, one));
+          const unsigned x = kc[p][ch], y = x >> 8;
+          a = as_f16x8(code_field<4, 0>(x, y), code_field<4, 1>(x, y), code_field<4, 2>(x, y),
+                       code_field<4, 3>(x, y));
         } else {
-          const unsigned x = kc[p][ch >> 1];
+          const unsigned x = kc[p][ch >> 1], y = x >> 8;
           if (ch & 1)
-            a = as_f16x8(code_pair<2, 4>(x, m2, one), code_pair<2, 5>(x, m2, one), code_pair<2, 6>(x, m2, one),
-                         code_pair<2, 7>(x, m2, one));
+            a = as_f16x8(code_field<2, 4>(x, y), code_field<2, 5>(x, y), code_field<2, 6>(x, y),
+                         code_field<2, 7>(x, y));
           else
-            a = as_f16x8(code_pair<2, 0>(x, m2, one), code_pair<2, 1>(x, m2, one), code_pair<2, 2>(x, m2, one),
-                         code_pair<2, 3>(x, m2, one));
+            a = as_f16x8(code_field<2, 0>(x, y), code_field<2, 1>(x, y), code_field<2, 2>(x, y),
+                         code_field<2, 3>(x, y));
         }
         d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_hi[ch], d[p], 0, 0, 0);
         d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_lo[ch], d[p], 0, 0, 0);
@@ -346,7 +414,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
       const f32x4 S = *reinterpret_cast<const f32x4*>(mK + p * META + 16 * grp);
       const f32x4 O = *reinterpret_cast<const f32x4*>(mK + p * META + 4 * kPage + 16 * grp);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[p][r] = __builtin_fmaf(sA * S[r], d[p][r], sB * __builtin_fmaf(-64.f, S[r], O[r]));
+      for (int r = 0; r < 4; ++r) s[p][r] = __builtin_fmaf(sA * S[r], d[p][r], sB * O[r]);
     }
     if (tile == ntiles - 1 && (L % T) != 0) {
 #pragma unroll
@@ -357,24 +425,49 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     }
 
     // -------------------------------------------- online softmax (base 2)
+    // the running max moves only when some score passes it; otherwise the
+    // accumulators need no rescale (checked for the whole wave at once)
     float tmax = s[0][0];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[p][r]);
     tmax = group_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][r] *= corr;
+    }
+    // P = p S enters the MFMA as fp16 hi + lo; a power of two 2^k per tile,
+    // carried by the exponent of p, puts max P at 2^14..2^15 so that lo stays
+    // a normal fp16 (its 11 bits are what make hi + lo nearly fp32-exact)
+    float smax = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const f32x4 S = *reinterpret_cast<const f32x4*>(mV + p * META + 16 * grp);
+      smax = fmaxf(smax, fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])));
+    }
+    smax = group_max(smax);   // scales are >= 0
+    int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
+    pe = min(max(pe, -100), 100);
+    const float pk = (float)(14 - pe);                                   // k
+    const float pinv = __uint_as_float((unsigned)(127 - 14 + pe) << 23);  // 2^-k
+    const float m_lo = m_run - pk, m_hi = m_lo + kL2Tok;
+    float psa = 0.f, psb = 0.f;
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[p][r] = __builtin_amdgcn_exp2f(s[p][r] - m_new);
-        psum += s[p][r];
+        s[p][r] = __builtin_amdgcn_exp2f(s[p][r] - (r < 2 ? m_lo : m_hi));
+        if (r < 2) psa += s[p][r];
+        else psb += s[p][r];
       }
-    l_run = __builtin_fmaf(l_run, corr, psum);
+    l_run = __builtin_fmaf(pinv, __builtin_fmaf(kTok, psb, psa), l_run);
 
     // -------------------------------------------- values of the tile's pages
     float vacc[8][4];
@@ -382,7 +475,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) vacc[i][r] = 0.f;
-    float sp = 0.f, spo = 0.f;
+    float spa = 0.f, spb = 0.f;
 #pragma unroll
     for (int pp = 0; pp < NP; pp += 2) {
       unsigned bh[4], bl[4];
@@ -394,8 +487,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pw[r] = s[pp + h2][r] * S[r];
-          sp += pw[r];
-          spo = __builtin_fmaf(s[pp + h2][r], O[r], spo);
+          if (r < 2) spa = __builtin_fmaf(s[pp + h2][r], O[r], spa);
+          else spb = __builtin_fmaf(s[pp + h2][r], O[r], spb);
         }
         split_pair(pw[0], pw[1], bh[2 * h2], bl[2 * h2]);
         split_pair(pw[2], pw[3], bh[2 * h2 + 1], bl[2 * h2 + 1]);
@@ -408,32 +501,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           if (BV == 4) {
-            const unsigned x = vc[pp + h2][i >> 1];
-            if (i & 1) { u[2 * h2] = code_pair<4, 2>(x, m4, one); u[2 * h2 + 1] = code_pair<4, 3>(x, m4, one); }
-            else { u[2 * h2] = code_pair<4, 0>(x, m4, one); u[2 * h2 + 1] = code_pair<4, 1>(x, m4, one); }
+            const unsigned x = vc[pp + h2][i >> 1], y = x >> 8;
+            if (i & 1) { u[2 * h2] = code_field<4, 2>(x, y); u[2 * h2 + 1] = code_field<4, 3>(x, y); }
+            else { u[2 * h2] = code_field<4, 0>(x, y); u[2 * h2 + 1] = code_field<4, 1>(x, y); }
           } else {
-            const unsigned x = vc[pp + h2][i >> 2];
+            const unsigned x = vc[pp + h2][i >> 2], y = x >> 8;
             switch (i & 3) {
-              case 0: u[2 * h2] = code_pair<2, 0>(x, m2, one); u[2 * h2 + 1] = code_pair<2, 1>(x, m2, one); break;
-              case 1: u[2 * h2] = code_pair<2, 2>(x, m2, one); u[2 * h2 + 1] = code_pair<2, 3>(x, m2, one); break;
-              case 2: u[2 * h2] = code_pair<2, 4>(x, m2, one); u[2 * h2 + 1] = code_pair<2, 5>(x, m2, one); break;
-              default: u[2 * h2] = code_pair<2, 6>(x, m2, one); u[2 * h2 + 1] = code_pair<2, 7>(x, m2, one); break;
+              case 0: u[2 * h2] = code_field<2, 0>(x, y); u[2 * h2 + 1] = code_field<2, 1>(x, y); break;
+              case 1: u[2 * h2] = code_field<2, 2>(x, y); u[2 * h2 + 1] = code_field<2, 3>(x, y); break;
+              case 2: u[2 * h2] = code_field<2, 4>(x, y); u[2 * h2 + 1] = code_field<2, 5>(x, y); break;
+              default: u[2 * h2] = code_field<2, 6>(x, y); u[2 * h2 + 1] = code_field<2, 7>(x, y); break;
             }
           }
         }
         const f16x8 a = as_f16x8(u[0], u[1], u[2], u[3]);
-        f32x4 d{vacc[i][0], vacc[i][1], vacc[i][2], vacc[i][3]};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph, d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pl, d, 0, 0, 0);
+        f32x4 dv{vacc[i][0], vacc[i][1], vacc[i][2], vacc[i][3]};
+        dv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph, dv, 0, 0, 0);
+        dv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pl, dv, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vacc[i][r] = d[r];
+        for (int r = 0; r < 4; ++r) vacc[i][r] = dv[r];
       }
     }
-    sp = group_sum(sp);
-    spo = group_sum(spo);
+    const float spo = group_sum(__builtin_fmaf(kTok, spb, spa)) * pinv;   // sum_t p_t O_t
 
-    // -------------------------------------------- fold: acc = acc corr + alpha_V (64 (D - sp) + spo)
-    const float kv = __builtin_fmaf(-64.f, sp, spo);
+    // -------------------------------------------- fold: acc += alpha_V (sum_t p_t S_t k_t + sum_t p_t O_t)
+    // (vacc carries 2^(k-24) times the V field weight of block i)
+    const float cf0 = kTwo24 * pinv, cf1 = (BV == 2) ? cf0 * (1.f / 16.f) : cf0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = 32 * grp + 8 * r;
@@ -443,8 +536,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float al = (i < 4) ? a0[i] : a1[i - 4];
-        const float val = al * __builtin_fmaf(64.f, vacc[i][r], kv);
-        acc[i][r] = __builtin_fmaf(acc[i][r], corr, val);
+        const float t = __builtin_fmaf(vacc[i][r], (i & 1) ? cf1 : cf0, spo);
+        acc[i][r] = __builtin_fmaf(al, t, acc[i][r]);
       }
     }
     buf ^= 1;
@@ -464,7 +557,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     sm.merge.l[wave][n16] = l_run;
   }
   __syncthreads();
-  if (wave != 0 || !real) return;
+  if (wave != 0 || n16 >= G) return;
   float M = sm.merge.m[0][n16];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.merge.m[w][n16]);
@@ -592,7 +685,9 @@ hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, 
     return by_bits(bits_k, [&](auto BK) {
       return by_bits(bits_v, [&](auto BV) {
         dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV()>), grid, dim3(64 * kWaves), 0, s, a);
+        if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1>), grid, dim3(64 * kWaves), 0, s, a);
+        else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2>), grid, dim3(64 * kWaves), 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4>), grid, dim3(64 * kWaves), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_combine(a, T(), true, s);
