@@ -39,14 +39,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // fp16 pair (low, high half of w) -> fp32 (low + high, low - high): the
-// conversion rides on the first butterfly stage (fma with fp16 operands).
+// conversion rides on the first butterfly stage, one v_fma_mix_f32 each (the
+// mixed-precision FMA reads the two fp16 halves directly; low * 1 + high is
+// rounded once, as the fp32 sum of the converted values would be).
 __device__ __forceinline__ void first_stage(unsigned w, float& y0, float& y1) {
-  _Float16 lo, hi;
-  const uint16_t l16 = (uint16_t)(w & 0xFFFFu), h16 = (uint16_t)(w >> 16);
-  __builtin_memcpy(&lo, &l16, 2);
-  __builtin_memcpy(&hi, &h16, 2);
-  y0 = __builtin_fmaf((float)lo, 1.0f, (float)hi);
-  y1 = __builtin_fmaf((float)lo, 1.0f, -(float)hi);
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(y0) : "v"(w));
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(y1) : "v"(w));
 }
 
 // Shared memory of one workgroup.
