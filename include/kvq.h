@@ -100,11 +100,12 @@ const char* kvq_version(void);
  * K-slot codes: 4 blocks of 32 channels; block k stores, token after token,
  *   channels 32k..32k+31 of each token packed low bits first (channel c at
  *   bits (c mod (8/bits))*bits of byte c*bits/8 within the token's block).
- * V-slot codes: 4 quads of 4 tokens; quad q holds 16 groups of 8 channels;
- *   group m is 4*bits bytes read as little-endian 32-bit words; word w holds
- *   channels 8m + w*F/4 + j (j < F/4, F = 32/bits fields per word) of tokens
- *   4q + r (r < 4), channel j / token r in field f = 2j + (r>>1) + (F/2)(r&1),
- *   field f being bits [bits*f, bits*(f+1)) of the word.
+ * V-slot codes: 64 runs of 4*bits bytes; run l (at byte 4*bits*l) holds the
+ *   channels l (h = 0) and 64 + l (h = 1) of the 16 tokens, read as
+ *   little-endian 32-bit words of F = 32/bits fields.  Token t = 4g + r
+ *   (quad g, r < 4) of channel half h forms the pair p = 2g + h, stored in word
+ *   p / (F/4) of the run, field f = 2m + (r>>1) + (F/2)(r&1) with
+ *   m = p mod (F/4), field f being bits [bits*f, bits*(f+1)) of the word.
  * Rows of a page past the sequence's end hold code 0, scale 0 and offset 0.
  * Contract: a sequence owns a page for every page of every tile it has
  * started (pages are allocated in whole tiles), so a partial tile's channel

@@ -77,6 +77,14 @@ int max_partitions(int max_seq_len, int tile, int tpp) {
   return (tiles + tpp - 1) / tpp;
 }
 
+// The quantized decode splits the context into 64-token chunks; a partition
+// holds whole tiles (an even number of chunks at tile 128).
+int chunks_per_partition(int num_seqs, int kv_heads, int max_seq_len, int tile) {
+  int cpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, 64);
+  if (tile == 128 && (cpp & 1)) ++cpp;
+  return cpp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,8 +219,8 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32
                                   int32_t kv_heads, int32_t max_seq_len) {
   if (check_config(cfg, true) != KVQ_OK) return 0;
   if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0) return 0;
-  const int tpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, cfg->tile_tokens);
-  const int parts = max_partitions(max_seq_len, cfg->tile_tokens, tpp);
+  const int cpp = chunks_per_partition(num_seqs, kv_heads, max_seq_len, cfg->tile_tokens);
+  const int parts = max_partitions(max_seq_len, 64, cpp);
   return (size_t)num_seqs * q_heads * parts * (kvq::kHeadDim + 2) * sizeof(float);
 }
 
@@ -245,10 +253,10 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
   const size_t need = kvq_decode_workspace_bytes(cfg, num_seqs, q_heads, kv_heads, max_seq_len);
   if (workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  const int tpp = tiles_per_partition(num_seqs, kv_heads, max_seq_len, tile);
-  const int parts = max_partitions(max_seq_len, tile, tpp);
+  const int tpp = chunks_per_partition(num_seqs, kv_heads, max_seq_len, tile);
+  const int parts = max_partitions(max_seq_len, 64, tpp);
   if (tpp > 64 || parts > 1024)
-    return fail(KVQ_ERR_UNSUPPORTED, "max_seq_len %d is beyond 65536 tiles", max_seq_len);
+    return fail(KVQ_ERR_UNSUPPORTED, "max_seq_len %d is beyond 65536 chunks of 64 tokens", max_seq_len);
   kvq::DecodeArgs a{};
   a.q = q;
   a.block_table = block_table;
@@ -265,9 +273,9 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
   a.max_blocks = max_blocks;
   a.tiles_per_part = tpp;
   a.max_parts = parts;
-  a.max_tiles = (max_seq_len + tile - 1) / tile;
+  a.max_tiles = (max_seq_len + 63) / 64;   // in 64-token chunks
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
-  a.unit_tokens = tile;
+  a.unit_tokens = 64;
   a.out_scale = 1.0f;
   return launched(kvq::launch_decode(a, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
                   "kvq_paged_decode_attn");

@@ -29,22 +29,19 @@
 // per lane) is exactly the B layout PV needs, so no shuffle sits between the
 // two.  Online softmax runs per tile; partitions are merged by a second
 // kernel that also applies the final Hadamard.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f16x8 as_f16x8(unsigned a, unsigned b, unsigned c, unsigned d) {
-  u32x4 v{a, b, c, d};
-  return __builtin_bit_cast(f16x8, v);
-}
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
@@ -73,20 +70,17 @@ __device__ __forceinline__ float max32(float v) {
 __device__ __forceinline__ float group_max(float v) { return max32(max16(v)); }
 __device__ __forceinline__ float group_sum(float v) { return sum32(sum16(v)); }
 
-constexpr int kWaves = 4;  // waves per decode workgroup
+constexpr int kWaves = 4;             // waves per decode workgroup
+constexpr int kChunk = 64;            // tokens per wave step (4 pages)
+constexpr int kMaxChunksPerPart = 64;
 
-// Metadata of one tile as staged in LDS: the slots' (scale, offset, alpha
-// slice) areas, K pages then V pages, each META bytes.
-template <int T>
-struct TileMeta {
-  static constexpr int NP = T / kPage;
-  static constexpr int META = 8 * kPage + 4 * slot_alpha_len(T);  // bytes per slot
-  static constexpr int BYTES = 2 * NP * META;
-  static constexpr int PIECES = BYTES / 16;                     // 16-byte loads
-  static constexpr int PER_LANE = (PIECES + 63) / 64;
-};
-
-constexpr int kMaxTilesPerPart = 64;
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Code fields of one 32-bit word (two 16-bit halves), masked in place so that
 // each half reads as the fp16 denormal m * 2^-24 whose mantissa m is the code
@@ -95,7 +89,7 @@ constexpr int kMaxTilesPerPart = 64;
 // of codes, no conversion and no offset term.
 template <int BITS, int X>
 __device__ __forceinline__ unsigned code_field(unsigned x, unsigned y) {
-  if (BITS == 4) {
+  if constexpr (BITS == 4) {
     constexpr unsigned m = (X & 1) ? 0x00F000F0u : 0x000F000Fu;
     return ((X < 2) ? x : y) & m;
   } else {
@@ -108,23 +102,22 @@ __host__ __device__ constexpr float field_weight(int x) {
   return BITS == 4 ? ((x & 1) ? 16.f : 1.f) : (float)(1 << (2 * (x & 3)));
 }
 
-template <int T, int U>
-struct alignas(16) DecodeSmem {
-  int32_t pages[kMaxTilesPerPart * (T / kPage)];  // the partition's page ids
-  union {
-    struct {
-      float hq[4 * U][kHeadDim];                       // (H q)_c / weight of channel c's K field
-      uint8_t meta[kWaves][2][TileMeta<T>::BYTES];     // per-wave double buffer
-      u32x4 qb[kWaves][2][4 * U][16];                  // per-wave QK B operands [hi/lo][head][unit]
-      float cab[kWaves][4 * U][2];                     // per-wave, per head: score factors
-    } loop;
-    struct {
-      float acc[kWaves][16][kHeadDim];
-      float m[kWaves][16];
-      float l[kWaves][16];
-    } merge;
-  };
-};
+// fp16x4 MFMA operand from two code-field words
+__device__ __forceinline__ f16x4 as_f16x4(unsigned a, unsigned b) {
+  return __builtin_bit_cast(f16x4, u32x2{a, b});
+}
+
+// fp32 pair -> fp16 pair hi (nearest even) and the fp16 pair lo of what is
+// left (x - hi is exact in fp32; v_fma_mix_f32 reads hi's halves as fp16).
+// hi + lo carries x to ~2^-22 relative, without bias.
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const unsigned hb = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, f16x2));
+  float r0, r1;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(hb), "v"(x0));
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r1) : "v"(hb), "v"(x1));
+  hi = hb;
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, f16x2));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, lane_xor<1>(v));
@@ -140,116 +133,169 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += lane_xor<8>(v);
   return group_sum(v);
 }
-
-// Sum / max over aligned groups of N lanes (N <= 16).
-template <int N>
-__device__ __forceinline__ float span_sum(float v) {
-  if (N > 1) v += lane_xor<1>(v);
-  if (N > 2) v += lane_xor<2>(v);
-  if (N > 4) v += lane_xor<4>(v);
-  if (N > 8) v += lane_xor<8>(v);
+// Sum / max over the lanes of one MFMA row index i = lane & 3 within groups of
+// NB blocks (NB = 8: each 32-lane half; NB = 16: the wave).
+template <int NB>
+__device__ __forceinline__ float blocks_sum(float v) {
+  v += lane_xor<4>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<16>(v);
+  if (NB == 16) v += xor32(v);
   return v;
 }
-template <int N>
-__device__ __forceinline__ float span_max(float v) {
-  if (N > 1) v = fmaxf(v, lane_xor<1>(v));
-  if (N > 2) v = fmaxf(v, lane_xor<2>(v));
-  if (N > 4) v = fmaxf(v, lane_xor<4>(v));
-  if (N > 8) v = fmaxf(v, lane_xor<8>(v));
+template <int NB>
+__device__ __forceinline__ float blocks_max(float v) {
+  v = fmaxf(v, lane_xor<4>(v));
+  v = fmaxf(v, lane_xor<8>(v));
+  v = fmaxf(v, lane_xor<16>(v));
+  if (NB == 16) v = fmaxf(v, xor32(v));
   return v;
 }
 
-// fp32 pair -> fp16 pair hi (nearest even) and the fp16 pair lo of what is
-// left (x - hi is exact in fp32; v_fma_mix_f32 reads hi's halves as fp16).
-// hi + lo carries x to ~2^-22 relative, without bias.
-__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
-  const unsigned hb = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, f16x2));
-  float r0, r1;
-  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(hb), "v"(x0));
-  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r1) : "v"(hb), "v"(x1));
-  hi = hb;
-  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, f16x2));
-}
+template <int T, int HG>
+struct alignas(16) DecodeSmem {
+  int32_t pages[kMaxChunksPerPart * 4];          // the partition's page ids
+  union {
+    struct {
+      float hq[4 * HG][kHeadDim];                // (H q)_c / weight of channel c's K field
+      float pt[kWaves][4 * HG][kChunk];          // per-wave transpose of the probabilities
+    } loop;
+    struct {
+      float acc[kWaves][4 * HG][kHeadDim];
+      float m[kWaves][4 * HG];
+      float l[kWaves][4 * HG];
+    } merge;
+  };
+};
 
-// One workgroup of 4 waves per (partition of tiles, kv head, sequence); wave
-// w takes tiles begin + w, begin + w + 4, ...  Each wave prefetches its next
-// tile's codes (registers) and metadata (registers, then LDS) while it works
-// on the current one; the 4 waves' softmax states are merged in LDS at the end.
-//
-// U = 1, 2, 4 for groups of up to 4, 8, 16 query heads.  Per tile, the query
-// fold qt = (H q) * alpha_K runs in a compact layout (lane = head, 8U
-// channels) and reaches the MFMA B layout through LDS; MFMA column n reads
-// head n mod 4U, so columns past the group repeat real heads and need no mask.
-template <int T, int BK, int BV, int U>
+// Decode attention over quantized pages; one workgroup of 4 waves per
+// (partition of 64-token chunks, kv head, sequence); wave w takes chunks
+// begin + w, begin + w + 4, ...  Both contractions run on
+// v_mfma_f32_4x4x4_16b_f16 (16 blocks of 4 x 4, K = 4), so that the lane
+// layouts fit a group of 4 query heads with no padding:
+//   QK:  D[b][head i][token j] = sum_k qt[i][c_k] K[4b + j][c_k] over 32 steps
+//        of 4 channels.  Lane 4b + j feeds its own token's codes (B); the
+//        query operand A is the same for every block and is broadcast from
+//        one block (CBSZ/ABID), so 16 steps' worth of qt sit in one register
+//        set spread over the 16 blocks.  Output: lane = token, 4 heads.
+//   PV:  D[b][head i][channel 4b + j] = sum_k P[t_k][i] V[t_k][4b + j] over 16
+//        steps of 4 tokens; A = probabilities (transposed once through LDS,
+//        broadcast from block = step), B = the lane's channel's codes.
+//        Output: lane = channel l (and 64 + l), 4 heads.
+// Groups of more than 4 heads run 4 at a time (HG groups) on the same codes.
+template <int T, int BK, int BV, int HG>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
-  using TM = TileMeta<T>;
-  constexpr int NP = TM::NP;
-  constexpr int META = TM::META;
+  constexpr int NH = 4 * HG;
+  constexpr int SETS = (T == 32) ? 4 : 2;        // QK A register sets
+  constexpr int BLK = 32 / SETS;                 // steps per set = blocks per broadcast group
+  constexpr int CB = (T == 32) ? 3 : 4;          // CBSZ of the QK broadcast
+  constexpr int TPC = (T == 32) ? 2 : 1;         // tiles per chunk
+  constexpr int PPT = T / kPage;                 // pages per tile
   constexpr int SLOT_K = slot_bytes(BK, T), SLOT_V = slot_bytes(BV, T);
   constexpr int CODE_K = slot_code_bytes(BK), CODE_V = slot_code_bytes(BV);
   constexpr int AL = slot_alpha_len(T);
-  constexpr int NH = 4 * U;      // heads laid out per kv head
-  constexpr int LPH = 16 / U;    // fold lanes per head
-  // V fields of tokens 2 and 3 of a quad weigh kTok times those of tokens 0, 1:
-  // their probabilities enter the B operand divided by kTok (2^-kL2Tok).
+  constexpr int D1 = (BK == 4) ? 4 : 8;          // QK step: channels c0, c0 + D1, c0 + 1, c0 + 1 + D1
+  // V fields of tokens 2 and 3 of a quad weigh kTok times those of tokens 0, 1;
+  // their probabilities enter the MFMA divided by kTok.
   constexpr float kTok = (BV == 4) ? 16.f : 4.f;
-  constexpr float kL2Tok = (BV == 4) ? 4.f : 2.f;
   constexpr float kTwo24 = 16777216.f;
-  __shared__ DecodeSmem<T, U> sm;
+  __shared__ DecodeSmem<T, HG> sm;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
-  const int n16 = lane & 15, grp = lane >> 4;
+  const int bq = lane >> 2, iq = lane & 3;       // MFMA block and row/column of this lane
   const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int G = A.group;
   const int L = A.seq_lens[seq];
-  const int ntiles = min((L + T - 1) / T, A.max_tiles);
-  const int tile_begin = part * A.tiles_per_part;
-  const int tile_end = min(ntiles, tile_begin + A.tiles_per_part);
-  if (tile_begin >= tile_end) return;  // uniform over the workgroup
+  const int nchunks = min((L + kChunk - 1) / kChunk, A.max_tiles);
+  const int c_begin = part * A.tiles_per_part;
+  const int c_end = min(nchunks, c_begin + A.tiles_per_part);
+  if (c_begin >= c_end) return;  // uniform over the workgroup
   const int H = A.kv_heads;
-  const int head = n16 % NH;           // query head of this lane's MFMA column
-  // the partition's page ids, staged once in LDS
+  const int npages = ((L + T - 1) / T) * PPT;   // pages the sequence owns (whole tiles)
+  // the partition's page ids (up to the end of its last tile), staged once in LDS
   {
-    const int32_t* row = A.block_table + (size_t)seq * A.max_blocks + tile_begin * NP;
-    const int n = (tile_end - tile_begin) * NP;
+    const int32_t* row = A.block_table + (size_t)seq * A.max_blocks + 4 * c_begin;
+    const int last = min(npages, ((4 * c_end + PPT - 1) / PPT) * PPT);
+    const int n = last - 4 * c_begin;
     for (int i = threadIdx.x; i < n; i += 64 * kWaves) sm.pages[i] = row[i];
   }
   __syncthreads();
+  // physical page of page pj of the sequence; a T = 32 chunk whose second tile
+  // was never started reads its first tile's pages instead (every token there
+  // is past the end and masked)
+  auto page_id = [&](int pj) { return sm.pages[(pj < npages ? pj : pj - 2) - 4 * c_begin]; };
+  auto kslot = [&](int pid) { return A.pool_k + ((size_t)pid * H + kvh) * SLOT_K; };
+  auto vslot = [&](int pid) { return A.pool_v + ((size_t)pid * H + kvh) * SLOT_V; };
 
-  // ------------------------------------------------ prefetch of one tile
-  u32x4 ck[NP], cv[NP], mpre[TM::PER_LANE];
-  auto issue = [&](int tl) {
-    const int32_t* tp = sm.pages + (tl - tile_begin) * NP;
+  // ------------------------------------------------ per-chunk operands (loaded one chunk ahead,
+  // each right after its last use in the current chunk)
+  u32x4 kq[4];            // K codes of token `lane`: 4 blocks of 32 channels
+  float sk, ok;           // its scale and offset
+  u32x4 vq[4];            // V codes of run `lane` (channels lane, 64 + lane), 4 pages
+  f32x4 svq, ovq;         // V scale / offset of tokens 4 bq .. 4 bq + 3
+  f32x4 ak[SETS];         // alpha_K of this lane's QK steps (fold layout)
+  float av[TPC][2];       // alpha_V of channels lane, 64 + lane
+  auto tile_page = [&](int c, int tile_in_chunk) {   // first page (in the sequence) of a tile of chunk c
+    return (T == 128) ? 4 * (c & ~1) : 4 * c + PPT * tile_in_chunk;
+  };
+  auto load_k = [&](int c) {
+    const uint8_t* sl = kslot(page_id(4 * c + (lane >> 4)));
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const size_t pg = (size_t)__builtin_amdgcn_readfirstlane(tp[p]) * H + kvh;
-      const uint8_t* sk = A.pool_k + pg * SLOT_K;
-      const uint8_t* sv = A.pool_v + pg * SLOT_V;
-      if (BK == 4) ck[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sk + 16 * lane));
-      else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sk + 8 * lane)); ck[p] = u32x4{x[0], x[1], 0u, 0u}; }
-      if (BV == 4) cv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sv + 16 * lane));
-      else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sv + 8 * lane)); cv[p] = u32x4{x[0], x[1], 0u, 0u}; }
+    for (int blk = 0; blk < 4; ++blk) {
+      if (BK == 4) kq[blk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 256 * blk + 16 * (lane & 15)));
+      else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 128 * blk + 8 * (lane & 15))); kq[blk] = u32x4{x[0], x[1], 0u, 0u}; }
     }
+    sk = __builtin_nontemporal_load(reinterpret_cast<const float*>(sl + CODE_K) + (lane & 15));
+    ok = __builtin_nontemporal_load(reinterpret_cast<const float*>(sl + CODE_K + 64) + (lane & 15));
+  };
+  auto load_v = [&](int c) {
 #pragma unroll
-    for (int j = 0; j < TM::PER_LANE; ++j) {
-      const int i = lane + 64 * j;
-      if (i < TM::PIECES) {
-        const int role = i / (NP * META / 16);
-        const int rem = i % (NP * META / 16);
-        const int p = rem / (META / 16), off = 16 * (rem % (META / 16));
-        const size_t pg = (size_t)tp[p] * H + kvh;
-        const uint8_t* src = role == 0 ? A.pool_k + pg * SLOT_K + CODE_K : A.pool_v + pg * SLOT_V + CODE_V;
-        mpre[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off));
+    for (int p = 0; p < 4; ++p) {
+      const uint8_t* sl = vslot(page_id(4 * c + p));
+      if (BV == 4) vq[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 16 * lane));
+      else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 8 * lane)); vq[p] = u32x4{x[0], x[1], 0u, 0u}; }
+    }
+    const uint8_t* sl = vslot(page_id(4 * c + (bq >> 2)));
+    svq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 16 * (bq & 3)));
+    ovq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 64 + 16 * (bq & 3)));
+  };
+  auto load_alpha = [&](int c) {
+    // QK steps of this lane: s = BLK st + bq % BLK; channels c0 + {0, D1, 1, 1 + D1}
+    const int tp = tile_page(c, (T == 32) ? (bq >> 3) : 0);
+#pragma unroll
+    for (int st = 0; st < SETS; ++st) {
+      const int s = BLK * st + (bq % BLK);
+      const int c0 = (BK == 4) ? 8 * (s >> 1) + 2 * (s & 1) : 16 * (s >> 2) + 2 * (s & 3);
+      const float* ap = reinterpret_cast<const float*>(kslot(page_id(tp + c0 / AL)) + CODE_K + 128) + (c0 % AL);
+      const f32x2 x0 = *reinterpret_cast<const f32x2*>(ap);
+      const f32x2 x1 = *reinterpret_cast<const f32x2*>(ap + D1);
+      ak[st] = f32x4{x0[0], x1[0], x0[1], x1[1]};   // k order: c0, c0 + D1, c0 + 1, c0 + 1 + D1
+    }
+  };
+  auto load_av = [&](int c) {
+#pragma unroll
+    for (int tt = 0; tt < TPC; ++tt) {
+      const int tpv = tile_page(c, tt);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ch = lane + 64 * h;
+        av[tt][h] = reinterpret_cast<const float*>(vslot(page_id(tpv + ch / AL)) + CODE_V + 128)[ch % AL];
       }
     }
   };
-  int tile = tile_begin + wave;
-  if (tile < tile_end) issue(tile);
+  int chunk = c_begin + wave;
+  if (chunk < c_end) {
+    load_alpha(chunk);
+    load_k(chunk);
+    load_v(chunk);
+    load_av(chunk);
+  }
 
   // ------------------------------------------------ H q of the group (wave 0), to LDS
   // stored divided by the weight of channel c's K code field (a power of two)
   if (wave == 0) {
+    const int n16 = lane & 15, grp = lane >> 4;
     const bool real = n16 < G;
     float hq[32];
     const uint16_t* qrow = A.q + ((size_t)seq * A.q_heads + kvh * G + (real ? n16 : 0)) * kHeadDim + 32 * grp;
@@ -289,301 +335,264 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   __syncthreads();
 
   const float c0 = A.sm_scale_log2;
-  // fold layout: lane -> head fh, units fu0 .. fu0 + U - 1 (unit = chunk + 4 lane group)
-  const int fh = lane / LPH;
-  const int fu0 = (lane % LPH) * U;
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[8][4];  // [block i][r]: channel 32 grp + 8 r + i, query head of column n16
+  float m_run[NH], l_run[NH];     // per head: running max (wave-uniform), partial sum (this lane's tokens)
+  float acc[2][NH];               // [channel half][head]: channels lane, 64 + lane
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[i][r] = 0.f;
+  for (int h = 0; h < NH; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+    acc[0][h] = 0.f;
+    acc[1][h] = 0.f;
+  }
 
-  int buf = 0;
-  for (; tile < tile_end; tile += kWaves) {
-    // stage this tile's metadata, then start loading the next tile
-    uint8_t* mb = sm.loop.meta[wave][buf];
-#pragma unroll
-    for (int j = 0; j < TM::PER_LANE; ++j) {
-      const int i = lane + 64 * j;
-      if (i < TM::PIECES) *reinterpret_cast<u32x4*>(mb + 16 * i) = mpre[j];
-    }
-    u32x4 kc[NP], vc[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) { kc[p] = ck[p]; vc[p] = cv[p]; }
-    if (tile + kWaves < tile_end) issue(tile + kWaves);
-    const uint8_t* mK = mb;              // page p: S at +0, O at +64, alpha slice at +128
-    const uint8_t* mV = mb + NP * META;
+  for (; chunk < c_end; chunk += kWaves) {
+    const int next = chunk + kWaves;
+    const bool more = next < c_end;   // uniform
 
-    // -------------------------------------------- query fold: qt = (H q) * alpha_K (compact)
-    {
-      constexpr int D1 = (BK == 4) ? 4 : 8;   // slot j -> channel cb + (j >> 1) + D1 (j & 1)
-      float qv[U][8];
-      float qsum = 0.f, qmax = 0.f;
+    // -------------------------------------------- query fold, in the QK A layout
+    // lane (bq, iq) holds qt[head 4 hg + iq][channels of step BLK st + bq % BLK]
+    // as fp16 hi / lo; qsum and the power-of-two scale per (head, tile)
+    f16x4 qa_hi[HG][SETS], qa_lo[HG][SETS];
+    float cA[HG], cB[HG];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int unit = fu0 + u, ch = unit & 3, g4 = unit >> 2;
-        const int cb = (BK == 4) ? 32 * g4 + 8 * ch : 32 * g4 + 16 * (ch >> 1) + 4 * (ch & 1);
-        const f32x4 h0 = *reinterpret_cast<const f32x4*>(&sm.loop.hq[fh][cb]);
-        const f32x4 h1 = *reinterpret_cast<const f32x4*>(&sm.loop.hq[fh][cb + D1]);
-        const uint8_t* ap = mK + (cb / AL) * META + 8 * kPage + 4 * (cb % AL);
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 4 * D1);
+    for (int hg = 0; hg < HG; ++hg) {
+      const int hh = 4 * hg + iq;
+      float x[SETS][4];
+      float qmax = 0.f, qsum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = (j & 1) ? h1[j >> 1] * a1[j >> 1] : h0[j >> 1] * a0[j >> 1];
-          qv[u][j] = x;
-          qmax = fmaxf(qmax, fabsf(x));
-        }
+      for (int st = 0; st < SETS; ++st) {
+        const int s = BLK * st + (bq % BLK);
+        const int cc = (BK == 4) ? 8 * (s >> 1) + 2 * (s & 1) : 16 * (s >> 2) + 2 * (s & 3);
+        const f32x2 h0 = *reinterpret_cast<const f32x2*>(&sm.loop.hq[hh][cc]);
+        const f32x2 h1 = *reinterpret_cast<const f32x2*>(&sm.loop.hq[hh][cc + D1]);
+        x[st][0] = h0[0] * ak[st][0];
+        x[st][1] = h1[0] * ak[st][1];
+        x[st][2] = h0[1] * ak[st][2];
+        x[st][3] = h1[1] * ak[st][3];
+        // field weights: c0 and c0 + D1 share c0's, c0 + 1 and c0 + 1 + D1 share c0 + 1's
+        const float w0 = (BK == 4) ? 1.f : ((s & 1) ? 16.f : 1.f);
+        const float w1 = (BK == 4) ? 16.f : w0 * 4.f;
+        qsum = __builtin_fmaf(x[st][0] + x[st][1], w0, qsum);
+        qsum = __builtin_fmaf(x[st][2] + x[st][3], w1, qsum);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qmax = fmaxf(qmax, fabsf(x[st][k]));
       }
-      qmax = span_max<LPH>(qmax);
-      // a power-of-two scale per head keeps the fp16 split in range
+      qmax = blocks_max<BLK>(qmax);
+      qsum = blocks_sum<BLK>(qsum);
       int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
       ex = min(max(ex, -100), 100);
       const float qscale = __uint_as_float((unsigned)(127 + 14 - ex) << 23);    // 2^(14-ex)
       const float qunscale = __uint_as_float((unsigned)(127 - 14 + ex) << 23);  // 2^(ex-14)
-      // The offset term uses the sum of the query exactly as the MFMA sees it
-      // (hi + lo), so that the split's rounding enters every score as
-      // sum_c err_c (S k_c + O), proportional to the restored key, instead of
-      // leaving S sum_c err_c k_c against O sum_c qt_c uncancelled.
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        u32x4 hi, lo;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          unsigned h, l;
-          split_pair(qv[u][2 * m] * qscale, qv[u][2 * m + 1] * qscale, h, l);
-          hi[m] = h;
-          lo[m] = l;
-          const f16x2 hh = __builtin_bit_cast(f16x2, h), ll = __builtin_bit_cast(f16x2, l);
-          const float w = field_weight<BK>(m);   // slots 2m, 2m + 1 share field m
-          qsum = __builtin_fmaf((float)hh[0], w, qsum);
-          qsum = __builtin_fmaf((float)ll[0], w, qsum);
-          qsum = __builtin_fmaf((float)hh[1], w, qsum);
-          qsum = __builtin_fmaf((float)ll[1], w, qsum);
-        }
-        sm.loop.qb[wave][0][fh][fu0 + u] = hi;
-        sm.loop.qb[wave][1][fh][fu0 + u] = lo;
+      for (int st = 0; st < SETS; ++st) {
+        unsigned h01, l01, h23, l23;
+        split_pair(x[st][0] * qscale, x[st][1] * qscale, h01, l01);
+        split_pair(x[st][2] * qscale, x[st][3] * qscale, h23, l23);
+        qa_hi[hg][st] = as_f16x4(h01, h23);
+        qa_lo[hg][st] = as_f16x4(l01, l23);
       }
-      qsum = span_sum<LPH>(qsum) * qunscale;
-      if ((lane % LPH) == 0) {
-        sm.loop.cab[wave][fh][0] = c0 * kTwo24 * qunscale;  // score = S D cab0 + O cab1
-        sm.loop.cab[wave][fh][1] = c0 * qsum;
-      }
+      cA[hg] = c0 * kTwo24 * qunscale;   // score = S D cA + O cB
+      cB[hg] = c0 * qsum;
     }
-    asm volatile("" ::: "memory");  // the reads below see this wave's writes (LDS keeps order)
-    f16x8 bq_hi[4], bq_lo[4];
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      bq_hi[ch] = __builtin_bit_cast(f16x8, sm.loop.qb[wave][0][head][ch + 4 * grp]);
-      bq_lo[ch] = __builtin_bit_cast(f16x8, sm.loop.qb[wave][1][head][ch + 4 * grp]);
-    }
-    const float sA = sm.loop.cab[wave][head][0];
-    const float sB = sm.loop.cab[wave][head][1];
+    if (more) load_alpha(next);
 
-    // -------------------------------------------- scores of the tile's pages
-    // chunk-major order: the NP pages' accumulation chains interleave
-    f32x4 d[NP];
+    // -------------------------------------------- QK: lane = token, 4 heads per group
+    f32x4 d[HG];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) d[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hg = 0; hg < HG; ++hg) d[hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_for<0, 32>([&](auto S_) {
+      constexpr int s = decltype(S_)::value;
+      f16x4 b;
+      if constexpr (BK == 4) {
+        const unsigned x = kq[s >> 3][(s >> 1) & 3], y = x >> 8;
+        if constexpr ((s & 1) == 0) b = as_f16x4(code_field<4, 0>(x, y), code_field<4, 1>(x, y));
+        else b = as_f16x4(code_field<4, 2>(x, y), code_field<4, 3>(x, y));
+      } else {
+        const unsigned x = kq[s >> 3][(s >> 2) & 1], y = x >> 8;
+        constexpr int X0 = 2 * (s & 3);
+        b = as_f16x4(code_field<2, X0>(x, y), code_field<2, X0 + 1>(x, y));
+      }
+      constexpr int st = s / BLK, abid = s % BLK;
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+      for (int hg = 0; hg < HG; ++hg) {
+        d[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(qa_hi[hg][st], b, d[hg], CB, abid, 0);
+        d[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(qa_lo[hg][st], b, d[hg], CB, abid, 0);
+      }
+    });
+    // per-head score factors of this token's tile: lane iq of its broadcast group
+    float sc[HG][4];
+    const bool past = chunk * kChunk + lane >= L;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        f16x8 a;
-        if (BK == 4) {
-          const unsigned x = kc[p][ch], y = x >> 8;
-          a = as_f16x8(code_field<4, 0>(x, y), code_field<4, 1>(x, y), code_field<4, 2>(x, y),
-                       code_field<4, 3>(x, y));
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float fa, fb;
+        if constexpr (T == 32) {
+          fa = __shfl(cA[hg], (lane & 32) + i);
+          fb = __shfl(cB[hg], (lane & 32) + i);
         } else {
-          const unsigned x = kc[p][ch >> 1], y = x >> 8;
-          if (ch & 1)
-            a = as_f16x8(code_field<2, 4>(x, y), code_field<2, 5>(x, y), code_field<2, 6>(x, y),
-                         code_field<2, 7>(x, y));
-          else
-            a = as_f16x8(code_field<2, 0>(x, y), code_field<2, 1>(x, y), code_field<2, 2>(x, y),
-                         code_field<2, 3>(x, y));
+          fa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cA[hg]), i));
+          fb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cB[hg]), i));
         }
-        d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_hi[ch], d[p], 0, 0, 0);
-        d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq_lo[ch], d[p], 0, 0, 0);
+        sc[hg][i] = past ? -INFINITY : __builtin_fmaf(fa * sk, d[hg][i], fb * ok);
+      }
+    if (more) load_k(next);
+
+    // -------------------------------------------- online softmax (base 2), per head
+    // the running max moves only when a chunk's scores pass it
+    float cmax[NH];
+    bool grow = false;
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cmax[4 * hg + i] = wave_max(sc[hg][i]);
+        grow |= cmax[4 * hg + i] > m_run[4 * hg + i];
+      }
+    if (grow) {   // wave-uniform
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const float m_new = fmaxf(m_run[h], cmax[h]);
+        const float corr = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+        m_run[h] = m_new;
+        l_run[h] *= corr;
+        acc[0][h] *= corr;
+        acc[1][h] *= corr;
       }
     }
-    float s[NP][4];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const f32x4 S = *reinterpret_cast<const f32x4*>(mK + p * META + 16 * grp);
-      const f32x4 O = *reinterpret_cast<const f32x4*>(mK + p * META + 4 * kPage + 16 * grp);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[p][r] = __builtin_fmaf(sA * S[r], d[p][r], sB * O[r]);
-    }
-    if (tile == ntiles - 1 && (L % T) != 0) {
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (tile * T + p * kPage + 4 * grp + r >= L) s[p][r] = -INFINITY;
-    }
-
-    // -------------------------------------------- online softmax (base 2)
-    // the running max moves only when some score passes it; otherwise the
-    // accumulators need no rescale (checked for the whole wave at once)
-    float tmax = s[0][0];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[p][r]);
-    tmax = group_max(tmax);
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= corr;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][r] *= corr;
-    }
-    // P = p S enters the MFMA as fp16 hi + lo; a power of two 2^k per tile,
-    // carried by the exponent of p, puts max P at 2^14..2^15 so that lo stays
-    // a normal fp16 (its 11 bits are what make hi + lo nearly fp32-exact)
-    float smax = 0.f;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const f32x4 S = *reinterpret_cast<const f32x4*>(mV + p * META + 16 * grp);
-      smax = fmaxf(smax, fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])));
-    }
-    smax = group_max(smax);   // scales are >= 0
+    // probabilities scaled by 2^k per chunk so that max P = p S_V sits at 2^14..2^15
+    float smax = fmaxf(fmaxf(svq[0], svq[1]), fmaxf(svq[2], svq[3]));
+    smax = wave_max(smax);   // scales are >= 0
     int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
     pe = min(max(pe, -100), 100);
-    const float pk = (float)(14 - pe);                                   // k
+    const float pk = (float)(14 - pe);
     const float pinv = __uint_as_float((unsigned)(127 - 14 + pe) << 23);  // 2^-k
-    const float m_lo = m_run - pk, m_hi = m_lo + kL2Tok;
-    float psa = 0.f, psb = 0.f;
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[p][r] = __builtin_amdgcn_exp2f(s[p][r] - (r < 2 ? m_lo : m_hi));
-        if (r < 2) psa += s[p][r];
-        else psb += s[p][r];
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * hg + i;
+        const float p = __builtin_amdgcn_exp2f(sc[hg][i] - (m_run[h] - pk));
+        l_run[h] = __builtin_fmaf(p, pinv, l_run[h]);
+        sm.loop.pt[wave][h][lane] = p;
       }
-    l_run = __builtin_fmaf(pinv, __builtin_fmaf(kTok, psb, psa), l_run);
+    asm volatile("" ::: "memory");  // the reads below see this wave's writes (LDS keeps order)
 
-    // -------------------------------------------- values of the tile's pages
-    float vacc[8][4];
+    // -------------------------------------------- PV A operands: P^T, lane (bq, iq) = tokens 4 bq.., head iq
+    f16x4 pa_hi[HG], pa_lo[HG];
+    float spo[HG];
+    {
+      const f32x4 sw{svq[0], svq[1], svq[2] * (1.f / kTok), svq[3] * (1.f / kTok)};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vacc[i][r] = 0.f;
-    float spa = 0.f, spb = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < NP; pp += 2) {
-      unsigned bh[4], bl[4];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const f32x4 S = *reinterpret_cast<const f32x4*>(mV + (pp + h2) * META + 16 * grp);
-        const f32x4 O = *reinterpret_cast<const f32x4*>(mV + (pp + h2) * META + 4 * kPage + 16 * grp);
-        float pw[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pw[r] = s[pp + h2][r] * S[r];
-          if (r < 2) spa = __builtin_fmaf(s[pp + h2][r], O[r], spa);
-          else spb = __builtin_fmaf(s[pp + h2][r], O[r], spb);
-        }
-        split_pair(pw[0], pw[1], bh[2 * h2], bl[2 * h2]);
-        split_pair(pw[2], pw[3], bh[2 * h2 + 1], bl[2 * h2 + 1]);
-      }
-      const f16x8 ph = as_f16x8(bh[0], bh[1], bh[2], bh[3]);
-      const f16x8 pl = as_f16x8(bl[0], bl[1], bl[2], bl[3]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        unsigned u[4];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          if (BV == 4) {
-            const unsigned x = vc[pp + h2][i >> 1], y = x >> 8;
-            if (i & 1) { u[2 * h2] = code_field<4, 2>(x, y); u[2 * h2 + 1] = code_field<4, 3>(x, y); }
-            else { u[2 * h2] = code_field<4, 0>(x, y); u[2 * h2 + 1] = code_field<4, 1>(x, y); }
-          } else {
-            const unsigned x = vc[pp + h2][i >> 2], y = x >> 8;
-            switch (i & 3) {
-              case 0: u[2 * h2] = code_field<2, 0>(x, y); u[2 * h2 + 1] = code_field<2, 1>(x, y); break;
-              case 1: u[2 * h2] = code_field<2, 2>(x, y); u[2 * h2 + 1] = code_field<2, 3>(x, y); break;
-              case 2: u[2 * h2] = code_field<2, 4>(x, y); u[2 * h2 + 1] = code_field<2, 5>(x, y); break;
-              default: u[2 * h2] = code_field<2, 6>(x, y); u[2 * h2 + 1] = code_field<2, 7>(x, y); break;
-            }
-          }
-        }
-        const f16x8 a = as_f16x8(u[0], u[1], u[2], u[3]);
-        f32x4 dv{vacc[i][0], vacc[i][1], vacc[i][2], vacc[i][3]};
-        dv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph, dv, 0, 0, 0);
-        dv = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pl, dv, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vacc[i][r] = dv[r];
+      for (int hg = 0; hg < HG; ++hg) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&sm.loop.pt[wave][4 * hg + iq][4 * bq]);
+        unsigned h01, l01, h23, l23;
+        split_pair(p4[0] * sw[0], p4[1] * sw[1], h01, l01);
+        split_pair(p4[2] * sw[2], p4[3] * sw[3], h23, l23);
+        pa_hi[hg] = as_f16x4(h01, h23);
+        pa_lo[hg] = as_f16x4(l01, l23);
+        float po = p4[0] * ovq[0];
+        po = __builtin_fmaf(p4[1], ovq[1], po);
+        po = __builtin_fmaf(p4[2], ovq[2], po);
+        po = __builtin_fmaf(p4[3], ovq[3], po);
+        spo[hg] = blocks_sum<(T == 32) ? 8 : 16>(po) * pinv;   // per tile: sum_t p_t O_t, head iq
       }
     }
-    const float spo = group_sum(__builtin_fmaf(kTok, spb, spa)) * pinv;   // sum_t p_t O_t
+
+    // -------------------------------------------- PV: lane = channel, 4 heads per group
+    f32x4 vacc[TPC][2][HG];
+#pragma unroll
+    for (int tt = 0; tt < TPC; ++tt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) vacc[tt][h][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_for<0, 16>([&](auto S_) {
+      constexpr int s = decltype(S_)::value;   // tokens 4 s .. 4 s + 3: page s / 4, quad g = s % 4
+      constexpr int g = s & 3, tt = (T == 32) ? (s >> 3) : 0;
+      f16x4 b[2];
+      if constexpr (BV == 4) {
+        const unsigned x = vq[s >> 2][g], y = x >> 8;
+        b[0] = as_f16x4(code_field<4, 0>(x, y), code_field<4, 1>(x, y));
+        b[1] = as_f16x4(code_field<4, 2>(x, y), code_field<4, 3>(x, y));
+      } else {
+        const unsigned x = vq[s >> 2][g >> 1], y = x >> 8;
+        constexpr int X0 = 4 * (g & 1);
+        b[0] = as_f16x4(code_field<2, X0>(x, y), code_field<2, X0 + 1>(x, y));
+        b[1] = as_f16x4(code_field<2, X0 + 2>(x, y), code_field<2, X0 + 3>(x, y));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          vacc[tt][h][hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa_hi[hg], b[h], vacc[tt][h][hg], 4, s, 0);
+          vacc[tt][h][hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa_lo[hg], b[h], vacc[tt][h][hg], 4, s, 0);
+        }
+    });
+    if (more) load_v(next);
 
     // -------------------------------------------- fold: acc += alpha_V (sum_t p_t S_t k_t + sum_t p_t O_t)
-    // (vacc carries 2^(k-24) times the V field weight of block i)
-    const float cf0 = kTwo24 * pinv, cf1 = (BV == 2) ? cf0 * (1.f / 16.f) : cf0;
+    // (vacc carries 2^(k-24) times the channel half's V field weight)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = 32 * grp + 8 * r;
-      const uint8_t* ap = mV + (c / AL) * META + 8 * kPage + 4 * (c % AL);
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 16);
+    for (int tt = 0; tt < TPC; ++tt)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float al = (i < 4) ? a0[i] : a1[i - 4];
-        const float t = __builtin_fmaf(vacc[i][r], (i & 1) ? cf1 : cf0, spo);
-        acc[i][r] = __builtin_fmaf(al, t, acc[i][r]);
-      }
-    }
-    buf ^= 1;
+      for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float so = (T == 32) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(spo[hg]), 32 * tt + i))
+                                     : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(spo[hg]), i));
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float cf = kTwo24 * pinv * ((BV == 2 && h == 1) ? (1.f / 16.f) : 1.f);
+            acc[h][4 * hg + i] = __builtin_fmaf(av[tt][h], __builtin_fmaf(vacc[tt][h][hg][i], cf, so), acc[h][4 * hg + i]);
+          }
+        }
+    if (more) load_av(next);
   }
 
   // ------------------------------------------------ merge the waves, write the partition's partial
-  l_run = group_sum(l_run);
+#pragma unroll
+  for (int h = 0; h < NH; ++h) l_run[h] = wave_sum(l_run[h]);
   __syncthreads();  // every wave is done with the loop buffers
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float* dst = &sm.merge.acc[wave][n16][32 * grp + 8 * r];
-    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+  for (int h = 0; h < NH; ++h) {
+    sm.merge.acc[wave][h][lane] = acc[0][h];
+    sm.merge.acc[wave][h][64 + lane] = acc[1][h];
   }
-  if (grp == 0) {
-    sm.merge.m[wave][n16] = m_run;
-    sm.merge.l[wave][n16] = l_run;
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      sm.merge.m[wave][h] = m_run[h];
+      sm.merge.l[wave][h] = l_run[h];
+    }
   }
   __syncthreads();
-  if (wave != 0 || n16 >= G) return;
-  float M = sm.merge.m[0][n16];
+  // thread -> (head, 4 channels)
+  for (int it = threadIdx.x; it < G * 32; it += 64 * kWaves) {
+    const int h = it >> 5, c = 4 * (it & 31);
+    float M = sm.merge.m[0][h];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.merge.m[w][n16]);
-  float wt[kWaves], lsum = 0.f;
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.merge.m[w][h]);
+    float wt[kWaves], lsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = sm.merge.m[w][n16];
-    wt[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    lsum = __builtin_fmaf(wt[w], sm.merge.l[w][n16], lsum);
-  }
-  const size_t pidx = ((size_t)seq * A.q_heads + kvh * G + n16) * A.max_parts + part;
-  float* dst = A.ws_acc + pidx * kHeadDim + 32 * grp;
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.merge.m[w][h];
+      wt[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      lsum = __builtin_fmaf(wt[w], sm.merge.l[w][h], lsum);
+    }
     f32x4 x{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.merge.acc[w][n16][32 * grp + 4 * v]);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.merge.acc[w][h][c]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(wt[w], y[e], x[e]);
     }
-    *reinterpret_cast<f32x4*>(dst + 4 * v) = x;
-  }
-  if (grp == 0) {
-    A.ws_ml[2 * pidx] = M;
-    A.ws_ml[2 * pidx + 1] = lsum;
+    const size_t pidx = ((size_t)seq * A.q_heads + kvh * G + h) * A.max_parts + part;
+    *reinterpret_cast<f32x4*>(A.ws_acc + pidx * kHeadDim + c) = x;
+    if (c == 0) {
+      A.ws_ml[2 * pidx] = M;
+      A.ws_ml[2 * pidx + 1] = lsum;
+    }
   }
 }
 
@@ -690,7 +699,7 @@ hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, 
         else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4>), grid, dim3(64 * kWaves), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        return launch_combine(a, T(), true, s);
+        return launch_combine(a, kChunk, true, s);
       });
     });
   });

@@ -60,9 +60,8 @@ struct alignas(16) Smem {
   float nmi[T];                   // -min * inv per row
 };
 
-// Packs 8 codes (values v[idx[i]] rounded to nearest even by v_cvt_pk_u8_f32)
-// into one 32-bit word whose field f (bits [BITS*f, BITS*(f+1))) takes the
-// code listed at position f of `order`.
+// Packs N codes into one 32-bit word: field f (bits [BITS*f, BITS*(f+1)))
+// takes v[f] rounded to nearest even by v_cvt_pk_u8_f32.
 template <int BITS, int N>
 __device__ __forceinline__ unsigned pack_fields(const float (&v)[N]) {
   constexpr int PER = 8 / BITS;  // fields per byte
@@ -455,27 +454,41 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
       }
     }
   } else {
-    // V slot: quads of 4 tokens, groups of 8 channels; word w holds channels
-    // j < F/4 of the group's word, field 2j + (r>>1) + (F/2)(r&1).
+    // V slot: run l (4*BITS bytes at 4*BITS*l) holds channels l and 64 + l of
+    // the page's 16 tokens; token 4g + r of half h is pair p = 2g + h, in word
+    // p / (F/4) of the run, field 2m + (r>>1) + (F/2)(r&1), m = p mod (F/4).
+    // This thread holds quad g (its 4 tokens) of the runs 8 cg + j (its
+    // channels j and 8 + j), so it builds its pairs' fields of every run.
     constexpr int F = 32 / BITS;
     uint8_t* slot = slot_ptr((4 * tq) / kPage);
-    const int quad = tq % (kPage / 4);
+    const int g = tq % (kPage / 4);
+    unsigned w8[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint8_t* dst = slot + quad * (16 * BITS * 4) + (8 * half + cg) * (4 * BITS);
-      unsigned words[BITS];
+    for (int j = 0; j < 8; ++j) {
+      float o[F];
 #pragma unroll
-      for (int w = 0; w < BITS; ++w) {
-        float o[F];
+      for (int f = 0; f < F; ++f) o[f] = 0.f;
 #pragma unroll
-        for (int j = 0; j < F / 4; ++j)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            o[2 * j + (r >> 1) + (F / 2) * (r & 1)] = R[r][8 * half + (F / 4) * w + j];
-        words[w] = pack_fields<BITS>(o);
+        for (int r = 0; r < 4; ++r) o[2 * h + (r >> 1) + (F / 2) * (r & 1)] = R[r][8 * h + j];
+      w8[j] = pack_fields<BITS>(o);   // fields of m = h; m = 2 (g & 1) + h for 2-bit is a shift
+    }
+    if (BITS == 4) {
+      // one word per (run, quad): this thread's alone
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(slot + 16 * (8 * cg + j) + 4 * g) = w8[j];
+    } else {
+      // one word per (run, quad pair): merge with the thread of quad g ^ 1
+      // (lane ^ 8); the even quad's thread writes runs j < 4, the odd one j >= 4
+      const bool odd = (g & 1) != 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned mine = (odd ? w8[j + 4] : w8[j]) << (odd ? 8 : 0);
+        const unsigned give = (odd ? w8[j] : w8[j + 4]) << (odd ? 8 : 0);
+        const unsigned got = (unsigned)__float_as_int(lane_xor<8>(__int_as_float((int)give)));
+        *reinterpret_cast<uint32_t*>(slot + 8 * (8 * cg + j + (odd ? 4 : 0)) + 4 * (g >> 1)) = mine | got;
       }
-      if (BITS == 4) *reinterpret_cast<u32x4*>(dst) = u32x4{words[0], words[1], words[2], words[3]};
-      else *reinterpret_cast<u32x2*>(dst) = u32x2{words[0], words[1]};
     }
   }
 }

@@ -267,11 +267,12 @@ def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits:
 # Code layouts of a slot (d = 128):
 #   K slots: four blocks of 32 channels; block k holds, token after token, the
 #     32 channels 32k..32k+31 of each of the 16 tokens in natural packing.
-#   V slots: four quads of 4 tokens; quad q holds 16 groups of 8 channels; a
-#     group is 4*bits bytes read as little-endian 32-bit words; word w holds
-#     channels 8m + w*F/4 + j (j < F/4, F = 32/bits fields per word) of the 4
-#     tokens 4q + r, channel j / token r in field 2j + (r >> 1) + (F/2)(r & 1),
-#     a field being bits [bits*f, bits*(f+1)) of the word.
+#   V slots: 64 runs of 4*bits bytes, run l (at byte 4*bits*l) holding the
+#     channels l (h = 0) and 64 + l (h = 1) of all 16 tokens, read as
+#     little-endian 32-bit words of F = 32/bits fields.  Token t = 4g + r
+#     (quad g, r < 4) of channel half h is pair p = 2g + h; word p // (F/4) of
+#     the run, field 2m + (r >> 1) + (F/2)(r & 1) with m = p % (F/4), a field
+#     being bits [bits*f, bits*(f+1)) of the word.
 # Rows of a page past the sequence's end hold code 0, scale 0 and offset 0.
 # ----------------------------------------------------------------------------
 
@@ -305,14 +306,17 @@ def bytes_to_k_codes(raw: np.ndarray, bits: int) -> np.ndarray:
     return codes
 
 
-def _v_field(bits: int, c: int, r: int):
-    """(byte offset inside a quad, word index, field index) of channel c, token-in-quad r."""
+def _v_field(bits: int, c: int, t: int):
+    """(byte offset of the 32-bit word in the V code area, field index) of
+    channel c, token t of a page."""
     f_per_word = 32 // bits
-    ch_per_word = f_per_word // 4
-    m, cw = divmod(c, 8)
-    w, j = divmod(cw, ch_per_word)
-    field = 2 * j + (r >> 1) + (f_per_word // 2) * (r & 1)
-    return m * 4 * bits + 4 * w, field
+    pairs_per_word = f_per_word // 4
+    run, h = c % 64, c // 64
+    g, r = divmod(t, 4)
+    p = 2 * g + h
+    word, m = divmod(p, pairs_per_word)
+    field = 2 * m + (r >> 1) + (f_per_word // 2) * (r & 1)
+    return 4 * bits * run + 4 * word, field
 
 
 _V_MAPS = {}
@@ -322,14 +326,12 @@ def _v_map(bits: int):
     """For every (token, channel) of a page: index of its 32-bit word in the
     V-slot code area and the bit shift of its field (from _v_field)."""
     if bits not in _V_MAPS:
-        quad_bytes = 4 * HEAD_DIM * bits // 8
         word = np.zeros((PAGE_TOKENS, HEAD_DIM), np.int64)
         shift = np.zeros((PAGE_TOKENS, HEAD_DIM), np.int64)
         for t in range(PAGE_TOKENS):
-            q, r = divmod(t, 4)
             for c in range(HEAD_DIM):
-                off, field = _v_field(bits, c, r)
-                word[t, c] = (q * quad_bytes + off) // 4
+                off, field = _v_field(bits, c, t)
+                word[t, c] = off // 4
                 shift[t, c] = bits * field
         _V_MAPS[bits] = (word, shift)
     return _V_MAPS[bits]
