@@ -489,22 +489,35 @@ def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: flo
     return p @ values.astype(np.float64)
 
 
+def attention_abs_scale(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: float) -> float:
+    """max over channels of sum_t p_t |v_t| for the attention above: the size
+    of the terms an output channel sums (its rounding scale in fp32)."""
+    s = sm_scale * (keys.astype(np.float64) @ np.asarray(q, np.float64))
+    p = np.exp(s - s.max())
+    p = p / p.sum()
+    return float((p @ np.abs(values.astype(np.float64))).max())
+
+
 def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
-                      sm_scale=None):
+                      sm_scale=None, return_scale=False):
     """q fp16 [S, Hq, d]; seq_lens count every cached token (the newest included).
-    Query head h reads kv head h // (Hq / Hkv).  Returns float64 [S, Hq, d]."""
+    Query head h reads kv head h // (Hq / Hkv).  Returns float64 [S, Hq, d]
+    (and, with return_scale, attention_abs_scale per [S, Hq])."""
     s_n, hq, d = q.shape
     hkv = pool_k.shape[1]
     g = hq // hkv
     sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
     out = np.zeros((s_n, hq, d))
+    scale = np.zeros((s_n, hq))
     for s in range(s_n):
         for kh in range(hkv):
             kx = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens)[0]
             vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens)[0]
             for h in range(kh * g, (kh + 1) * g):
                 out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
-    return out
+                if return_scale:
+                    scale[s, h] = attention_abs_scale(q[s, h], kx, vx, sm)
+    return (out, scale) if return_scale else out
 
 
 # ----------------------------------------------------------------------------

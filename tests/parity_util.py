@@ -18,7 +18,12 @@
   The codes check above is the binding one: it fails if a metadata error
   moves any code outside the window.
 * Restored values: |gpu - ref| <= DEQ_RTOL * max(|ref|, rms of the token row).
-* Attention outputs: absolute error <= ATTN_ATOL (fp32 accumulation).
+* Attention outputs: absolute error <= ATTN_ATOL (fp32 accumulation), plus
+  ATTN_ULPS units of 2^-24 times the output's own scale max_c sum_t p_t |v_t,c|
+  where the oracle supplies it.  For outputs of unit size the second term is
+  negligible; for heavy-tailed values (|v| ~ 1e4, where 2e-3 is about two fp32
+  ulps and plain fp32 attention over the same restored pages already errs by
+  ~1.4e-3) it admits a fixed number of fp32 roundings of that scale.
 """
 import numpy as np
 
@@ -26,6 +31,7 @@ WINDOW = 1e-3
 META_RTOL = 1e-4
 DEQ_RTOL = 1e-3
 ATTN_ATOL = 2e-3
+ATTN_ULPS = 16
 SHORT_TILE = 16
 SHORT_DEQ_RTOL = 1e-2
 
@@ -75,11 +81,21 @@ def assert_dequant(gpu, ref, what="", rtol=DEQ_RTOL):
     return float((np.abs(gpu - ref) / np.maximum(np.abs(ref), rms)).max())
 
 
-def assert_attn(gpu, ref, what=""):
+def attn_tol(scale=None):
+    """Per-row attention tolerance; scale [..., ] as from the oracle's
+    attention_abs_scale (None: the absolute bar alone)."""
+    if scale is None:
+        return ATTN_ATOL
+    return ATTN_ATOL + ATTN_ULPS * 2.0 ** -24 * np.asarray(scale, np.float64)[..., None]
+
+
+def assert_attn(gpu, ref, what="", scale=None):
     err = np.abs(np.asarray(gpu, np.float64) - np.asarray(ref, np.float64))
-    if not (err <= ATTN_ATOL).all():
-        i = np.argwhere(err > ATTN_ATOL)[0]
-        raise AssertionError(f"{what}: attention abs err {err.max():.3e} > {ATTN_ATOL} at {tuple(i)}")
+    tol = np.broadcast_to(attn_tol(scale), err.shape)
+    if not (err <= tol).all():
+        i = np.argwhere(err > tol)[0]
+        raise AssertionError(f"{what}: attention abs err {err[tuple(i)]:.3e} > {tol[tuple(i)]:.3e} at {tuple(i)} "
+                             f"(ref {np.asarray(ref)[tuple(i)]:.6g}); max err {err.max():.3e}")
     return float(err.max())
 
 

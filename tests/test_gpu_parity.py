@@ -212,8 +212,8 @@ def test_paged_decode_parity(case):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
-    ref = orc.paged_decode_attn(q, table, seq_lens, gpk, gpv, tile, bk, bv)
-    err = pu.assert_attn(got, ref, f"decode {case}")
+    ref, sc = orc.paged_decode_attn(q, table, seq_lens, gpk, gpv, tile, bk, bv, return_scale=True)
+    err = pu.assert_attn(got, ref, f"decode {case}", sc)
     # informative: against the oracle's own pages (quantization error included)
     ref_pk = orc.new_pool(npages, hkv, bk, tile)
     ref_pv = orc.new_pool(npages, hkv, bv, tile)
@@ -246,9 +246,9 @@ def test_append_then_decode_matches_oracle():
     q = inputs.gen_q(wl, step=0)
     out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(lens + 1).cuda(), int(lens.max()) + 1)
     torch.cuda.synchronize()
-    ref = orc.paged_decode_attn(q, table, lens + 1, cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy(),
-                                64, 4, 4)
-    pu.assert_attn(out.cpu().numpy(), ref, "append+decode")
+    ref, sc = orc.paged_decode_attn(q, table, lens + 1, cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy(),
+                                    64, 4, 4, return_scale=True)
+    pu.assert_attn(out.cpu().numpy(), ref, "append+decode", sc)
 
 
 BASELINE_CASES = [
@@ -340,9 +340,10 @@ def _sampled_tile_checks(wl, k, v, table, gpk, gpv, rng, n_samples, what):
 def _sampled_decode_checks(wl, q, table, lens, gpk, gpv, got, pairs, what):
     g = wl.group
     for s, kh in pairs:
-        ref = orc.paged_decode_attn(q[s:s + 1, kh * g:(kh + 1) * g], table[s:s + 1], lens[s:s + 1],
-                                    gpk[:, kh:kh + 1], gpv[:, kh:kh + 1], wl.tile_tokens, wl.bits_k, wl.bits_v)
-        err = pu.assert_attn(got[s, kh * g:(kh + 1) * g], ref[0], f"{what} s{s} kv head {kh}")
+        ref, sc = orc.paged_decode_attn(q[s:s + 1, kh * g:(kh + 1) * g], table[s:s + 1], lens[s:s + 1],
+                                        gpk[:, kh:kh + 1], gpv[:, kh:kh + 1], wl.tile_tokens, wl.bits_k, wl.bits_v,
+                                        return_scale=True)
+        err = pu.assert_attn(got[s, kh * g:(kh + 1) * g], ref[0], f"{what} s{s} kv head {kh}", sc[0])
         print(f"[attn] {what} s{s} kv head {kh} (L={int(lens[s])}): max abs err {err:.2e}", flush=True)
 
 

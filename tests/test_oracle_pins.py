@@ -369,6 +369,21 @@ def test_attention_degenerate_cases():
     np.testing.assert_allclose(orc.attention(q, same, v, 0.1), v.mean(0), atol=1e-14)
 
 
+def test_attention_abs_scale_special_cases():
+    """sum_t p_t |v_t| (max over channels): one token gives max |v|; equal keys
+    give the largest channel mean of |v|; v >= 0 gives the largest output."""
+    rng = _rng(23)
+    q = rng.standard_normal(128)
+    v = rng.standard_normal((6, 128))
+    k1 = rng.standard_normal((1, 128))
+    assert orc.attention_abs_scale(q, k1, v[:1], 0.1) == np.abs(v[0]).max()
+    same = np.repeat(rng.standard_normal((1, 128)), 6, axis=0)
+    np.testing.assert_allclose(orc.attention_abs_scale(q, same, v, 0.1), np.abs(v).mean(0).max(), rtol=1e-14)
+    k = rng.standard_normal((6, 128))
+    np.testing.assert_allclose(orc.attention_abs_scale(q, k, np.abs(v), 0.1), orc.attention(q, k, np.abs(v), 0.1).max(),
+                               rtol=1e-13)
+
+
 def _paged_case(shuffled, seq_len=150, hkv=2, hq=8):
     base = inputs.workload(1)
     import dataclasses
