@@ -211,6 +211,28 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * kvq_append_and_decode - one decode step in one launch (plus the partition
+ * merge): the new token is compressed into the cache inside the pipeline and
+ * the attention reads the compressed pages, the new token included (ttj.kr
+ * page, section "양자화로 캐시를 다이어트시킨다"; aitrends.kr article 74976,
+ * TL;DR).  Equivalent to kvq_append_and_requant of (k_new, v_new) at position
+ * seq_lens_before[s] followed by kvq_paged_decode_attn over
+ * seq_lens_before[s] + 1 tokens: arguments as those two functions
+ * (max_seq_len bounds seq_lens_before + 1; the workspace is sized by
+ * kvq_decode_workspace_bytes for max_seq_len), and the pages, staging rows and
+ * output are bit-identical to those of the two calls made in order.  The
+ * re-quantized tile is read only by the last partition of its (sequence, kv
+ * head), whose workgroup writes it before attending.  Errors as those two
+ * functions.
+ */
+kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                 const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                 kvq_half* staging_k, kvq_half* staging_v, const int32_t* block_table,
+                                 int32_t max_blocks, void* pool_k, void* pool_v, const kvq_half* q,
+                                 int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Baselines (fp16 and fp8 paged KV without the quantizer), for comparing the
  * quantized read path with the two modes the aitrends.kr page (article
  * 74976, TL;DR) runs on the same workload.  Page layout per (page, kv head):

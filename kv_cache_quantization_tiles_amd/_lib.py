@@ -20,7 +20,7 @@ EXPORTED = (
     "kvq_quantize_to_pages", "kvq_append_and_requant", "kvq_decode_workspace_bytes",
     "kvq_paged_decode_attn", "kvq_bandwidth_probe", "kvq_baseline_page_bytes", "kvq_fill_pages_fp16",
     "kvq_fill_pages_fp8", "kvq_baseline_workspace_bytes", "kvq_paged_decode_attn_fp16",
-    "kvq_paged_decode_attn_fp8",
+    "kvq_paged_decode_attn_fp8", "kvq_append_and_decode",
 )
 
 
@@ -69,6 +69,8 @@ def load():
                                           ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
     lib.kvq_bandwidth_probe.argtypes = [_P, _P, ctypes.c_size_t, _P]
     _F = ctypes.c_float
+    lib.kvq_append_and_decode.argtypes = [_CFG, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I, _F, _P,
+                                          _P, ctypes.c_size_t, _P]
     lib.kvq_baseline_page_bytes.argtypes = [_I]
     lib.kvq_baseline_page_bytes.restype = ctypes.c_size_t
     lib.kvq_fill_pages_fp16.argtypes = [_CFG, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P]
@@ -82,7 +84,7 @@ def load():
     for name in ("kvq_quantize_tiles", "kvq_dequantize", "kvq_quantize_to_pages",
                  "kvq_append_and_requant", "kvq_paged_decode_attn", "kvq_bandwidth_probe",
                  "kvq_fill_pages_fp16", "kvq_fill_pages_fp8", "kvq_paged_decode_attn_fp16",
-                 "kvq_paged_decode_attn_fp8"):
+                 "kvq_paged_decode_attn_fp8", "kvq_append_and_decode"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -204,3 +206,13 @@ def kvq_paged_decode_attn_fp8(cfg, q, num_seqs, q_heads, kv_heads, block_table, 
                                             _ptr(pool_k), _ptr(pool_v), float(k_scale), float(v_scale),
                                             float(sm_scale), _ptr(out), _ptr(workspace), workspace_bytes,
                                             _stream(stream)))
+
+
+def kvq_append_and_decode(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, staging_k, staging_v,
+                          block_table, max_blocks, pool_k, pool_v, q, q_heads, max_seq_len, sm_scale, out,
+                          workspace, workspace_bytes, stream=None):
+    _check(load().kvq_append_and_decode(ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(seq_lens_before),
+                                        num_seqs, kv_heads, _ptr(staging_k), _ptr(staging_v), _ptr(block_table),
+                                        max_blocks, _ptr(pool_k), _ptr(pool_v), _ptr(q), q_heads, max_seq_len,
+                                        float(sm_scale), _ptr(out), _ptr(workspace), workspace_bytes,
+                                        _stream(stream)))

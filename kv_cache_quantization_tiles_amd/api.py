@@ -11,7 +11,7 @@ import math
 import torch
 
 from . import _lib
-from ._lib import (config, kvq_append_and_requant, kvq_baseline_page_bytes,  # noqa: F401
+from ._lib import (config, kvq_append_and_decode, kvq_append_and_requant, kvq_baseline_page_bytes,  # noqa: F401
                    kvq_baseline_workspace_bytes, kvq_decode_workspace_bytes, kvq_dequantize,
                    kvq_fill_pages_fp8, kvq_fill_pages_fp16, kvq_paged_decode_attn,
                    kvq_paged_decode_attn_fp8, kvq_paged_decode_attn_fp16, kvq_quantize_tiles,
@@ -95,6 +95,22 @@ class PagedCache:
                               self.max_blocks, seq_lens, int(max_seq_len), self.pool_k, self.pool_v, sm,
                               out, workspace, workspace.numel())
         return out
+
+    def append_decode(self, k_new, v_new, lens_before, q, max_seq_len, out=None, workspace=None, sm_scale=None):
+        """Append one token per sequence and attend over every cached token, in one
+        launch (max_seq_len bounds the lengths after the append)."""
+        _require_cuda(k_new, v_new, lens_before, q)
+        s, hq, d = q.shape
+        if out is None:
+            out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(hq, max_seq_len)
+        sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        kvq_append_and_decode(self.cfg, k_new, v_new, lens_before, self.num_seqs, self.kv_heads, self.staging_k,
+                              self.staging_v, self.block_table, self.max_blocks, self.pool_k, self.pool_v,
+                              q.contiguous(), hq, int(max_seq_len), sm, out, workspace, workspace.numel())
+        return out
+
 
 
 class BaselineCache:

@@ -281,6 +281,79 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
                   "kvq_paged_decode_attn");
 }
 
+kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                 const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                 kvq_half* staging_k, kvq_half* staging_v, const int32_t* block_table,
+                                 int32_t max_blocks, void* pool_k, void* pool_v, const kvq_half* q,
+                                 int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  KVQ_TRY(check_config(cfg, true));
+  KVQ_NONNULL(k_new);
+  KVQ_NONNULL(v_new);
+  KVQ_NONNULL(seq_lens_before);
+  KVQ_NONNULL(staging_k);
+  KVQ_NONNULL(staging_v);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  KVQ_NONNULL(q);
+  KVQ_NONNULL(out);
+  KVQ_NONNULL(workspace);
+  if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, q_heads, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (q_heads % kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "q_heads %d is not a multiple of kv_heads %d", q_heads, kv_heads);
+  const int group = q_heads / kv_heads;
+  if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d larger than 16", group);
+  if (kv_heads > 65535 || num_seqs > 65535 || (long)num_seqs * q_heads > 2147483647L)
+    return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  const int tile = cfg->tile_tokens;
+  const long need_blocks = (long)((max_seq_len + tile - 1) / tile) * (tile / kvq::kPage);
+  if (need_blocks > max_blocks)
+    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens in whole tiles", max_blocks, max_seq_len);
+  const size_t need = kvq_decode_workspace_bytes(cfg, num_seqs, q_heads, kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const int tpp = chunks_per_partition(num_seqs, kv_heads, max_seq_len, tile);
+  const int parts = max_partitions(max_seq_len, 64, tpp);
+  if (tpp > 64 || parts > 1024)
+    return fail(KVQ_ERR_UNSUPPORTED, "max_seq_len %d is beyond 65536 chunks of 64 tokens", max_seq_len);
+  kvq::DecodeArgs a{};
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens_before;
+  a.pool_k = (const uint8_t*)pool_k;
+  a.pool_v = (const uint8_t*)pool_v;
+  a.out = out;
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = (float*)workspace + (size_t)num_seqs * q_heads * parts * kvq::kHeadDim;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks;
+  a.tiles_per_part = tpp;
+  a.max_parts = parts;
+  a.max_tiles = (max_seq_len + 63) / 64;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.unit_tokens = 64;
+  a.out_scale = 1.0f;
+  kvq::QuantArgs qa{};
+  qa.src[0] = k_new;
+  qa.src[1] = v_new;
+  qa.pool[0] = (uint8_t*)pool_k;
+  qa.pool[1] = (uint8_t*)pool_v;
+  qa.staging[0] = staging_k;
+  qa.staging[1] = staging_v;
+  qa.lens_before = seq_lens_before;
+  qa.block_table = block_table;
+  qa.max_blocks = max_blocks;
+  qa.kv_heads = kv_heads;
+  qa.iters = cfg->sinkhorn_iters;
+  return launched(kvq::launch_append_decode(a, qa, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
+                  "kvq_append_and_decode");
+}
+
 size_t kvq_baseline_page_bytes(int32_t fp8) { return (size_t)kvq::kPage * kvq::kHeadDim * (fp8 ? 1 : 2); }
 
 static kvq_status fill_baseline(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,

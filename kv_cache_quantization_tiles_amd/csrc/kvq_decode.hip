@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "kvq_internal.h"
+#include "kvq_tile.h"
 
 namespace kvq {
 namespace {
@@ -107,17 +108,21 @@ __device__ __forceinline__ f16x4 as_f16x4(unsigned a, unsigned b) {
   return __builtin_bit_cast(f16x4, u32x2{a, b});
 }
 
-// fp32 pair -> fp16 pair hi (nearest even) and the fp16 pair lo of what is
-// left (x - hi is exact in fp32; v_fma_mix_f32 reads hi's halves as fp16).
-// hi + lo carries x to ~2^-22 relative, without bias.
-__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
-  const unsigned hb = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, f16x2));
-  float r0, r1;
-  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(hb), "v"(x0));
-  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r1) : "v"(hb), "v"(x1));
-  hi = hb;
-  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, f16x2));
+// fp32 pair -> fp16 pair hi, x rounded (nearest even) to a multiple of 1/w,
+// and the fp16 pair lo = x - hi (the subtraction is exact; lo is rounded).
+// m = 1.5 * 2^23 / w: adding it leaves 1/w as the ulp, so (x + m) - m is
+// the rounded x for |x| w < 2^22.  With w the code field's weight and
+// |x| w <= 2^11, hi is exact in fp16 and every product hi * (code w 2^-24)
+// is an integer multiple of 2^-24: an MFMA chain over hi then sums exactly
+// (its partial sums stay below 2^24 units), where products of unrelated
+// exponents would lose low bits in the MFMA's adder.  lo runs in a chain of
+// its own, 2^-11 smaller.
+__device__ __forceinline__ void split_grid(float x0, float x1, float m0, float m1, unsigned& hi, unsigned& lo) {
+  const float h0 = (x0 + m0) - m0, h1 = (x1 + m1) - m1;
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{h0, h1}, f16x2));
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, f16x2));
 }
+constexpr float kGrid = 12582912.f;   // 1.5 * 2^23
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, lane_xor<1>(v));
@@ -183,8 +188,25 @@ struct alignas(16) DecodeSmem {
 //        broadcast from block = step), B = the lane's channel's codes.
 //        Output: lane = channel l (and 64 + l), 4 heads.
 // Groups of more than 4 heads run 4 at a time (HG groups) on the same codes.
-template <int T, int BK, int BV, int HG>
-__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
+// Shared memory of the decode kernel; with FUSED, the tile quantizer's
+// buffers (one per concurrent quantizer group of 2T threads) overlay it.
+template <int T, int HG, bool FUSED>
+struct alignas(16) DecodeSmemU {
+  static constexpr int QG = FUSED ? (64 * kWaves) / (2 * T) : 0;
+  union {
+    DecodeSmem<T, HG> dec;
+    Smem<T> q[QG > 0 ? QG : 1];
+  };
+};
+
+// FUSED: the same decode step preceded by the append of one token per
+// sequence (A.seq_lens then holds the lengths before it; the attention covers
+// one more token).  The append re-quantizes the token's (partial) tile, whose
+// pages only the last partition of each (sequence, kv head) reads, so that
+// workgroup does it first (K and V tiles side by side, 2T threads each) and
+// the write-to-read order stays inside one workgroup.
+template <int T, int BK, int BV, int HG, bool FUSED>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, QuantArgs Q) {
   constexpr int NH = 4 * HG;
   constexpr int SETS = (T == 32) ? 4 : 2;        // QK A register sets
   constexpr int BLK = 32 / SETS;                 // steps per set = blocks per broadcast group
@@ -199,19 +221,43 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
   // their probabilities enter the MFMA divided by kTok.
   constexpr float kTok = (BV == 4) ? 16.f : 4.f;
   constexpr float kTwo24 = 16777216.f;
-  __shared__ DecodeSmem<T, HG> sm;
+  __shared__ DecodeSmemU<T, HG, FUSED> smu;
+  auto& sm = smu.dec;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
   const int bq = lane >> 2, iq = lane & 3;       // MFMA block and row/column of this lane
   const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int G = A.group;
-  const int L = A.seq_lens[seq];
+  const int L = A.seq_lens[seq] + (FUSED ? 1 : 0);
   const int nchunks = min((L + kChunk - 1) / kChunk, A.max_tiles);
   const int c_begin = part * A.tiles_per_part;
   const int c_end = min(nchunks, c_begin + A.tiles_per_part);
   if (c_begin >= c_end) return;  // uniform over the workgroup
   const int H = A.kv_heads;
+  if constexpr (FUSED) {
+    if (c_end == nchunks) {   // the last partition: append, then attend
+      const int tile_idx = (L - 1) / T;
+      if ((tile_idx + 1) * (T / kPage) <= Q.max_blocks) {
+        constexpr int QG = DecodeSmemU<T, HG, FUSED>::QG;
+        const int g = threadIdx.x / (2 * T), tid = threadIdx.x % (2 * T);
+        if constexpr (QG == 1) {
+          quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[0], 0, kvh, seq, tile_idx, tid);
+          __syncthreads();
+          quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[0], 1, kvh, seq, tile_idx, tid);
+        } else {
+          // groups 2j and 2j + 1 quantize K and V; with 4 groups (tile 32) the
+          // second pair repeats the first, writing the same bytes, so that every
+          // wave meets the quantizer's barriers
+          if ((g & 1) == 0) quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[g], 0, kvh, seq, tile_idx, tid);
+          else quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[g], 1, kvh, seq, tile_idx, tid);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
   const int npages = ((L + T - 1) / T) * PPT;   // pages the sequence owns (whole tiles)
   // the partition's page ids (up to the end of its last tile), staged once in LDS
   {
@@ -354,6 +400,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     // as fp16 hi / lo; qsum and the power-of-two scale per (head, tile)
     f16x4 qa_hi[HG][SETS], qa_lo[HG][SETS];
     float cA[HG], cB[HG];
+    // field weights of this lane's steps: c0 and c0 + D1 share c0's, c0 + 1 and
+    // c0 + 1 + D1 share c0 + 1's (for 2-bit codes, c0's depends on the step's
+    // parity, which is bq's)
+    const float w0 = (BK == 4) ? 1.f : ((bq & 1) ? 16.f : 1.f);
+    const float w1 = (BK == 4) ? 16.f : w0 * 4.f;
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
       const int hh = 4 * hg + iq;
@@ -369,37 +420,52 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
         x[st][1] = h1[0] * ak[st][1];
         x[st][2] = h0[1] * ak[st][2];
         x[st][3] = h1[1] * ak[st][3];
-        // field weights: c0 and c0 + D1 share c0's, c0 + 1 and c0 + 1 + D1 share c0 + 1's
-        const float w0 = (BK == 4) ? 1.f : ((s & 1) ? 16.f : 1.f);
-        const float w1 = (BK == 4) ? 16.f : w0 * 4.f;
-        qsum = __builtin_fmaf(x[st][0] + x[st][1], w0, qsum);
-        qsum = __builtin_fmaf(x[st][2] + x[st][3], w1, qsum);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) qmax = fmaxf(qmax, fabsf(x[st][k]));
+        // the bound is on qt itself: x times the field weight
+        qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(x[st][0]), fabsf(x[st][1])) * w0, fmaxf(fabsf(x[st][2]), fabsf(x[st][3])) * w1));
       }
       qmax = blocks_max<BLK>(qmax);
-      qsum = blocks_sum<BLK>(qsum);
       int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
       ex = min(max(ex, -100), 100);
-      const float qscale = __uint_as_float((unsigned)(127 + 14 - ex) << 23);    // 2^(14-ex)
-      const float qunscale = __uint_as_float((unsigned)(127 - 14 + ex) << 23);  // 2^(ex-14)
+      // scaled qt below 2^11: its hi part is an integer of at most 11 bits
+      const float qscale = __uint_as_float((unsigned)(127 + 10 - ex) << 23);    // 2^(10-ex)
+      const float qunscale = __uint_as_float((unsigned)(127 - 10 + ex) << 23);  // 2^(ex-10)
+      // The offset term takes the sum of the query as the MFMA sees it (hi + lo):
+      // the split's rounding then enters each score as sum_c err_c (S k_c + O),
+      // in proportion to the restored key.  (With the exact sum it would leave
+      // S sum_c err_c k_c against O sum_c qt_c, and in tiles of a few tokens,
+      // where S and O reach 1e4..1e5 and nearly cancel, that costs ~1e-3.)
+      const float g0 = kGrid / w0, g1 = kGrid / w1;
 #pragma unroll
       for (int st = 0; st < SETS; ++st) {
         unsigned h01, l01, h23, l23;
-        split_pair(x[st][0] * qscale, x[st][1] * qscale, h01, l01);
-        split_pair(x[st][2] * qscale, x[st][3] * qscale, h23, l23);
+        split_grid(x[st][0] * qscale, x[st][1] * qscale, g0, g0, h01, l01);
+        split_grid(x[st][2] * qscale, x[st][3] * qscale, g1, g1, h23, l23);
         qa_hi[hg][st] = as_f16x4(h01, h23);
         qa_lo[hg][st] = as_f16x4(l01, l23);
+        const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, l01);
+        const f16x2 c = __builtin_bit_cast(f16x2, h23), e = __builtin_bit_cast(f16x2, l23);
+        qsum = __builtin_fmaf((float)a[0], w0, qsum);
+        qsum = __builtin_fmaf((float)b[0], w0, qsum);
+        qsum = __builtin_fmaf((float)a[1], w0, qsum);
+        qsum = __builtin_fmaf((float)b[1], w0, qsum);
+        qsum = __builtin_fmaf((float)c[0], w1, qsum);
+        qsum = __builtin_fmaf((float)e[0], w1, qsum);
+        qsum = __builtin_fmaf((float)c[1], w1, qsum);
+        qsum = __builtin_fmaf((float)e[1], w1, qsum);
       }
+      qsum = blocks_sum<BLK>(qsum) * qunscale;
       cA[hg] = c0 * kTwo24 * qunscale;   // score = S D cA + O cB
       cB[hg] = c0 * qsum;
     }
     if (more) load_alpha(next);
 
     // -------------------------------------------- QK: lane = token, 4 heads per group
-    f32x4 d[HG];
+    f32x4 d[HG], dl[HG];   // hi chain (exact) and lo chain
 #pragma unroll
-    for (int hg = 0; hg < HG; ++hg) d[hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hg = 0; hg < HG; ++hg) {
+      d[hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dl[hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     static_for<0, 32>([&](auto S_) {
       constexpr int s = decltype(S_)::value;
       f16x4 b;
@@ -416,7 +482,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         d[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(qa_hi[hg][st], b, d[hg], CB, abid, 0);
-        d[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(qa_lo[hg][st], b, d[hg], CB, abid, 0);
+        dl[hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(qa_lo[hg][st], b, dl[hg], CB, abid, 0);
       }
     });
     // per-head score factors of this token's tile: lane iq of its broadcast group
@@ -434,7 +500,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
           fa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cA[hg]), i));
           fb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cB[hg]), i));
         }
-        sc[hg][i] = past ? -INFINITY : __builtin_fmaf(fa * sk, d[hg][i], fb * ok);
+        sc[hg][i] = past ? -INFINITY : __builtin_fmaf(fa * sk, d[hg][i] + dl[hg][i], fb * ok);
       }
     if (more) load_k(next);
 
@@ -460,13 +526,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
         acc[1][h] *= corr;
       }
     }
-    // probabilities scaled by 2^k per chunk so that max P = p S_V sits at 2^14..2^15
+    // probabilities scaled by 2^k per chunk so that P = p S_V stays below 2^11
+    // (its hi part is an integer of at most 11 bits)
     float smax = fmaxf(fmaxf(svq[0], svq[1]), fmaxf(svq[2], svq[3]));
     smax = wave_max(smax);   // scales are >= 0
     int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
     pe = min(max(pe, -100), 100);
-    const float pk = (float)(14 - pe);
-    const float pinv = __uint_as_float((unsigned)(127 - 14 + pe) << 23);  // 2^-k
+    const float pk = (float)(10 - pe);
+    const float pinv = __uint_as_float((unsigned)(127 - 10 + pe) << 23);  // 2^-k
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
@@ -482,71 +549,101 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A) {
     f16x4 pa_hi[HG], pa_lo[HG];
     float spo[HG];
     {
+      // As on the K side, the offset term sum_t p_t O_t is taken through the
+      // represented P (hi + lo): p_t O_t = P_t (O_t / sw_t); a row of zero range
+      // (sw = 0, P = 0) keeps its exact p_t O_t.
       const f32x4 sw{svq[0], svq[1], svq[2] * (1.f / kTok), svq[3] * (1.f / kTok)};
+      f32x4 zr;   // O / sw, nearest (reciprocal refined by one Newton step)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float rc = __builtin_amdgcn_rcpf(sw[k]);
+        const float z0 = ovq[k] * rc;
+        zr[k] = sw[k] > 0.f ? __builtin_fmaf(__builtin_fmaf(-sw[k], z0, ovq[k]), rc, z0) : 0.f;
+      }
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         const f32x4 p4 = *reinterpret_cast<const f32x4*>(&sm.loop.pt[wave][4 * hg + iq][4 * bq]);
         unsigned h01, l01, h23, l23;
-        split_pair(p4[0] * sw[0], p4[1] * sw[1], h01, l01);
-        split_pair(p4[2] * sw[2], p4[3] * sw[3], h23, l23);
+        split_grid(p4[0] * sw[0], p4[1] * sw[1], kGrid, kGrid, h01, l01);
+        split_grid(p4[2] * sw[2], p4[3] * sw[3], kGrid / kTok, kGrid / kTok, h23, l23);
         pa_hi[hg] = as_f16x4(h01, h23);
         pa_lo[hg] = as_f16x4(l01, l23);
-        float po = p4[0] * ovq[0];
-        po = __builtin_fmaf(p4[1], ovq[1], po);
-        po = __builtin_fmaf(p4[2], ovq[2], po);
-        po = __builtin_fmaf(p4[3], ovq[3], po);
+        const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, l01);
+        const f16x2 c = __builtin_bit_cast(f16x2, h23), e = __builtin_bit_cast(f16x2, l23);
+        float po = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (!(sw[k] > 0.f)) po = __builtin_fmaf(p4[k], ovq[k], po);
+        po = __builtin_fmaf((float)a[0], zr[0], po);
+        po = __builtin_fmaf((float)b[0], zr[0], po);
+        po = __builtin_fmaf((float)a[1], zr[1], po);
+        po = __builtin_fmaf((float)b[1], zr[1], po);
+        po = __builtin_fmaf((float)c[0], zr[2], po);
+        po = __builtin_fmaf((float)e[0], zr[2], po);
+        po = __builtin_fmaf((float)c[1], zr[3], po);
+        po = __builtin_fmaf((float)e[1], zr[3], po);
         spo[hg] = blocks_sum<(T == 32) ? 8 : 16>(po) * pinv;   // per tile: sum_t p_t O_t, head iq
       }
     }
 
     // -------------------------------------------- PV: lane = channel, 4 heads per group
-    f32x4 vacc[TPC][2][HG];
-#pragma unroll
-    for (int tt = 0; tt < TPC; ++tt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int hg = 0; hg < HG; ++hg) vacc[tt][h][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
-    static_for<0, 16>([&](auto S_) {
-      constexpr int s = decltype(S_)::value;   // tokens 4 s .. 4 s + 3: page s / 4, quad g = s % 4
-      constexpr int g = s & 3, tt = (T == 32) ? (s >> 3) : 0;
-      f16x4 b[2];
-      if constexpr (BV == 4) {
-        const unsigned x = vq[s >> 2][g], y = x >> 8;
-        b[0] = as_f16x4(code_field<4, 0>(x, y), code_field<4, 1>(x, y));
-        b[1] = as_f16x4(code_field<4, 2>(x, y), code_field<4, 3>(x, y));
-      } else {
-        const unsigned x = vq[s >> 2][g >> 1], y = x >> 8;
-        constexpr int X0 = 4 * (g & 1);
-        b[0] = as_f16x4(code_field<2, X0>(x, y), code_field<2, X0 + 1>(x, y));
-        b[1] = as_f16x4(code_field<2, X0 + 2>(x, y), code_field<2, X0 + 3>(x, y));
-      }
+    // one tile at a time (a T = 32 chunk holds two, each with its own alpha_V)
+    f32x4 vh[2][HG], vl[2][HG];   // [channel half][group]: hi chain (exact) and lo chain
+    auto pv_tile = [&](auto TT_) {
+      constexpr int tt = decltype(TT_)::value;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) {
-          vacc[tt][h][hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa_hi[hg], b[h], vacc[tt][h][hg], 4, s, 0);
-          vacc[tt][h][hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa_lo[hg], b[h], vacc[tt][h][hg], 4, s, 0);
+          vh[h][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
+          vl[h][hg] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    });
-    if (more) load_v(next);
-
-    // -------------------------------------------- fold: acc += alpha_V (sum_t p_t S_t k_t + sum_t p_t O_t)
-    // (vacc carries 2^(k-24) times the channel half's V field weight)
+      static_for<tt * (16 / TPC), (tt + 1) * (16 / TPC)>([&](auto S_) {
+        constexpr int s = decltype(S_)::value;   // tokens 4 s .. 4 s + 3: page s / 4, quad g = s % 4
+        constexpr int g = s & 3;
+        f16x4 b[2];
+        if constexpr (BV == 4) {
+          const unsigned x = vq[s >> 2][g], y = x >> 8;
+          b[0] = as_f16x4(code_field<4, 0>(x, y), code_field<4, 1>(x, y));
+          b[1] = as_f16x4(code_field<4, 2>(x, y), code_field<4, 3>(x, y));
+        } else {
+          const unsigned x = vq[s >> 2][g >> 1], y = x >> 8;
+          constexpr int X0 = 4 * (g & 1);
+          b[0] = as_f16x4(code_field<2, X0>(x, y), code_field<2, X0 + 1>(x, y));
+          b[1] = as_f16x4(code_field<2, X0 + 2>(x, y), code_field<2, X0 + 3>(x, y));
+        }
 #pragma unroll
-    for (int tt = 0; tt < TPC; ++tt)
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            vh[h][hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa_hi[hg], b[h], vh[h][hg], 4, s, 0);
+            vl[h][hg] = __builtin_amdgcn_mfma_f32_4x4x4f16(pa_lo[hg], b[h], vl[h][hg], 4, s, 0);
+          }
+      });
+    };
+    // acc += alpha_V (sum_t p_t S_t k_t + sum_t p_t O_t) over the tile
+    // (vh, vl carry 2^(k-24) times the channel half's V field weight)
+    auto pv_fold = [&](int tt) {
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float so = (T == 32) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(spo[hg]), 32 * tt + i))
-                                     : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(spo[hg]), i));
+          const float so = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(spo[hg]), 32 * tt + i));
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const float cf = kTwo24 * pinv * ((BV == 2 && h == 1) ? (1.f / 16.f) : 1.f);
-            acc[h][4 * hg + i] = __builtin_fmaf(av[tt][h], __builtin_fmaf(vacc[tt][h][hg][i], cf, so), acc[h][4 * hg + i]);
+            const float y = __builtin_fmaf(vl[h][hg][i], cf, __builtin_fmaf(vh[h][hg][i], cf, so));
+            acc[h][4 * hg + i] = __builtin_fmaf(av[tt][h], y, acc[h][4 * hg + i]);
           }
         }
+    };
+    pv_tile(std::integral_constant<int, 0>{});
+    if constexpr (TPC == 2) {
+      pv_fold(0);
+      pv_tile(std::integral_constant<int, 1>{});
+    }
+    if (more) load_v(next);
+    pv_fold(TPC - 1);
     if (more) load_av(next);
   }
 
@@ -605,7 +702,7 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
   __shared__ float wts[1024];
   const int lane = threadIdx.x;
   const int seq = blockIdx.x / A.q_heads;
-  const int L = A.seq_lens[seq];
+  const int L = A.seq_lens[seq] + A.seq_lens_plus_one;
   const int T = A.unit_tokens;
   const int ntiles = min((L + T - 1) / T, A.max_tiles);
   const int nparts = min((ntiles + A.tiles_per_part - 1) / A.tiles_per_part, A.max_parts);
@@ -694,12 +791,32 @@ hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, 
     return by_bits(bits_k, [&](auto BK) {
       return by_bits(bits_v, [&](auto BV) {
         dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
-        if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1>), grid, dim3(64 * kWaves), 0, s, a);
-        else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2>), grid, dim3(64 * kWaves), 0, s, a);
-        else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4>), grid, dim3(64 * kWaves), 0, s, a);
+        const QuantArgs q{};
+        if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false>), grid, dim3(64 * kWaves), 0, s, a, q);
+        else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false>), grid, dim3(64 * kWaves), 0, s, a, q);
+        else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, false>), grid, dim3(64 * kWaves), 0, s, a, q);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_combine(a, kChunk, true, s);
+      });
+    });
+  });
+}
+
+hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
+                                hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_bits(bits_k, [&](auto BK) {
+      return by_bits(bits_v, [&](auto BV) {
+        dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
+        if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, true>), grid, dim3(64 * kWaves), 0, s, a, q);
+        else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, true>), grid, dim3(64 * kWaves), 0, s, a, q);
+        else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, true>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        DecodeArgs b = a;
+        b.seq_lens_plus_one = 1;
+        return launch_combine(b, kChunk, true, s);
       });
     });
   });

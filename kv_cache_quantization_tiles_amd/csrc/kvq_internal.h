@@ -72,6 +72,7 @@ struct DecodeArgs {
   float sm_scale_log2;        // sm_scale * log2(e) (times the K scale for fp8 pages)
   int unit_tokens;            // tokens per partition unit (tile, or 64 for the baselines)
   float out_scale;            // output multiplier (the V scale for fp8 pages, else 1)
+  int seq_lens_plus_one;      // 1: seq_lens are the lengths before an appended token
 };
 
 struct BaseFillArgs {
@@ -96,6 +97,8 @@ hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream
 hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s);
+hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
+                                hipStream_t s);
 hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, int max_seq_len, hipStream_t s);
 hipError_t launch_decode_baseline(const DecodeArgs& a, bool fp8, hipStream_t s);
 

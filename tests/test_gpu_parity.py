@@ -420,3 +420,48 @@ def test_full_size_qwen3_32b_tp2_burst_sampled():
             pu.check_tile_metadata(ref.codes, ga[0], gs, go, ref.alpha, ref.scale, ref.offset,
                                    orc.dequantize_tile, f"burst last tile s{s} h{h}")
     _sampled_decode_checks(wl, q, table, lens_now, gpk, gpv, got, [(0, 0), (31, 3)], "32x16k decode")
+
+
+FUSED_CASES = [
+    # (recipe, lens, hkv, hq, tile, bits_k, bits_v, iters)
+    (2, (200, 131, 64, 17), 2, 8, 64, 4, 4, 3),
+    (5, (300, 97, 33), 2, 16, 32, 4, 2, 5),
+    (2, (260, 128, 1000), 1, 4, 128, 2, 2, 3),
+    (1, (1024,), 1, 8, 64, 4, 4, 3),
+    (2, (700, 513, 64, 1), 2, 8, 32, 4, 4, 3),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES)
+def test_append_and_decode_fused_matches_two_calls(case):
+    """One launch of append + decode equals kvq_append_and_requant followed by
+    kvq_paged_decode_attn: identical pages, staging rows and outputs, step after
+    step (tiles fill and new ones start), and the outputs match the oracle."""
+    recipe, lens, hkv, hq, tile, bk, bv, iters = case
+    steps = tile + 2
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters, decode_steps=steps)
+    k, v, table, npages, fused = _gpu_prefill(wl)
+    _, _, _, _, split = _gpu_prefill(wl)
+    lens_now = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    max_len = max(wl.seq_lens) + steps
+    ws_f, ws_s = fused.workspace(hq, max_len), split.workspace(hq, max_len)
+    for step in range(steps):
+        kn = torch.from_numpy(inputs.gen_decode_kv(wl, "K", step)).cuda()
+        vn = torch.from_numpy(inputs.gen_decode_kv(wl, "V", step)).cuda()
+        q = torch.from_numpy(inputs.gen_q(wl, step)).cuda()
+        of = fused.append_decode(kn, vn, lens_now, q, max_len, workspace=ws_f)
+        split.append(kn, vn, lens_now)
+        os_ = split.decode(q, lens_now + 1, max_len, workspace=ws_s)
+        lens_now = lens_now + 1
+        torch.cuda.synchronize()
+        assert torch.equal(fused.pool_k, split.pool_k), step
+        assert torch.equal(fused.pool_v, split.pool_v), step
+        assert torch.equal(fused.staging_k, split.staging_k), step
+        assert torch.equal(fused.staging_v, split.staging_v), step
+        assert torch.equal(of, os_), (step, (of - os_).abs().max().item())
+        if step in (0, tile - 1, steps - 1):
+            ref, sc = orc.paged_decode_attn(q.cpu().numpy(), table, lens_now.cpu().numpy(), fused.pool_k.cpu().numpy(),
+                                            fused.pool_v.cpu().numpy(), tile, bk, bv, return_scale=True)
+            err = pu.assert_attn(of.cpu().numpy(), ref, f"fused {case} step {step}", sc)
+            print(f"[attn] fused {case} step {step}: max abs err {err:.2e} (largest output scale {sc.max():.3g})",
+                  flush=True)
