@@ -3,8 +3,9 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
   1. quantize every page of the prefill (K and V, all sequences and heads),
-  2. append one decode token per sequence and re-quantize its tile,
-  3. one decode-attention step over every cached token, read from the pages.
+  2. one decode step in a single launch (kvq_append_and_decode): append one
+     token per sequence, re-quantize its tile, and attend over every cached
+     token straight from the pages.
 Default workload: a Qwen3-4B-shaped layer, 8 KV heads / 32 query heads,
 4 sequences x 16K context, 16-token pages, tile 64, 4-bit K and V, 3
 normalization iterations.
@@ -44,22 +45,27 @@ def quantize_valu_ops_per_element(iters: int) -> int:
     return 1 + 7 + 3 * max(2 * iters - 1, 0) + 4
 
 
-def measured_traffic(kernel_source: str, profile: str):
+def measured_traffic(kernel_sources, profile: str):
     """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    measurement, if it was taken on the current kernel source (else None)."""
+    measurement, if it was taken on the current kernel sources (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", profile)
-    src = os.path.join(ROOT, "kv_cache_quantization_tiles_amd", "csrc", kernel_source)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    h = hashlib.sha256()
+    for name in kernel_sources:
+        with open(os.path.join(ROOT, "kv_cache_quantization_tiles_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if rec.get("source_sha256") != h.hexdigest():
         return None
     return {"read_bytes": rec["read_bytes"], "write_bytes": rec["write_bytes"],
             "total_bytes": rec["read_bytes"] + rec["write_bytes"], "source": "profiles/" + profile}
+
+
+# sources the quantize kernel is built from (the traffic record names their hash)
+QUANTIZE_SOURCES = ("kvq_quantize.hip", "kvq_tile.h", "kvq_internal.h")
 
 
 # ----------------------------------------------------------------------------- byte model
@@ -281,26 +287,33 @@ def main():
         c.quantize_prefill(ks[i % n_in], vs[i % n_in], cu, max_len)
         if ev is not None:
             ev[1].record()
-        c.append(kn, vn, lens_before)
+        c.append_decode(kn, vn, lens_before, q, max_len + 1, out=out, workspace=ws)
         if ev is not None:
             ev[2].record()
-        c.decode(q, lens_after, max_len + 1, out=out, workspace=ws)
-        if ev is not None:
-            ev[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tq = [e[0].elapsed_time(e[1]) for e in evs]
-    ta = [e[1].elapsed_time(e[2]) for e in evs]
-    td = [e[2].elapsed_time(e[3]) for e in evs]
+    tad = [e[1].elapsed_time(e[2]) for e in evs]
     ms_step = wall * 1e3 / args.steps
+
+    # the same decode step as two calls (append, then decode), for comparison
+    n_split = max(20, args.steps)
+    sp_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_split)]
+    for j in range(n_split):
+        c = caches[j % n_pools]
+        sp_ev[j][0].record()
+        c.append(kn, vn, lens_before)
+        sp_ev[j][1].record()
+        c.decode(q, lens_after, max_len + 1, out=out, workspace=ws)
+        sp_ev[j][2].record()
 
     # decode attention alone, pools rotated so every call reads cold pages
     n_dec = max(20, args.steps)
@@ -322,12 +335,15 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * nb * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     td_cold = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+    ta = [e[0].elapsed_time(e[1]) for e in sp_ev]
+    td = [e[1].elapsed_time(e[2]) for e in sp_ev]
 
     ntok_heads = wl.total_tokens * wl.hkv
     qbytes = quantize_bytes(ntok_heads, wl.bits_k, wl.tile_tokens) + quantize_bytes(ntok_heads, wl.bits_v, wl.tile_tokens)
     abytes = append_bytes(wl, wl.seq_lens)
     dbytes = decode_bytes(wl, [l + 1 for l in wl.seq_lens])
-    q_ms, a_ms, d_ms = float(np.mean(tq)), float(np.mean(ta)), float(np.mean(td))
+    q_ms, ad_ms = float(np.mean(tq)), float(np.mean(tad))
+    a_ms, d_ms = float(np.mean(ta)), float(np.mean(td))
     q_gbps = qbytes / (q_ms * 1e-3) / 1e9
     n_elem = 2 * ntok_heads * D
     q_tops = n_elem * quantize_valu_ops_per_element(wl.iters) / (q_ms * 1e-3) / 1e12
@@ -346,11 +362,12 @@ def main():
                    "bits_k": wl.bits_k, "bits_v": wl.bits_v, "sinkhorn_iters": wl.iters},
         "quantize_ms": round(q_ms, 4), "quantize_GBps": round(q_gbps, 1),
         "quantize_hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
-        "append_ms": round(a_ms, 4),
-        "decode_attn_ms": round(d_ms, 4), "decode_attn_cold_ms": round(td_cold, 4),
+        "append_decode_ms": round(ad_ms, 4),
+        "split_append_ms": round(a_ms, 4), "split_decode_attn_ms": round(d_ms, 4),
+        "decode_attn_cold_ms": round(td_cold, 4),
         "decode_attn_GBps_cold": round(d_gbps_cold, 1),
         "decode_hbm_frac_cold": round(d_gbps_cold / HBM_PEAK_GBPS, 4),
-        "decode_tok_per_s": round(wl.num_seqs / ((a_ms + d_ms) * 1e-3), 1),
+        "decode_tok_per_s": round(wl.num_seqs / (ad_ms * 1e-3), 1),
         "decode_attn_only_tok_per_s": round(wl.num_seqs / (td_cold * 1e-3), 1),
         "copy_probe_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "alu", "kernel": "quantize_paged_kernel",
@@ -358,7 +375,7 @@ def main():
                      "frac": round(q_tops / VALU_PEAK_TOPS, 4),
                      "ops_per_element": quantize_valu_ops_per_element(wl.iters),
                      "hbm_GBps": round(q_gbps, 1), "hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic("kvq_quantize.hip", f"traffic-quantize_paged_kernel-{wl.name}.json")},
+                     "traffic": measured_traffic(QUANTIZE_SOURCES, f"traffic-quantize_paged_kernel-{wl.name}.json")},
         "cpu_baseline": cpu,
     }
     del caches, ks, vs, src, dst
