@@ -219,6 +219,26 @@ def unpack_natural(packed: np.ndarray, bits: int) -> np.ndarray:
     return out
 
 
+# Unit order of a token's 128 codes (the stored order of dense codes and of K
+# slots): 16 units of 8 fields, a unit being 8*bits bits (a 32-bit word at 4
+# bits, a 16-bit half at 2 bits) taken low bits first; field m of unit u holds
+# channel u + 16 m.  Equivalently: natural packing of the channels permuted by
+# CODE_ORDER (position 8 u + m <- channel u + 16 m).
+CODE_ORDER = np.array([(p // 8) + 16 * (p % 8) for p in range(HEAD_DIM)])
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes uint8 [..., 128] -> bytes [..., 16 * bits] in unit order."""
+    return pack_natural(np.asarray(codes, np.uint8)[..., CODE_ORDER], bits)
+
+
+def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
+    q = unpack_natural(packed, bits)
+    out = np.zeros_like(q)
+    out[..., CODE_ORDER] = q
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Dense (logical) layout: one token run whose tile 0 starts at token 0
 # ----------------------------------------------------------------------------
@@ -242,13 +262,13 @@ def quantize_dense(x: np.ndarray, tile_tokens: int, bits: int, iters: int):
             alpha[j, h] = tq.alpha
             scale[a:b, h] = tq.scale
             offset[a:b, h] = tq.offset
-    return dict(codes=pack_natural(codes, bits), codes_raw=codes, alpha=alpha, scale=scale,
+    return dict(codes=pack_codes(codes, bits), codes_raw=codes, alpha=alpha, scale=scale,
                 offset=offset, pre=pre)
 
 
 def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits: int) -> np.ndarray:
     """Inverse of quantize_dense from the stored codes and fp32 metadata: float64 [n, H, d]."""
-    q = unpack_natural(codes_packed, bits)
+    q = unpack_codes(codes_packed, bits)
     n, heads, d = q.shape
     out = np.zeros((n, heads, d))
     for h in range(heads):
@@ -265,8 +285,9 @@ def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits:
 #   codes (16 * d * bits / 8 bytes) | scale fp32[16] | offset fp32[16] | alpha slice fp32[16 d / T]
 # The page with index j inside its tile stores alpha[j * 16d/T : (j+1) * 16d/T].
 # Code layouts of a slot (d = 128):
-#   K slots: four blocks of 32 channels; block k holds, token after token, the
-#     32 channels 32k..32k+31 of each of the 16 tokens in natural packing.
+#   K slots: each token's codes in unit order (see CODE_ORDER), cut into four
+#     blocks of 4 units (4*bits bytes); block k holds, token after token, units
+#     4k..4k+3 of each of the 16 tokens.
 #   V slots: 64 runs of 4*bits bytes, run l (at byte 4*bits*l) holding the
 #     channels l (h = 0) and 64 + l (h = 1) of all 16 tokens, read as
 #     little-endian 32-bit words of F = 32/bits fields.  Token t = 4g + r
@@ -289,21 +310,20 @@ def slot_bytes(bits: int, tile_tokens: int) -> int:
 
 def k_codes_to_bytes(codes: np.ndarray, bits: int) -> np.ndarray:
     """codes uint8 [16, 128] -> K-slot code bytes."""
-    per_tok = 32 * bits // 8
+    per_blk = 4 * bits                                  # bytes of 4 units
+    tok = pack_codes(codes, bits)                       # [16, 16 * bits]
     out = np.zeros(PAGE_TOKENS * HEAD_DIM * bits // 8, np.uint8)
     for k in range(4):
-        blk = pack_natural(codes[:, 32 * k:32 * (k + 1)], bits)   # [16, per_tok]
-        out[k * 16 * per_tok:(k + 1) * 16 * per_tok] = blk.reshape(-1)
+        out[k * 16 * per_blk:(k + 1) * 16 * per_blk] = tok[:, k * per_blk:(k + 1) * per_blk].reshape(-1)
     return out
 
 
 def bytes_to_k_codes(raw: np.ndarray, bits: int) -> np.ndarray:
-    per_tok = 32 * bits // 8
-    codes = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
+    per_blk = 4 * bits
+    tok = np.zeros((PAGE_TOKENS, 16 * bits), np.uint8)
     for k in range(4):
-        blk = raw[k * 16 * per_tok:(k + 1) * 16 * per_tok].reshape(16, per_tok)
-        codes[:, 32 * k:32 * (k + 1)] = unpack_natural(blk, bits)
-    return codes
+        tok[:, k * per_blk:(k + 1) * per_blk] = raw[k * 16 * per_blk:(k + 1) * 16 * per_blk].reshape(16, per_blk)
+    return unpack_codes(tok, bits)
 
 
 def _v_field(bits: int, c: int, t: int):

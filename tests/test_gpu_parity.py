@@ -54,7 +54,7 @@ def test_dense_quantize_and_dequantize(tile, bits, iters, n, heads, recipe):
     torch.cuda.synchronize()
     got = {k: v.cpu().numpy() for k, v in q.items()}
     ref = orc.quantize_dense(x, tile, bits, iters)
-    codes = orc.unpack_natural(got["codes"], bits)
+    codes = orc.unpack_codes(got["codes"], bits)
     _report(f"dense T{tile} b{bits} it{iters} n{n} h{heads}",
             pu.compare_codes(codes, ref["codes_raw"], ref["pre"], "dense"))
     pu.assert_rel(got["alpha"], ref["alpha"], pu.META_RTOL, "alpha")

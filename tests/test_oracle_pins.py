@@ -251,11 +251,28 @@ def _one_hot_page(t, c, value):
     return codes
 
 
+def test_unit_order_hand_examples():
+    for ex in _golden("packing.json")["unit_order"]:
+        codes = np.zeros(128, np.uint8)
+        codes[ex["channel"]] = ex["code"]
+        packed = orc.pack_codes(codes, ex["bits"])
+        want = np.zeros(16 * ex["bits"], np.uint8)
+        want[ex["byte"]] = int(ex["value"], 16)
+        np.testing.assert_array_equal(packed, want)
+        np.testing.assert_array_equal(orc.unpack_codes(packed, ex["bits"]), codes)
+
+
 def test_k_slot_positions_hand_examples():
-    for ex in _golden("packing.json")["k_slot_4bit"]:
+    g = _golden("packing.json")
+    for ex in g["k_slot_4bit"]:
         raw = orc.k_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0xB), 4)
         want = np.zeros_like(raw)
         want[ex["byte"]] = 0x0B if ex["nibble"] == "low" else 0xB0
+        np.testing.assert_array_equal(raw, want)
+    for ex in g["k_slot_2bit"]:
+        raw = orc.k_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0x3), 2)
+        want = np.zeros_like(raw)
+        want[ex["byte"]] = 0x3 << ex["shift"]
         np.testing.assert_array_equal(raw, want)
 
 
