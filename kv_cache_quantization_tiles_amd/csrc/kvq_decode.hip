@@ -85,7 +85,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Code fields of one 32-bit word (two 16-bit halves), masked in place so that
 // each half reads as the fp16 denormal m * 2^-24 whose mantissa m is the code
-// times the power of two fixed by the field's bit position (field_weight).
+// times the power of two fixed by the field's bit position (the field's
+// weight: 16^(X mod 2) at 4 bits, 4^(X mod 4) at 2 bits).
 // Fields in bits 8..15 of a half are taken from y = x >> 8.  One AND per pair
 // of codes, no conversion and no offset term.
 template <int BITS, int X>
@@ -98,9 +99,33 @@ __device__ __forceinline__ unsigned code_field(unsigned x, unsigned y) {
     return ((X < 4) ? x : y) & m;
   }
 }
+// Channel of operand element k (< 4) of QK step s (< 32): the step takes
+// fields X, X + 1 of a code word, each from both 16-bit halves (K codes in
+// unit order: field m of unit u holds channel u + 16 m; a unit is a 32-bit
+// word at 4 bits, a 16-bit half at 2 bits).
 template <int BITS>
-__host__ __device__ constexpr float field_weight(int x) {
-  return BITS == 4 ? ((x & 1) ? 16.f : 1.f) : (float)(1 << (2 * (x & 3)));
+__host__ __device__ constexpr int qk_channel(int s, int k) {
+  if constexpr (BITS == 4) {
+    // word s / 2; even s: fields 0, 4 | 1, 5; odd s: 2, 6 | 3, 7
+    const int m = 2 * (s & 1) + 4 * (k & 1) + (k >> 1);
+    return (s >> 1) + 16 * m;
+  } else {
+    // word s / 4 = units 2 (s / 4) (low half), + 1 (high half); fields 2 (s % 4) + k / 2
+    return 2 * (s >> 2) + (k & 1) + 16 * (2 * (s & 3) + (k >> 1));
+  }
+}
+// Inverse: the step / element of channel c, as 4 s + k.
+template <int BITS>
+__host__ __device__ constexpr int qk_slot(int c) {
+  const int u = c & 15, m = c >> 4;
+  if constexpr (BITS == 4) return 4 * (2 * u + ((m >> 1) & 1)) + 2 * (m & 1) + (m >> 2);
+  else return 4 * (4 * (u >> 1) + (m >> 1)) + 2 * (m & 1) + (u & 1);
+}
+// Weight of channel c's K code field as read in place (16^(m mod 2) at 4 bits,
+// 4^(m mod 4) at 2 bits, m = c / 16).
+template <int BITS>
+__host__ __device__ constexpr float k_field_weight(int c) {
+  return BITS == 4 ? (((c >> 4) & 1) ? 16.f : 1.f) : (float)(1 << (2 * ((c >> 4) & 3)));
 }
 
 // fp16x4 MFMA operand from two code-field words
@@ -162,7 +187,7 @@ struct alignas(16) DecodeSmem {
   int32_t pages[kMaxChunksPerPart * 4];          // the partition's page ids
   union {
     struct {
-      float hq[4 * HG][kHeadDim];                // (H q)_c / weight of channel c's K field
+      float hq[4 * HG][kHeadDim];                // (H q)_c / weight of c's K field, at qk_slot(c)
       float pt[kWaves][4 * HG][kChunk];          // per-wave transpose of the probabilities
     } loop;
     struct {
@@ -216,7 +241,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
   constexpr int SLOT_K = slot_bytes(BK, T), SLOT_V = slot_bytes(BV, T);
   constexpr int CODE_K = slot_code_bytes(BK), CODE_V = slot_code_bytes(BV);
   constexpr int AL = slot_alpha_len(T);
-  constexpr int D1 = (BK == 4) ? 4 : 8;          // QK step: channels c0, c0 + D1, c0 + 1, c0 + 1 + D1
   // V fields of tokens 2 and 3 of a quad weigh kTok times those of tokens 0, 1;
   // their probabilities enter the MFMA divided by kTok.
   constexpr float kTok = (BV == 4) ? 16.f : 4.f;
@@ -307,16 +331,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     ovq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 64 + 16 * (bq & 3)));
   };
   auto load_alpha = [&](int c) {
-    // QK steps of this lane: s = BLK st + bq % BLK; channels c0 + {0, D1, 1, 1 + D1}
+    // QK steps of this lane: s = BLK st + bq % BLK; element k is channel qk_channel(s, k)
     const int tp = tile_page(c, (T == 32) ? (bq >> 3) : 0);
 #pragma unroll
     for (int st = 0; st < SETS; ++st) {
       const int s = BLK * st + (bq % BLK);
-      const int c0 = (BK == 4) ? 8 * (s >> 1) + 2 * (s & 1) : 16 * (s >> 2) + 2 * (s & 3);
-      const float* ap = reinterpret_cast<const float*>(kslot(page_id(tp + c0 / AL)) + CODE_K + 128) + (c0 % AL);
-      const f32x2 x0 = *reinterpret_cast<const f32x2*>(ap);
-      const f32x2 x1 = *reinterpret_cast<const f32x2*>(ap + D1);
-      ak[st] = f32x4{x0[0], x1[0], x0[1], x1[1]};   // k order: c0, c0 + D1, c0 + 1, c0 + 1 + D1
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ch = qk_channel<BK>(s, k);
+        ak[st][k] = reinterpret_cast<const float*>(kslot(page_id(tp + ch / AL)) + CODE_K + 128)[ch % AL];
+      }
     }
   };
   auto load_av = [&](int c) {
@@ -370,11 +394,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     for (int i = 0; i < 32; ++i) hq[i] = __builtin_fmaf(hq[i], s32, xor32(hq[i]));
     if (n16 < NH) {
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = hq[4 * v + e] * (kInvSqrtD / field_weight<BK>(e));
-        *reinterpret_cast<f32x4*>(&sm.loop.hq[n16][32 * grp + 4 * v]) = x;
+      for (int i = 0; i < 32; ++i) {   // channel 32 grp + i, stored in QK step order
+        const int c = 32 * grp + i;
+        sm.loop.hq[n16][qk_slot<BK>(c)] = hq[i] * (kInvSqrtD / k_field_weight<BK>(c));
       }
     }
   }
@@ -400,9 +422,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     // as fp16 hi / lo; qsum and the power-of-two scale per (head, tile)
     f16x4 qa_hi[HG][SETS], qa_lo[HG][SETS];
     float cA[HG], cB[HG];
-    // field weights of this lane's steps: c0 and c0 + D1 share c0's, c0 + 1 and
-    // c0 + 1 + D1 share c0 + 1's (for 2-bit codes, c0's depends on the step's
-    // parity, which is bq's)
+    // field weights of this lane's steps: elements 0, 1 weigh w0 and 2, 3 w1
+    // (4 bits: 1 and 16; 2 bits: w0 = 16 on odd steps, else 1, and w1 = 4 w0;
+    // a step's parity is bq's)
     const float w0 = (BK == 4) ? 1.f : ((bq & 1) ? 16.f : 1.f);
     const float w1 = (BK == 4) ? 16.f : w0 * 4.f;
 #pragma unroll
@@ -413,13 +435,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
 #pragma unroll
       for (int st = 0; st < SETS; ++st) {
         const int s = BLK * st + (bq % BLK);
-        const int cc = (BK == 4) ? 8 * (s >> 1) + 2 * (s & 1) : 16 * (s >> 2) + 2 * (s & 3);
-        const f32x2 h0 = *reinterpret_cast<const f32x2*>(&sm.loop.hq[hh][cc]);
-        const f32x2 h1 = *reinterpret_cast<const f32x2*>(&sm.loop.hq[hh][cc + D1]);
-        x[st][0] = h0[0] * ak[st][0];
-        x[st][1] = h1[0] * ak[st][1];
-        x[st][2] = h0[1] * ak[st][2];
-        x[st][3] = h1[1] * ak[st][3];
+        const f32x4 hv = *reinterpret_cast<const f32x4*>(&sm.loop.hq[hh][4 * s]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[st][k] = hv[k] * ak[st][k];
         // the bound is on qt itself: x times the field weight
         qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(x[st][0]), fabsf(x[st][1])) * w0, fmaxf(fabsf(x[st][2]), fabsf(x[st][3])) * w1));
       }

@@ -35,14 +35,14 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int T, int BITS>
-__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(3))) void quantize_dense_kernel(QuantArgs A) {
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void quantize_dense_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
   quantize_tile_body<T, BITS, false, kDense>(A, sm, 0, blockIdx.y, 0, blockIdx.x, threadIdx.x);
 }
 
 // grid: x = tile index in the sequence, y = head + Hkv * role (0 K, 1 V), z = sequence
 template <int T, int BK, int BV>
-__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(3))) void quantize_paged_kernel(QuantArgs A) {
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void quantize_paged_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
   const int seq = blockIdx.z;
   const int len = A.cu_seqlens[seq + 1] - A.cu_seqlens[seq];
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(3))) void
 
 // grid: x = head, y = role, z = sequence
 template <int T, int BK, int BV>
-__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(3))) void append_kernel(QuantArgs A) {
+__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void append_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
   const int seq = blockIdx.z;
   const int tile_idx = A.lens_before[seq] / T;
@@ -79,15 +79,34 @@ __global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
   const uint8_t* crow = A.codes + rr * (kHeadDim * BITS / 8);
   const float* al = A.alpha + ((size_t)(t / T) * A.heads + h) * kHeadDim;
   const float S = A.scale[rr], O = A.offset[rr];
+  // Codes in unit order (channel u + 16 m in field m of unit u): this
+  // thread's channels 64 half + 8 cg + j are field 4 half + (cg >> 1) of the
+  // units 8 (cg & 1) + j.
+  unsigned units[8];
+  if (BITS == 4) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(crow + 32 * (cg & 1));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(crow + 32 * (cg & 1) + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      units[i] = lo[i];
+      units[4 + i] = hi[i];
+    }
+  } else {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(crow + 16 * (cg & 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      units[2 * i] = v[i] & 0xFFFFu;
+      units[2 * i + 1] = v[i] >> 16;
+    }
+  }
   float x[16];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    unsigned w = (BITS == 4) ? *reinterpret_cast<const uint32_t*>(crow + BITS * (8 * half + cg))
-                             : *reinterpret_cast<const uint16_t*>(crow + BITS * (8 * half + cg));
+    const int m = 4 * half + (cg >> 1);
     const int c0 = 64 * half + 8 * cg;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float q = (float)((w >> (BITS * j)) & ((1u << BITS) - 1u));
+      const float q = (float)((units[j] >> (BITS * m)) & ((1u << BITS) - 1u));
       x[8 * half + j] = al[c0 + j] * __builtin_fmaf(S, q, O);
     }
   }

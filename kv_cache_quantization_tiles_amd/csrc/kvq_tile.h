@@ -8,13 +8,18 @@
 // section "양자화로 캐시를 다이어트시킨다".
 //
 // One workgroup quantizes one tile of T tokens x 128 channels with 2T
-// threads.  Thread (tq, cg) holds the 4 tokens 4tq..4tq+3 and the 16
-// channels 8cg+j and 64+8cg+j (j < 8) in registers for the whole kernel:
-//   * the fp16 rows are read once (two 16-byte loads per token, the 8 cg
-//     threads of a token covering its 256-byte row);
-//   * the Hadamard butterfly runs 4 stages in registers (channel bits 0,1,2,6)
-//     and 3 stages across the 8 cg lanes with ds_swizzle (channel bits 3,4,5);
-//     it is left unnormalized and the 1/sqrt(128) is folded into the factors;
+// threads (T/32 waves).  Wave w takes tokens 32w..32w+31 as two 16-token
+// blocks; lane l = 16 g + j ends up holding, for the whole kernel, the 8
+// tokens 32w + 16 bb + 4g + r (bb < 2, r < 4) of the 8 channels j + 16 m
+// (m < 8), in registers:
+//   * rotation on the matrix cores: with channel c = 32p + k (k < 32), one
+//     v_mfma_f32_16x16x32_f16 per (block, p, sign) multiplies 16 fp16 rows
+//     by [H16; +-H16], which is the Sylvester transform over channel bits
+//     0..4 (the fp16 input enters the MFMA as loaded; every product is exact
+//     and a single instruction sums 32 of them); the transform over bits 5, 6
+//     (the four p) is a 4-point butterfly in registers.  Lane 16g + j then
+//     holds rows 4g..4g+3 of output channels j + 16 sigma + 32 p'.  The
+//     transform is left unnormalized, the 1/sqrt(128) folded into the factors;
 //   * the normalization never rewrites the tile: with weights b = 1/beta and
 //     a = 1/alpha, the channel step needs the spread over t of u = b_t R_tc
 //     and the token step that over c of u = a_c R_tc.  Each is one pass of
@@ -26,7 +31,10 @@
 //   * the last token step is skipped: its factor cancels exactly in the
 //     stored scale, offset and codes (rounding is per token row);
 //   * codes: z = R * a, per-row min/max through LDS, v = (z - min) / step,
-//     round half to even, packed and stored straight into the output layout.
+//     round half to even; a lane's 8 codes of a token are one unit of the
+//     stored unit order (channel u + 16 m in field m of unit u), so K codes
+//     and dense codes are stored straight from registers, and V runs (channels
+//     l and 64 + l) are built from the lane's own quad of tokens.
 #pragma once
 
 #include "kvq_internal.h"
@@ -40,27 +48,22 @@ typedef unsigned int qt_u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int qt_u32x2 __attribute__((ext_vector_type(2)));
 typedef float qt_f32x4 __attribute__((ext_vector_type(4)));
 
-// fp16 pair (low, high half of w) -> fp32 (low + high, low - high): the
-// conversion rides on the first butterfly stage, one v_fma_mix_f32 each (the
-// mixed-precision FMA reads the two fp16 halves directly; low * 1 + high is
-// rounded once, as the fp32 sum of the converted values would be).
-__device__ __forceinline__ void first_stage(unsigned w, float& y0, float& y1) {
-  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(y0) : "v"(w));
-  asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(y1) : "v"(w));
-}
-
-// Shared memory of one workgroup.
+// Shared memory of one workgroup.  Per-channel arrays marked "lane order"
+// keep channel j + 16 m at index 8 j + m (a lane's 8 channels side by side).
 template <int T>
 struct alignas(16) Smem {
-  float red[2][T / 4][kHeadDim];  // channel partials; token partials and row min/max alias it
-  float a[kHeadDim];              // 1/alpha in unnormalized units
-  float alpha[kHeadDim];          // channel factors (normalized units)
-  float ref_c[kHeadDim];          // R of the tile's first token (channel-step shift)
-  float b[T];                     // 1/beta
-  float ref_t[T];                 // R of channel 0 of each token (token-step shift)
-  float inv[T];                   // levels / range per row (0 for empty rows)
-  float nmi[T];                   // -min * inv per row
+  float red[2][16 * T];   // partial sums (channel step: [s][row 4w+g][lane order];
+                          // token step and row min / max: [s][j][token])
+  float a[kHeadDim];      // 1/alpha in unnormalized units (lane order)
+  float alpha[kHeadDim];  // channel factors, normalized units (natural order)
+  float ref_c[kHeadDim];  // R of the tile's first token (lane order)
+  float b[T];             // 1/beta
+  float ref_t[T];         // R of channel 0 of each token (token-step shift)
+  float inv[T];           // levels / range per row (0 for empty rows)
+  float nmi[T];           // -min * inv per row
 };
+
+typedef _Float16 qt_f16x8 __attribute__((ext_vector_type(8)));
 
 // Packs N codes into one 32-bit word: field f (bits [BITS*f, BITS*(f+1)))
 // takes v[f] rounded to nearest even by v_cvt_pk_u8_f32.
@@ -83,8 +86,11 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
                                                    int head, int seq, int tile_idx, int tid) {
   constexpr int NT = 2 * T;
   constexpr float LEVELS = (float)((1 << BITS) - 1);
-  const int cg = tid & 7;
-  const int tq = tid >> 3;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  // token (in the tile) of register row q = 4 bb + r
+  auto tok = [&](int q) { return 32 * w + 16 * (q >> 2) + 4 * g + (q & 3); };
 
   // ---------------------------------------------------------------- rows of this tile
   const int t0 = tile_idx * T;
@@ -106,253 +112,254 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     rows_base = A.staging[role] + ((size_t)seq * T * H + head) * kHeadDim;
   }
 
-  // ---------------------------------------------------------------- load fp16 rows
+  // ---------------------------------------------------------------- load fp16 rows (MFMA A layout)
+  // raw[bb][p]: row j of block bb, channels 32p + 8g .. 32p + 8g + 7.
   // Rows past the tile's end load row 0 again: their values are then exact
   // copies of row 0, which the statistics below exclude exactly.
-  qt_u32x4 raw[4][2];
+  qt_u32x4 raw[2][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = 4 * tq + r;
+  for (int bb = 0; bb < 2; ++bb) {
+    const int t = 32 * w + 16 * bb + j;
     const int src_t = (t < n_valid) ? t : 0;
     const uint16_t* row = rows_base + (size_t)src_t * row_stride;
     if (MODE == kAppend && src_t == r_new) row = A.src[role] + ((size_t)seq * H + head) * kHeadDim;
-    raw[r][0] = __builtin_nontemporal_load(reinterpret_cast<const qt_u32x4*>(row + 8 * cg));
-    raw[r][1] = __builtin_nontemporal_load(reinterpret_cast<const qt_u32x4*>(row + 64 + 8 * cg));
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      raw[bb][p] = __builtin_nontemporal_load(reinterpret_cast<const qt_u32x4*>(row + 32 * p + 8 * g));
   }
   // Keep the fp16 rows of a partial tile for later appends.
   if (MODE != kDense && A.staging[role] != nullptr) {
     uint16_t* stg = A.staging[role] + ((size_t)seq * T * H + head) * kHeadDim;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * tq + r;
+    for (int bb = 0; bb < 2; ++bb) {
+      const int t = 32 * w + 16 * bb + j;
       const bool write = (MODE == kPaged) ? (n_valid < T && t < n_valid) : (t == r_new);
       if (write) {
-        *reinterpret_cast<qt_u32x4*>(stg + (size_t)t * row_stride + 8 * cg) = raw[r][0];
-        *reinterpret_cast<qt_u32x4*>(stg + (size_t)t * row_stride + 64 + 8 * cg) = raw[r][1];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          *reinterpret_cast<qt_u32x4*>(stg + (size_t)t * row_stride + 32 * p + 8 * g) = raw[bb][p];
       }
     }
   }
 
   // ---------------------------------------------------------------- Hadamard (unnormalized)
-  // register index k = 8*half + j  <->  channel 64*half + 8*cg + j
-  float R[4][16];
+  // B+ = [H16; H16], B- = [H16; -H16] in the MFMA B layout: lane (g, j) holds
+  // rows 8g..8g+7 of column j, H16[k][j] = (-1)^popcount(k & j).
+  // Bit a of hrow is the sign of H16[a][j]: the parity of a & j, the XOR of
+  // the patterns of a's bits 0..3 over the bits set in j.
+  const unsigned jb = (unsigned)j;
+  const unsigned hrow = ((0u - (jb & 1u)) & 0xAAAAu) ^ ((0u - ((jb >> 1) & 1u)) & 0xCCCCu) ^
+                        ((0u - ((jb >> 2) & 1u)) & 0xF0F0u) ^ ((0u - ((jb >> 3) & 1u)) & 0xFF00u);
+  const unsigned sp = (hrow >> (8 * (g & 1))) & 0xFFu;   // rows 8g..8g+7 (mod 16)
+  const unsigned sn = sp ^ ((g >= 2) ? 0xFFu : 0u);
+  qt_u32x4 bpw, bnw;   // fp16 pairs of +-1.0 (0x3C00, sign in bit 15 of each half)
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) first_stage(raw[r][half][i], R[r][8 * half + 2 * i], R[r][8 * half + 2 * i + 1]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int bit = 2; bit < 16; bit <<= 1) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (k & bit) continue;
-        const float lo = R[r][k], hi = R[r][k | bit];
-        R[r][k] = lo + hi;
-        R[r][k | bit] = lo - hi;
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    bpw[i] = 0x3C003C00u | ((sp << (15 - 2 * i)) & 0x8000u) | ((sp << (30 - 2 * i)) & 0x80000000u);
+    bnw[i] = 0x3C003C00u | ((sn << (15 - 2 * i)) & 0x8000u) | ((sn << (30 - 2 * i)) & 0x80000000u);
   }
-  {
-    const float s1 = (cg & 1) ? -1.f : 1.f;
-    const float s2 = (cg & 2) ? -1.f : 1.f;
-    const float s4 = (cg & 4) ? -1.f : 1.f;
+  const qt_f16x8 bpos = __builtin_bit_cast(qt_f16x8, bpw), bneg = __builtin_bit_cast(qt_f16x8, bnw);
+  float R[8][8];   // [q = 4 bb + r][m = sigma + 2 p']: token tok(q), channel j + 16 m
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    qt_f32x4 zp[4], zn[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const qt_f16x8 x = __builtin_bit_cast(qt_f16x8, raw[bb][p]);
+      zp[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, bpos, qt_f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      zn[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, bneg, qt_f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+    // channel bits 5, 6: y[p'] = sum_p (-1)^popcount(p & p') z[p]
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], s1, lane_xor<1>(R[r][k]));
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], s2, lane_xor<2>(R[r][k]));
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], s4, lane_xor<4>(R[r][k]));
+      for (int sg = 0; sg < 2; ++sg) {
+        const qt_f32x4* z = sg ? zn : zp;
+        const float e0 = z[0][r] + z[1][r], e1 = z[0][r] - z[1][r];
+        const float e2 = z[2][r] + z[3][r], e3 = z[2][r] - z[3][r];
+        R[4 * bb + r][sg + 0] = e0 + e2;
+        R[4 * bb + r][sg + 4] = e0 - e2;
+        R[4 * bb + r][sg + 2] = e1 + e3;
+        R[4 * bb + r][sg + 6] = e1 - e3;
+      }
   }
 
   // ---------------------------------------------------------------- normalization
   // Spread sums are taken over values shifted by a reference (channel step:
   // the tile's first token; token step: the token's channel 0), so that
   // E[d^2] - E[d]^2 does not cancel when a mean dwarfs the spread.
-  if (tq == 0) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      *reinterpret_cast<qt_f32x4*>(&sm.ref_c[64 * half + 8 * cg]) =
-          qt_f32x4{R[0][8 * half], R[0][8 * half + 1], R[0][8 * half + 2], R[0][8 * half + 3]};
-      *reinterpret_cast<qt_f32x4*>(&sm.ref_c[64 * half + 8 * cg + 4]) =
-          qt_f32x4{R[0][8 * half + 4], R[0][8 * half + 5], R[0][8 * half + 6], R[0][8 * half + 7]};
-    }
+  if (w == 0 && g == 0) {
+    *reinterpret_cast<qt_f32x4*>(&sm.ref_c[8 * j]) = qt_f32x4{R[0][0], R[0][1], R[0][2], R[0][3]};
+    *reinterpret_cast<qt_f32x4*>(&sm.ref_c[8 * j + 4]) = qt_f32x4{R[0][4], R[0][5], R[0][6], R[0][7]};
   }
-  if (cg == 0)
-    *reinterpret_cast<qt_f32x4*>(&sm.ref_t[4 * tq]) = qt_f32x4{R[0][0], R[1][0], R[2][0], R[3][0]};
+  if (j == 0) {
+    *reinterpret_cast<qt_f32x4*>(&sm.ref_t[tok(0)]) = qt_f32x4{R[0][0], R[1][0], R[2][0], R[3][0]};
+    *reinterpret_cast<qt_f32x4*>(&sm.ref_t[tok(4)]) = qt_f32x4{R[4][0], R[5][0], R[6][0], R[7][0]};
+  }
   for (int c = tid; c < kHeadDim; c += NT) {
     sm.a[c] = kInvSqrtD;
     sm.alpha[c] = 1.0f;
   }
   if (tid < T) sm.b[tid] = 1.0f;
   __syncthreads();
-  float a[16], b[4], refc[16], reft[4];
+  // (the references are re-read from LDS in each step, to keep registers free)
+  float a[8], b[8];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const qt_f32x4 lo = *reinterpret_cast<const qt_f32x4*>(&sm.ref_c[64 * half + 8 * cg]);
-    const qt_f32x4 hi = *reinterpret_cast<const qt_f32x4*>(&sm.ref_c[64 * half + 8 * cg + 4]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { refc[8 * half + i] = lo[i]; refc[8 * half + 4 + i] = hi[i]; }
+  for (int i = 0; i < 8; ++i) {
+    a[i] = kInvSqrtD;
+    b[i] = 1.0f;
   }
-  {
-    const qt_f32x4 rt = *reinterpret_cast<const qt_f32x4*>(&sm.ref_t[4 * tq]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) reft[r] = rt[r];
-  }
-#pragma unroll
-  for (int k = 0; k < 16; ++k) a[k] = kInvSqrtD;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) b[r] = 1.0f;
   const float inv_n = 1.0f / (float)n_valid;
   const float n_copies = (float)(T - n_valid);  // rows that are copies of row 0
   const int iters = A.iters;
   float b0 = 1.0f;
+  float* red0 = sm.red[0];
+  float* red1 = sm.red[1];
 
   for (int it = 0; it < iters; ++it) {
     // channel step: spread over the tile's valid tokens of u = b_t R_tc
     {
-      float s1[16], s2[16], kc[16];
+      float s1[8], s2[8], kc[8];
+      {
+        const qt_f32x4 r0 = *reinterpret_cast<const qt_f32x4*>(&sm.ref_c[8 * j]);
+        const qt_f32x4 r1 = *reinterpret_cast<const qt_f32x4*>(&sm.ref_c[8 * j + 4]);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) kc[k] = b0 * refc[k];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float d = __builtin_fmaf(b[0], R[0][k], -kc[k]);
-        s1[k] = d;
-        s2[k] = d * d;
-      }
-#pragma unroll
-      for (int r = 1; r < 4; ++r) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float d = __builtin_fmaf(b[r], R[r][k], -kc[k]);
-          s1[k] += d;
-          s2[k] = __builtin_fmaf(d, d, s2[k]);
+        for (int i = 0; i < 4; ++i) {
+          kc[i] = b0 * r0[i];
+          kc[4 + i] = b0 * r1[i];
         }
       }
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int c0 = 64 * half + 8 * cg;
-        *reinterpret_cast<qt_f32x4*>(&sm.red[0][tq][c0]) =
-            qt_f32x4{s1[8 * half], s1[8 * half + 1], s1[8 * half + 2], s1[8 * half + 3]};
-        *reinterpret_cast<qt_f32x4*>(&sm.red[0][tq][c0 + 4]) =
-            qt_f32x4{s1[8 * half + 4], s1[8 * half + 5], s1[8 * half + 6], s1[8 * half + 7]};
-        *reinterpret_cast<qt_f32x4*>(&sm.red[1][tq][c0]) =
-            qt_f32x4{s2[8 * half], s2[8 * half + 1], s2[8 * half + 2], s2[8 * half + 3]};
-        *reinterpret_cast<qt_f32x4*>(&sm.red[1][tq][c0 + 4]) =
-            qt_f32x4{s2[8 * half + 4], s2[8 * half + 5], s2[8 * half + 6], s2[8 * half + 7]};
+      for (int m = 0; m < 8; ++m) {
+        const float d = __builtin_fmaf(b[0], R[0][m], -kc[m]);
+        s1[m] = d;
+        s2[m] = d * d;
       }
+#pragma unroll
+      for (int q = 1; q < 8; ++q) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float d = __builtin_fmaf(b[q], R[q][m], -kc[m]);
+          s1[m] += d;
+          s2[m] = __builtin_fmaf(d, d, s2[m]);
+        }
+      }
+      float* p1 = red0 + (4 * w + g) * kHeadDim + 8 * j;
+      float* p2 = red1 + (4 * w + g) * kHeadDim + 8 * j;
+      *reinterpret_cast<qt_f32x4*>(p1) = qt_f32x4{s1[0], s1[1], s1[2], s1[3]};
+      *reinterpret_cast<qt_f32x4*>(p1 + 4) = qt_f32x4{s1[4], s1[5], s1[6], s1[7]};
+      *reinterpret_cast<qt_f32x4*>(p2) = qt_f32x4{s2[0], s2[1], s2[2], s2[3]};
+      *reinterpret_cast<qt_f32x4*>(p2 + 4) = qt_f32x4{s2[4], s2[5], s2[6], s2[7]};
     }
     __syncthreads();
-    for (int c = tid; c < kHeadDim; c += NT) {
+    for (int i = tid; i < kHeadDim; i += NT) {   // lane-order index i: channel (i >> 3) + 16 (i & 7)
       float S1 = 0.f, S2 = 0.f;
 #pragma unroll
-      for (int g = 0; g < T / 4; ++g) {
-        S1 += sm.red[0][g][c];
-        S2 += sm.red[1][g][c];
+      for (int row = 0; row < T / 8; ++row) {
+        S1 += red0[row * kHeadDim + i];
+        S2 += red1[row * kHeadDim + i];
       }
       // copies of row 0 each added row 0's own shifted value rho (the fma
       // residual of the shift); take them out
-      const float rc = sm.ref_c[c];
+      const float rc = sm.ref_c[i];
       const float kcc = b0 * rc;
       const float rho = __builtin_fmaf(b0, rc, -kcc);
       S1 = __builtin_fmaf(-n_copies, rho, S1);
       S2 = __builtin_fmaf(-n_copies, rho * rho, S2);
-      const float m = S1 * inv_n;                                   // mean of the shifted values
-      const float var = fmaxf(__builtin_fmaf(-m, m, S2 * inv_n), 0.f);
-      const float mu = m + kcc;                                     // mean of u
+      const float mn = S1 * inv_n;                                  // mean of the shifted values
+      const float var = fmaxf(__builtin_fmaf(-mn, mn, S2 * inv_n), 0.f);
+      const float mu = mn + kcc;                                    // mean of u
       const float ms = __builtin_fmaf(mu, mu, var);                 // mean square of u
       if (var > kGuard2 * ms) {
-        sm.a[c] = __builtin_amdgcn_rsqf(var);
-        sm.alpha[c] = __builtin_sqrtf(var * (1.0f / kHeadDim));
+        sm.a[i] = __builtin_amdgcn_rsqf(var);
+        sm.alpha[(i >> 3) + 16 * (i & 7)] = __builtin_sqrtf(var * (1.0f / kHeadDim));
       }
     }
     __syncthreads();
+    {
+      const qt_f32x4 lo = *reinterpret_cast<const qt_f32x4*>(&sm.a[8 * j]);
+      const qt_f32x4 hi = *reinterpret_cast<const qt_f32x4*>(&sm.a[8 * j + 4]);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const qt_f32x4 lo = *reinterpret_cast<const qt_f32x4*>(&sm.a[64 * half + 8 * cg]);
-      const qt_f32x4 hi = *reinterpret_cast<const qt_f32x4*>(&sm.a[64 * half + 8 * cg + 4]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { a[8 * half + i] = lo[i]; a[8 * half + 4 + i] = hi[i]; }
+      for (int i = 0; i < 4; ++i) { a[i] = lo[i]; a[4 + i] = hi[i]; }
     }
     if (it + 1 == iters) break;  // the final token step cancels in every stored value
 
     // token step: spread over the 128 channels of u = a_c R_tc
-    const float a0 = sm.a[0];
+    const float a0 = sm.a[0];   // channel 0
     {
-      float t1[4], t2[4];
+      float t1[8], t2[8];
+      const qt_f32x4 u0 = *reinterpret_cast<const qt_f32x4*>(&sm.ref_t[tok(0)]);
+      const qt_f32x4 u1 = *reinterpret_cast<const qt_f32x4*>(&sm.ref_t[tok(4)]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float kt = a0 * reft[r];
+      for (int q = 0; q < 8; ++q) {
+        const float kt = a0 * ((q < 4) ? u0[q] : u1[q - 4]);
         float x1, x2;
         {
-          const float d = __builtin_fmaf(a[0], R[r][0], -kt);
+          const float d = __builtin_fmaf(a[0], R[q][0], -kt);
           x1 = d;
           x2 = d * d;
         }
 #pragma unroll
-        for (int k = 1; k < 16; ++k) {
-          const float d = __builtin_fmaf(a[k], R[r][k], -kt);
+        for (int m = 1; m < 8; ++m) {
+          const float d = __builtin_fmaf(a[m], R[q][m], -kt);
           x1 += d;
           x2 = __builtin_fmaf(d, d, x2);
         }
-        t1[r] = x1;
-        t2[r] = x2;
+        t1[q] = x1;
+        t2[q] = x2;
       }
-      float* tr = &sm.red[0][0][0];  // [2][8][T] view
-      *reinterpret_cast<qt_f32x4*>(&tr[(0 * 8 + cg) * T + 4 * tq]) = qt_f32x4{t1[0], t1[1], t1[2], t1[3]};
-      *reinterpret_cast<qt_f32x4*>(&tr[(1 * 8 + cg) * T + 4 * tq]) = qt_f32x4{t2[0], t2[1], t2[2], t2[3]};
+      *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(0)]) = qt_f32x4{t1[0], t1[1], t1[2], t1[3]};
+      *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(4)]) = qt_f32x4{t1[4], t1[5], t1[6], t1[7]};
+      *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(0)]) = qt_f32x4{t2[0], t2[1], t2[2], t2[3]};
+      *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(4)]) = qt_f32x4{t2[4], t2[5], t2[6], t2[7]};
     }
     __syncthreads();
     if (tid < T) {
-      const float* tr = &sm.red[0][0][0];
       float T1 = 0.f, T2 = 0.f;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        T1 += tr[(0 * 8 + g) * T + tid];
-        T2 += tr[(1 * 8 + g) * T + tid];
+      for (int jj = 0; jj < 16; ++jj) {
+        T1 += red0[jj * T + tid];
+        T2 += red1[jj * T + tid];
       }
-      const float m = T1 * (1.0f / kHeadDim);
-      const float var = fmaxf(__builtin_fmaf(-m, m, T2 * (1.0f / kHeadDim)), 0.f);
-      const float mu = __builtin_fmaf(a0, sm.ref_t[tid], m);
+      const float mn = T1 * (1.0f / kHeadDim);
+      const float var = fmaxf(__builtin_fmaf(-mn, mn, T2 * (1.0f / kHeadDim)), 0.f);
+      const float mu = __builtin_fmaf(a0, sm.ref_t[tid], mn);
       const float ms = __builtin_fmaf(mu, mu, var);
       if (var > kGuard2 * ms) sm.b[tid] = __builtin_amdgcn_rsqf(var);
     }
     __syncthreads();
     {
       b0 = sm.b[0];
-      const qt_f32x4 bb = *reinterpret_cast<const qt_f32x4*>(&sm.b[4 * tq]);
+      const qt_f32x4 u0 = *reinterpret_cast<const qt_f32x4*>(&sm.b[tok(0)]);
+      const qt_f32x4 u1 = *reinterpret_cast<const qt_f32x4*>(&sm.b[tok(4)]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) b[r] = (4 * tq + r < n_valid) ? bb[r] : b0;  // copies weigh as row 0
+      for (int i = 0; i < 4; ++i) {   // copies weigh as row 0
+        b[i] = (tok(i) < n_valid) ? u0[i] : b0;
+        b[4 + i] = (tok(4 + i) < n_valid) ? u1[i] : b0;
+      }
     }
   }
 
   // ---------------------------------------------------------------- rounding
-  float zmin[4], zmax[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) R[r][k] *= a[k];
-    float mn = fminf(R[r][0], R[r][1]), mx = fmaxf(R[r][0], R[r][1]);
-#pragma unroll
-    for (int k = 2; k < 16; k += 2) {
-      mn = fminf(mn, fminf(R[r][k], R[r][k + 1]));
-      mx = fmaxf(mx, fmaxf(R[r][k], R[r][k + 1]));
-    }
-    zmin[r] = mn;
-    zmax[r] = mx;
-  }
   {
-    float* tr = &sm.red[0][0][0];
-    *reinterpret_cast<qt_f32x4*>(&tr[(0 * 8 + cg) * T + 4 * tq]) = qt_f32x4{zmin[0], zmin[1], zmin[2], zmin[3]};
-    *reinterpret_cast<qt_f32x4*>(&tr[(1 * 8 + cg) * T + 4 * tq]) = qt_f32x4{zmax[0], zmax[1], zmax[2], zmax[3]};
+    float zmin[8], zmax[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) R[q][m] *= a[m];
+      float mn = fminf(R[q][0], R[q][1]), mx = fmaxf(R[q][0], R[q][1]);
+#pragma unroll
+      for (int m = 2; m < 8; m += 2) {
+        mn = fminf(mn, fminf(R[q][m], R[q][m + 1]));
+        mx = fmaxf(mx, fmaxf(R[q][m], R[q][m + 1]));
+      }
+      zmin[q] = mn;
+      zmax[q] = mx;
+    }
+    *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(0)]) = qt_f32x4{zmin[0], zmin[1], zmin[2], zmin[3]};
+    *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(4)]) = qt_f32x4{zmin[4], zmin[5], zmin[6], zmin[7]};
+    *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(0)]) = qt_f32x4{zmax[0], zmax[1], zmax[2], zmax[3]};
+    *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(4)]) = qt_f32x4{zmax[4], zmax[5], zmax[6], zmax[7]};
   }
   __syncthreads();
 
@@ -370,12 +377,11 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
   };
 
   if (tid < T) {
-    const float* tr = &sm.red[0][0][0];
-    float mn = tr[(0 * 8) * T + tid], mx = tr[(1 * 8) * T + tid];
+    float mn = red0[tid], mx = red1[tid];
 #pragma unroll
-    for (int g = 1; g < 8; ++g) {
-      mn = fminf(mn, tr[(0 * 8 + g) * T + tid]);
-      mx = fmaxf(mx, tr[(1 * 8 + g) * T + tid]);
+    for (int jj = 1; jj < 16; ++jj) {
+      mn = fminf(mn, red0[jj * T + tid]);
+      mx = fmaxf(mx, red1[jj * T + tid]);
     }
     float step = 0.f, off = 0.f, inv = 0.f, nmi = 0.f;
     if (tid < n_valid) {
@@ -413,82 +419,75 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
 
   // values before rounding: v = (z - min) * levels / range, in [0, levels]
   {
-    const qt_f32x4 iv = *reinterpret_cast<const qt_f32x4*>(&sm.inv[4 * tq]);
-    const qt_f32x4 nm = *reinterpret_cast<const qt_f32x4*>(&sm.nmi[4 * tq]);
+    const qt_f32x4 i0 = *reinterpret_cast<const qt_f32x4*>(&sm.inv[tok(0)]);
+    const qt_f32x4 i1 = *reinterpret_cast<const qt_f32x4*>(&sm.inv[tok(4)]);
+    const qt_f32x4 n0 = *reinterpret_cast<const qt_f32x4*>(&sm.nmi[tok(0)]);
+    const qt_f32x4 n1 = *reinterpret_cast<const qt_f32x4*>(&sm.nmi[tok(4)]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int q = 0; q < 8; ++q) {
+      const float iv = (q < 4) ? i0[q] : i1[q - 4];
+      const float nm = (q < 4) ? n0[q] : n1[q - 4];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) R[r][k] = __builtin_fmaf(R[r][k], iv[r], nm[r]);
+      for (int m = 0; m < 8; ++m) R[q][m] = __builtin_fmaf(R[q][m], iv, nm);
+    }
   }
 
   if (MODE == kDense || !VLAYOUT) {
-    // natural packing, 8 channels of one token per 8*BITS bits
+    // unit j of each of the lane's tokens: field m <- channel j + 16 m
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * tq + r;
+    for (int q = 0; q < 8; ++q) {
+      const int t = tok(q);
       if (MODE == kDense && t >= n_valid) continue;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = R[r][8 * half + j];
-        unsigned w;
-        if (BITS == 4) {
-          // fields in order 0..7; bytes take fields (0,1), (2,3), ...
-          float o[8] = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
-          w = pack_fields<4>(o);
-        } else {
-          w = pack_fields<2>(v);
-        }
-        if (MODE == kDense) {
-          uint8_t* row = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8);
-          if (BITS == 4) *reinterpret_cast<uint32_t*>(row + BITS * (8 * half + cg)) = w;
-          else *reinterpret_cast<uint16_t*>(row + BITS * (8 * half + cg)) = (uint16_t)w;
-        } else {
-          // K slot: 4 blocks of 32 channels, token after token
-          constexpr int CB = 4 * BITS;  // bytes per token per block
-          uint8_t* dst = slot_ptr((4 * tq) / kPage) + (2 * half + (cg >> 2)) * (kPage * CB) +
-                         ((4 * tq) % kPage + r) * CB + BITS * (cg & 3);
-          if (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = w;
-          else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
-        }
+      const unsigned wd = pack_fields<BITS>(R[q]);
+      if (MODE == kDense) {
+        uint8_t* row = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8);
+        if (BITS == 4) *reinterpret_cast<uint32_t*>(row + 4 * j) = wd;
+        else *reinterpret_cast<uint16_t*>(row + 2 * j) = (uint16_t)wd;
+      } else {
+        // K slot: 4 blocks of 4 units (4 BITS bytes per token), token after token
+        uint8_t* dst = slot_ptr(t / kPage) + (j >> 2) * (kPage * 4 * BITS) + (t % kPage) * (4 * BITS) + BITS * (j & 3);
+        if (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = wd;
+        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wd;
       }
     }
   } else {
     // V slot: run l (4*BITS bytes at 4*BITS*l) holds channels l and 64 + l of
     // the page's 16 tokens; token 4g + r of half h is pair p = 2g + h, in word
-    // p / (F/4) of the run, field 2m + (r>>1) + (F/2)(r&1), m = p mod (F/4).
-    // This thread holds quad g (its 4 tokens) of the runs 8 cg + j (its
-    // channels j and 8 + j), so it builds its pairs' fields of every run.
+    // p / (F/4) of the run, field 2m' + (r>>1) + (F/2)(r&1), m' = p mod (F/4).
+    // The lane holds quad g of page 2w + bb for the runs j + 16 m (m < 4),
+    // channels j + 16 m (h = 0) and j + 16 (m + 4) (h = 1).
     constexpr int F = 32 / BITS;
-    uint8_t* slot = slot_ptr((4 * tq) / kPage);
-    const int g = tq % (kPage / 4);
-    unsigned w8[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float o[F];
+    for (int bb = 0; bb < 2; ++bb) {
+      uint8_t* slot = slot_ptr(2 * w + bb);
+      unsigned part[4];
 #pragma unroll
-      for (int f = 0; f < F; ++f) o[f] = 0.f;
+      for (int m = 0; m < 4; ++m) {
+        float o[F];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int f = 0; f < F; ++f) o[f] = 0.f;
+        const int mq = (BITS == 4) ? 0 : 2 * (g & 1);   // m' = 2 (g mod 2) + h at 2 bits
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[2 * h + (r >> 1) + (F / 2) * (r & 1)] = R[r][8 * h + j];
-      w8[j] = pack_fields<BITS>(o);   // fields of m = h; m = 2 (g & 1) + h for 2-bit is a shift
-    }
-    if (BITS == 4) {
-      // one word per (run, quad): this thread's alone
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(slot + 16 * (8 * cg + j) + 4 * g) = w8[j];
-    } else {
-      // one word per (run, quad pair): merge with the thread of quad g ^ 1
-      // (lane ^ 8); the even quad's thread writes runs j < 4, the odd one j >= 4
-      const bool odd = (g & 1) != 0;
+          for (int r = 0; r < 4; ++r) o[2 * h + (r >> 1) + (F / 2) * (r & 1)] = R[4 * bb + r][m + 4 * h];
+        // fields 2 m' + ... with m' = mq + h: the mq part is a shift of the word
+        part[m] = pack_fields<BITS>(o) << (BITS * 2 * mq);
+      }
+      if (BITS == 4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned mine = (odd ? w8[j + 4] : w8[j]) << (odd ? 8 : 0);
-        const unsigned give = (odd ? w8[j] : w8[j + 4]) << (odd ? 8 : 0);
-        const unsigned got = (unsigned)__float_as_int(lane_xor<8>(__int_as_float((int)give)));
-        *reinterpret_cast<uint32_t*>(slot + 8 * (8 * cg + j + (odd ? 4 : 0)) + 4 * (g >> 1)) = mine | got;
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<uint32_t*>(slot + 16 * (j + 16 * m) + 4 * g) = part[m];
+      } else {
+        // one word per (run, quad pair): merge with the lane of quad g ^ 1
+        // (lane ^ 16); the even quad's lane writes runs m < 2, the odd one m >= 2
+        const bool odd = (g & 1) != 0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const unsigned mine = odd ? part[k + 2] : part[k];
+          const unsigned give = odd ? part[k] : part[k + 2];
+          const unsigned got = (unsigned)__shfl_xor((int)give, 16);
+          *reinterpret_cast<uint32_t*>(slot + 8 * (j + 16 * (k + (odd ? 2 : 0))) + 4 * (g >> 1)) = mine | got;
+        }
       }
     }
   }
