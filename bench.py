@@ -38,11 +38,12 @@ D = 128
 
 
 def quantize_valu_ops_per_element(iters: int) -> int:
-    """Algorithmic VALU lane-ops per element of the quantizer: fp16->fp32 (1),
-    the 7-stage butterfly (7), 3 per normalization half-step (shifted value,
-    sum, sum of squares) over 2*iters-1 half-steps (the last token step
-    cancels), and rounding (scale, min/max, affine map, convert: 4)."""
-    return 1 + 7 + 3 * max(2 * iters - 1, 0) + 4
+    """Algorithmic VALU lane-ops per element of the quantizer: the rotation's
+    channel bits 0..4 run on the matrix cores (fp16 in, exact products), bits
+    5 and 6 are a 4-point butterfly (2); 3 per normalization half-step
+    (shifted value, sum, sum of squares) over 2*iters-1 half-steps (the last
+    token step cancels); rounding (scale, min/max, affine map, convert: 4)."""
+    return 2 + 3 * max(2 * iters - 1, 0) + 4
 
 
 def measured_traffic(kernel_sources, profile: str):
