@@ -97,9 +97,14 @@ const char* kvq_version(void);
  *   offset: float32[16]   per token O   (0 for rows past the sequence end)
  *   alpha : float32[16*128/tile_tokens] the slice j*L..(j+1)*L-1 (L = 2048/T)
  *           of the tile's channel factors, j = the page's index in its tile.
- * K-slot codes: 4 blocks of 32 channels; block k stores, token after token,
- *   channels 32k..32k+31 of each token packed low bits first (channel c at
- *   bits (c mod (8/bits))*bits of byte c*bits/8 within the token's block).
+ * Unit order of a token's 128 codes (dense codes and K slots): 16 units of
+ *   8 fields, a unit being 8*bits bits (a little-endian 32-bit word at 4
+ *   bits, a 16-bit half at 2 bits), unit u at bit 8*bits*u of the token's
+ *   codes; field m (bits [bits*m, bits*(m+1)) of the unit) holds channel
+ *   u + 16*m.
+ * K-slot codes: each token's units cut into 4 blocks of 4 units (4*bits
+ *   bytes); block k stores, token after token, units 4k..4k+3 of each of the
+ *   16 tokens (block k of token t at byte 4*bits*(16*k + t)).
  * V-slot codes: 64 runs of 4*bits bytes; run l (at byte 4*bits*l) holds the
  *   channels l (h = 0) and 64 + l (h = 1) of the 16 tokens, read as
  *   little-endian 32-bit words of F = 32/bits fields.  Token t = 4g + r
@@ -120,8 +125,8 @@ size_t kvq_slot_bytes(const kvq_config* cfg, int32_t is_v);
  *   x          fp16 [n_tokens][heads][128]; tile j of each head covers tokens
  *              j*T .. min(n_tokens, (j+1)*T)-1.
  *   bits       2 or 4 (cfg->bits_k/bits_v are ignored here).
- *   codes      uint8 [n_tokens][heads][128*bits/8], channels packed low bits
- *              first (natural order).
+ *   codes      uint8 [n_tokens][heads][128*bits/8], each token's codes in
+ *              unit order (see the page-pool layout below).
  *   alpha      float32 [ceil(n_tokens/T)][heads][128] channel factors.
  *   tok_scale  float32 [n_tokens][heads] per token S.
  *   tok_offset float32 [n_tokens][heads] per token O.
