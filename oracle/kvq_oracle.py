@@ -613,6 +613,23 @@ def read_baseline_sequence(pool, table_row, seq_len, head, role, fp8=False, scal
     return out
 
 
+def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bits_v, base_k, base_v):
+    """The re-materializing read path's first half: every cached token restored
+    from the quantized pages (read_sequence, float64) and written, rounded to
+    fp16, into fp16 baseline pools with the same block table (in place).  Pages
+    past a sequence's last token are left alone; rows of its last page past the
+    end are 0 (as fill_pages_baseline writes them)."""
+    heads = pool_k.shape[1]
+    for s in range(len(seq_lens)):
+        n = int(seq_lens[s])
+        if n == 0:
+            continue
+        kx = np.stack([read_sequence(pool_k, table[s], n, h, "K", bits_k, tile_tokens)[0] for h in range(heads)], 1)
+        vx = np.stack([read_sequence(pool_v, table[s], n, h, "V", bits_v, tile_tokens)[0] for h in range(heads)], 1)
+        fill_pages_baseline(kx.astype(np.float16), vx.astype(np.float16), np.array([0, n]), table[s:s + 1],
+                            base_k, base_v)
+
+
 def paged_decode_attn_baseline(q, table, seq_lens, pool_k, pool_v, fp8=False, k_scale=1.0, v_scale=1.0,
                                sm_scale=None):
     s_n, hq, d = q.shape

@@ -472,3 +472,37 @@ def test_baseline_pages_round_trip_and_attention():
         vt = torch.tensor(orc.read_baseline_sequence(pv, table[1], 33, 0, "V", fp8, vs))[None].expand(4, -1, -1)
         ref = torch.nn.functional.scaled_dot_product_attention(qt[:4], kt, vt)[:, 0].numpy()
         np.testing.assert_allclose(out[1, :4], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_rematerialized_pages_hold_the_restored_tokens():
+    """Restoring quantized pages into fp16 pages: each token equals the dense
+    restore of the same tile rounded to fp16, rows past the end are 0, and fp16
+    attention over them matches attention over the quantized pages within the
+    fp16 rounding of the restored values."""
+    import dataclasses
+    wl = dataclasses.replace(inputs.workload(2), seq_lens=(150, 37), hkv=2, hq=8, tile_tokens=32, bits_k=4, bits_v=2)
+    k, v = inputs.gen_kv(wl, "K"), inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    cu = wl.cu_seqlens()
+    pk, pv = orc.new_pool(npages, 2, 4, 32), orc.new_pool(npages, 2, 2, 32)
+    orc.quantize_to_pages(k, v, cu, table, 32, 4, 2, 3, pk, pv)
+    bk, bv = orc.new_baseline_pool(npages, 2, False), orc.new_baseline_pool(npages, 2, False)
+    lens = np.array(wl.seq_lens)
+    orc.rematerialize_pages(pk, pv, table, lens, 32, 4, 2, bk, bv)
+    for s in range(2):
+        a0, a1 = int(cu[s]), int(cu[s + 1])
+        dk = orc.quantize_dense(k[a0:a1], 32, 4, 3)
+        dv = orc.quantize_dense(v[a0:a1], 32, 2, 3)
+        rk = orc.dequantize_dense(dk["codes"], dk["alpha"], dk["scale"], dk["offset"], 32, 4).astype(np.float16)
+        rv = orc.dequantize_dense(dv["codes"], dv["alpha"], dv["scale"], dv["offset"], 32, 2).astype(np.float16)
+        for h in range(2):
+            np.testing.assert_array_equal(orc.read_baseline_sequence(bk, table[s], lens[s], h, "K"), rk[:, h])
+            np.testing.assert_array_equal(orc.read_baseline_sequence(bv, table[s], lens[s], h, "V"), rv[:, h])
+    # sequence 1 ends 5 rows into its third page: the rest of that page is 0
+    last = int(table[1][37 // 16])
+    assert not bk[last, :, 5 * 128:].any()
+    assert not bv[last].reshape(2, 128, 16)[:, :, 5:].any()
+    q = inputs.gen_q(wl)
+    ref = orc.paged_decode_attn(q, table, lens, pk, pv, 32, 4, 2)
+    got = orc.paged_decode_attn_baseline(q, table, lens, bk, bv)
+    assert np.abs(got - ref).max() < 5e-3 * np.abs(ref).max()
