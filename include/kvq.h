@@ -283,6 +283,27 @@ kvq_status kvq_paged_decode_attn_fp8(const kvq_config* cfg, const kvq_half* q, i
                                      void* stream);
 
 /*
+ * kvq_rematerialize_fp16_pages - the read path the direct decode avoids:
+ * restore every cached token of the quantized pages to fp16 before attention
+ * (aitrends.kr article 74976, TL;DR, and its glossary entry on the attention
+ * backend: reading compressed pages directly instead of re-materializing).
+ * Each token of sequence s (seq_lens[s] tokens, device) is rebuilt as
+ * kvq_dequantize does (Hadamard(alpha * (S*code + O)), fp32, rounded to fp16)
+ * and written into the fp16 pools base_k, base_v (the layout of
+ * kvq_fill_pages_fp16) at the same page ids (block_table).  Rows of a
+ * sequence's last page past its end are written 0; pages past that are not
+ * touched.  kvq_paged_decode_attn_fp16 then reads them.
+ *   max_seq_len  host bound of seq_lens; max_blocks must hold the pages of
+ *                whole tiles up to it.
+ * Errors: as kvq_quantize_to_pages (KVQ_ERR_ARG for null pointers, sizes <= 0,
+ * too small a block table; KVQ_ERR_UNSUPPORTED for the config).
+ */
+kvq_status kvq_rematerialize_fp16_pages(const kvq_config* cfg, const void* pool_k, const void* pool_v,
+                                        const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                        int32_t num_seqs, int32_t max_seq_len, int32_t kv_heads, kvq_half* base_k,
+                                        kvq_half* base_v, void* stream);
+
+/*
  * kvq_bandwidth_probe - measurement helper, not part of the method: copies
  * `bytes` (a positive multiple of 16) from src to dst with a plain streaming
  * kernel, so that achieved HBM bandwidth and profiler byte counters can be

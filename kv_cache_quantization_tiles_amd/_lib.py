@@ -20,7 +20,7 @@ EXPORTED = (
     "kvq_quantize_to_pages", "kvq_append_and_requant", "kvq_decode_workspace_bytes",
     "kvq_paged_decode_attn", "kvq_bandwidth_probe", "kvq_baseline_page_bytes", "kvq_fill_pages_fp16",
     "kvq_fill_pages_fp8", "kvq_baseline_workspace_bytes", "kvq_paged_decode_attn_fp16",
-    "kvq_paged_decode_attn_fp8", "kvq_append_and_decode",
+    "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages",
 )
 
 
@@ -71,6 +71,7 @@ def load():
     _F = ctypes.c_float
     lib.kvq_append_and_decode.argtypes = [_CFG, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I, _F, _P,
                                           _P, ctypes.c_size_t, _P]
+    lib.kvq_rematerialize_fp16_pages.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P]
     lib.kvq_baseline_page_bytes.argtypes = [_I]
     lib.kvq_baseline_page_bytes.restype = ctypes.c_size_t
     lib.kvq_fill_pages_fp16.argtypes = [_CFG, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P]
@@ -84,7 +85,7 @@ def load():
     for name in ("kvq_quantize_tiles", "kvq_dequantize", "kvq_quantize_to_pages",
                  "kvq_append_and_requant", "kvq_paged_decode_attn", "kvq_bandwidth_probe",
                  "kvq_fill_pages_fp16", "kvq_fill_pages_fp8", "kvq_paged_decode_attn_fp16",
-                 "kvq_paged_decode_attn_fp8", "kvq_append_and_decode"):
+                 "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -164,6 +165,13 @@ def kvq_paged_decode_attn(cfg, q, num_seqs, q_heads, kv_heads, block_table, max_
 
 def kvq_bandwidth_probe(src, dst, nbytes, stream=None):
     _check(load().kvq_bandwidth_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def kvq_rematerialize_fp16_pages(cfg, pool_k, pool_v, block_table, max_blocks, seq_lens, num_seqs, max_seq_len,
+                                 kv_heads, base_k, base_v, stream=None):
+    _check(load().kvq_rematerialize_fp16_pages(ctypes.byref(cfg), _ptr(pool_k), _ptr(pool_v), _ptr(block_table),
+                                               max_blocks, _ptr(seq_lens), num_seqs, max_seq_len, kv_heads,
+                                               _ptr(base_k), _ptr(base_v), _stream(stream)))
 
 
 def kvq_baseline_page_bytes(fp8: bool) -> int:

@@ -15,7 +15,7 @@ from ._lib import (config, kvq_append_and_decode, kvq_append_and_requant, kvq_ba
                    kvq_baseline_workspace_bytes, kvq_decode_workspace_bytes, kvq_dequantize,
                    kvq_fill_pages_fp8, kvq_fill_pages_fp16, kvq_paged_decode_attn,
                    kvq_paged_decode_attn_fp8, kvq_paged_decode_attn_fp16, kvq_quantize_tiles,
-                   kvq_quantize_to_pages, kvq_slot_bytes)
+                   kvq_quantize_to_pages, kvq_rematerialize_fp16_pages, kvq_slot_bytes)
 
 HEAD_DIM = 128
 PAGE_TOKENS = 16
@@ -111,6 +111,14 @@ class PagedCache:
                               q.contiguous(), hq, int(max_seq_len), sm, out, workspace, workspace.numel())
         return out
 
+    def rematerialize_into(self, base: "BaselineCache", seq_lens, max_seq_len):
+        """Restore every cached token into the fp16 pools of `base` (same page ids),
+        the read path that re-materializes fp16 before attention."""
+        _require_cuda(seq_lens)
+        if base.fp8:
+            raise ValueError("re-materialization writes fp16 pools")
+        kvq_rematerialize_fp16_pages(self.cfg, self.pool_k, self.pool_v, self.block_table, self.max_blocks, seq_lens,
+                                     self.num_seqs, int(max_seq_len), self.kv_heads, base.pool_k, base.pool_v)
 
 
 class BaselineCache:

@@ -387,6 +387,30 @@ kvq_status kvq_fill_pages_fp16(const kvq_config* cfg, const kvq_half* k, const k
                        pool_k, pool_v, false, 1.f, 1.f, stream, "kvq_fill_pages_fp16");
 }
 
+kvq_status kvq_rematerialize_fp16_pages(const kvq_config* cfg, const void* pool_k, const void* pool_v,
+                                        const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                        int32_t num_seqs, int32_t max_seq_len, int32_t kv_heads, kvq_half* base_k,
+                                        kvq_half* base_v, void* stream) {
+  KVQ_TRY(check_config(cfg, true));
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(seq_lens);
+  KVQ_NONNULL(base_k);
+  KVQ_NONNULL(base_v);
+  if (num_seqs <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (kv_heads > 32767 || num_seqs > 65535) return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  const int T = cfg->tile_tokens;
+  if ((max_seq_len + T - 1) / T * (T / kvq::kPage) > max_blocks)
+    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold whole tiles of %d tokens", max_blocks, max_seq_len);
+  kvq::RematArgs a{(const uint8_t*)pool_k, (const uint8_t*)pool_v, block_table, max_blocks, seq_lens, kv_heads,
+                   base_k, base_v};
+  return launched(kvq::launch_rematerialize(a, T, cfg->bits_k, cfg->bits_v, num_seqs, max_seq_len,
+                                            (hipStream_t)stream),
+                  "kvq_rematerialize_fp16_pages");
+}
+
 kvq_status kvq_fill_pages_fp8(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seq_len,
                               int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,

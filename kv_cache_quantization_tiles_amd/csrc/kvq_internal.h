@@ -88,12 +88,25 @@ struct BaseFillArgs {
   float v_scale;
 };
 
+struct RematArgs {
+  const uint8_t* pool_k;      // quantized page pools
+  const uint8_t* pool_v;
+  const int32_t* block_table; // [S][max_blocks]
+  int max_blocks;
+  const int32_t* seq_lens;    // [S]
+  int kv_heads;
+  uint16_t* base_k;           // fp16 pools: K [pages][Hkv][16][D], V [pages][Hkv][D][16]
+  uint16_t* base_v;
+};
+
 hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s);
 hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v,
                                  int num_seqs, int max_seq_len, hipStream_t s);
 hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
                          hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream_t s);
+hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
+                                int max_seq_len, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s);

@@ -33,6 +33,8 @@ namespace kvq {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int T, int BITS>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void quantize_dense_kernel(QuantArgs A) {
@@ -139,6 +141,150 @@ __global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
   }
 }
 
+// ---------------------------------------------------------------- quantized pages -> fp16 pages
+// The re-materializing read path's restore: every token of a quantized page
+// rebuilt as H (alpha (S code + O)) / sqrt(128) in fp32 and stored as fp16 in
+// the fp16 pool's page of the same id (K token-major, V channel-major), as
+// kvq_fill_pages_fp16 lays them out.  128 threads = 16 tokens x 8 channel
+// groups, the dense restore's register layout and butterfly.
+template <int T, int BITS, bool VL>
+__device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj, int head, int n,
+                                             uint16_t (*vt)[kPage + 2]) {
+  constexpr int PPT = T / kPage, AL = slot_alpha_len(T);
+  constexpr int SLOT = slot_bytes(BITS, T), CODE = slot_code_bytes(BITS);
+  constexpr unsigned MASK = (1u << BITS) - 1u;
+  const int H = A.kv_heads;
+  const int tid = threadIdx.x, t = tid >> 3, cg = tid & 7;
+  const int32_t* row_tab = A.block_table + (size_t)seq * A.max_blocks;
+  const uint8_t* pool = VL ? A.pool_v : A.pool_k;
+  const int pid = row_tab[pj];
+  const uint8_t* slot = pool + ((size_t)pid * H + head) * SLOT;
+  // channel factors of the page's tile: channel c sits in the tile's page c / AL
+  const int pt0 = (pj / PPT) * PPT;
+  float al[16];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int c0 = 64 * half + 8 * cg;   // 8 channels inside one page's slice (AL is a multiple of 16)
+    const float* ap = reinterpret_cast<const float*>(pool + ((size_t)row_tab[pt0 + c0 / AL] * H + head) * SLOT +
+                                                     CODE + 8 * kPage) + (c0 % AL);
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      al[8 * half + i] = a0[i];
+      al[8 * half + 4 + i] = a1[i];
+    }
+  }
+  const float S = reinterpret_cast<const float*>(slot + CODE)[t];
+  const float O = reinterpret_cast<const float*>(slot + CODE + 4 * kPage)[t];
+  float x[16];
+  if (!VL) {
+    // unit order: channel 64 half + 8 cg + j is field 4 half + (cg >> 1) of unit
+    // 8 (cg & 1) + j; block b of token t at 4 BITS (16 b + t)
+    unsigned units[8];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const uint8_t* bp = slot + (16 * (2 * (cg & 1) + bb) + t) * 4 * BITS;
+      if (BITS == 4) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(bp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) units[4 * bb + i] = w[i];
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(bp);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          units[4 * bb + 2 * i] = w[i] & 0xFFFFu;
+          units[4 * bb + 2 * i + 1] = w[i] >> 16;
+        }
+      }
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int m = 4 * half + (cg >> 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[8 * half + j] = al[8 * half + j] * __builtin_fmaf(S, (float)((units[j] >> (BITS * m)) & MASK), O);
+    }
+  } else {
+    // runs: run l = 8 cg + j holds channels l (h = 0) and 64 + l (h = 1); token
+    // t = 4g + r of half h is pair p = 2g + h: word p / (F/4), field
+    // 2 (p mod F/4) + (r >> 1) + (F/2)(r & 1)
+    constexpr int F = 32 / BITS;
+    const int g = t >> 2, r = t & 3;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int l = 8 * cg + j;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = 2 * g + h;
+        const unsigned w = *reinterpret_cast<const uint32_t*>(slot + 4 * BITS * l + 4 * (p / (F / 4)));
+        const int f = 2 * (p % (F / 4)) + (r >> 1) + (F / 2) * (r & 1);
+        x[8 * h + j] = al[8 * h + j] * __builtin_fmaf(S, (float)((w >> (BITS * f)) & MASK), O);
+      }
+    }
+  }
+#pragma unroll
+  for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k & bit) continue;
+      const float lo = x[k], hi = x[k | bit];
+      x[k] = lo + hi;
+      x[k | bit] = lo - hi;
+    }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {   // channel bit 6: the two halves
+    const float lo = x[k], hi = x[k + 8];
+    x[k] = lo + hi;
+    x[k + 8] = lo - hi;
+  }
+  const float s1 = (cg & 1) ? -1.f : 1.f, s2 = (cg & 2) ? -1.f : 1.f, s4 = (cg & 4) ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s1, lane_xor<1>(x[k]));
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s2, lane_xor<2>(x[k]));
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s4, lane_xor<4>(x[k]));
+  uint16_t hv[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) hv[k] = (t < n) ? float_to_half_bits(x[k] * kInvSqrtD) : (uint16_t)0;
+  const size_t page = ((size_t)pid * H + head) * (kPage * kHeadDim);
+  if (!VL) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (unsigned)hv[8 * half + 2 * i] | ((unsigned)hv[8 * half + 2 * i + 1] << 16);
+      *reinterpret_cast<u32x4*>(A.base_k + page + t * kHeadDim + 64 * half + 8 * cg) = w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) vt[64 * (k >> 3) + 8 * cg + (k & 7)][t] = hv[k];
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {   // 256 chunks of 8 tokens of one channel
+      const int i = tid + 128 * it, c = i >> 1, t0 = 8 * (i & 1);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (unsigned)vt[c][t0 + 2 * e] | ((unsigned)vt[c][t0 + 2 * e + 1] << 16);
+      *reinterpret_cast<u32x4*>(A.base_v + page + c * kPage + t0) = w;
+    }
+  }
+}
+
+// grid: x = page of the sequence, y = head + Hkv * role (0 K, 1 V), z = sequence
+template <int T, int BK, int BV>
+__global__ __launch_bounds__(128) void rematerialize_kernel(RematArgs A) {
+  __shared__ uint16_t vt[kHeadDim][kPage + 2];
+  const int seq = blockIdx.z, pj = blockIdx.x;
+  const int role = blockIdx.y / A.kv_heads, head = blockIdx.y % A.kv_heads;
+  const int L = A.seq_lens[seq];
+  if (pj * kPage >= L) return;   // uniform over the workgroup
+  const int n = min(kPage, L - pj * kPage);
+  if (role == 0) restore_page<T, BK, false>(A, seq, pj, head, n, vt);
+  else restore_page<T, BV, true>(A, seq, pj, head, n, vt);
+}
+
 // ---------------------------------------------------------------- bandwidth probe
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
                                                    u32x4* __restrict__ dst, size_t n) {
@@ -211,6 +357,19 @@ hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream
       dim3 grid((unsigned)((rows + 15) / 16));
       hipLaunchKernelGGL((dequantize_kernel<T(), B()>), grid, dim3(128), 0, s, a);
       return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
+                                int max_seq_len, hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_bits(bits_k, [&](auto BK) {
+      return by_bits(bits_v, [&](auto BV) {
+        dim3 grid((max_seq_len + kPage - 1) / kPage, 2 * a.kv_heads, num_seqs);
+        hipLaunchKernelGGL((rematerialize_kernel<T(), BK(), BV()>), grid, dim3(128), 0, s, a);
+        return hipGetLastError();
+      });
     });
   });
 }

@@ -110,3 +110,15 @@ def test_baseline_validation(lib):
                                           None) == L.KVQ_ERR_WORKSPACE
     assert lib.kvq_paged_decode_attn_fp16(c, 16, 4, 64, 2, 16, 1028, 16, 16385, 16, 16, 0.1, 16, 16, 1 << 30,
                                           None) == L.KVQ_ERR_UNSUPPORTED
+
+
+def test_rematerialize_validation(lib):
+    cfg = L.config(64, 4, 4, 3)
+    c = ctypes.byref(cfg)
+    # a block table that cannot hold whole tiles (65 tokens at tile 64 = 8 pages), NULL fp16 pool
+    assert lib.kvq_rematerialize_fp16_pages(c, 16, 16, 16, 4, 16, 1, 65, 1, 16, 16, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_rematerialize_fp16_pages(c, 16, 16, 16, 8, 16, 1, 65, 1, None, 16, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_rematerialize_fp16_pages(c, 16, 16, 16, 8, 16, 0, 65, 1, 16, 16, None) == L.KVQ_ERR_ARG
+    bad = L.config(64, 3, 4, 3)
+    assert lib.kvq_rematerialize_fp16_pages(ctypes.byref(bad), 16, 16, 16, 8, 16, 1, 65, 1, 16, 16,
+                                            None) == L.KVQ_ERR_UNSUPPORTED

@@ -422,6 +422,63 @@ def test_full_size_qwen3_32b_tp2_burst_sampled():
     _sampled_decode_checks(wl, q, table, lens_now, gpk, gpv, got, [(0, 0), (31, 3)], "32x16k decode")
 
 
+REMAT_CASES = [
+    # (recipe, lens, hkv, hq, tile, bits_k, bits_v, iters)
+    (2, (200, 131, 64, 17), 2, 8, 64, 4, 4, 3),
+    (5, (300, 97, 33), 2, 16, 32, 4, 2, 5),
+    (2, (260, 128, 1000), 1, 4, 128, 2, 2, 3),
+    (1, (1024, 1), 1, 8, 64, 2, 4, 3),
+]
+
+
+@pytest.mark.parametrize("case", REMAT_CASES)
+def test_rematerialized_fp16_pages_match_oracle(case):
+    """Quantized pages restored into fp16 pages: each token within the restore
+    bar of the oracle's restore of the same (GPU) pages, rows past the ends 0,
+    pages past them untouched; the fp16 decode over them matches the oracle's
+    fp16 attention over the same pages."""
+    recipe, lens, hkv, hq, tile, bk, bv, iters = case
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    seq_lens = np.array(wl.seq_lens, np.int32)
+    base = api.BaselineCache(npages, hkv, torch.from_numpy(table), wl.num_seqs)
+    base.pool_k.fill_(1.0)   # pages the restore must leave alone keep this
+    base.pool_v.fill_(1.0)
+    cache.rematerialize_into(base, torch.from_numpy(seq_lens).cuda(), max(lens))
+    torch.cuda.synchronize()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    bk_got, bv_got = base.pool_k.cpu().numpy(), base.pool_v.cpu().numpy()
+    ref_k = np.ones_like(bk_got)
+    ref_v = np.ones_like(bv_got)
+    orc.rematerialize_pages(gpk, gpv, table, seq_lens, tile, bk, bv, ref_k, ref_v)
+    for s in range(wl.num_seqs):
+        n = int(seq_lens[s])
+        for h in range(hkv):
+            for role, got_pool, ref_pool in (("K", bk_got, ref_k), ("V", bv_got, ref_v)):
+                got = orc.read_baseline_sequence(got_pool, table[s], n, h, role)
+                ref = orc.read_baseline_sequence(ref_pool, table[s], n, h, role)
+                pu.assert_dequant(got, ref, f"remat {case} s{s} h{h} {role}")
+    # every page outside the sequences' tokens, and every row past an end, as the oracle left it
+    used = np.zeros((npages, 16), bool)
+    for s in range(wl.num_seqs):
+        for t in range(int(seq_lens[s])):
+            used[table[s][t // 16], t % 16] = True
+    kk = bk_got.reshape(npages, hkv, 16, 128)
+    vv = bv_got.reshape(npages, hkv, 128, 16)
+    rk = ref_k.reshape(npages, hkv, 16, 128)
+    rv = ref_v.reshape(npages, hkv, 128, 16)
+    for pg in range(npages):
+        for t in range(16):
+            if not used[pg, t]:
+                np.testing.assert_array_equal(kk[pg, :, t], rk[pg, :, t])
+                np.testing.assert_array_equal(vv[pg, :, :, t], rv[pg, :, :, t])
+    q = inputs.gen_q(wl)
+    out = base.decode(torch.from_numpy(q).cuda(), torch.from_numpy(seq_lens).cuda(), max(lens))
+    torch.cuda.synchronize()
+    ref = orc.paged_decode_attn_baseline(q, table, seq_lens, bk_got, bv_got)
+    pu.assert_attn(out.cpu().numpy(), ref, f"remat decode {case}")
+
+
 FUSED_CASES = [
     # (recipe, lens, hkv, hq, tile, bits_k, bits_v, iters)
     (2, (200, 131, 64, 17), 2, 8, 64, 4, 4, 3),
