@@ -164,7 +164,9 @@ def long_context_leg(n_iter: int = 10):
     """One layer of the 36-layer, 6 x 128K Qwen3-4B-shaped workload (8 kv /
     32 query heads, tile 128): the decode-attention step on fp16 pages, fp8
     (E4M3, per-tensor scale) pages, and 4-bit and 2-bit quantized pages, all
-    filled from the same inputs.  Attention only (no append), context 131072,
+    filled from the same inputs, and the 4-bit pages read the other way:
+    restored to fp16 pages first, then the fp16 decode (kvq4_rematerialize).
+    Attention only (no append), context 131072,
     pages far larger than the 256 MB last-level cache, so every call streams
     from HBM.  tok/s is for all 36 layers (36 such steps per token)."""
     import torch
@@ -220,6 +222,21 @@ def long_context_leg(n_iter: int = 10):
                        "tok_per_s_36_layers_attn_only": round(wl.num_seqs / (wl.layers * dec_ms * 1e-3), 1),
                        "fill_ms": round(fill_ms, 3),
                        "fill_GBps": round(fill_bytes / (fill_ms * 1e-3) / 1e9, 1)}
+        if name == "kvq4":
+            # the read path the direct decode avoids: restore every page to fp16, then the fp16 decode
+            base16 = api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+            ws16 = base16.workspace(wl.hq, max_len)
+            restore_ms = timed(lambda: cache.rematerialize_into(base16, lens, max_len), n_iter)
+            step_ms = timed(lambda: (cache.rematerialize_into(base16, lens, max_len),
+                                     base16.decode(q, lens, max_len, out=out, workspace=ws16)), n_iter)
+            rbytes = token_heads * (per_token_head + 2 * 2 * D)   # slots read, fp16 K and V written
+            modes["kvq4_rematerialize"] = {
+                "decode_attn_ms": round(step_ms, 4), "restore_ms": round(restore_ms, 4),
+                "restore_GBps": round(rbytes / (restore_ms * 1e-3) / 1e9, 1),
+                "restore_hbm_frac": round(rbytes / (restore_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "kv_bytes_per_layer_GB": round(dbytes / 1e9, 3),
+                "tok_per_s_36_layers_attn_only": round(wl.num_seqs / (wl.layers * step_ms * 1e-3), 1)}
+            del base16, ws16
         del cache, ws
         torch.cuda.empty_cache()
     del k, v
