@@ -46,6 +46,15 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
+// max of two floats as one v_max_f32.  fmaxf on a value that arrives from
+// another lane gets a canonicalizing v_max (x, x) first (NaN quieting); the
+// reductions here never see a NaN (finite inputs, -inf for masked scores).
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // v_permlane16_swap / v_permlane32_swap with both operands a copy of v return
 // a pair whose two members are v and the value of lane l^16 (resp. l^32) in
 // some order, so a symmetric op over the pair reduces over that lane pair in
@@ -60,11 +69,11 @@ __device__ __forceinline__ float sum32(float v) {
 }
 __device__ __forceinline__ float max16(float v) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  return vmax(__int_as_float(p[0]), __int_as_float(p[1]));
 }
 __device__ __forceinline__ float max32(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-  return fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  return vmax(__int_as_float(p[0]), __int_as_float(p[1]));
 }
 
 // Reductions over the 4 lanes l, l^16, l^32, l^48 (one query head's lanes).
@@ -150,10 +159,10 @@ __device__ __forceinline__ void split_grid(float x0, float x1, float m0, float m
 constexpr float kGrid = 12582912.f;   // 1.5 * 2^23
 
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, lane_xor<1>(v));
-  v = fmaxf(v, lane_xor<2>(v));
-  v = fmaxf(v, lane_xor<4>(v));
-  v = fmaxf(v, lane_xor<8>(v));
+  v = vmax(v, lane_xor<1>(v));
+  v = vmax(v, lane_xor<2>(v));
+  v = vmax(v, lane_xor<4>(v));
+  v = vmax(v, lane_xor<8>(v));
   return group_max(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
@@ -175,16 +184,17 @@ __device__ __forceinline__ float blocks_sum(float v) {
 }
 template <int NB>
 __device__ __forceinline__ float blocks_max(float v) {
-  v = fmaxf(v, lane_xor<4>(v));
-  v = fmaxf(v, lane_xor<8>(v));
-  v = fmaxf(v, lane_xor<16>(v));
-  if (NB == 16) v = fmaxf(v, xor32(v));
+  v = vmax(v, lane_xor<4>(v));
+  v = vmax(v, lane_xor<8>(v));
+  v = vmax(v, lane_xor<16>(v));
+  if (NB == 16) v = vmax(v, xor32(v));
   return v;
 }
 
 template <int T, int HG>
 struct alignas(16) DecodeSmem {
-  int32_t pages[kMaxChunksPerPart * 4];          // the partition's page ids
+  const uint8_t* kp[kMaxChunksPerPart * 4];      // the partition's K and V slots (this kv head)
+  const uint8_t* vp[kMaxChunksPerPart * 4];
   union {
     struct {
       float hq[4 * HG][kHeadDim];                // (H q)_c / weight of c's K field, at qk_slot(c)
@@ -283,20 +293,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     }
   }
   const int npages = ((L + T - 1) / T) * PPT;   // pages the sequence owns (whole tiles)
-  // the partition's page ids (up to the end of its last tile), staged once in LDS
+  // the partition's K and V slot addresses (up to the end of its last tile), staged once in LDS
   {
     const int32_t* row = A.block_table + (size_t)seq * A.max_blocks + 4 * c_begin;
     const int last = min(npages, ((4 * c_end + PPT - 1) / PPT) * PPT);
     const int n = last - 4 * c_begin;
-    for (int i = threadIdx.x; i < n; i += 64 * kWaves) sm.pages[i] = row[i];
+    for (int i = threadIdx.x; i < n; i += 64 * kWaves) {
+      const size_t slot = (size_t)row[i] * H + kvh;
+      sm.kp[i] = A.pool_k + slot * SLOT_K;
+      sm.vp[i] = A.pool_v + slot * SLOT_V;
+    }
   }
   __syncthreads();
-  // physical page of page pj of the sequence; a T = 32 chunk whose second tile
+  // LDS index of page pj of the sequence; a T = 32 chunk whose second tile
   // was never started reads its first tile's pages instead (every token there
   // is past the end and masked)
-  auto page_id = [&](int pj) { return sm.pages[(pj < npages ? pj : pj - 2) - 4 * c_begin]; };
-  auto kslot = [&](int pid) { return A.pool_k + ((size_t)pid * H + kvh) * SLOT_K; };
-  auto vslot = [&](int pid) { return A.pool_v + ((size_t)pid * H + kvh) * SLOT_V; };
+  auto page_ix = [&](int pj) { return (pj < npages ? pj : pj - 2) - 4 * c_begin; };
+  auto kslot = [&](int pj) { return sm.kp[page_ix(pj)]; };   // K slot of page pj of the sequence
+  auto vslot = [&](int pj) { return sm.vp[page_ix(pj)]; };
 
   // ------------------------------------------------ per-chunk operands (loaded one chunk ahead,
   // each right after its last use in the current chunk)
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     return (T == 128) ? 4 * (c & ~1) : 4 * c + PPT * tile_in_chunk;
   };
   auto load_k = [&](int c) {
-    const uint8_t* sl = kslot(page_id(4 * c + (lane >> 4)));
+    const uint8_t* sl = kslot(4 * c + (lane >> 4));
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       if (BK == 4) kq[blk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 256 * blk + 16 * (lane & 15)));
@@ -322,11 +336,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
   auto load_v = [&](int c) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint8_t* sl = vslot(page_id(4 * c + p));
+      const uint8_t* sl = vslot(4 * c + p);
       if (BV == 4) vq[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 16 * lane));
       else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 8 * lane)); vq[p] = u32x4{x[0], x[1], 0u, 0u}; }
     }
-    const uint8_t* sl = vslot(page_id(4 * c + (bq >> 2)));
+    const uint8_t* sl = vslot(4 * c + (bq >> 2));
     svq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 16 * (bq & 3)));
     ovq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 64 + 16 * (bq & 3)));
   };
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int ch = qk_channel<BK>(s, k);
-        ak[st][k] = reinterpret_cast<const float*>(kslot(page_id(tp + ch / AL)) + CODE_K + 128)[ch % AL];
+        ak[st][k] = reinterpret_cast<const float*>(kslot(tp + ch / AL) + CODE_K + 128)[ch % AL];
       }
     }
   };
@@ -350,7 +364,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int ch = lane + 64 * h;
-        av[tt][h] = reinterpret_cast<const float*>(vslot(page_id(tpv + ch / AL)) + CODE_V + 128)[ch % AL];
+        av[tt][h] = reinterpret_cast<const float*>(vslot(tpv + ch / AL) + CODE_V + 128)[ch % AL];
       }
     }
   };
