@@ -368,7 +368,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
       }
     }
   };
-  int chunk = c_begin + wave;
+  // At tile 128 a wave takes the two chunks of a tile back to back (partitions
+  // cover whole tiles, c_begin is even), so the query fold and its channel
+  // factors serve both; otherwise wave w takes chunks begin + w, + 4, ...
+  constexpr bool PAIRS = (T == 128);
+  auto next_chunk = [&](int c) { return PAIRS ? (((c - c_begin) & 1) ? c + 2 * kWaves - 1 : c + 1) : c + kWaves; };
+  auto new_tile = [&](int c) { return !PAIRS || ((c - c_begin) & 1) == 0; };
+  int chunk = c_begin + (PAIRS ? 2 * wave : wave);
   if (chunk < c_end) {
     load_alpha(chunk);
     load_k(chunk);
@@ -427,69 +433,73 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     acc[1][h] = 0.f;
   }
 
-  for (; chunk < c_end; chunk += kWaves) {
-    const int next = chunk + kWaves;
+  // query fold, in the QK A layout: lane (bq, iq) holds qt[head 4 hg + iq]
+  // [channels of step BLK st + bq % BLK] as fp16 hi / lo; qsum and the
+  // power-of-two scale per (head, tile)
+  f16x4 qa_hi[HG][SETS], qa_lo[HG][SETS];
+  float cA[HG], cB[HG];
+  // field weights of this lane's steps: elements 0, 1 weigh w0 and 2, 3 w1
+  // (4 bits: 1 and 16; 2 bits: w0 = 16 on odd steps, else 1, and w1 = 4 w0;
+  // a step's parity is bq's)
+  const float w0 = (BK == 4) ? 1.f : ((bq & 1) ? 16.f : 1.f);
+  const float w1 = (BK == 4) ? 16.f : w0 * 4.f;
+
+  for (; chunk < c_end; chunk = next_chunk(chunk)) {
+    const int next = next_chunk(chunk);
     const bool more = next < c_end;   // uniform
 
-    // -------------------------------------------- query fold, in the QK A layout
-    // lane (bq, iq) holds qt[head 4 hg + iq][channels of step BLK st + bq % BLK]
-    // as fp16 hi / lo; qsum and the power-of-two scale per (head, tile)
-    f16x4 qa_hi[HG][SETS], qa_lo[HG][SETS];
-    float cA[HG], cB[HG];
-    // field weights of this lane's steps: elements 0, 1 weigh w0 and 2, 3 w1
-    // (4 bits: 1 and 16; 2 bits: w0 = 16 on odd steps, else 1, and w1 = 4 w0;
-    // a step's parity is bq's)
-    const float w0 = (BK == 4) ? 1.f : ((bq & 1) ? 16.f : 1.f);
-    const float w1 = (BK == 4) ? 16.f : w0 * 4.f;
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      const int hh = 4 * hg + iq;
-      float x[SETS][4];
-      float qmax = 0.f, qsum = 0.f;
-#pragma unroll
-      for (int st = 0; st < SETS; ++st) {
-        const int s = BLK * st + (bq % BLK);
-        const f32x4 hv = *reinterpret_cast<const f32x4*>(&sm.loop.hq[hh][4 * s]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[st][k] = hv[k] * ak[st][k];
-        // the bound is on qt itself: x times the field weight
-        qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(x[st][0]), fabsf(x[st][1])) * w0, fmaxf(fabsf(x[st][2]), fabsf(x[st][3])) * w1));
+    // -------------------------------------------- query fold (once per tile)
+    if (new_tile(chunk)) {
+  #pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        const int hh = 4 * hg + iq;
+        float x[SETS][4];
+        float qmax = 0.f, qsum = 0.f;
+  #pragma unroll
+        for (int st = 0; st < SETS; ++st) {
+          const int s = BLK * st + (bq % BLK);
+          const f32x4 hv = *reinterpret_cast<const f32x4*>(&sm.loop.hq[hh][4 * s]);
+  #pragma unroll
+          for (int k = 0; k < 4; ++k) x[st][k] = hv[k] * ak[st][k];
+          // the bound is on qt itself: x times the field weight
+          qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(x[st][0]), fabsf(x[st][1])) * w0, fmaxf(fabsf(x[st][2]), fabsf(x[st][3])) * w1));
+        }
+        qmax = blocks_max<BLK>(qmax);
+        int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
+        ex = min(max(ex, -100), 100);
+        // scaled qt below 2^11: its hi part is an integer of at most 11 bits
+        const float qscale = __uint_as_float((unsigned)(127 + 10 - ex) << 23);    // 2^(10-ex)
+        const float qunscale = __uint_as_float((unsigned)(127 - 10 + ex) << 23);  // 2^(ex-10)
+        // The offset term takes the sum of the query as the MFMA sees it (hi + lo):
+        // the split's rounding then enters each score as sum_c err_c (S k_c + O),
+        // in proportion to the restored key.  (With the exact sum it would leave
+        // S sum_c err_c k_c against O sum_c qt_c, and in tiles of a few tokens,
+        // where S and O reach 1e4..1e5 and nearly cancel, that costs ~1e-3.)
+        const float g0 = kGrid / w0, g1 = kGrid / w1;
+  #pragma unroll
+        for (int st = 0; st < SETS; ++st) {
+          unsigned h01, l01, h23, l23;
+          split_grid(x[st][0] * qscale, x[st][1] * qscale, g0, g0, h01, l01);
+          split_grid(x[st][2] * qscale, x[st][3] * qscale, g1, g1, h23, l23);
+          qa_hi[hg][st] = as_f16x4(h01, h23);
+          qa_lo[hg][st] = as_f16x4(l01, l23);
+          const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, l01);
+          const f16x2 c = __builtin_bit_cast(f16x2, h23), e = __builtin_bit_cast(f16x2, l23);
+          qsum = __builtin_fmaf((float)a[0], w0, qsum);
+          qsum = __builtin_fmaf((float)b[0], w0, qsum);
+          qsum = __builtin_fmaf((float)a[1], w0, qsum);
+          qsum = __builtin_fmaf((float)b[1], w0, qsum);
+          qsum = __builtin_fmaf((float)c[0], w1, qsum);
+          qsum = __builtin_fmaf((float)e[0], w1, qsum);
+          qsum = __builtin_fmaf((float)c[1], w1, qsum);
+          qsum = __builtin_fmaf((float)e[1], w1, qsum);
+        }
+        qsum = blocks_sum<BLK>(qsum) * qunscale;
+        cA[hg] = c0 * kTwo24 * qunscale;   // score = S D cA + O cB
+        cB[hg] = c0 * qsum;
       }
-      qmax = blocks_max<BLK>(qmax);
-      int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
-      ex = min(max(ex, -100), 100);
-      // scaled qt below 2^11: its hi part is an integer of at most 11 bits
-      const float qscale = __uint_as_float((unsigned)(127 + 10 - ex) << 23);    // 2^(10-ex)
-      const float qunscale = __uint_as_float((unsigned)(127 - 10 + ex) << 23);  // 2^(ex-10)
-      // The offset term takes the sum of the query as the MFMA sees it (hi + lo):
-      // the split's rounding then enters each score as sum_c err_c (S k_c + O),
-      // in proportion to the restored key.  (With the exact sum it would leave
-      // S sum_c err_c k_c against O sum_c qt_c, and in tiles of a few tokens,
-      // where S and O reach 1e4..1e5 and nearly cancel, that costs ~1e-3.)
-      const float g0 = kGrid / w0, g1 = kGrid / w1;
-#pragma unroll
-      for (int st = 0; st < SETS; ++st) {
-        unsigned h01, l01, h23, l23;
-        split_grid(x[st][0] * qscale, x[st][1] * qscale, g0, g0, h01, l01);
-        split_grid(x[st][2] * qscale, x[st][3] * qscale, g1, g1, h23, l23);
-        qa_hi[hg][st] = as_f16x4(h01, h23);
-        qa_lo[hg][st] = as_f16x4(l01, l23);
-        const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, l01);
-        const f16x2 c = __builtin_bit_cast(f16x2, h23), e = __builtin_bit_cast(f16x2, l23);
-        qsum = __builtin_fmaf((float)a[0], w0, qsum);
-        qsum = __builtin_fmaf((float)b[0], w0, qsum);
-        qsum = __builtin_fmaf((float)a[1], w0, qsum);
-        qsum = __builtin_fmaf((float)b[1], w0, qsum);
-        qsum = __builtin_fmaf((float)c[0], w1, qsum);
-        qsum = __builtin_fmaf((float)e[0], w1, qsum);
-        qsum = __builtin_fmaf((float)c[1], w1, qsum);
-        qsum = __builtin_fmaf((float)e[1], w1, qsum);
-      }
-      qsum = blocks_sum<BLK>(qsum) * qunscale;
-      cA[hg] = c0 * kTwo24 * qunscale;   // score = S D cA + O cB
-      cB[hg] = c0 * qsum;
     }
-    if (more) load_alpha(next);
+    if (more && new_tile(next)) load_alpha(next);
 
     // -------------------------------------------- QK: lane = token, 4 heads per group
     f32x4 d[HG], dl[HG];   // hi chain (exact) and lo chain
