@@ -450,16 +450,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
 
     // -------------------------------------------- query fold (once per tile)
     if (new_tile(chunk)) {
-  #pragma unroll
+#pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         const int hh = 4 * hg + iq;
         float x[SETS][4];
         float qmax = 0.f, qsum = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int st = 0; st < SETS; ++st) {
           const int s = BLK * st + (bq % BLK);
           const f32x4 hv = *reinterpret_cast<const f32x4*>(&sm.loop.hq[hh][4 * s]);
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < 4; ++k) x[st][k] = hv[k] * ak[st][k];
           // the bound is on qt itself: x times the field weight
           qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(x[st][0]), fabsf(x[st][1])) * w0, fmaxf(fabsf(x[st][2]), fabsf(x[st][3])) * w1));
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
         // S sum_c err_c k_c against O sum_c qt_c, and in tiles of a few tokens,
         // where S and O reach 1e4..1e5 and nearly cancel, that costs ~1e-3.)
         const float g0 = kGrid / w0, g1 = kGrid / w1;
-  #pragma unroll
+#pragma unroll
         for (int st = 0; st < SETS; ++st) {
           unsigned h01, l01, h23, l23;
           split_grid(x[st][0] * qscale, x[st][1] * qscale, g0, g0, h01, l01);
