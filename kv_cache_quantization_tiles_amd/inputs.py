@@ -168,6 +168,14 @@ def gen_q(wl: Workload, step: int = 0, layer: int = 0) -> np.ndarray:
     return _to_fp16(rng.standard_normal(size=(wl.num_seqs, wl.hq, wl.head_dim)))
 
 
+def hadamard_signs(seed: int) -> np.ndarray:
+    """A seeded 128-bit sign mask for the randomized rotation (4 x uint32; bit
+    c mod 32 of word c // 32 set = channel c negated).  Random numbers the
+    method draws are inputs: the library and the oracle both take this mask."""
+    rng = np.random.default_rng(np.random.SeedSequence([20261202, 77, int(seed)]))
+    return rng.integers(0, 1 << 32, size=4, dtype=np.uint64).astype(np.uint32)
+
+
 def block_table(wl: Workload, capacity_tokens=None, layer: int = 0):
     """Shuffled page table, pages allocated in whole tiles.
 

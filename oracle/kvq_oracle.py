@@ -106,6 +106,20 @@ def fwht(x: np.ndarray) -> np.ndarray:
     return y / math.sqrt(d)
 
 
+def signs_from_mask(mask) -> np.ndarray:
+    """The randomized rotation's diagonal: a 128-bit mask (4 x uint32, bit c
+    mod 32 of word c // 32 set = channel c negated) as a +-1 vector; None or
+    all zero is the plain transform.  The rotation is then H diag(s) and the
+    restore diag(s) H (H symmetric and orthonormal, s^2 = 1)."""
+    if mask is None:
+        return np.ones(HEAD_DIM)
+    words = [int(w) & 0xFFFFFFFF for w in np.asarray(mask).reshape(-1)]
+    if len(words) != HEAD_DIM // 32:
+        raise ValueError("mask must hold 4 32-bit words")
+    bits = np.array([(words[c // 32] >> (c % 32)) & 1 for c in range(HEAD_DIM)], np.float64)
+    return 1.0 - 2.0 * bits
+
+
 # ----------------------------------------------------------------------------
 # Step 3: Sinkhorn-like iterative variance normalization [axbrief §diff, §flag]
 # ----------------------------------------------------------------------------
@@ -171,12 +185,13 @@ class TileQuant:
     beta: np.ndarray      # float64 [n]
 
 
-def quantize_tile(x: np.ndarray, bits: int, iters: int) -> TileQuant:
-    """The four steps on one tile of 1..T tokens: x fp16 [n, d]."""
+def quantize_tile(x: np.ndarray, bits: int, iters: int, signs=None) -> TileQuant:
+    """The four steps on one tile of 1..T tokens: x fp16 [n, d] (signs: the
+    optional sign mask of the randomized rotation, see signs_from_mask)."""
     x = np.asarray(x)
     if x.ndim != 2 or x.shape[0] < 1:
         raise ValueError("tile must be [n>=1, d]")
-    r = fwht(x.astype(np.float64))
+    r = fwht(x.astype(np.float64) * signs_from_mask(signs)[None, :])
     y, alpha, beta = sinkhorn(r, iters)
     codes, step, zero, pre = rtn(y, bits)
     return TileQuant(codes=codes, alpha=alpha.astype(np.float32),
@@ -185,13 +200,13 @@ def quantize_tile(x: np.ndarray, bits: int, iters: int) -> TileQuant:
                      pre=pre, rotated=r, normalized=y, beta=beta)
 
 
-def dequantize_tile(codes, alpha, scale, offset) -> np.ndarray:
+def dequantize_tile(codes, alpha, scale, offset, signs=None) -> np.ndarray:
     """Restore a tile [ttj §quant]: rotated row alpha * (S * code + O), rotated
-    back with the same (self-inverse) Hadamard.  float64 [n, d]."""
+    back with the same (self-inverse) Hadamard, then the signs.  float64 [n, d]."""
     codes = np.asarray(codes, dtype=np.float64)
     rot = np.asarray(alpha, np.float64)[None, :] * (
         np.asarray(scale, np.float64)[:, None] * codes + np.asarray(offset, np.float64)[:, None])
-    return fwht(rot)
+    return fwht(rot) * signs_from_mask(signs)[None, :]
 
 
 # ----------------------------------------------------------------------------
@@ -243,7 +258,7 @@ def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
 # Dense (logical) layout: one token run whose tile 0 starts at token 0
 # ----------------------------------------------------------------------------
 
-def quantize_dense(x: np.ndarray, tile_tokens: int, bits: int, iters: int):
+def quantize_dense(x: np.ndarray, tile_tokens: int, bits: int, iters: int, signs=None):
     """x fp16 [n, H, d] -> dict(codes packed [n, H, d*bits/8], alpha [ntiles, H, d],
     scale [n, H], offset [n, H], pre [n, H, d], codes_raw [n, H, d])."""
     n, heads, d = x.shape
@@ -256,7 +271,7 @@ def quantize_dense(x: np.ndarray, tile_tokens: int, bits: int, iters: int):
     for h in range(heads):
         for j in range(ntiles):
             a, b = j * tile_tokens, min(n, (j + 1) * tile_tokens)
-            tq = quantize_tile(x[a:b, h, :], bits, iters)
+            tq = quantize_tile(x[a:b, h, :], bits, iters, signs)
             codes[a:b, h] = tq.codes
             pre[a:b, h] = tq.pre
             alpha[j, h] = tq.alpha
@@ -266,7 +281,7 @@ def quantize_dense(x: np.ndarray, tile_tokens: int, bits: int, iters: int):
                 offset=offset, pre=pre)
 
 
-def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits: int) -> np.ndarray:
+def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits: int, signs=None) -> np.ndarray:
     """Inverse of quantize_dense from the stored codes and fp32 metadata: float64 [n, H, d]."""
     q = unpack_codes(codes_packed, bits)
     n, heads, d = q.shape
@@ -275,7 +290,7 @@ def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits:
         for a in range(0, n, tile_tokens):
             b = min(n, a + tile_tokens)
             out[a:b, h] = dequantize_tile(q[a:b, h], alpha[a // tile_tokens, h], scale[a:b, h],
-                                          offset[a:b, h])
+                                          offset[a:b, h], signs)
     return out
 
 
@@ -419,7 +434,7 @@ def _store_tile(pool, table_row, head, role, bits, tile_tokens, tile_index, tq: 
 
 
 def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iters,
-                      pool_k, pool_v, staging_k=None, staging_v=None):
+                      pool_k, pool_v, staging_k=None, staging_v=None, signs=None):
     """Quantize every tile of every sequence into the page pools (in place).
 
     k, v: fp16 [total_tokens, Hkv, d]; table: int32 [S, max_blocks].  A tail
@@ -437,7 +452,7 @@ def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iter
                 pre_rows = np.zeros((n, HEAD_DIM))
                 for j in range((n + tile_tokens - 1) // tile_tokens):
                     a, b = j * tile_tokens, min(n, (j + 1) * tile_tokens)
-                    tq = quantize_tile(x[a0 + a:a0 + b, h, :], bits, iters)
+                    tq = quantize_tile(x[a0 + a:a0 + b, h, :], bits, iters, signs)
                     pre_rows[a:b] = tq.pre
                     _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq)
                 pre[(s, h, role)] = pre_rows
@@ -448,7 +463,7 @@ def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iter
 
 
 def append_and_requant(k_new, v_new, lens_before, table, tile_tokens, bits_k, bits_v, iters,
-                       pool_k, pool_v, staging_k, staging_v):
+                       pool_k, pool_v, staging_k, staging_v, signs=None):
     """Append one token per sequence and re-quantize its (partial) tile from the
     fp16 staging rows.  k_new, v_new fp16 [S, Hkv, d].  Returns pre-rounding
     values per (seq, head, role) of the re-quantized tile rows."""
@@ -461,13 +476,13 @@ def append_and_requant(k_new, v_new, lens_before, table, tile_tokens, bits_k, bi
         staging_v[s, r] = v_new[s]
         for role, stg, pool, bits in (("K", staging_k, pool_k, bits_k), ("V", staging_v, pool_v, bits_v)):
             for h in range(heads):
-                tq = quantize_tile(stg[s, :r + 1, h, :], bits, iters)
+                tq = quantize_tile(stg[s, :r + 1, h, :], bits, iters, signs)
                 _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq)
                 pre[(s, h, role)] = tq.pre
     return pre
 
 
-def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens):
+def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens, signs=None):
     """Decode one (sequence, kv head) from the pages with this module's own
     reader: returns (restored tokens float64 [L, d], codes [L, d], alpha per
     tile [ntiles, d], scale [L], offset [L])."""
@@ -490,7 +505,7 @@ def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens):
     out = np.zeros((seq_len, HEAD_DIM))
     for j in range(ntiles):
         a, b = j * tile_tokens, min(seq_len, (j + 1) * tile_tokens)
-        out[a:b] = dequantize_tile(codes[a:b], alpha[j], scale[a:b], offset[a:b])
+        out[a:b] = dequantize_tile(codes[a:b], alpha[j], scale[a:b], offset[a:b], signs)
     return out, codes[:seq_len], alpha, scale[:seq_len], offset[:seq_len]
 
 
@@ -519,7 +534,7 @@ def attention_abs_scale(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_
 
 
 def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
-                      sm_scale=None, return_scale=False):
+                      sm_scale=None, return_scale=False, signs=None):
     """q fp16 [S, Hq, d]; seq_lens count every cached token (the newest included).
     Query head h reads kv head h // (Hq / Hkv).  Returns float64 [S, Hq, d]
     (and, with return_scale, attention_abs_scale per [S, Hq])."""
@@ -531,8 +546,8 @@ def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, b
     scale = np.zeros((s_n, hq))
     for s in range(s_n):
         for kh in range(hkv):
-            kx = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens)[0]
-            vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens)[0]
+            kx = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens, signs)[0]
+            vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens, signs)[0]
             for h in range(kh * g, (kh + 1) * g):
                 out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
                 if return_scale:
@@ -613,7 +628,8 @@ def read_baseline_sequence(pool, table_row, seq_len, head, role, fp8=False, scal
     return out
 
 
-def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bits_v, base_k, base_v):
+def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bits_v, base_k, base_v,
+                        signs=None):
     """The re-materializing read path's first half: every cached token restored
     from the quantized pages (read_sequence, float64) and written, rounded to
     fp16, into fp16 baseline pools with the same block table (in place).  Pages
@@ -624,8 +640,10 @@ def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bi
         n = int(seq_lens[s])
         if n == 0:
             continue
-        kx = np.stack([read_sequence(pool_k, table[s], n, h, "K", bits_k, tile_tokens)[0] for h in range(heads)], 1)
-        vx = np.stack([read_sequence(pool_v, table[s], n, h, "V", bits_v, tile_tokens)[0] for h in range(heads)], 1)
+        kx = np.stack([read_sequence(pool_k, table[s], n, h, "K", bits_k, tile_tokens, signs)[0]
+                       for h in range(heads)], 1)
+        vx = np.stack([read_sequence(pool_v, table[s], n, h, "V", bits_v, tile_tokens, signs)[0]
+                       for h in range(heads)], 1)
         fill_pages_baseline(kx.astype(np.float16), vx.astype(np.float16), np.array([0, n]), table[s:s + 1],
                             base_k, base_v)
 

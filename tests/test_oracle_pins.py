@@ -506,3 +506,60 @@ def test_rematerialized_pages_hold_the_restored_tokens():
     ref = orc.paged_decode_attn(q, table, lens, pk, pv, 32, 4, 2)
     got = orc.paged_decode_attn_baseline(q, table, lens, bk, bv)
     assert np.abs(got - ref).max() < 5e-3 * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- randomized rotation
+
+def test_sign_mask_bits():
+    s = orc.signs_from_mask(np.array([1, 0, 0, 0x80000000], np.uint32))
+    want = np.ones(128)
+    want[0] = want[127] = -1
+    np.testing.assert_array_equal(s, want)
+    np.testing.assert_array_equal(orc.signs_from_mask(None), np.ones(128))
+    np.testing.assert_array_equal(orc.signs_from_mask(np.zeros(4, np.uint32)), np.ones(128))
+    m = inputs.hadamard_signs(3)
+    assert m.dtype == np.uint32 and m.shape == (4,) and 30 < int((orc.signs_from_mask(m) < 0).sum()) < 98
+
+
+def test_signed_rotation_is_scipy_hadamard_times_the_diagonal():
+    """rotated rows = x diag(s) H / sqrt(128) with scipy's Sylvester H, and the
+    transform stays orthonormal (the restore undoes it)."""
+    mask = inputs.hadamard_signs(5)
+    s = orc.signs_from_mask(mask)
+    x = _rng(31).standard_normal((7, 128)).astype(np.float16)
+    tq = orc.quantize_tile(x, 4, 0, mask)
+    want = x.astype(np.float64) @ np.diag(s) @ scipy.linalg.hadamard(128) / math.sqrt(128)
+    np.testing.assert_allclose(tq.rotated, want, rtol=0, atol=1e-12)
+    # zero iterations leave alpha = 1, beta = 1: the restore of the unrounded
+    # rotated rows is x itself, only with the signs
+    back = orc.fwht(tq.rotated) * s[None, :]
+    np.testing.assert_allclose(back, x.astype(np.float64), rtol=0, atol=1e-12)
+    assert np.abs(orc.fwht(tq.rotated) - x.astype(np.float64)).max() > 0.1   # the signs matter
+
+
+def test_signed_round_trip_within_rounding_bound_and_attention():
+    import dataclasses
+    wl = dataclasses.replace(inputs.workload(2), seq_lens=(150, 37), hkv=2, hq=8, tile_tokens=64)
+    k = inputs.gen_kv(wl, "K")
+    mask = inputs.hadamard_signs(11)
+    d = orc.quantize_dense(k, 64, 4, 3, mask)
+    deq = orc.dequantize_dense(d["codes"], d["alpha"], d["scale"], d["offset"], 64, 4, mask)
+    # per token: |x - restore| <= (S/2) |alpha| (orthonormal rotation, |rounding| <= 1/2 step)
+    err = np.linalg.norm(deq - k.astype(np.float64), axis=-1)
+    bound = d["scale"] / 2 * np.linalg.norm(d["alpha"], axis=-1)[np.arange(k.shape[0]) // 64]
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-9)
+    # paged: the direct read with signs is brute-force attention over the signed restore
+    v = inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    pk, pv = orc.new_pool(npages, 2, 4, 64), orc.new_pool(npages, 2, 4, 64)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, 64, 4, 4, 3, pk, pv, signs=mask)
+    q = inputs.gen_q(wl)
+    out = orc.paged_decode_attn(q, table, np.array(wl.seq_lens), pk, pv, 64, 4, 4, signs=mask)
+    cu = wl.cu_seqlens()
+    dk = orc.quantize_dense(k[cu[1]:cu[2]], 64, 4, 3, mask)
+    dv = orc.quantize_dense(v[cu[1]:cu[2]], 64, 4, 3, mask)
+    kx = orc.dequantize_dense(dk["codes"], dk["alpha"], dk["scale"], dk["offset"], 64, 4, mask)
+    vx = orc.dequantize_dense(dv["codes"], dv["alpha"], dv["scale"], dv["offset"], 64, 4, mask)
+    for h in range(4, 8):
+        np.testing.assert_allclose(out[1, h], orc.attention(q[1, h], kx[:, 1], vx[:, 1], 1 / math.sqrt(128)),
+                                   rtol=1e-12, atol=1e-12)
