@@ -357,8 +357,17 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * nb * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # the randomized rotation (a seeded +-1 diagonal before H): same kernels, signs on
+    cfg_s = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, hadamard_signs=inputs.hadamard_signs(1))
+    caches_s = [api.PagedCache(cfg_s, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
+    qs_batch = batch_ms(lambda j: caches_s[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
+    ds_batch = batch_ms(lambda j: caches_s[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
+    torch.cuda.synchronize()
     q_kernel_ms = q_batch[0].elapsed_time(q_batch[1]) / q_batch[2]
     td_cold = d_batch[0].elapsed_time(d_batch[1]) / d_batch[2]
+    qs_ms = qs_batch[0].elapsed_time(qs_batch[1]) / qs_batch[2]
+    ds_ms = ds_batch[0].elapsed_time(ds_batch[1]) / ds_batch[2]
+    del caches_s
     ta = [e[0].elapsed_time(e[1]) for e in sp_ev]
     td = [e[1].elapsed_time(e[2]) for e in sp_ev]
 
@@ -395,6 +404,8 @@ def main():
         "decode_tok_per_s": round(wl.num_seqs / (ad_ms * 1e-3), 1),
         "decode_attn_only_tok_per_s": round(wl.num_seqs / (td_cold * 1e-3), 1),
         "copy_probe_GBps": round(copy_gbps, 1),
+        "randomized_rotation": {"quantize_kernel_ms": round(qs_ms, 4), "decode_attn_ms": round(ds_ms, 4),
+                                "quantize_GBps": round(qbytes / (qs_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "alu", "kernel": "quantize_paged_kernel",
                      "achieved": round(q_tops, 3), "peak": round(VALU_PEAK_TOPS, 3), "unit": "Tlane-op/s",
                      "frac": round(q_tops / VALU_PEAK_TOPS, 4),

@@ -20,8 +20,11 @@
  * backend).
  *
  * What the pages leave open is fixed here as follows (every function uses it):
- *   - Hadamard: orthonormal Sylvester order, no random signs, on every token
- *     row of K and of V (head_dim 128).
+ *   - Hadamard: orthonormal Sylvester order, on every token row of K and of V
+ *     (head_dim 128); with cfg->hadamard_signs non-zero the rotation is
+ *     H * diag(s) (a seeded +-1 diagonal first, the common randomized variant;
+ *     the pages do not say whether signs are used) and the restore diag(s) * H.
+ *     Every call on the same pages must pass the same signs.
  *   - One normalization iteration = channel step (each channel divided by its
  *     population std over the tile's valid tokens) then token step (each token
  *     divided by its population std over the 128 channels).  A channel/token
@@ -81,6 +84,9 @@ typedef struct {
   int32_t bits_k;         /* code width of K: 2 or 4 */
   int32_t bits_v;         /* code width of V: 2 or 4 */
   int32_t sinkhorn_iters; /* normalization iterations, 0..16 */
+  uint32_t hadamard_signs[4]; /* randomized rotation: bit c mod 32 of word c/32
+                                 set = channel c negated before the Hadamard
+                                 (and after the inverse); all 0 = plain H */
 } kvq_config;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */

@@ -85,6 +85,12 @@ int chunks_per_partition(int num_seqs, int kv_heads, int max_seq_len, int tile) 
   return cpp;
 }
 
+// The randomized rotation's sign mask travels with every launch on quantized pages.
+template <class Args>
+void set_signs(Args& a, const kvq_config* cfg) {
+  for (int i = 0; i < 4; ++i) a.signs[i] = cfg->hadamard_signs[i];
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,6 +126,7 @@ kvq_status kvq_quantize_tiles(const kvq_config* cfg, const kvq_half* x, int32_t 
   a.n_tokens = n_tokens;
   a.heads = heads;
   a.iters = cfg->sinkhorn_iters;
+  set_signs(a, cfg);
   return launched(kvq::launch_quantize_dense(a, cfg->tile_tokens, bits, (hipStream_t)stream),
                   "kvq_quantize_tiles");
 }
@@ -136,6 +143,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const uint8_t* codes, const flo
   KVQ_NONNULL(out);
   if (n_tokens <= 0 || heads <= 0) return fail(KVQ_ERR_ARG, "n_tokens %d and heads %d must be > 0", n_tokens, heads);
   kvq::DequantArgs a{codes, alpha, tok_scale, tok_offset, n_tokens, heads, out};
+  set_signs(a, cfg);
   return launched(kvq::launch_dequantize(a, cfg->tile_tokens, bits, (hipStream_t)stream), "kvq_dequantize");
 }
 
@@ -174,6 +182,7 @@ kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const
   a.max_blocks = max_blocks;
   a.kv_heads = kv_heads;
   a.iters = cfg->sinkhorn_iters;
+  set_signs(a, cfg);
   return launched(kvq::launch_quantize_paged(a, tile, cfg->bits_k, cfg->bits_v, num_seqs, max_seq_len,
                                              (hipStream_t)stream),
                   "kvq_quantize_to_pages");
@@ -210,6 +219,7 @@ kvq_status kvq_append_and_requant(const kvq_config* cfg, const kvq_half* k_new,
   a.max_blocks = max_blocks;
   a.kv_heads = kv_heads;
   a.iters = cfg->sinkhorn_iters;
+  set_signs(a, cfg);
   return launched(kvq::launch_append(a, cfg->tile_tokens, cfg->bits_k, cfg->bits_v, num_seqs,
                                      (hipStream_t)stream),
                   "kvq_append_and_requant");
@@ -277,6 +287,7 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.unit_tokens = 64;
   a.out_scale = 1.0f;
+  set_signs(a, cfg);
   return launched(kvq::launch_decode(a, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
                   "kvq_paged_decode_attn");
 }
@@ -350,6 +361,8 @@ kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, c
   qa.max_blocks = max_blocks;
   qa.kv_heads = kv_heads;
   qa.iters = cfg->sinkhorn_iters;
+  set_signs(a, cfg);
+  set_signs(qa, cfg);
   return launched(kvq::launch_append_decode(a, qa, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
                   "kvq_append_and_decode");
 }
@@ -406,6 +419,7 @@ kvq_status kvq_rematerialize_fp16_pages(const kvq_config* cfg, const void* pool_
     return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold whole tiles of %d tokens", max_blocks, max_seq_len);
   kvq::RematArgs a{(const uint8_t*)pool_k, (const uint8_t*)pool_v, block_table, max_blocks, seq_lens, kv_heads,
                    base_k, base_v};
+  set_signs(a, cfg);
   return launched(kvq::launch_rematerialize(a, T, cfg->bits_k, cfg->bits_v, num_seqs, max_seq_len,
                                             (hipStream_t)stream),
                   "kvq_rematerialize_fp16_pages");

@@ -391,7 +391,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     const uint16_t* qrow = A.q + ((size_t)seq * A.q_heads + kvh * G + (real ? n16 : 0)) * kHeadDim + 32 * grp;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const u32x4 w = real ? *reinterpret_cast<const u32x4*>(qrow + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 w = real ? *reinterpret_cast<const u32x4*>(qrow + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+      // randomized rotation: q's channels take the signs before H (keys are H s k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] ^= sign_pair_mask(A.signs, 32 * grp + 8 * v, i);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         hq[8 * v + 2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFF));
@@ -796,8 +799,11 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
   stage(y0, lane_xor<8>(y0), 8);   stage(y1, lane_xor<8>(y1), 8);
   stage(y0, lane_xor<16>(y0), 16); stage(y1, lane_xor<16>(y1), 16);
   stage(y0, xor32(y0), 32);        stage(y1, xor32(y1), 32);
-  o[lane] = y0 * inv;
-  o[lane + 64] = y1 * inv;
+  // randomized rotation: the restore ends with the sign of each channel
+  const float s0 = ((A.signs[lane >> 5] >> (lane & 31)) & 1u) ? -inv : inv;
+  const float s1 = ((A.signs[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -inv : inv;
+  o[lane] = y0 * s0;
+  o[lane + 64] = y1 * s1;
 }
 
 template <typename F>

@@ -40,6 +40,7 @@ struct QuantArgs {
   int max_blocks;
   int kv_heads;
   int iters;
+  uint32_t signs[4];          // randomized rotation (bit c = channel c negated); all 0 = plain
 };
 
 struct DequantArgs {
@@ -50,6 +51,7 @@ struct DequantArgs {
   int n_tokens;
   int heads;
   uint16_t* out;
+  uint32_t signs[4];
 };
 
 struct DecodeArgs {
@@ -73,6 +75,7 @@ struct DecodeArgs {
   int unit_tokens;            // tokens per partition unit (tile, or 64 for the baselines)
   float out_scale;            // output multiplier (the V scale for fp8 pages, else 1)
   int seq_lens_plus_one;      // 1: seq_lens are the lengths before an appended token
+  uint32_t signs[4];          // randomized rotation of the quantized pages (0 for the baselines)
 };
 
 struct BaseFillArgs {
@@ -97,6 +100,7 @@ struct RematArgs {
   int kv_heads;
   uint16_t* base_k;           // fp16 pools: K [pages][Hkv][16][D], V [pages][Hkv][D][16]
   uint16_t* base_v;
+  uint32_t signs[4];
 };
 
 hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s);
@@ -116,6 +120,17 @@ hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, i
 hipError_t launch_decode_baseline(const DecodeArgs& a, bool fp8, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
+
+// Sign flips of the randomized rotation: the 8 sign bits of channels c0..c0+7
+// (c0 a multiple of 8) spread to the fp16 sign bits of 4 words of fp16 pairs
+// (channel c0 + 2w in the low half of word w, c0 + 2w + 1 in the high half).
+__device__ __forceinline__ unsigned sign_pair_mask(const uint32_t* signs, int c0, int w) {
+  const unsigned b = (signs[c0 >> 5] >> (c0 & 31)) & 0xFFu;
+  return ((b << (15 - 2 * w)) & 0x8000u) | ((b << (30 - 2 * w)) & 0x80000000u);
+}
+__device__ __forceinline__ bool any_sign(const uint32_t* signs) {
+  return (signs[0] | signs[1] | signs[2] | signs[3]) != 0u;
+}
 
 // Value of lane (lane ^ M) for M in {1, 2, 4, 8, 16} (ds_swizzle bit mode,
 // within each group of 32 lanes).

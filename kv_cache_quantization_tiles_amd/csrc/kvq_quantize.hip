@@ -128,6 +128,15 @@ __global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
   for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s2, lane_xor<2>(x[k]));
 #pragma unroll
   for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s4, lane_xor<4>(x[k]));
+  if (any_sign(A.signs)) {   // randomized rotation: the restore ends with the signs
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c0 = 64 * half + 8 * cg;
+      const unsigned b = (A.signs[c0 >> 5] >> (c0 & 31)) & 0xFFu;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[8 * half + j] = ((b >> j) & 1u) ? -x[8 * half + j] : x[8 * half + j];
+    }
+  }
   if (!valid) return;
   uint16_t* orow = A.out + rr * kHeadDim;
 #pragma unroll
@@ -245,6 +254,15 @@ __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj
   for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s2, lane_xor<2>(x[k]));
 #pragma unroll
   for (int k = 0; k < 16; ++k) x[k] = __builtin_fmaf(x[k], s4, lane_xor<4>(x[k]));
+  if (any_sign(A.signs)) {   // randomized rotation: the restore ends with the signs
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c0 = 64 * half + 8 * cg;
+      const unsigned b = (A.signs[c0 >> 5] >> (c0 & 31)) & 0xFFu;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[8 * half + j] = ((b >> j) & 1u) ? -x[8 * half + j] : x[8 * half + j];
+    }
+  }
   uint16_t hv[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) hv[k] = (t < n) ? float_to_half_bits(x[k] * kInvSqrtD) : (uint16_t)0;

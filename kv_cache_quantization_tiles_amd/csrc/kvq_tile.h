@@ -142,6 +142,17 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     }
   }
 
+  // randomized rotation: channel c negated first (the fp16 sign bits of the
+  // MFMA operand; the staged rows above stay as given)
+  if (any_sign(A.signs)) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[bb][p][i] ^= sign_pair_mask(A.signs, 32 * p + 8 * g, i);
+  }
+
   // ---------------------------------------------------------------- Hadamard (unnormalized)
   // B+ = [H16; H16], B- = [H16; -H16] in the MFMA B layout: lane (g, j) holds
   // rows 8g..8g+7 of column j, H16[k][j] = (-1)^popcount(k & j).

@@ -94,11 +94,11 @@ PAGED_CASES = [
 ]
 
 
-def _gpu_prefill(wl, shuffled=True):
+def _gpu_prefill(wl, shuffled=True, signs=None):
     k = inputs.gen_kv(wl, "K")
     v = inputs.gen_kv(wl, "V")
     table, npages = (inputs.block_table if shuffled else inputs.identity_block_table)(wl)
-    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, hadamard_signs=signs)
     cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
     cu = torch.from_numpy(wl.cu_seqlens()).cuda()
     cache.quantize_prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), cu, max(wl.seq_lens))
@@ -522,3 +522,87 @@ def test_append_and_decode_fused_matches_two_calls(case):
             err = pu.assert_attn(of.cpu().numpy(), ref, f"fused {case} step {step}", sc)
             print(f"[attn] fused {case} step {step}: max abs err {err:.2e} (largest output scale {sc.max():.3g})",
                   flush=True)
+
+
+# ---------------------------------------------------------------- randomized rotation (H diag(s))
+
+SIGNED_CASES = [
+    # (recipe, lens, hkv, hq, tile, bits_k, bits_v, iters, mask seed)
+    (2, (200, 131, 64, 17), 2, 8, 64, 4, 4, 3, 1),
+    (5, (300, 97, 33), 2, 16, 32, 4, 2, 5, 2),
+    (2, (260, 128, 1000), 1, 4, 128, 2, 2, 3, 3),
+]
+
+
+@pytest.mark.parametrize("case", SIGNED_CASES)
+def test_randomized_rotation_paged_decode_fused_and_restore(case):
+    """With a random sign mask: pages match the oracle's (codes within the
+    window), the decode matches the oracle's attention with the same signs,
+    the fused step equals the two calls bit for bit and matches the oracle,
+    and the fp16 re-materialization matches the oracle's restore."""
+    recipe, lens, hkv, hq, tile, bk, bv, iters, seed = case
+    mask = inputs.hadamard_signs(seed)
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    k, v, table, npages, cache = _gpu_prefill(wl, signs=mask)
+    ref_pk, ref_pv = orc.new_pool(npages, hkv, bk, tile), orc.new_pool(npages, hkv, bv, tile)
+    pre = orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, tile, bk, bv, iters, ref_pk, ref_pv, signs=mask)
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    _compare_pools(wl, table, wl.seq_lens, gpk, gpv, ref_pk, ref_pv, pre, f"signed prefill {case}")
+    lens_np = np.array(wl.seq_lens, np.int32)
+    q = inputs.gen_q(wl)
+    out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(lens_np).cuda(), max(lens))
+    torch.cuda.synchronize()
+    ref, sc = orc.paged_decode_attn(q, table, lens_np, gpk, gpv, tile, bk, bv, return_scale=True, signs=mask)
+    pu.assert_attn(out.cpu().numpy(), ref, f"signed decode {case}", sc)
+    # the mask is in effect: restoring the same pages without it gives other outputs
+    plain = orc.paged_decode_attn(q, table, lens_np, gpk, gpv, tile, bk, bv)
+    assert np.abs(plain - ref).max() > 1e-2
+    # one fused append + decode step against the two calls
+    _, _, _, _, split = _gpu_prefill(wl, signs=mask)
+    lens_t = torch.from_numpy(lens_np).cuda()
+    kn = torch.from_numpy(inputs.gen_decode_kv(wl, "K", 0)).cuda()
+    vn = torch.from_numpy(inputs.gen_decode_kv(wl, "V", 0)).cuda()
+    q1 = torch.from_numpy(inputs.gen_q(wl, 1)).cuda()
+    max_len = max(lens) + 1
+    of = cache.append_decode(kn, vn, lens_t, q1, max_len)
+    split.append(kn, vn, lens_t)
+    os_ = split.decode(q1, lens_t + 1, max_len)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.pool_k, split.pool_k) and torch.equal(cache.pool_v, split.pool_v)
+    assert torch.equal(of, os_)
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    ref1, sc1 = orc.paged_decode_attn(q1.cpu().numpy(), table, lens_np + 1, gpk, gpv, tile, bk, bv,
+                                      return_scale=True, signs=mask)
+    pu.assert_attn(of.cpu().numpy(), ref1, f"signed fused {case}", sc1)
+    # fp16 re-materialization with the signs
+    base = api.BaselineCache(npages, hkv, torch.from_numpy(table), wl.num_seqs)
+    cache.rematerialize_into(base, lens_t + 1, max_len)
+    torch.cuda.synchronize()
+    ref_k = np.zeros((npages, hkv, 16 * 128), np.float16)
+    ref_v = np.zeros_like(ref_k)
+    orc.rematerialize_pages(gpk, gpv, table, lens_np + 1, tile, bk, bv, ref_k, ref_v, signs=mask)
+    bk_got, bv_got = base.pool_k.cpu().numpy(), base.pool_v.cpu().numpy()
+    for s in range(wl.num_seqs):
+        for h in range(hkv):
+            for role, got_pool, ref_pool in (("K", bk_got, ref_k), ("V", bv_got, ref_v)):
+                pu.assert_dequant(orc.read_baseline_sequence(got_pool, table[s], int(lens_np[s]) + 1, h, role),
+                                  orc.read_baseline_sequence(ref_pool, table[s], int(lens_np[s]) + 1, h, role),
+                                  f"signed remat {case} s{s} h{h} {role}")
+
+
+@pytest.mark.parametrize("tile,bits", [(64, 4), (32, 2), (128, 4)])
+def test_randomized_rotation_dense(tile, bits):
+    mask = inputs.hadamard_signs(7 + tile)
+    x = _x(300, 3, 2)
+    cfg = api.config(tile, bits, bits, 3, hadamard_signs=mask)
+    q = api.quantize_tiles(torch.from_numpy(x).cuda(), cfg, bits)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in q.items()}
+    ref = orc.quantize_dense(x, tile, bits, 3, mask)
+    _report(f"signed dense T{tile} b{bits}",
+            pu.compare_codes(orc.unpack_codes(got["codes"], bits), ref["codes_raw"], ref["pre"], "signed dense"))
+    pu.assert_rel(got["alpha"], ref["alpha"], pu.META_RTOL, "alpha")
+    pu.assert_rel(got["scale"], ref["scale"], pu.META_RTOL, "scale")
+    deq = api.dequantize(q, cfg, bits).cpu().numpy().astype(np.float64)
+    ref_deq = orc.dequantize_dense(got["codes"], got["alpha"], got["scale"], got["offset"], tile, bits, mask)
+    pu.assert_dequant(deq, ref_deq, "signed dequantize")
