@@ -101,6 +101,7 @@ def append_bytes(wl, lens_before) -> float:
 # ----------------------------------------------------------------------------- CPU oracle leg
 def _oracle_quantize_unit(args):
     import oracle as orc
+    from oracle import kvq_oracle as orc_impl
     wl, s, h, role = args
     x = inputs.gen_kv(wl, role, seqs=[s])[:, h:h + 1]
     n = x.shape[0]
@@ -108,12 +109,11 @@ def _oracle_quantize_unit(args):
     bits = wl.bits_k if role == "K" else wl.bits_v
     pool = orc.new_pool(table.shape[1], 1, bits, wl.tile_tokens)
     t0 = time.perf_counter()
-    if role == "K":
-        orc.quantize_to_pages(x, x, np.array([0, n], np.int32), table, wl.tile_tokens, bits, bits, wl.iters,
-                              pool, orc.new_pool(table.shape[1], 1, bits, wl.tile_tokens))
-    else:
-        orc.quantize_to_pages(x, x, np.array([0, n], np.int32), table, wl.tile_tokens, bits, bits, wl.iters,
-                              orc.new_pool(table.shape[1], 1, bits, wl.tile_tokens), pool)
+    # this unit's role only: every tile through the oracle's quantizer into its pages
+    t = wl.tile_tokens
+    for j in range((n + t - 1) // t):
+        tq = orc.quantize_tile(x[j * t:min(n, (j + 1) * t), 0, :], bits, wl.iters)
+        orc_impl._store_tile(pool, table[0], 0, role, bits, t, j, tq)
     return (s, h, role), pool, time.perf_counter() - t0
 
 
@@ -148,14 +148,21 @@ def cpu_baseline(wl, max_seqs: int):
         t1 = time.perf_counter()
         pool.map(_oracle_decode_unit, dunits, chunksize=1)
         td = time.perf_counter() - t1
+    # one unit (sequence 0, kv head 0, K) on one core, in this process
+    t2 = time.perf_counter()
+    _oracle_quantize_unit(units[0])
+    t_unit = time.perf_counter() - t2
     ntok_heads = sum(wl.seq_lens[s] for s in seqs) * wl.hkv
     qb = quantize_bytes(ntok_heads, wl.bits_k, wl.tile_tokens) + quantize_bytes(ntok_heads, wl.bits_v, wl.tile_tokens)
     db = decode_bytes(wl, [wl.seq_lens[s] for s in seqs])
+    unit_bytes = quantize_bytes(wl.seq_lens[0], wl.bits_k, wl.tile_tokens)
     return {"value": round((qb + db) / (tq + td) / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(seqs)} of {wl.num_seqs} sequences x {wl.seq_lens[0]} tokens, all {wl.hkv} kv heads: "
                       f"quantize K and V to pages, then one decode step (fp64 NumPy oracle, "
                       f"{cores} worker processes)",
             "quantize_s": round(tq, 3), "decode_s": round(td, 3),
+            "single_core_quantize_GBps": round(unit_bytes / t_unit / 1e9, 6),
+            "single_core_unit": f"quantize one (sequence, kv head) of K, {wl.seq_lens[0]} tokens: {t_unit:.3f} s",
             "machine_cores": os.cpu_count()}
 
 
