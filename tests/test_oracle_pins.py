@@ -274,6 +274,11 @@ def test_k_slot_positions_hand_examples():
         want = np.zeros_like(raw)
         want[ex["byte"]] = 0x3 << ex["shift"]
         np.testing.assert_array_equal(raw, want)
+    for ex in g["k_slot_8bit"]:
+        raw = orc.k_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0xAB), 8)
+        want = np.zeros_like(raw)
+        want[ex["byte"]] = 0xAB
+        np.testing.assert_array_equal(raw, want)
 
 
 def test_v_slot_positions_hand_examples():
@@ -287,6 +292,11 @@ def test_v_slot_positions_hand_examples():
         raw = orc.v_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0x3), 2)
         want = np.zeros_like(raw)
         want[ex["byte"]] = 0x3 << ex["shift"]
+        np.testing.assert_array_equal(raw, want)
+    for ex in g["v_slot_8bit"]:
+        raw = orc.v_codes_to_bytes(_one_hot_page(ex["token"], ex["channel"], 0xAB), 8)
+        want = np.zeros_like(raw)
+        want[ex["byte"]] = 0xAB
         np.testing.assert_array_equal(raw, want)
 
 
@@ -308,6 +318,7 @@ def test_slot_sizes(tile):
     assert orc.slot_bytes(4, 64) == 1280
     assert orc.slot_bytes(4, tile) == 1024 + 128 + 4 * (16 * 128 // tile)
     assert orc.slot_bytes(2, tile) == 512 + 128 + 4 * (16 * 128 // tile)
+    assert orc.slot_bytes(8, tile) == 2048 + 128 + 4 * (16 * 128 // tile)
 
 
 def test_pages_hold_the_same_values_as_dense_layout():
@@ -563,3 +574,14 @@ def test_signed_round_trip_within_rounding_bound_and_attention():
     for h in range(4, 8):
         np.testing.assert_allclose(out[1, h], orc.attention(q[1, h], kx[:, 1], vx[:, 1], 1 / math.sqrt(128)),
                                    rtol=1e-12, atol=1e-12)
+
+
+def test_eight_bit_tiles_round_trip_within_the_rounding_bound():
+    """8-bit codes (255 levels): every restored token within half a step of the
+    rotated row per element, through the orthonormal rotation."""
+    x = _rng(41).standard_normal((64, 128)).astype(np.float16) * np.float16(3)
+    tq = orc.quantize_tile(x, 8, 3)
+    assert tq.codes.max() == 255 and tq.codes.min() == 0
+    rec = orc.dequantize_tile(tq.codes, tq.alpha, tq.scale, tq.offset)
+    err = np.linalg.norm(rec - x.astype(np.float64), axis=1)
+    assert np.all(err <= tq.scale / 2 * np.linalg.norm(tq.alpha) * (1 + 1e-9) + 1e-9)
