@@ -16,6 +16,7 @@ append + decode) over the step time, in GB/s.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import multiprocessing as mp
@@ -170,7 +171,7 @@ def cpu_baseline(wl, max_seqs: int):
 def long_context_leg(n_iter: int = 10):
     """One layer of the 36-layer, 6 x 128K Qwen3-4B-shaped workload (8 kv /
     32 query heads, tile 128): the decode-attention step on fp16 pages, fp8
-    (E4M3, per-tensor scale) pages, and 4-bit and 2-bit quantized pages, all
+    (E4M3, per-tensor scale) pages, and 4-, 2- and 8-bit quantized pages, all
     filled from the same inputs, and the 4-bit pages read the other way:
     restored to fp16 pages first, then the fp16 decode (kvq4_rematerialize).
     Attention only (no append), context 131072,
@@ -203,7 +204,7 @@ def long_context_leg(n_iter: int = 10):
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     modes = {}
-    for name in ("fp16", "fp8", "kvq4", "kvq2"):
+    for name in ("fp16", "fp8", "kvq4", "kvq2", "kvq8"):
         if name in ("fp16", "fp8"):
             fp8 = name == "fp8"
             ks = float(k.abs().max()) / 448.0 if fp8 else 1.0
@@ -213,7 +214,7 @@ def long_context_leg(n_iter: int = 10):
             per_token_head = 2 * 128 * (1 if fp8 else 2)
             fill_bytes = token_heads * (2 * 2 * D + per_token_head)
         else:
-            bits = 4 if name == "kvq4" else 2
+            bits = int(name[3:])
             cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
             cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
             fill_ms = timed(lambda: cache.quantize_prefill(k, v, cu, max_len), 3)
@@ -370,17 +371,28 @@ def main():
     qs_batch = batch_ms(lambda j: caches_s[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
     ds_batch = batch_ms(lambda j: caches_s[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
     torch.cuda.synchronize()
+    del caches_s
+    # 8-bit codes for K and V: same kernels at the wider width
+    cfg_8 = api.config(wl.tile_tokens, 8, 8, wl.iters)
+    caches_8 = [api.PagedCache(cfg_8, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
+    q8_batch = batch_ms(lambda j: caches_8[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
+    d8_batch = batch_ms(lambda j: caches_8[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
+    torch.cuda.synchronize()
+    q8_ms = q8_batch[0].elapsed_time(q8_batch[1]) / q8_batch[2]
+    d8_ms = d8_batch[0].elapsed_time(d8_batch[1]) / d8_batch[2]
+    del caches_8
     q_kernel_ms = q_batch[0].elapsed_time(q_batch[1]) / q_batch[2]
     td_cold = d_batch[0].elapsed_time(d_batch[1]) / d_batch[2]
     qs_ms = qs_batch[0].elapsed_time(qs_batch[1]) / qs_batch[2]
     ds_ms = ds_batch[0].elapsed_time(ds_batch[1]) / ds_batch[2]
-    del caches_s
     ta = [e[0].elapsed_time(e[1]) for e in sp_ev]
     td = [e[1].elapsed_time(e[2]) for e in sp_ev]
 
     ntok_heads = wl.total_tokens * wl.hkv
     qbytes = quantize_bytes(ntok_heads, wl.bits_k, wl.tile_tokens) + quantize_bytes(ntok_heads, wl.bits_v, wl.tile_tokens)
     abytes = append_bytes(wl, wl.seq_lens)
+    q8_bytes = 2 * quantize_bytes(ntok_heads, 8, wl.tile_tokens)
+    d8_bytes = decode_bytes(dataclasses.replace(wl, bits_k=8, bits_v=8), [l + 1 for l in wl.seq_lens])
     dbytes = decode_bytes(wl, [l + 1 for l in wl.seq_lens])
     q_ms, ad_ms = float(np.mean(tq)), float(np.mean(tad))
     a_ms, d_ms = float(np.mean(ta)), float(np.mean(td))
@@ -413,6 +425,9 @@ def main():
         "copy_probe_GBps": round(copy_gbps, 1),
         "randomized_rotation": {"quantize_kernel_ms": round(qs_ms, 4), "decode_attn_ms": round(ds_ms, 4),
                                 "quantize_GBps": round(qbytes / (qs_ms * 1e-3) / 1e9, 1)},
+        "codes_8bit": {"quantize_kernel_ms": round(q8_ms, 4), "decode_attn_ms": round(d8_ms, 4),
+                       "quantize_GBps": round(q8_bytes / (q8_ms * 1e-3) / 1e9, 1),
+                       "decode_attn_GBps": round(d8_bytes / (d8_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "alu", "kernel": "quantize_paged_kernel",
                      "achieved": round(q_tops, 3), "peak": round(VALU_PEAK_TOPS, 3), "unit": "Tlane-op/s",
                      "frac": round(q_tops / VALU_PEAK_TOPS, 4),

@@ -38,6 +38,9 @@
  *     token = Hadamard(rotated row).
  *   - Tiles start at token 0 of each sequence; the last may be partial and
  *     its statistics use only its valid rows.
+ *   - Code widths: 4 and 2 bits, and 8 bits (the integer widths the ttj.kr
+ *     page names in its section "양자화로 캐시를 다이어트시킨다" are 8 and 4);
+ *     K and V may mix 2 and 4, while 8 is used for both or neither.
  *
  * Conventions for every function:
  *   - Pointers to data are DEVICE pointers (hipMalloc'd or torch CUDA
@@ -72,7 +75,8 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_ARG = -1,         /* null pointer, non-positive size, inconsistent shapes */
   KVQ_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 16, tile not 32/64/128,
-                               bits not 2/4, iters outside 0..16, GQA group > 16 */
+                               bits not 2/4/8 (or 8 on one of K/V only),
+                               iters outside 0..16, GQA group > 16 */
   KVQ_ERR_HIP = -3,         /* a kernel launch failed */
   KVQ_ERR_WORKSPACE = -4    /* workspace smaller than kvq_decode_workspace_bytes() */
 } kvq_status;
@@ -81,8 +85,8 @@ typedef struct {
   int32_t head_dim;       /* must be 128 */
   int32_t page_tokens;    /* must be 16 */
   int32_t tile_tokens;    /* 32, 64 or 128 (a multiple of page_tokens) */
-  int32_t bits_k;         /* code width of K: 2 or 4 */
-  int32_t bits_v;         /* code width of V: 2 or 4 */
+  int32_t bits_k;         /* code width of K: 2 or 4, or 8 with bits_v = 8 */
+  int32_t bits_v;         /* code width of V: 2 or 4, or 8 with bits_k = 8 */
   int32_t sinkhorn_iters; /* normalization iterations, 0..16 */
   uint32_t hadamard_signs[4]; /* randomized rotation: bit c mod 32 of word c/32
                                  set = channel c negated before the Hadamard
@@ -105,7 +109,7 @@ const char* kvq_version(void);
  *           of the tile's channel factors, j = the page's index in its tile.
  * Unit order of a token's 128 codes (dense codes and K slots): 16 units of
  *   8 fields, a unit being 8*bits bits (a little-endian 32-bit word at 4
- *   bits, a 16-bit half at 2 bits), unit u at bit 8*bits*u of the token's
+ *   bits, a 16-bit half at 2 bits, a little-endian 64-bit pair of words at 8), unit u at bit 8*bits*u of the token's
  *   codes; field m (bits [bits*m, bits*(m+1)) of the unit) holds channel
  *   u + 16*m.
  * K-slot codes: each token's units cut into 4 blocks of 4 units (4*bits
@@ -130,7 +134,7 @@ size_t kvq_slot_bytes(const kvq_config* cfg, int32_t is_v);
  * kvq_quantize_tiles - quantize one token run per head in the dense layout.
  *   x          fp16 [n_tokens][heads][128]; tile j of each head covers tokens
  *              j*T .. min(n_tokens, (j+1)*T)-1.
- *   bits       2 or 4 (cfg->bits_k/bits_v are ignored here).
+ *   bits       2, 4 or 8 (cfg->bits_k/bits_v are ignored here).
  *   codes      uint8 [n_tokens][heads][128*bits/8], each token's codes in
  *              unit order (see the page-pool layout below).
  *   alpha      float32 [ceil(n_tokens/T)][heads][128] channel factors.

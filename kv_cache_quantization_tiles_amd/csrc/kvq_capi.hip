@@ -30,16 +30,20 @@ kvq_status check_config(const kvq_config* cfg, bool need_paged_bits) {
   if (cfg->sinkhorn_iters < 0 || cfg->sinkhorn_iters > 16)
     return fail(KVQ_ERR_UNSUPPORTED, "sinkhorn_iters %d outside 0..16", cfg->sinkhorn_iters);
   if (need_paged_bits) {
-    if (cfg->bits_k != 2 && cfg->bits_k != 4)
-      return fail(KVQ_ERR_UNSUPPORTED, "bits_k %d unsupported (2 or 4)", cfg->bits_k);
-    if (cfg->bits_v != 2 && cfg->bits_v != 4)
-      return fail(KVQ_ERR_UNSUPPORTED, "bits_v %d unsupported (2 or 4)", cfg->bits_v);
+    if (cfg->bits_k != 2 && cfg->bits_k != 4 && cfg->bits_k != 8)
+      return fail(KVQ_ERR_UNSUPPORTED, "bits_k %d unsupported (2, 4 or 8)", cfg->bits_k);
+    if (cfg->bits_v != 2 && cfg->bits_v != 4 && cfg->bits_v != 8)
+      return fail(KVQ_ERR_UNSUPPORTED, "bits_v %d unsupported (2, 4 or 8)", cfg->bits_v);
+    if ((cfg->bits_k == 8) != (cfg->bits_v == 8))
+      return fail(KVQ_ERR_UNSUPPORTED, "8-bit codes need bits_k == bits_v == 8 (got %d, %d)", cfg->bits_k,
+                  cfg->bits_v);
   }
   return KVQ_OK;
 }
 
 kvq_status check_bits(int bits) {
-  if (bits != 2 && bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "bits %d unsupported (2 or 4)", bits);
+  if (bits != 2 && bits != 4 && bits != 8)
+    return fail(KVQ_ERR_UNSUPPORTED, "bits %d unsupported (2, 4 or 8)", bits);
   return KVQ_OK;
 }
 

@@ -95,12 +95,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Code fields of one 32-bit word (two 16-bit halves), masked in place so that
 // each half reads as the fp16 denormal m * 2^-24 whose mantissa m is the code
 // times the power of two fixed by the field's bit position (the field's
-// weight: 16^(X mod 2) at 4 bits, 4^(X mod 4) at 2 bits).
+// weight: 16^(X mod 2) at 4 bits, 4^(X mod 4) at 2 bits, 1 at 8 bits, where
+// X = 0 takes fields 0, 2 and X = 1 fields 1, 3).
 // Fields in bits 8..15 of a half are taken from y = x >> 8.  One AND per pair
 // of codes, no conversion and no offset term.
 template <int BITS, int X>
 __device__ __forceinline__ unsigned code_field(unsigned x, unsigned y) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 8) {
+    return (X == 0 ? x : y) & 0x00FF00FFu;
+  } else if constexpr (BITS == 4) {
     constexpr unsigned m = (X & 1) ? 0x00F000F0u : 0x000F000Fu;
     return ((X < 2) ? x : y) & m;
   } else {
@@ -111,10 +114,14 @@ __device__ __forceinline__ unsigned code_field(unsigned x, unsigned y) {
 // Channel of operand element k (< 4) of QK step s (< 32): the step takes
 // fields X, X + 1 of a code word, each from both 16-bit halves (K codes in
 // unit order: field m of unit u holds channel u + 16 m; a unit is a 32-bit
-// word at 4 bits, a 16-bit half at 2 bits).
+// word at 4 bits, a 16-bit half at 2 bits, two words at 8 bits).
 template <int BITS>
 __host__ __device__ constexpr int qk_channel(int s, int k) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 8) {
+    // word s = half s % 2 of unit s / 2; elements: fields 0, 2, 1, 3 of the word
+    const int m = 4 * (s & 1) + 2 * (k & 1) + (k >> 1);
+    return (s >> 1) + 16 * m;
+  } else if constexpr (BITS == 4) {
     // word s / 2; even s: fields 0, 4 | 1, 5; odd s: 2, 6 | 3, 7
     const int m = 2 * (s & 1) + 4 * (k & 1) + (k >> 1);
     return (s >> 1) + 16 * m;
@@ -127,13 +134,15 @@ __host__ __device__ constexpr int qk_channel(int s, int k) {
 template <int BITS>
 __host__ __device__ constexpr int qk_slot(int c) {
   const int u = c & 15, m = c >> 4;
-  if constexpr (BITS == 4) return 4 * (2 * u + ((m >> 1) & 1)) + 2 * (m & 1) + (m >> 2);
+  if constexpr (BITS == 8) return 4 * (2 * u + (m >> 2)) + 2 * (m & 1) + ((m >> 1) & 1);
+  else if constexpr (BITS == 4) return 4 * (2 * u + ((m >> 1) & 1)) + 2 * (m & 1) + (m >> 2);
   else return 4 * (4 * (u >> 1) + (m >> 1)) + 2 * (m & 1) + (u & 1);
 }
 // Weight of channel c's K code field as read in place (16^(m mod 2) at 4 bits,
-// 4^(m mod 4) at 2 bits, m = c / 16).
+// 4^(m mod 4) at 2 bits, 1 at 8 bits, m = c / 16).
 template <int BITS>
 __host__ __device__ constexpr float k_field_weight(int c) {
+  if (BITS == 8) return 1.f;
   return BITS == 4 ? (((c >> 4) & 1) ? 16.f : 1.f) : (float)(1 << (2 * ((c >> 4) & 3)));
 }
 
@@ -253,7 +262,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
   constexpr int AL = slot_alpha_len(T);
   // V fields of tokens 2 and 3 of a quad weigh kTok times those of tokens 0, 1;
   // their probabilities enter the MFMA divided by kTok.
-  constexpr float kTok = (BV == 4) ? 16.f : 4.f;
+  constexpr float kTok = (BV == 8) ? 1.f : (BV == 4) ? 16.f : 4.f;
+  // Exponents that bound the MFMA operands' hi parts (the query fold below
+  // 2^(QE+1), p S_V below 2^(PE+1)): with codes below 2^BITS every product
+  // and every chain's partial sum stays an integer of at most 22 bits in
+  // units of 2^-24 (as at 4 bits with QE = PE = 10), so the chains sum exactly.
+  constexpr int QE = (BK == 8) ? 6 : 10, PE = (BV == 8) ? 6 : 10;
+  constexpr int KQ = (BK == 8) ? 8 : 4, VQ = (BV == 8) ? 8 : 4;   // code registers (u32x4)
   constexpr float kTwo24 = 16777216.f;
   __shared__ DecodeSmemU<T, HG, FUSED> smu;
   auto& sm = smu.dec;
@@ -314,9 +329,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
 
   // ------------------------------------------------ per-chunk operands (loaded one chunk ahead,
   // each right after its last use in the current chunk)
-  u32x4 kq[4];            // K codes of token `lane`: 4 blocks of 32 channels
+  u32x4 kq[KQ];           // K codes of token `lane`, in unit order (the 4 blocks of its slot)
   float sk, ok;           // its scale and offset
-  u32x4 vq[4];            // V codes of run `lane` (channels lane, 64 + lane), 4 pages
+  u32x4 vq[VQ];           // V codes of run `lane` (channels lane, 64 + lane), 4 pages
   f32x4 svq, ovq;         // V scale / offset of tokens 4 bq .. 4 bq + 3
   f32x4 ak[SETS];         // alpha_K of this lane's QK steps (fold layout)
   float av[TPC][2];       // alpha_V of channels lane, 64 + lane
@@ -327,7 +342,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     const uint8_t* sl = kslot(4 * c + (lane >> 4));
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      if (BK == 4) kq[blk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 256 * blk + 16 * (lane & 15)));
+      if (BK == 8) {
+        kq[2 * blk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 512 * blk + 32 * (lane & 15)));
+        kq[2 * blk + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 512 * blk + 32 * (lane & 15) + 16));
+      } else if (BK == 4) kq[blk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 256 * blk + 16 * (lane & 15)));
       else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 128 * blk + 8 * (lane & 15))); kq[blk] = u32x4{x[0], x[1], 0u, 0u}; }
     }
     sk = __builtin_nontemporal_load(reinterpret_cast<const float*>(sl + CODE_K) + (lane & 15));
@@ -337,7 +355,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint8_t* sl = vslot(4 * c + p);
-      if (BV == 4) vq[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 16 * lane));
+      if (BV == 8) {
+        vq[2 * p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 32 * lane));
+        vq[2 * p + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 32 * lane + 16));
+      } else if (BV == 4) vq[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 16 * lane));
       else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 8 * lane)); vq[p] = u32x4{x[0], x[1], 0u, 0u}; }
     }
     const uint8_t* sl = vslot(4 * c + (bq >> 2));
@@ -442,10 +463,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
   f16x4 qa_hi[HG][SETS], qa_lo[HG][SETS];
   float cA[HG], cB[HG];
   // field weights of this lane's steps: elements 0, 1 weigh w0 and 2, 3 w1
-  // (4 bits: 1 and 16; 2 bits: w0 = 16 on odd steps, else 1, and w1 = 4 w0;
-  // a step's parity is bq's)
-  const float w0 = (BK == 4) ? 1.f : ((bq & 1) ? 16.f : 1.f);
-  const float w1 = (BK == 4) ? 16.f : w0 * 4.f;
+  // (8 bits: 1 and 1; 4 bits: 1 and 16; 2 bits: w0 = 16 on odd steps, else 1,
+  // and w1 = 4 w0; a step's parity is bq's)
+  const float w0 = (BK != 2) ? 1.f : ((bq & 1) ? 16.f : 1.f);
+  const float w1 = (BK == 8) ? 1.f : (BK == 4) ? 16.f : w0 * 4.f;
 
   for (; chunk < c_end; chunk = next_chunk(chunk)) {
     const int next = next_chunk(chunk);
@@ -470,9 +491,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
         qmax = blocks_max<BLK>(qmax);
         int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
         ex = min(max(ex, -100), 100);
-        // scaled qt below 2^11: its hi part is an integer of at most 11 bits
-        const float qscale = __uint_as_float((unsigned)(127 + 10 - ex) << 23);    // 2^(10-ex)
-        const float qunscale = __uint_as_float((unsigned)(127 - 10 + ex) << 23);  // 2^(ex-10)
+        // scaled qt below 2^(QE+1): its hi part is an integer of at most QE + 1 bits
+        const float qscale = __uint_as_float((unsigned)(127 + QE - ex) << 23);    // 2^(QE-ex)
+        const float qunscale = __uint_as_float((unsigned)(127 - QE + ex) << 23);  // 2^(ex-QE)
         // The offset term takes the sum of the query as the MFMA sees it (hi + lo):
         // the split's rounding then enters each score as sum_c err_c (S k_c + O),
         // in proportion to the restored key.  (With the exact sum it would leave
@@ -514,7 +535,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     static_for<0, 32>([&](auto S_) {
       constexpr int s = decltype(S_)::value;
       f16x4 b;
-      if constexpr (BK == 4) {
+      if constexpr (BK == 8) {
+        const unsigned x = kq[s >> 2][s & 3], y = x >> 8;
+        b = as_f16x4(code_field<8, 0>(x, y), code_field<8, 1>(x, y));
+      } else if constexpr (BK == 4) {
         const unsigned x = kq[s >> 3][(s >> 1) & 3], y = x >> 8;
         if constexpr ((s & 1) == 0) b = as_f16x4(code_field<4, 0>(x, y), code_field<4, 1>(x, y));
         else b = as_f16x4(code_field<4, 2>(x, y), code_field<4, 3>(x, y));
@@ -571,14 +595,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
         acc[1][h] *= corr;
       }
     }
-    // probabilities scaled by 2^k per chunk so that P = p S_V stays below 2^11
-    // (its hi part is an integer of at most 11 bits)
+    // probabilities scaled by 2^k per chunk so that P = p S_V stays below 2^(PE+1)
+    // (its hi part is an integer of at most PE + 1 bits)
     float smax = fmaxf(fmaxf(svq[0], svq[1]), fmaxf(svq[2], svq[3]));
     smax = wave_max(smax);   // scales are >= 0
     int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
     pe = min(max(pe, -100), 100);
-    const float pk = (float)(10 - pe);
-    const float pinv = __uint_as_float((unsigned)(127 - 10 + pe) << 23);  // 2^-k
+    const float pk = (float)(PE - pe);
+    const float pinv = __uint_as_float((unsigned)(127 - PE + pe) << 23);  // 2^-k
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
@@ -647,7 +671,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
         constexpr int s = decltype(S_)::value;   // tokens 4 s .. 4 s + 3: page s / 4, quad g = s % 4
         constexpr int g = s & 3;
         f16x4 b[2];
-        if constexpr (BV == 4) {
+        if constexpr (BV == 8) {
+          // word 2 g + h of the page's run: tokens 4 g .. 4 g + 3 in fields 0, 2, 1, 3
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const unsigned x = vq[2 * (s >> 2) + (g >> 1)][2 * (g & 1) + h], y = x >> 8;
+            b[h] = as_f16x4(code_field<8, 0>(x, y), code_field<8, 1>(x, y));
+          }
+        } else if constexpr (BV == 4) {
           const unsigned x = vq[s >> 2][g], y = x >> 8;
           b[0] = as_f16x4(code_field<4, 0>(x, y), code_field<4, 1>(x, y));
           b[1] = as_f16x4(code_field<4, 2>(x, y), code_field<4, 3>(x, y));
@@ -815,12 +846,17 @@ hipError_t by_tile(int tile, F&& f) {
   }
   return hipErrorInvalidValue;
 }
+// K and V code widths: 2 and 4 in any pairing, 8 for both
 template <typename F>
-hipError_t by_bits(int bits, F&& f) {
-  switch (bits) {
-    case 2: return f(std::integral_constant<int, 2>{});
-    case 4: return f(std::integral_constant<int, 4>{});
-  }
+hipError_t by_bits_pair(int bits_k, int bits_v, F&& f) {
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  if (bits_k == 8 && bits_v == 8) return f(I8{}, I8{});
+  if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{});
+  if (bits_k == 4 && bits_v == 2) return f(I4{}, I2{});
+  if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{});
+  if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{});
   return hipErrorInvalidValue;
 }
 
@@ -836,8 +872,7 @@ hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hip
 
 hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_bits(bits_k, [&](auto BK) {
-      return by_bits(bits_v, [&](auto BV) {
+    return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
         dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
         const QuantArgs q{};
         if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false>), grid, dim3(64 * kWaves), 0, s, a, q);
@@ -846,7 +881,6 @@ hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_combine(a, kChunk, true, s);
-      });
     });
   });
 }
@@ -854,8 +888,7 @@ hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, 
 hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
                                 hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_bits(bits_k, [&](auto BK) {
-      return by_bits(bits_v, [&](auto BV) {
+    return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
         dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
         if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, true>), grid, dim3(64 * kWaves), 0, s, a, q);
         else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, true>), grid, dim3(64 * kWaves), 0, s, a, q);
@@ -865,7 +898,6 @@ hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int til
         DecodeArgs b = a;
         b.seq_lens_plus_one = 1;
         return launch_combine(b, kChunk, true, s);
-      });
     });
   });
 }

@@ -84,8 +84,19 @@ __global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
   // Codes in unit order (channel u + 16 m in field m of unit u): this
   // thread's channels 64 half + 8 cg + j are field 4 half + (cg >> 1) of the
   // units 8 (cg & 1) + j.
-  unsigned units[8];
-  if (BITS == 4) {
+  unsigned units[8];       // fields 0..3 of the unit (fields 4..7 in units8_hi at 8 bits)
+  unsigned units8_hi[8];
+  if (BITS == 8) {
+    // a unit is 8 bytes: word 2j holds fields 0..3, word 2j + 1 fields 4..7
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(crow + 64 * (cg & 1) + 16 * v4);
+      units[2 * v4] = w[0];
+      units8_hi[2 * v4] = w[1];
+      units[2 * v4 + 1] = w[2];
+      units8_hi[2 * v4 + 1] = w[3];
+    }
+  } else if (BITS == 4) {
     const u32x4 lo = *reinterpret_cast<const u32x4*>(crow + 32 * (cg & 1));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(crow + 32 * (cg & 1) + 16);
 #pragma unroll
@@ -108,7 +119,9 @@ __global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
     const int c0 = 64 * half + 8 * cg;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float q = (float)((units[j] >> (BITS * m)) & ((1u << BITS) - 1u));
+      const unsigned u = (BITS == 8 && m >= 4) ? units8_hi[j] : units[j];
+      const int mm = (BITS == 8) ? (m & 3) : m;
+      const float q = (float)((u >> (BITS * mm)) & ((1u << BITS) - 1u));
       x[8 * half + j] = al[c0 + j] * __builtin_fmaf(S, q, O);
     }
   }
@@ -190,11 +203,20 @@ __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj
   if (!VL) {
     // unit order: channel 64 half + 8 cg + j is field 4 half + (cg >> 1) of unit
     // 8 (cg & 1) + j; block b of token t at 4 BITS (16 b + t)
-    unsigned units[8];
+    unsigned units[8], units8_hi[8];   // at 8 bits a unit is two words (fields 0..3, 4..7)
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const uint8_t* bp = slot + (16 * (2 * (cg & 1) + bb) + t) * 4 * BITS;
-      if (BITS == 4) {
+      if (BITS == 8) {
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(bp + 16 * v2);
+          units[4 * bb + 2 * v2] = w[0];
+          units8_hi[4 * bb + 2 * v2] = w[1];
+          units[4 * bb + 2 * v2 + 1] = w[2];
+          units8_hi[4 * bb + 2 * v2 + 1] = w[3];
+        }
+      } else if (BITS == 4) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(bp);
 #pragma unroll
         for (int i = 0; i < 4; ++i) units[4 * bb + i] = w[i];
@@ -211,8 +233,11 @@ __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj
     for (int half = 0; half < 2; ++half) {
       const int m = 4 * half + (cg >> 1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        x[8 * half + j] = al[8 * half + j] * __builtin_fmaf(S, (float)((units[j] >> (BITS * m)) & MASK), O);
+      for (int j = 0; j < 8; ++j) {
+        const unsigned u = (BITS == 8 && m >= 4) ? units8_hi[j] : units[j];
+        const int mm = (BITS == 8) ? (m & 3) : m;
+        x[8 * half + j] = al[8 * half + j] * __builtin_fmaf(S, (float)((u >> (BITS * mm)) & MASK), O);
+      }
     }
   } else {
     // runs: run l = 8 cg + j holds channels l (h = 0) and 64 + l (h = 1); token
@@ -326,8 +351,26 @@ hipError_t by_bits(int bits, F&& f) {
   switch (bits) {
     case 2: return f(std::integral_constant<int, 2>{});
     case 4: return f(std::integral_constant<int, 4>{});
+    case 8: return f(std::integral_constant<int, 8>{});
   }
   return hipErrorInvalidValue;
+}
+
+// K and V code widths: 2 and 4 in any pairing, 8 for both
+template <typename F>
+hipError_t by_bits_pair(int bits_k, int bits_v, F&& f) {
+  if (bits_k == 8 || bits_v == 8) {
+    if (bits_k != bits_v) return hipErrorInvalidValue;
+    return f(std::integral_constant<int, 8>{}, std::integral_constant<int, 8>{});
+  }
+  if (bits_k != 2 && bits_k != 4) return hipErrorInvalidValue;
+  if (bits_v != 2 && bits_v != 4) return hipErrorInvalidValue;
+  return by_bits(bits_k, [&](auto BK) {
+    return by_bits(bits_v, [&](auto BV) {
+      if constexpr (BK() == 8 || BV() == 8) return hipErrorInvalidValue;
+      else return f(BK, BV);
+    });
+  });
 }
 
 }  // namespace
@@ -345,12 +388,10 @@ hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStre
 hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v,
                                  int num_seqs, int max_seq_len, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_bits(bits_k, [&](auto BK) {
-      return by_bits(bits_v, [&](auto BV) {
-        dim3 grid((max_seq_len + T() - 1) / T(), 2 * a.kv_heads, num_seqs);
-        hipLaunchKernelGGL((quantize_paged_kernel<T(), BK(), BV()>), grid, dim3(2 * T()), 0, s, a);
-        return hipGetLastError();
-      });
+    return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
+      dim3 grid((max_seq_len + T() - 1) / T(), 2 * a.kv_heads, num_seqs);
+      hipLaunchKernelGGL((quantize_paged_kernel<T(), BK(), BV()>), grid, dim3(2 * T()), 0, s, a);
+      return hipGetLastError();
     });
   });
 }
@@ -358,12 +399,10 @@ hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int b
 hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
                          hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_bits(bits_k, [&](auto BK) {
-      return by_bits(bits_v, [&](auto BV) {
-        dim3 grid(a.kv_heads, 2, num_seqs);
-        hipLaunchKernelGGL((append_kernel<T(), BK(), BV()>), grid, dim3(2 * T()), 0, s, a);
-        return hipGetLastError();
-      });
+    return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
+      dim3 grid(a.kv_heads, 2, num_seqs);
+      hipLaunchKernelGGL((append_kernel<T(), BK(), BV()>), grid, dim3(2 * T()), 0, s, a);
+      return hipGetLastError();
     });
   });
 }
@@ -382,12 +421,10 @@ hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream
 hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
                                 int max_seq_len, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_bits(bits_k, [&](auto BK) {
-      return by_bits(bits_v, [&](auto BV) {
-        dim3 grid((max_seq_len + kPage - 1) / kPage, 2 * a.kv_heads, num_seqs);
-        hipLaunchKernelGGL((rematerialize_kernel<T(), BK(), BV()>), grid, dim3(128), 0, s, a);
-        return hipGetLastError();
-      });
+    return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
+      dim3 grid((max_seq_len + kPage - 1) / kPage, 2 * a.kv_heads, num_seqs);
+      hipLaunchKernelGGL((rematerialize_kernel<T(), BK(), BV()>), grid, dim3(128), 0, s, a);
+      return hipGetLastError();
     });
   });
 }

@@ -445,20 +445,42 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
 
   if (MODE == kDense || !VLAYOUT) {
     // unit j of each of the lane's tokens: field m <- channel j + 16 m
+    // (a unit is BITS bytes: half a word at 2 bits, a word at 4, two words at 8)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int t = tok(q);
       if (MODE == kDense && t >= n_valid) continue;
-      const unsigned wd = pack_fields<BITS>(R[q]);
-      if (MODE == kDense) {
-        uint8_t* row = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8);
-        if (BITS == 4) *reinterpret_cast<uint32_t*>(row + 4 * j) = wd;
-        else *reinterpret_cast<uint16_t*>(row + 2 * j) = (uint16_t)wd;
+      uint8_t* dst;
+      if (MODE == kDense) dst = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8) + BITS * j;
+      else   // K slot: 4 blocks of 4 units (4 BITS bytes per token), token after token
+        dst = slot_ptr(t / kPage) + (j >> 2) * (kPage * 4 * BITS) + (t % kPage) * (4 * BITS) + BITS * (j & 3);
+      if constexpr (BITS == 8) {
+        const float lo[4] = {R[q][0], R[q][1], R[q][2], R[q][3]};
+        const float hi[4] = {R[q][4], R[q][5], R[q][6], R[q][7]};
+        *reinterpret_cast<qt_u32x2*>(dst) = qt_u32x2{pack_fields<8>(lo), pack_fields<8>(hi)};
       } else {
-        // K slot: 4 blocks of 4 units (4 BITS bytes per token), token after token
-        uint8_t* dst = slot_ptr(t / kPage) + (j >> 2) * (kPage * 4 * BITS) + (t % kPage) * (4 * BITS) + BITS * (j & 3);
+        const unsigned wd = pack_fields<BITS>(R[q]);
         if (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = wd;
         else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wd;
+      }
+    }
+  } else if constexpr (BITS == 8) {
+    // V slot at 8 bits: run l (32 bytes) holds word p = 2g + h per token quad g and
+    // channel half h, field (r >> 1) + 2 (r & 1) for token 4g + r
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      uint8_t* slot = slot_ptr(2 * w + bb);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        unsigned wd[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[(r >> 1) + 2 * (r & 1)] = R[4 * bb + r][m + 4 * h];
+          wd[h] = pack_fields<8>(o);
+        }
+        *reinterpret_cast<qt_u32x2*>(slot + 32 * (j + 16 * m) + 8 * g) = qt_u32x2{wd[0], wd[1]};
       }
     }
   } else {

@@ -36,17 +36,17 @@ def test_exports_every_declared_function(lib):
 def test_version_and_slot_sizes_match_oracle_layout(lib):
     assert "gfx950" in L.kvq_version()
     for tile in (32, 64, 128):
-        for bk in (2, 4):
-            for bv in (2, 4):
-                cfg = L.config(tile, bk, bv, 3)
-                assert L.kvq_slot_bytes(cfg, False) == orc.slot_bytes(bk, tile)
-                assert L.kvq_slot_bytes(cfg, True) == orc.slot_bytes(bv, tile)
+        for bk, bv in ((2, 2), (2, 4), (4, 2), (4, 4), (8, 8)):
+            cfg = L.config(tile, bk, bv, 3)
+            assert L.kvq_slot_bytes(cfg, False) == orc.slot_bytes(bk, tile)
+            assert L.kvq_slot_bytes(cfg, True) == orc.slot_bytes(bv, tile)
 
 
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, L.KVQ_ERR_UNSUPPORTED), ("page_tokens", 32, L.KVQ_ERR_UNSUPPORTED),
     ("tile_tokens", 48, L.KVQ_ERR_UNSUPPORTED), ("bits_k", 3, L.KVQ_ERR_UNSUPPORTED),
-    ("bits_v", 8, L.KVQ_ERR_UNSUPPORTED), ("sinkhorn_iters", -1, L.KVQ_ERR_UNSUPPORTED),
+    ("bits_v", 8, L.KVQ_ERR_UNSUPPORTED), ("bits_k", 8, L.KVQ_ERR_UNSUPPORTED),   # 8 bits on one side only
+    ("bits_v", 16, L.KVQ_ERR_UNSUPPORTED), ("sinkhorn_iters", -1, L.KVQ_ERR_UNSUPPORTED),
     ("sinkhorn_iters", 17, L.KVQ_ERR_UNSUPPORTED)])
 def test_bad_config_rejected(lib, field, value, status):
     cfg = L.config(64, 4, 4, 3)
@@ -64,6 +64,7 @@ def test_null_and_size_errors(lib):
     assert "x is NULL" in L.kvq_last_error()
     assert lib.kvq_quantize_tiles(cfg, 16, 0, 1, 4, 16, 16, 16, 16, None) == L.KVQ_ERR_ARG
     assert lib.kvq_quantize_tiles(cfg, 16, 8, 1, 3, 16, 16, 16, 16, None) == L.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_quantize_tiles(cfg, 16, 8, 1, 16, 16, 16, 16, 16, None) == L.KVQ_ERR_UNSUPPORTED
     assert lib.kvq_dequantize(cfg, 16, 16, 16, None, 8, 1, 4, 16, None) == L.KVQ_ERR_ARG
     # staging must be both or neither
     assert lib.kvq_quantize_to_pages(cfg, 16, 16, 16, 1, 64, 1, 16, 4, 16, 16, 16, None, None) == L.KVQ_ERR_ARG

@@ -43,6 +43,9 @@ DENSE_CASES = [
     (128, 2, 1, 129, 1, 2),     # one-row last tile
     (64, 4, 3, 1, 1, 2),        # a single token
     (32, 4, 3, 33, 2, 1),
+    (64, 8, 3, 1000, 2, 2),     # 8-bit codes, ragged tail
+    (32, 8, 5, 77, 3, 5),       # 8-bit, heavy-tailed K
+    (128, 8, 0, 129, 1, 2),     # 8-bit, no normalization, one-row last tile
 ]
 
 
@@ -91,6 +94,8 @@ PAGED_CASES = [
     (2, (200, 131, 64, 17), 2, 8, 64, 4, 4, 3),
     (5, (300, 97, 33), 2, 16, 32, 4, 2, 5),
     (2, (260, 128), 1, 4, 128, 2, 2, 3),
+    (2, (200, 131, 64, 17), 2, 8, 64, 8, 8, 3),     # 8-bit codes
+    (5, (300, 97, 33), 2, 16, 32, 8, 8, 5),
 ]
 
 
@@ -146,7 +151,7 @@ def test_paged_prefill_parity(case):
         np.testing.assert_array_equal(gsv[s, :tail], stg_v[s, :tail])
 
 
-@pytest.mark.parametrize("case", [PAGED_CASES[1], PAGED_CASES[2], PAGED_CASES[3]])
+@pytest.mark.parametrize("case", [PAGED_CASES[1], PAGED_CASES[2], PAGED_CASES[3], PAGED_CASES[4]])
 def test_append_and_requant_parity(case):
     recipe, lens, hkv, hq, tile, bk, bv, iters = case
     wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters, decode_steps=tile + 3)
@@ -198,6 +203,9 @@ DECODE_CASES = [
     (2, (900, 129), 2, 8, 128, 2, 2, 3),             # 2-bit, tile 128
     (2, (300,), 1, 1, 64, 4, 4, 3),                  # G = 1 (padded)
     (2, (257, 40), 1, 16, 64, 4, 2, 3),              # G = 16
+    (2, (700, 513, 64, 1), 2, 8, 64, 8, 8, 3),       # 8-bit codes
+    (5, (611, 33, 96), 2, 16, 32, 8, 8, 5),          # 8-bit, tile 32, G = 8
+    (2, (900, 129), 1, 16, 128, 8, 8, 3),            # 8-bit, tile 128, G = 16
 ]
 
 
@@ -428,6 +436,7 @@ REMAT_CASES = [
     (5, (300, 97, 33), 2, 16, 32, 4, 2, 5),
     (2, (260, 128, 1000), 1, 4, 128, 2, 2, 3),
     (1, (1024, 1), 1, 8, 64, 2, 4, 3),
+    (2, (200, 131, 64, 17), 2, 8, 64, 8, 8, 3),
 ]
 
 
@@ -486,6 +495,8 @@ FUSED_CASES = [
     (2, (260, 128, 1000), 1, 4, 128, 2, 2, 3),
     (1, (1024,), 1, 8, 64, 4, 4, 3),
     (2, (700, 513, 64, 1), 2, 8, 32, 4, 4, 3),
+    (2, (300, 97, 33), 2, 8, 64, 8, 8, 3),
+    (5, (200, 64, 17), 1, 16, 32, 8, 8, 5),
 ]
 
 
@@ -531,6 +542,7 @@ SIGNED_CASES = [
     (2, (200, 131, 64, 17), 2, 8, 64, 4, 4, 3, 1),
     (5, (300, 97, 33), 2, 16, 32, 4, 2, 5, 2),
     (2, (260, 128, 1000), 1, 4, 128, 2, 2, 3, 3),
+    (2, (200, 64, 17), 2, 8, 64, 8, 8, 3, 4),
 ]
 
 
@@ -590,7 +602,7 @@ def test_randomized_rotation_paged_decode_fused_and_restore(case):
                                   f"signed remat {case} s{s} h{h} {role}")
 
 
-@pytest.mark.parametrize("tile,bits", [(64, 4), (32, 2), (128, 4)])
+@pytest.mark.parametrize("tile,bits", [(64, 4), (32, 2), (128, 4), (64, 8)])
 def test_randomized_rotation_dense(tile, bits):
     mask = inputs.hadamard_signs(7 + tile)
     x = _x(300, 3, 2)
