@@ -30,7 +30,7 @@ PAGE_TOKENS = 16
 FP16_MAX = 65504.0
 
 _ROLE_IDS = {"K": 1, "V": 2, "Q": 3, "outlier": 4, "lens": 5, "table": 6, "decode_k": 7,
-             "decode_v": 8, "decode_q": 9}
+             "decode_v": 8, "decode_q": 9, "multi_q": 10}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -166,6 +166,13 @@ def gen_q(wl: Workload, step: int = 0, layer: int = 0) -> np.ndarray:
     """fp16 queries of one decode step: [num_seqs, hq, head_dim]."""
     rng = _rng(wl.index, layer, "decode_q", step)
     return _to_fp16(rng.standard_normal(size=(wl.num_seqs, wl.hq, wl.head_dim)))
+
+
+def gen_q_multi(wl: Workload, n_q: int, step: int = 0, layer: int = 0) -> np.ndarray:
+    """fp16 queries of the n_q newest tokens of each sequence (a verify or
+    chunk step): [num_seqs, n_q, hq, head_dim]."""
+    rng = _rng(wl.index, layer, "multi_q", step * 1000 + n_q)
+    return _to_fp16(rng.standard_normal(size=(wl.num_seqs, n_q, wl.hq, wl.head_dim)))
 
 
 def hadamard_signs(seed: int) -> np.ndarray:

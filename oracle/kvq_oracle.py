@@ -33,8 +33,9 @@ Sources (the pages, cited by title and section):
 
 Readings where the pages are silent (each is a documented parameter or choice):
 
-* Hadamard: Sylvester order, orthonormal (divided by sqrt(d)), no random signs,
-  applied to every token row of K and of V.
+* Hadamard: Sylvester order, orthonormal (divided by sqrt(d)), applied to every
+  token row of K and of V; no random signs unless a sign mask is passed in (the
+  randomized variant H diag(s), restored by diag(s) H).
 * "Variance": population standard deviation (divide by n), mean-centered; the
   data themselves are only scaled, never shifted (the per-token zero-point of
   the rounding step absorbs offsets).
@@ -552,6 +553,36 @@ def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, b
                 out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
                 if return_scale:
                     scale[s, h] = attention_abs_scale(q[s, h], kx, vx, sm)
+    return (out, scale) if return_scale else out
+
+
+def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
+                           sm_scale=None, return_scale=False, signs=None):
+    """Several queries per sequence over the same compressed pages (the read
+    path of [aitrends §TL;DR], with a causal mask): q fp16 [S, n_q, Hq, d]
+    holds the n_q newest tokens of each sequence, already in the cache, so
+    seq_lens counts them; query i sits at position seq_lens[s] - n_q + i and
+    attends to the cached tokens 0 .. that position.  n_q = 1 is the decode
+    step.  Returns float64 [S, n_q, Hq, d] (and, with return_scale,
+    attention_abs_scale per [S, n_q, Hq])."""
+    s_n, n_q, hq, d = q.shape
+    hkv = pool_k.shape[1]
+    g = hq // hkv
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+    out = np.zeros((s_n, n_q, hq, d))
+    scale = np.zeros((s_n, n_q, hq))
+    for s in range(s_n):
+        n = int(seq_lens[s])
+        for kh in range(hkv):
+            kx = read_sequence(pool_k, table[s], n, kh, "K", bits_k, tile_tokens, signs)[0]
+            vx = read_sequence(pool_v, table[s], n, kh, "V", bits_v, tile_tokens, signs)[0]
+            for i in range(n_q):
+                visible = n - n_q + i + 1
+                for h in range(kh * g, (kh + 1) * g):
+                    qv = q[s, i, h].astype(np.float64)
+                    out[s, i, h] = attention(qv, kx[:visible], vx[:visible], sm)
+                    if return_scale:
+                        scale[s, i, h] = attention_abs_scale(qv, kx[:visible], vx[:visible], sm)
     return (out, scale) if return_scale else out
 
 

@@ -585,3 +585,75 @@ def test_eight_bit_tiles_round_trip_within_the_rounding_bound():
     rec = orc.dequantize_tile(tq.codes, tq.alpha, tq.scale, tq.offset)
     err = np.linalg.norm(rec - x.astype(np.float64), axis=1)
     assert np.all(err <= tq.scale / 2 * np.linalg.norm(tq.alpha) * (1 + 1e-9) + 1e-9)
+
+
+# ---------------------------------------------------------------- several queries per sequence
+
+def _multi_query_case(n_q, seq_lens=(150, 41), hkv=2, hq=8, tile=32, bk=4, bv=2):
+    import dataclasses
+    wl = dataclasses.replace(inputs.workload(1), seq_lens=seq_lens, hkv=hkv, hq=hq, tile_tokens=tile)
+    k, v = inputs.gen_kv(wl, "K"), inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    pk, pv = orc.new_pool(npages, hkv, bk, tile), orc.new_pool(npages, hkv, bv, tile)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, tile, bk, bv, 3, pk, pv)
+    q = inputs.gen_q_multi(wl, n_q)
+    return wl, k, v, table, pk, pv, q
+
+
+def test_multi_query_equals_sdpa_with_a_bottom_right_causal_mask():
+    """torch SDPA over the restored tokens, query i of n_q at position L - n_q + i
+    seeing keys 0..L - n_q + i (the mask built from positions), GQA by repetition."""
+    n_q = 5
+    wl, k, v, table, pk, pv, q = _multi_query_case(n_q)
+    lens = np.array(wl.seq_lens)
+    out = orc.paged_multi_query_attn(q, table, lens, pk, pv, 32, 4, 2)
+    cu = wl.cu_seqlens()
+    for s in range(wl.num_seqs):
+        n = int(lens[s])
+        kd = orc.quantize_dense(k[cu[s]:cu[s + 1]], 32, 4, 3)
+        vd = orc.quantize_dense(v[cu[s]:cu[s + 1]], 32, 2, 3)
+        kx = orc.dequantize_dense(kd["codes"], kd["alpha"], kd["scale"], kd["offset"], 32, 4)
+        vx = orc.dequantize_dense(vd["codes"], vd["alpha"], vd["scale"], vd["offset"], 32, 2)
+        g = wl.hq // wl.hkv
+        qt = torch.tensor(q[s].astype(np.float64)).permute(1, 0, 2)          # [Hq, n_q, d]
+        kt = torch.tensor(kx).permute(1, 0, 2).repeat_interleave(g, dim=0)  # [Hq, n, d]
+        vt = torch.tensor(vx).permute(1, 0, 2).repeat_interleave(g, dim=0)
+        qpos = torch.arange(n - n_q, n)[:, None]
+        kpos = torch.arange(n)[None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=kpos <= qpos)
+        np.testing.assert_allclose(out[s], ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_multi_query_with_zero_keys_is_the_running_mean_of_values():
+    """All-zero keys restore to zero, every score is 0, and query i's output is
+    the mean of the restored values 0..L - n_q + i (closed form)."""
+    import dataclasses
+    n_q = 7
+    wl = dataclasses.replace(inputs.workload(1), seq_lens=(70, 9), hkv=1, hq=2, tile_tokens=32)
+    v = inputs.gen_kv(wl, "V")
+    k = np.zeros_like(v)
+    table, npages = inputs.block_table(wl)
+    pk, pv = orc.new_pool(npages, 1, 4, 32), orc.new_pool(npages, 1, 4, 32)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, 32, 4, 4, 3, pk, pv)
+    q = inputs.gen_q_multi(wl, n_q)
+    out = orc.paged_multi_query_attn(q, table, np.array(wl.seq_lens), pk, pv, 32, 4, 4)
+    for s, n in enumerate(wl.seq_lens):
+        vx = orc.read_sequence(pv, table[s], n, 0, "V", 4, 32)[0]
+        for i in range(n_q):
+            want = vx[:n - n_q + i + 1].mean(axis=0)
+            np.testing.assert_allclose(out[s, i, 0], want, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(out[s, i, 1], want, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_query_rows_are_decode_steps_at_their_own_lengths():
+    """Query i equals the single-query decode with the cache cut at its own
+    position (n_q = 1 is the decode itself)."""
+    n_q = 4
+    wl, k, v, table, pk, pv, q = _multi_query_case(n_q, seq_lens=(97, 33))
+    lens = np.array(wl.seq_lens)
+    out = orc.paged_multi_query_attn(q, table, lens, pk, pv, 32, 4, 2)
+    for i in range(n_q):
+        dec = orc.paged_decode_attn(q[:, i], table, lens - n_q + i + 1, pk, pv, 32, 4, 2)
+        np.testing.assert_array_equal(out[:, i], dec)
+    one = orc.paged_multi_query_attn(q[:, -1:], table, lens, pk, pv, 32, 4, 2)
+    np.testing.assert_array_equal(one[:, 0], orc.paged_decode_attn(q[:, -1], table, lens, pk, pv, 32, 4, 2))
