@@ -247,6 +247,45 @@ kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, c
                                  int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace kvq_paged_multi_query_attn needs for these sizes (0 for
+ * invalid sizes, n_q > max_seq_len included). */
+size_t kvq_multi_query_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t n_q,
+                                       int32_t q_heads, int32_t kv_heads, int32_t max_seq_len);
+
+/*
+ * kvq_paged_multi_query_attn - several queries per sequence read straight
+ * from the quantized pages (aitrends.kr article 74976, TL;DR: the attention
+ * backend reads the compressed pages; no fp16 K/V is rebuilt), e.g. the
+ * tokens of a chunked prefill or a speculative draft being verified.
+ *   q            fp16 [num_seqs][n_q][q_heads][128]: the n_q newest tokens of
+ *                each sequence, already in the cache (appended beforehand);
+ *                query head h reads kv head h / (q_heads / kv_heads).
+ *   seq_lens     int32 [num_seqs], device: cached tokens, the n_q queries
+ *                included.  Query i of sequence s sits at position
+ *                seq_lens[s] - n_q + i and attends to the tokens 0 .. that
+ *                position (causal).  A query at a negative position (a
+ *                sequence shorter than n_q) sees no token and gets zeros.
+ *   max_seq_len  host upper bound of seq_lens (sizes the grid; not checked
+ *                against the device lengths); n_q <= max_seq_len.
+ *   sm_scale     softmax scale (1/sqrt(128) for standard attention).
+ *   out          float32 [num_seqs][n_q][q_heads][128], computed as in
+ *                kvq_paged_decode_attn (with n_q = 1 the two give the same
+ *                values).
+ *   workspace    device scratch of at least kvq_multi_query_workspace_bytes().
+ * The (query, head) pairs of a kv head run in workgroups of up to 16; each
+ * such workgroup reads the pages of its partition, so very long query runs
+ * read the pages several times (from L2 where they fit).
+ * Errors: KVQ_ERR_ARG for null pointers, sizes <= 0, q_heads not a multiple
+ * of kv_heads, n_q > max_seq_len, too many rows; KVQ_ERR_UNSUPPORTED for a
+ * GQA group above 16; KVQ_ERR_WORKSPACE for a small workspace.
+ */
+kvq_status kvq_paged_multi_query_attn(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs,
+                                      int32_t n_q, int32_t q_heads, int32_t kv_heads,
+                                      const int32_t* block_table, int32_t max_blocks,
+                                      const int32_t* seq_lens, int32_t max_seq_len, const void* pool_k,
+                                      const void* pool_v, float sm_scale, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /*
  * Baselines (fp16 and fp8 paged KV without the quantizer), for comparing the
  * quantized read path with the two modes the aitrends.kr page (article

@@ -21,6 +21,7 @@ EXPORTED = (
     "kvq_paged_decode_attn", "kvq_bandwidth_probe", "kvq_baseline_page_bytes", "kvq_fill_pages_fp16",
     "kvq_fill_pages_fp8", "kvq_baseline_workspace_bytes", "kvq_paged_decode_attn_fp16",
     "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages",
+    "kvq_multi_query_workspace_bytes", "kvq_paged_multi_query_attn",
 )
 
 
@@ -74,6 +75,10 @@ def load():
     lib.kvq_paged_decode_attn.argtypes = [_CFG, _P, _I, _I, _I, _P, _I, _P, _I, _P, _P,
                                           ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
     lib.kvq_bandwidth_probe.argtypes = [_P, _P, ctypes.c_size_t, _P]
+    lib.kvq_multi_query_workspace_bytes.argtypes = [_CFG, _I, _I, _I, _I, _I]
+    lib.kvq_multi_query_workspace_bytes.restype = ctypes.c_size_t
+    lib.kvq_paged_multi_query_attn.argtypes = [_CFG, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P,
+                                               ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
     _F = ctypes.c_float
     lib.kvq_append_and_decode.argtypes = [_CFG, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I, _F, _P,
                                           _P, ctypes.c_size_t, _P]
@@ -91,7 +96,8 @@ def load():
     for name in ("kvq_quantize_tiles", "kvq_dequantize", "kvq_quantize_to_pages",
                  "kvq_append_and_requant", "kvq_paged_decode_attn", "kvq_bandwidth_probe",
                  "kvq_fill_pages_fp16", "kvq_fill_pages_fp8", "kvq_paged_decode_attn_fp16",
-                 "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages"):
+                 "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages",
+                 "kvq_paged_multi_query_attn"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -167,6 +173,20 @@ def kvq_paged_decode_attn(cfg, q, num_seqs, q_heads, kv_heads, block_table, max_
                                         _ptr(block_table), max_blocks, _ptr(seq_lens), max_seq_len,
                                         _ptr(pool_k), _ptr(pool_v), float(sm_scale), _ptr(out),
                                         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def kvq_multi_query_workspace_bytes(cfg, num_seqs, n_q, q_heads, kv_heads, max_seq_len) -> int:
+    return int(load().kvq_multi_query_workspace_bytes(ctypes.byref(cfg), num_seqs, n_q, q_heads, kv_heads,
+                                                      max_seq_len))
+
+
+def kvq_paged_multi_query_attn(cfg, q, num_seqs, n_q, q_heads, kv_heads, block_table, max_blocks, seq_lens,
+                               max_seq_len, pool_k, pool_v, sm_scale, out, workspace, workspace_bytes,
+                               stream=None):
+    _check(load().kvq_paged_multi_query_attn(ctypes.byref(cfg), _ptr(q), num_seqs, n_q, q_heads, kv_heads,
+                                             _ptr(block_table), max_blocks, _ptr(seq_lens), max_seq_len,
+                                             _ptr(pool_k), _ptr(pool_v), float(sm_scale), _ptr(out),
+                                             _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def kvq_bandwidth_probe(src, dst, nbytes, stream=None):

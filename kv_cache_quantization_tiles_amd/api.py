@@ -13,7 +13,8 @@ import torch
 from . import _lib
 from ._lib import (config, kvq_append_and_decode, kvq_append_and_requant, kvq_baseline_page_bytes,  # noqa: F401
                    kvq_baseline_workspace_bytes, kvq_decode_workspace_bytes, kvq_dequantize,
-                   kvq_fill_pages_fp8, kvq_fill_pages_fp16, kvq_paged_decode_attn,
+                   kvq_fill_pages_fp8, kvq_fill_pages_fp16, kvq_multi_query_workspace_bytes,
+                   kvq_paged_decode_attn, kvq_paged_multi_query_attn,
                    kvq_paged_decode_attn_fp8, kvq_paged_decode_attn_fp16, kvq_quantize_tiles,
                    kvq_quantize_to_pages, kvq_rematerialize_fp16_pages, kvq_slot_bytes)
 
@@ -109,6 +110,22 @@ class PagedCache:
         kvq_append_and_decode(self.cfg, k_new, v_new, lens_before, self.num_seqs, self.kv_heads, self.staging_k,
                               self.staging_v, self.block_table, self.max_blocks, self.pool_k, self.pool_v,
                               q.contiguous(), hq, int(max_seq_len), sm, out, workspace, workspace.numel())
+        return out
+
+    def multi_query(self, q, seq_lens, max_seq_len, out=None, workspace=None, sm_scale=None):
+        """q fp16 [S, n_q, Hq, 128]: the n_q newest cached tokens of each sequence,
+        each attending causally up to its own position; returns fp32 [S, n_q, Hq, 128]."""
+        _require_cuda(q, seq_lens)
+        s, n_q, hq, d = q.shape
+        if out is None:
+            out = torch.empty((s, n_q, hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            nbytes = kvq_multi_query_workspace_bytes(self.cfg, s, n_q, hq, self.kv_heads, int(max_seq_len))
+            workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=q.device)
+        sm = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+        kvq_paged_multi_query_attn(self.cfg, q.contiguous(), s, n_q, hq, self.kv_heads, self.block_table,
+                                   self.max_blocks, seq_lens, int(max_seq_len), self.pool_k, self.pool_v, sm,
+                                   out, workspace, workspace.numel())
         return out
 
     def rematerialize_into(self, base: "BaselineCache", seq_lens, max_seq_len):

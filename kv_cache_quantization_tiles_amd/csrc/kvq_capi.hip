@@ -290,10 +290,90 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
   a.max_tiles = (max_seq_len + 63) / 64;   // in 64-token chunks
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.unit_tokens = 64;
+  a.n_q = 1;
   a.out_scale = 1.0f;
   set_signs(a, cfg);
   return launched(kvq::launch_decode(a, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
                   "kvq_paged_decode_attn");
+}
+
+// Row blocks of the multi-query kernel per (sequence, kv head): up to 8 rows
+// run in one workgroup, more in blocks of 16.
+static int mq_row_blocks(int n_q, int group) {
+  const long rows = (long)n_q * group;
+  return rows <= 8 ? 1 : (int)((rows + 15) / 16);
+}
+
+size_t kvq_multi_query_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t n_q, int32_t q_heads,
+                                       int32_t kv_heads, int32_t max_seq_len) {
+  if (check_config(cfg, true) != KVQ_OK) return 0;
+  if (num_seqs <= 0 || n_q <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0) return 0;
+  if (q_heads % kv_heads != 0 || n_q > max_seq_len) return 0;
+  const int rb = mq_row_blocks(n_q, q_heads / kv_heads);
+  const int cpp = chunks_per_partition(num_seqs * rb, kv_heads, max_seq_len, cfg->tile_tokens);
+  const int parts = max_partitions(max_seq_len, 64, cpp);
+  return (size_t)num_seqs * n_q * q_heads * parts * (kvq::kHeadDim + 2) * sizeof(float);
+}
+
+kvq_status kvq_paged_multi_query_attn(const kvq_config* cfg, const kvq_half* q, int32_t num_seqs, int32_t n_q,
+                                      int32_t q_heads, int32_t kv_heads, const int32_t* block_table,
+                                      int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                                      const void* pool_k, const void* pool_v, float sm_scale, float* out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  KVQ_TRY(check_config(cfg, true));
+  KVQ_NONNULL(q);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(seq_lens);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  KVQ_NONNULL(out);
+  KVQ_NONNULL(workspace);
+  if (num_seqs <= 0 || n_q <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, n_q, q_heads, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (q_heads % kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "q_heads %d is not a multiple of kv_heads %d", q_heads, kv_heads);
+  if (n_q > max_seq_len)
+    return fail(KVQ_ERR_ARG, "n_q %d exceeds max_seq_len %d (the queries are cached tokens)", n_q, max_seq_len);
+  const int group = q_heads / kv_heads;
+  if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d larger than 16", group);
+  const int rb = mq_row_blocks(n_q, group);
+  if (num_seqs > 65535 || (long)kv_heads * rb > 65535 || (long)num_seqs * n_q * q_heads > 2147483647L)
+    return fail(KVQ_ERR_ARG, "too many heads, queries or sequences");
+  const int tile = cfg->tile_tokens;
+  const long need_blocks = (long)((max_seq_len + tile - 1) / tile) * (tile / kvq::kPage);
+  if (need_blocks > max_blocks)
+    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens in whole tiles", max_blocks, max_seq_len);
+  const size_t need = kvq_multi_query_workspace_bytes(cfg, num_seqs, n_q, q_heads, kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const int tpp = chunks_per_partition(num_seqs * rb, kv_heads, max_seq_len, tile);
+  const int parts = max_partitions(max_seq_len, 64, tpp);
+  if (tpp > 64 || parts > 1024)
+    return fail(KVQ_ERR_UNSUPPORTED, "max_seq_len %d is beyond 65536 chunks of 64 tokens", max_seq_len);
+  kvq::DecodeArgs a{};
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.pool_k = (const uint8_t*)pool_k;
+  a.pool_v = (const uint8_t*)pool_v;
+  a.out = out;
+  a.ws_acc = (float*)workspace;
+  a.ws_ml = (float*)workspace + (size_t)num_seqs * n_q * q_heads * parts * kvq::kHeadDim;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks;
+  a.tiles_per_part = tpp;
+  a.max_parts = parts;
+  a.max_tiles = (max_seq_len + 63) / 64;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.unit_tokens = 64;
+  a.n_q = n_q;
+  a.out_scale = 1.0f;
+  set_signs(a, cfg);
+  return launched(kvq::launch_multi_query(a, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
+                  "kvq_paged_multi_query_attn");
 }
 
 kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
@@ -352,6 +432,7 @@ kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, c
   a.max_tiles = (max_seq_len + 63) / 64;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.unit_tokens = 64;
+  a.n_q = 1;
   a.out_scale = 1.0f;
   kvq::QuantArgs qa{};
   qa.src[0] = k_new;
@@ -496,6 +577,7 @@ static kvq_status decode_baseline(const kvq_config* cfg, const kvq_half* q, int3
   a.max_tiles = (max_seq_len + 63) / 64;
   a.sm_scale_log2 = sm_scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;
   a.unit_tokens = 64;
+  a.n_q = 1;
   a.out_scale = fp8 ? v_scale : 1.f;
   return launched(kvq::launch_decode_baseline(a, fp8, (hipStream_t)stream), what);
 }

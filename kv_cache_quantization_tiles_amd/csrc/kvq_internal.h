@@ -75,6 +75,7 @@ struct DecodeArgs {
   int unit_tokens;            // tokens per partition unit (tile, or 64 for the baselines)
   float out_scale;            // output multiplier (the V scale for fp8 pages, else 1)
   int seq_lens_plus_one;      // 1: seq_lens are the lengths before an appended token
+  int n_q;                    // queries per sequence (1 for a decode step); q, out: [S][n_q][Hq][D]
   uint32_t signs[4];          // randomized rotation of the quantized pages (0 for the baselines)
 };
 
@@ -114,6 +115,7 @@ hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bi
 hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s);
+hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
                                 hipStream_t s);
 hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, int max_seq_len, hipStream_t s);

@@ -563,8 +563,10 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
     holds the n_q newest tokens of each sequence, already in the cache, so
     seq_lens counts them; query i sits at position seq_lens[s] - n_q + i and
     attends to the cached tokens 0 .. that position.  n_q = 1 is the decode
-    step.  Returns float64 [S, n_q, Hq, d] (and, with return_scale,
-    attention_abs_scale per [S, n_q, Hq])."""
+    step.  A query at a negative position (a sequence shorter than n_q) sees
+    no token: its output row is zero, as the library defines it.  Returns
+    float64 [S, n_q, Hq, d] (and, with return_scale, attention_abs_scale per
+    [S, n_q, Hq])."""
     s_n, n_q, hq, d = q.shape
     hkv = pool_k.shape[1]
     g = hq // hkv
@@ -578,6 +580,8 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
             vx = read_sequence(pool_v, table[s], n, kh, "V", bits_v, tile_tokens, signs)[0]
             for i in range(n_q):
                 visible = n - n_q + i + 1
+                if visible <= 0:
+                    continue
                 for h in range(kh * g, (kh + 1) * g):
                     qv = q[s, i, h].astype(np.float64)
                     out[s, i, h] = attention(qv, kx[:visible], vx[:visible], sm)

@@ -123,3 +123,30 @@ def test_rematerialize_validation(lib):
     bad = L.config(64, 3, 4, 3)
     assert lib.kvq_rematerialize_fp16_pages(ctypes.byref(bad), 16, 16, 16, 8, 16, 1, 65, 1, 16, 16,
                                             None) == L.KVQ_ERR_UNSUPPORTED
+
+
+def test_multi_query_validation(lib):
+    cfg = L.config(64, 4, 4, 3)
+    c = ctypes.byref(cfg)
+    need = L.kvq_multi_query_workspace_bytes(cfg, 4, 4, 32, 8, 16388)
+    assert need > 0 and need % (130 * 4) == 0
+    # one query per sequence takes what the decode takes
+    assert L.kvq_multi_query_workspace_bytes(cfg, 4, 1, 32, 8, 16385) == L.kvq_decode_workspace_bytes(cfg, 4, 32, 8,
+                                                                                                       16385)
+    assert L.kvq_multi_query_workspace_bytes(cfg, 4, 0, 32, 8, 16388) == 0
+    assert L.kvq_multi_query_workspace_bytes(cfg, 1, 65, 4, 1, 64) == 0       # n_q > max_seq_len
+    args = (16, 4, 4, 32, 8, 16, 1028, 16, 16388, 16, 16, 0.1, 16, 16)
+    assert lib.kvq_paged_multi_query_attn(c, *args, need - 1, None) == L.KVQ_ERR_WORKSPACE
+    assert "needed" in L.kvq_last_error()
+    # n_q = 0, n_q above max_seq_len, q_heads not a multiple of kv_heads, group above 16
+    assert lib.kvq_paged_multi_query_attn(c, 16, 4, 0, 32, 8, 16, 1028, 16, 16388, 16, 16, 0.1, 16, 16, need,
+                                          None) == L.KVQ_ERR_ARG
+    assert lib.kvq_paged_multi_query_attn(c, 16, 1, 65, 4, 1, 16, 4, 16, 64, 16, 16, 0.1, 16, 16, 1 << 30,
+                                          None) == L.KVQ_ERR_ARG
+    assert lib.kvq_paged_multi_query_attn(c, 16, 4, 4, 30, 8, 16, 1028, 16, 16388, 16, 16, 0.1, 16, 16, need,
+                                          None) == L.KVQ_ERR_ARG
+    assert lib.kvq_paged_multi_query_attn(c, 16, 4, 4, 64, 2, 16, 1028, 16, 16388, 16, 16, 0.1, 16, 16, 1 << 30,
+                                          None) == L.KVQ_ERR_UNSUPPORTED
+    # NULL output
+    assert lib.kvq_paged_multi_query_attn(c, 16, 4, 4, 32, 8, 16, 1028, 16, 16388, 16, 16, 0.1, None, 16, need,
+                                          None) == L.KVQ_ERR_ARG

@@ -618,3 +618,72 @@ def test_randomized_rotation_dense(tile, bits):
     deq = api.dequantize(q, cfg, bits).cpu().numpy().astype(np.float64)
     ref_deq = orc.dequantize_dense(got["codes"], got["alpha"], got["scale"], got["offset"], tile, bits, mask)
     pu.assert_dequant(deq, ref_deq, "signed dequantize")
+
+
+MQ_CASES = [
+    # (recipe, lens, hkv, hq, tile, bits_k, bits_v, iters, n_q)
+    (2, (700, 513, 64, 5), 2, 8, 64, 4, 4, 3, 4),        # G = 4, 4 queries: 16 rows in one workgroup
+    (5, (611, 200, 33), 2, 16, 32, 4, 2, 5, 3),          # G = 8, 24 rows: blocks of 16 + 8
+    (2, (900, 129), 2, 8, 128, 2, 2, 3, 2),              # 8 rows, 2-bit, tile 128
+    (2, (300, 70), 1, 1, 64, 4, 4, 3, 1),                # one row
+    (2, (257, 40), 1, 16, 64, 4, 2, 3, 5),               # G = 16, 80 rows in 5 blocks
+    (2, (700, 100), 2, 8, 64, 8, 8, 3, 4),               # 8-bit codes
+    (2, (400, 300), 1, 4, 64, 4, 4, 3, 70),              # a 70-token chunk: the mask spans two chunks
+    (2, (100, 3), 1, 4, 64, 4, 4, 3, 6),                 # a sequence shorter than n_q: zero rows
+]
+
+
+@pytest.mark.parametrize("case", MQ_CASES)
+def test_paged_multi_query_parity(case):
+    """Several queries per sequence, causal, against the oracle on the GPU's pages."""
+    recipe, lens, hkv, hq, tile, bk, bv, iters, n_q = case
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    q = inputs.gen_q_multi(wl, n_q)
+    seq_lens = np.array(wl.seq_lens, np.int32)
+    out = cache.multi_query(torch.from_numpy(q).cuda(), torch.from_numpy(seq_lens).cuda(), max(lens))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    ref, sc = orc.paged_multi_query_attn(q, table, seq_lens, gpk, gpv, tile, bk, bv, return_scale=True)
+    err = pu.assert_attn(got, ref, f"multi-query {case}", sc)
+    assert np.isfinite(got).all()
+    print(f"[attn] multi-query {case}: max abs err vs oracle on GPU pages {err:.2e}", flush=True)
+
+
+def test_multi_query_with_one_query_is_the_decode_bit_for_bit():
+    recipe, lens, hkv, hq, tile, bk, bv, iters = DECODE_CASES[2]
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    _, _, _, _, cache = _gpu_prefill(wl)
+    q = torch.from_numpy(inputs.gen_q(wl)).cuda()
+    sl = torch.tensor(wl.seq_lens, dtype=torch.int32, device="cuda")
+    dec = cache.decode(q, sl, max(lens))
+    mq = cache.multi_query(q[:, None], sl, max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(mq[:, 0], dec)
+
+
+def test_full_size_qwen3_4b_layer_4x16k_verify_4_sampled():
+    """The 4 x 16K, 8/32-head layer: 4 draft tokens per sequence appended, then
+    verified with one multi-query launch; sampled (sequence, kv head) outputs
+    against the oracle."""
+    wl = inputs.workload(2)
+    k, v, table, npages, cache = _gpu_prefill(wl)
+    lens = np.array(wl.seq_lens, np.int32)
+    n_q = 4
+    for step in range(n_q):
+        kn, vn = inputs.gen_decode_kv(wl, "K", step), inputs.gen_decode_kv(wl, "V", step)
+        cache.append(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens + step).cuda())
+    q = inputs.gen_q_multi(wl, n_q)
+    out = cache.multi_query(torch.from_numpy(q).cuda(), torch.from_numpy(lens + n_q).cuda(), int(lens.max()) + n_q)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    g = wl.group
+    for s, kh in [(0, 0), (3, 7), (2, 3)]:
+        ref, sc = orc.paged_multi_query_attn(q[s:s + 1, :, kh * g:(kh + 1) * g], table[s:s + 1], lens[s:s + 1] + n_q,
+                                             gpk[:, kh:kh + 1], gpv[:, kh:kh + 1], wl.tile_tokens, wl.bits_k,
+                                             wl.bits_v, return_scale=True)
+        err = pu.assert_attn(got[s, :, kh * g:(kh + 1) * g], ref[0], f"verify s{s} kv head {kh}", sc[0])
+        print(f"[attn] 4x16k verify-4 s{s} kv head {kh}: max abs err {err:.2e}", flush=True)

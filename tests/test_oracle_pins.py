@@ -657,3 +657,16 @@ def test_multi_query_rows_are_decode_steps_at_their_own_lengths():
         np.testing.assert_array_equal(out[:, i], dec)
     one = orc.paged_multi_query_attn(q[:, -1:], table, lens, pk, pv, 32, 4, 2)
     np.testing.assert_array_equal(one[:, 0], orc.paged_decode_attn(q[:, -1], table, lens, pk, pv, 32, 4, 2))
+
+
+def test_multi_query_rows_before_the_sequence_start_are_zero():
+    """A sequence shorter than n_q: its first queries sit at negative positions,
+    see no token and give zero rows; the rest are decode steps at their lengths."""
+    n_q = 6
+    wl, k, v, table, pk, pv, q = _multi_query_case(n_q, seq_lens=(40, 3))
+    lens = np.array(wl.seq_lens)
+    out = orc.paged_multi_query_attn(q, table, lens, pk, pv, 32, 4, 2)
+    assert not out[1, :3].any()
+    for i in range(3, n_q):
+        dec = orc.paged_decode_attn(q[1:, i], table[1:], np.array([i - 2]), pk, pv, 32, 4, 2)
+        np.testing.assert_array_equal(out[1, i], dec[0])
