@@ -320,15 +320,21 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps carry no events: a timing event between launches leaves
+    # the GPU idle (each step would take ~9x its kernel time)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    # per-phase split of the same step, in a separate untimed-for-value loop
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
     tq = [e[0].elapsed_time(e[1]) for e in evs]
     tad = [e[1].elapsed_time(e[2]) for e in evs]
-    ms_step = wall * 1e3 / args.steps
 
     # the same decode step as two calls (append, then decode), for comparison
     n_split = max(20, args.steps)
@@ -381,6 +387,25 @@ def main():
     q8_ms = q8_batch[0].elapsed_time(q8_batch[1]) / q8_batch[2]
     d8_ms = d8_batch[0].elapsed_time(d8_batch[1]) / d8_batch[2]
     del caches_8
+    # several queries per sequence (a speculative verify of 4 and of 16 draft
+    # tokens) over the same pages: tokens past the appended one are stale
+    # pool bytes (timing only; parity is in the tests)
+    mq = {}
+    for n_mq in (4, 16):
+        qm = torch.from_numpy(inputs.gen_q_multi(wl, n_mq)).to(dev)
+        sl = lens_before + n_mq
+        mo = torch.empty((wl.num_seqs, n_mq, wl.hq, D), dtype=torch.float32, device=dev)
+        nb = api.kvq_multi_query_workspace_bytes(cfg, wl.num_seqs, n_mq, wl.hq, wl.hkv, max_len + n_mq)
+        mw = torch.empty(nb, dtype=torch.uint8, device=dev)
+        caches[0].multi_query(qm, sl, max_len + n_mq, out=mo, workspace=mw)
+        mb = batch_ms(lambda j: caches[j % n_pools].multi_query(qm, sl, max_len + n_mq, out=mo, workspace=mw), n_q)
+        torch.cuda.synchronize()
+        mq_ms = mb[0].elapsed_time(mb[1]) / mb[2]
+        mq_bytes = decode_bytes(wl, [l + n_mq for l in wl.seq_lens])
+        mq[f"n_q_{n_mq}"] = {"attn_ms": round(mq_ms, 4), "GBps": round(mq_bytes / (mq_ms * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(mq_bytes / (mq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                             "query_tokens_per_s": round(wl.num_seqs * n_mq / (mq_ms * 1e-3), 1)}
+        del mw
     q_kernel_ms = q_batch[0].elapsed_time(q_batch[1]) / q_batch[2]
     td_cold = d_batch[0].elapsed_time(d_batch[1]) / d_batch[2]
     qs_ms = qs_batch[0].elapsed_time(qs_batch[1]) / qs_batch[2]
@@ -423,6 +448,7 @@ def main():
         "decode_tok_per_s": round(wl.num_seqs / (ad_ms * 1e-3), 1),
         "decode_attn_only_tok_per_s": round(wl.num_seqs / (td_cold * 1e-3), 1),
         "copy_probe_GBps": round(copy_gbps, 1),
+        "multi_query_verify": mq,
         "randomized_rotation": {"quantize_kernel_ms": round(qs_ms, 4), "decode_attn_ms": round(ds_ms, 4),
                                 "quantize_GBps": round(qbytes / (qs_ms * 1e-3) / 1e9, 1)},
         "codes_8bit": {"quantize_kernel_ms": round(q8_ms, 4), "decode_attn_ms": round(d8_ms, 4),
