@@ -221,16 +221,21 @@ def identity_block_table(wl: Workload, capacity_tokens=None):
 def gen_kv_device(wl: Workload, role: str, layer: int = 0, device="cuda"):
     """fp16 K or V of the whole prefill drawn on the device with a seeded torch
     generator, for workloads too large to draw on the host (the 36-layer 128K
-    one): [total_tokens, hkv, head_dim].  Same recipe as gen_kv (normal values,
-    K channels scaled by channel_scales, clamped, rounded to fp16), a different
-    stream of numbers."""
+    one, the 64-sequence mixed-length one): [total_tokens, hkv, head_dim].
+    Same recipe as gen_kv (normal or Student-t(3) values, K channels scaled by
+    channel_scales, clamped, rounded to fp16), a different stream of numbers.
+    Student-t(3) is drawn as z / sqrt(c / 3) with z standard normal and c
+    chi-square with 3 degrees of freedom (twice a Gamma(3/2) variate)."""
     import torch
     assert role in ("K", "V")
-    if wl.k_recipe == "student_t3_loguniform":
-        raise ValueError("device generation covers the normal recipes only")
     g = torch.Generator(device=device)
     g.manual_seed(20261202 * 1000 + wl.index * 100 + layer * 10 + _ROLE_IDS[role])
-    x = torch.randn((wl.total_tokens, wl.hkv, wl.head_dim), generator=g, device=device, dtype=torch.float32)
+    shape = (wl.total_tokens, wl.hkv, wl.head_dim)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if role == "K" and wl.k_recipe == "student_t3_loguniform":
+        c = torch._standard_gamma(torch.full(shape, 1.5, device=device, dtype=torch.float32), generator=g)
+        x /= torch.sqrt(c * (2.0 / 3.0))
+        del c
     if role == "K":
         x *= torch.from_numpy(channel_scales(wl, layer)).to(device=device, dtype=torch.float32)[None]
     return x.clamp_(-FP16_MAX, FP16_MAX).to(torch.float16)

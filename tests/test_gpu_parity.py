@@ -388,13 +388,15 @@ def test_full_size_qwen3_4b_layer_4x16k_sampled():
 
 def test_full_size_qwen3_32b_tp2_burst_sampled():
     """One GPU's share of the 32 x 16K burst (4 kv heads, 32 query heads):
-    quantize the prefill, then 66 decode steps of append + attend (every
-    sequence crosses a tile boundary); sampled checks at the end."""
+    quantize the prefill, then the workload's 256 decode steps of append +
+    attend (every sequence crosses four tile boundaries); sampled checks at
+    the end."""
     wl = inputs.workload(3)
     k, v, table, npages, cache = _gpu_prefill(wl)
     lens = np.array(wl.seq_lens, np.int32)
     q = None
-    steps = 66
+    steps = wl.decode_steps
+    assert steps == 256
     d_lens = torch.from_numpy(lens).cuda()
     for step in range(steps):
         kn = torch.from_numpy(inputs.gen_decode_kv(wl, "K", step)).cuda()
@@ -687,3 +689,97 @@ def test_full_size_qwen3_4b_layer_4x16k_verify_4_sampled():
                                              wl.bits_v, return_scale=True)
         err = pu.assert_attn(got[s, :, kh * g:(kh + 1) * g], ref[0], f"verify s{s} kv head {kh}", sc[0])
         print(f"[attn] 4x16k verify-4 s{s} kv head {kh}: max abs err {err:.2e}", flush=True)
+
+
+def _appended_row_checks(wl, kn, vn, lens, table, gpk, gpv, seqs, what):
+    """The token appended after a prefill of whole tiles opens a one-row tile."""
+    t = wl.tile_tokens
+    ppt = t // 16
+    for s in seqs:
+        j = int(lens[s]) // t
+        assert int(lens[s]) % t == 0
+        for h in range(wl.hkv):
+            for role, new, gp, bits in (("K", kn, gpk, wl.bits_k), ("V", vn, gpv, wl.bits_v)):
+                ref = orc.quantize_tile(new[s, h][None], bits, wl.iters)
+                _, gc, ga, gs, go = orc.read_sequence(gp, table[s, j * ppt:(j + 1) * ppt], 1, h, role, bits, t)
+                pu.compare_codes(gc, ref.codes, ref.pre, f"{what} append s{s} h{h} {role}")
+                pu.check_tile_metadata(ref.codes, ga[0], gs, go, ref.alpha, ref.scale, ref.offset,
+                                       orc.dequantize_tile, f"{what} append s{s} h{h} {role}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_full_size_long_context_layer_6x128k_sampled(bits):
+    """One layer of the 6 x 128K long-context workload (8 kv / 32 query heads,
+    tile 128, 3 iterations) at 4- and 2-bit codes, in the launch configuration
+    the bench times: quantize the prefill (drawn on the device), then one
+    fused append + decode step; sampled tiles, the appended rows and attention
+    outputs over 131073 tokens against the oracle."""
+    wl = dataclasses.replace(inputs.workload(4), bits_k=bits, bits_v=bits)
+    max_len = max(wl.seq_lens)
+    k = inputs.gen_kv_device(wl, "K")
+    v = inputs.gen_kv_device(wl, "V")
+    table, npages = inputs.block_table(wl, capacity_tokens=max_len + 1)
+    cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
+    cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+    cache.quantize_prefill(k, v, torch.from_numpy(wl.cu_seqlens()).cuda(), max_len)
+    lens = np.array(wl.seq_lens, np.int32)
+    kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
+    q = inputs.gen_q(wl)
+    out = cache.append_decode(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens).cuda(),
+                              torch.from_numpy(q).cuda(), max_len + 1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    k_np, v_np = k.cpu().numpy(), v.cpu().numpy()
+    del k, v
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    what = f"6x128k b{bits}"
+    _sampled_tile_checks(wl, k_np, v_np, table, gpk, gpv, np.random.default_rng(44 + bits), 24, what)
+    _appended_row_checks(wl, kn, vn, lens, table, gpk, gpv, (0, 5), what)
+    pairs = [(0, 0), (5, 7)] if bits == 4 else [(3, 2)]
+    _sampled_decode_checks(wl, q, table, lens + 1, gpk, gpv, got, pairs, f"{what} decode")
+
+
+def test_full_size_mixed_64_seqs_1k_32k_sampled():
+    """The mixed-precision stress workload at full size: 64 sequences of 1K-32K
+    tokens, 8 kv / 64 query heads, heavy-tailed K (Student-t(3) times
+    log-uniform channel scales, drawn on the device), tile 32, 4-bit K, 2-bit
+    V, 5 iterations; quantize, then one fused append + decode step; sampled
+    tiles and attention outputs against the oracle."""
+    wl = inputs.workload(5)
+    max_len = max(wl.seq_lens)
+    k = inputs.gen_kv_device(wl, "K")
+    v = inputs.gen_kv_device(wl, "V")
+    table, npages = inputs.block_table(wl)
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+    cache.quantize_prefill(k, v, torch.from_numpy(wl.cu_seqlens()).cuda(), max_len)
+    lens = np.array(wl.seq_lens, np.int32)
+    kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
+    q = inputs.gen_q(wl)
+    out = cache.append_decode(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens).cuda(),
+                              torch.from_numpy(q).cuda(), max_len + 1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    k_np, v_np = k.cpu().numpy(), v.cpu().numpy()
+    del k, v
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    _sampled_tile_checks(wl, k_np, v_np, table, gpk, gpv, np.random.default_rng(45), 32, "mixed-64")
+    # the appended token's tile (partial for most lengths): rebuilt from its fp16 rows
+    t = wl.tile_tokens
+    cu = wl.cu_seqlens()
+    for s in (int(np.argmin(lens)), int(np.argmax(lens)), 17):
+        j = int(lens[s]) // t
+        n = int(lens[s]) - j * t + 1
+        for h in (0, wl.hkv - 1):
+            for role, src, new, gp, bits in (("K", k_np, kn, gpk, wl.bits_k), ("V", v_np, vn, gpv, wl.bits_v)):
+                x = np.concatenate([src[cu[s] + j * t:cu[s] + int(lens[s]), h], new[s, h][None]])
+                ref = orc.quantize_tile(x, bits, wl.iters)
+                _, gc, ga, gs, go = orc.read_sequence(gp, table[s, j * (t // 16):(j + 1) * (t // 16)], n, h, role,
+                                                      bits, t)
+                pu.compare_codes(gc, ref.codes, ref.pre, f"mixed-64 last tile s{s} h{h} {role}")
+                pu.check_tile_metadata(ref.codes, ga[0], gs, go, ref.alpha, ref.scale, ref.offset,
+                                       orc.dequantize_tile, f"mixed-64 last tile s{s} h{h} {role}")
+    _sampled_decode_checks(wl, q, table, lens + 1, gpk, gpv, got,
+                           [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 5), (37, 7)], "mixed-64 decode")
