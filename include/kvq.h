@@ -272,7 +272,7 @@ size_t kvq_multi_query_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, 
  *                kvq_paged_decode_attn (with n_q = 1 the two give the same
  *                values).
  *   workspace    device scratch of at least kvq_multi_query_workspace_bytes().
- * The (query, head) pairs of a kv head run in workgroups of up to 16; each
+ * The (query, head) pairs of a kv head run in workgroups of up to 8; each
  * such workgroup reads the pages of its partition, so very long query runs
  * read the pages several times (from L2 where they fit).
  * Errors: KVQ_ERR_ARG for null pointers, sizes <= 0, q_heads not a multiple

@@ -297,11 +297,10 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
                   "kvq_paged_decode_attn");
 }
 
-// Row blocks of the multi-query kernel per (sequence, kv head): up to 8 rows
-// run in one workgroup, more in blocks of 16.
+// Row blocks of the multi-query kernel per (sequence, kv head): 8 rows each.
 static int mq_row_blocks(int n_q, int group) {
   const long rows = (long)n_q * group;
-  return rows <= 8 ? 1 : (int)((rows + 15) / 16);
+  return (int)((rows + 7) / 8);
 }
 
 size_t kvq_multi_query_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t n_q, int32_t q_heads,

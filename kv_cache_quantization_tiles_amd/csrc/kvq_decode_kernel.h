@@ -29,7 +29,7 @@
 // Query rows: a decode step has one row per query head of the GQA group.
 // With several queries per sequence (the newest n_q tokens, already cached,
 // each attending causally to the tokens up to its own position) the rows are
-// (query, head) pairs, 16 at most per workgroup, and a row's scores past its
+// (query, head) pairs, 8 at most per workgroup, and a row's scores past its
 // position are masked.
 #pragma once
 #include <type_traits>
