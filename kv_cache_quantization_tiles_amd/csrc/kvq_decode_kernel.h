@@ -598,20 +598,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
     if (more) load_k(next);
 
     // -------------------------------------------- online softmax (base 2), per head
-    // the running max moves only when a chunk's scores pass it
-    float cmax[NH];
-    bool grow = false;
+    // the running max moves only when a chunk's scores pass it: a test in
+    // each lane and one vote over the wave decide, and only then are the
+    // chunk's maxima reduced over the wave (m_run is the same in every lane)
+    bool pass = false;
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        cmax[4 * hg + i] = wave_max(sc[hg][i]);
-        grow |= cmax[4 * hg + i] > m_run[4 * hg + i];
-      }
-    if (grow) {   // wave-uniform
+      for (int i = 0; i < 4; ++i) pass |= sc[hg][i] > m_run[4 * hg + i];
+    if (__builtin_amdgcn_ballot_w64(pass) != 0) {   // wave-uniform
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const float m_new = fmaxf(m_run[h], cmax[h]);
+        const float m_new = fmaxf(m_run[h], wave_max(sc[h >> 2][h & 3]));
         // (MQ: a row may have seen no visible token yet; -inf - -inf is no number)
         const float corr = (MQ && m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[h] - m_new);
         m_run[h] = m_new;
