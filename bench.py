@@ -259,6 +259,63 @@ def long_context_leg(n_iter: int = 10):
                              "fp16 / fp8 / compressed KV (other hardware, end-to-end; context only)"}
 
 
+def burst_leg():
+    """One GPU's TP=2 share of the Qwen3-32B-shaped 16K burst (32 sequences x
+    16384 tokens, 4 kv / 32 query heads, tile 64, 4-bit K and V, 3
+    iterations): quantize the burst prefill, then the workload's 256 decode
+    steps, each one fused append + re-quantize + attend launch (plus the
+    partition merge).  Inputs drawn on the device; the new tokens and queries
+    of every step are resident before timing."""
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+
+    wl = inputs.workload(3)
+    dev = torch.device("cuda:0")
+    table, npages = inputs.block_table(wl)
+    max_len = max(wl.seq_lens)
+    cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+    k = inputs.gen_kv_device(wl, "K", device=dev)
+    v = inputs.gen_kv_device(wl, "V", device=dev)
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    steps = wl.decode_steps
+    kn = torch.stack([torch.from_numpy(inputs.gen_decode_kv(wl, "K", i)) for i in range(steps)]).to(dev)
+    vn = torch.stack([torch.from_numpy(inputs.gen_decode_kv(wl, "V", i)) for i in range(steps)]).to(dev)
+    qs = torch.stack([torch.from_numpy(inputs.gen_q(wl, i)) for i in range(steps)]).to(dev)
+    lens0 = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    lens = [lens0 + i for i in range(steps)]
+    out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+    caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(2)]
+    ws = caches[0].workspace(wl.hq, max_len + steps)
+    caches[1].quantize_prefill(k, v, cu, max_len)   # warm-up
+    torch.cuda.synchronize()
+    c = caches[0]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    c.quantize_prefill(k, v, cu, max_len)
+    e[1].record()
+    for i in range(steps):
+        c.append_decode(kn[i], vn[i], lens[i], qs[i], max_len + steps, out=out, workspace=ws)
+    e[2].record()
+    torch.cuda.synchronize()
+    q_ms = e[0].elapsed_time(e[1])
+    d_ms = e[1].elapsed_time(e[2]) / steps
+    th = wl.total_tokens * wl.hkv
+    qbytes = quantize_bytes(th, wl.bits_k, wl.tile_tokens) + quantize_bytes(th, wl.bits_v, wl.tile_tokens)
+    mid = [l + steps // 2 for l in wl.seq_lens]
+    dbytes = decode_bytes(wl, mid)
+    del caches, k, v, kn, vn, qs
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "num_seqs": wl.num_seqs, "context": max_len, "kv_heads": wl.hkv, "q_heads": wl.hq,
+            "tile_tokens": wl.tile_tokens, "decode_steps": steps,
+            "quantize_prefill_ms": round(q_ms, 4), "quantize_GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            "decode_step_ms": round(d_ms, 4),
+            "decode_tok_per_s": round(wl.num_seqs / (d_ms * 1e-3), 1),
+            "decode_slot_GBps": round(dbytes / (d_ms * 1e-3) / 1e9, 1),
+            "decode_hbm_frac": round(dbytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "decode step = fused append + re-quantize of the partial tile + attention + merge; "
+                    "slot bytes at the middle step's lengths"}
+
+
 # ----------------------------------------------------------------------------- GPU leg
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -269,7 +326,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the fp16 / fp8 / 4-bit / 2-bit comparison at 6 x 128K")
+                    help="skip the fp16 / fp8 / 4-bit / 2-bit comparison at 6 x 128K and the 32 x 16K burst")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards "
@@ -406,6 +463,42 @@ def main():
                              "hbm_frac": round(mq_bytes / (mq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                              "query_tokens_per_s": round(wl.num_seqs * n_mq / (mq_ms * 1e-3), 1)}
         del mw
+    # the dense entry points (one token run [n, H, 128], codes and scale vectors
+    # in their own arrays) on the same rows: quantize, then restore to fp16
+    n_tok = wl.total_tokens
+    dq = [dict(codes=torch.empty((n_tok, wl.hkv, D * wl.bits_k // 8), dtype=torch.uint8, device=dev),
+               alpha=torch.empty(((n_tok + wl.tile_tokens - 1) // wl.tile_tokens, wl.hkv, D), dtype=torch.float32,
+                                 device=dev),
+               scale=torch.empty((n_tok, wl.hkv), dtype=torch.float32, device=dev),
+               offset=torch.empty((n_tok, wl.hkv), dtype=torch.float32, device=dev)) for _ in range(n_in)]
+    restored = [torch.empty_like(ks[0]) for _ in range(n_in)]
+
+    def dense_q(j):
+        o = dq[j % n_in]
+        api.kvq_quantize_tiles(cfg, ks[j % n_in], n_tok, wl.hkv, wl.bits_k, o["codes"], o["alpha"], o["scale"],
+                               o["offset"])
+
+    def dense_dq(j):
+        o = dq[j % n_in]
+        api.kvq_dequantize(cfg, o["codes"], o["alpha"], o["scale"], o["offset"], n_tok, wl.hkv, wl.bits_k,
+                           restored[j % n_in])
+    dense_q(0)
+    dense_q(1)
+    dqz_batch = batch_ms(dense_q, n_q)
+    ddq_batch = batch_ms(dense_dq, n_q)
+    torch.cuda.synchronize()
+    dqz_ms = dqz_batch[0].elapsed_time(dqz_batch[1]) / dqz_batch[2]
+    ddq_ms = ddq_batch[0].elapsed_time(ddq_batch[1]) / ddq_batch[2]
+    th_k = n_tok * wl.hkv
+    stored = th_k * (D * wl.bits_k / 8 + 8 + 4 * D / wl.tile_tokens)   # codes, scale, offset, alpha share
+    dq_bytes = stored + th_k * 2 * D                                   # ... read, fp16 rows written
+    dense = {"quantize_ms": round(dqz_ms, 4),
+             "quantize_GBps": round(quantize_bytes(th_k, wl.bits_k, wl.tile_tokens) / (dqz_ms * 1e-3) / 1e9, 1),
+             "dequantize_ms": round(ddq_ms, 4),
+             "dequantize_GBps": round(dq_bytes / (ddq_ms * 1e-3) / 1e9, 1),
+             "dequantize_hbm_frac": round(dq_bytes / (ddq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+             "note": f"K only, one token run of {n_tok} tokens x {wl.hkv} heads, {wl.bits_k}-bit"}
+    del dq, restored
     q_kernel_ms = q_batch[0].elapsed_time(q_batch[1]) / q_batch[2]
     td_cold = d_batch[0].elapsed_time(d_batch[1]) / d_batch[2]
     qs_ms = qs_batch[0].elapsed_time(qs_batch[1]) / qs_batch[2]
@@ -449,6 +542,7 @@ def main():
         "decode_attn_only_tok_per_s": round(wl.num_seqs / (td_cold * 1e-3), 1),
         "copy_probe_GBps": round(copy_gbps, 1),
         "multi_query_verify": mq,
+        "dense_entry_points": dense,
         "randomized_rotation": {"quantize_kernel_ms": round(qs_ms, 4), "decode_attn_ms": round(ds_ms, 4),
                                 "quantize_GBps": round(qbytes / (qs_ms * 1e-3) / 1e9, 1)},
         "codes_8bit": {"quantize_kernel_ms": round(q8_ms, 4), "decode_attn_ms": round(d8_ms, 4),
@@ -465,6 +559,7 @@ def main():
     del caches, ks, vs, src, dst
     torch.cuda.empty_cache()
     rec["long_context"] = None if args.no_long_context else long_context_leg()
+    rec["burst_32x16k"] = None if args.no_long_context else burst_leg()
     print(json.dumps(rec), flush=True)
 
 

@@ -336,7 +336,8 @@ kvq_status kvq_paged_multi_query_attn(const kvq_config* cfg, const kvq_half* q, 
   const int group = q_heads / kv_heads;
   if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d larger than 16", group);
   const int rb = mq_row_blocks(n_q, group);
-  if (num_seqs > 65535 || (long)kv_heads * rb > 65535 || (long)num_seqs * n_q * q_heads > 2147483647L)
+  if (num_seqs > 65535 || (long)kv_heads * rb * num_seqs > 2147483647L ||
+      (long)num_seqs * n_q * q_heads > 2147483647L)
     return fail(KVQ_ERR_ARG, "too many heads, queries or sequences");
   const int tile = cfg->tile_tokens;
   const long need_blocks = (long)((max_seq_len + tile - 1) / tile) * (tile / kvq::kPage);

@@ -88,7 +88,7 @@ hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hip
 hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
     return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
-        dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
+        dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
         const QuantArgs q{};
         if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false>), grid, dim3(64 * kWaves), 0, s, a, q);
         else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false>), grid, dim3(64 * kWaves), 0, s, a, q);
@@ -104,7 +104,7 @@ hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int til
                                 hipStream_t s) {
   return by_tile(tile, [&](auto T) {
     return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
-        dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
+        dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
         if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, true>), grid, dim3(64 * kWaves), 0, s, a, q);
         else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, true>), grid, dim3(64 * kWaves), 0, s, a, q);
         else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, true>), grid, dim3(64 * kWaves), 0, s, a, q);

@@ -253,9 +253,14 @@ struct alignas(16) DecodeSmemU {
 // pages only the last partition of each (sequence, kv head) reads, so that
 // workgroup does it first (K and V tiles side by side, 2T threads each) and
 // the write-to-read order stays inside one workgroup.
+// Grid: x = kv head + kv_heads * (row block + blocks * sequence), y =
+// partition.  The partition index varies slowest, so the short last
+// partitions of every (sequence, kv head) are dispatched after the full ones
+// and do not hold back full ones behind them when the grid exceeds what the
+// chip holds at once.
 // MQ: several queries per sequence (A.n_q of them, the newest cached tokens);
-// blockIdx.y = kv head + kv_heads * (block of NH rows), row r = query
-// r / G, head r % G, and query i sees the tokens before L - n_q + i + 1.
+// row blocks of NH rows, row r = query r / G, head r % G, and query i sees
+// the tokens before L - n_q + i + 1.
 template <int T, int BK, int BV, int HG, bool FUSED, bool MQ = false>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, QuantArgs Q) {
   constexpr int NH = 4 * HG;
@@ -284,9 +289,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
   const int lane = threadIdx.x & 63;
   const int bq = lane >> 2, iq = lane & 3;       // MFMA block and row/column of this lane
   const int H = A.kv_heads;
-  const int part = blockIdx.x, kvh = MQ ? (int)blockIdx.y % H : (int)blockIdx.y, seq = blockIdx.z;
   const int G = A.group;
-  const int r0 = MQ ? ((int)blockIdx.y / H) * NH : 0;   // first query row of this workgroup
+  const int RB = MQ ? (A.n_q * G + NH - 1) / NH : 1;     // row blocks per (sequence, kv head)
+  const int part = blockIdx.y;
+  const int seq = (int)blockIdx.x / (H * RB);
+  const int hb = (int)blockIdx.x - seq * H * RB;
+  const int kvh = hb % H;
+  const int r0 = MQ ? (hb / H) * NH : 0;                  // first query row of this workgroup
   const int nrows = MQ ? min(NH, A.n_q * G - r0) : G;   // its real rows
   const int L = A.seq_lens[seq] + (FUSED ? 1 : 0);
   const int nchunks = min((L + kChunk - 1) / kChunk, A.max_tiles);

@@ -20,10 +20,10 @@ hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bit
       // 4 x 16K, 8 kv / 32 query heads: 97 us against 67 us), as did blocks
       // of 4 (88 us)
       if (rows <= 4) {
-        dim3 grid(a.max_parts, a.kv_heads, a.num_seqs);
+        dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
         hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false, true>), grid, dim3(64 * kWaves), 0, s, a, q);
       } else {
-        dim3 grid(a.max_parts, a.kv_heads * ((rows + 7) / 8), a.num_seqs);
+        dim3 grid(a.kv_heads * ((rows + 7) / 8) * a.num_seqs, a.max_parts);
         hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false, true>), grid, dim3(64 * kWaves), 0, s, a, q);
       }
       hipError_t e = hipGetLastError();
