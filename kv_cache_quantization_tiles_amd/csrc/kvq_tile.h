@@ -50,10 +50,15 @@ typedef float qt_f32x4 __attribute__((ext_vector_type(4)));
 
 // Shared memory of one workgroup.  Per-channel arrays marked "lane order"
 // keep channel j + 16 m at index 8 j + m (a lane's 8 channels side by side).
+// Partial sums are laid out so that the 16 lanes of a row group write to
+// distinct banks: channel step [row][half h][j][4] (channels j + 16 (4h + m)),
+// token step and row min / max [j][token] with rows of T + 4 floats.
+template <int T>
+constexpr int kRedStride = T + 4;
 template <int T>
 struct alignas(16) Smem {
-  float red[2][16 * T];   // partial sums (channel step: [s][row 4w+g][lane order];
-                          // token step and row min / max: [s][j][token])
+  float red[2][16 * kRedStride<T>];   // partial sums (channel step: [s][row 4w+g][h][j][4];
+                                      // token step and row min / max: [s][j][token])
   float a[kHeadDim];      // 1/alpha in unnormalized units (lane order)
   float alpha[kHeadDim];  // channel factors, normalized units (natural order)
   float ref_c[kHeadDim];  // R of the tile's first token (lane order)
@@ -255,20 +260,21 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
           s2[m] = __builtin_fmaf(d, d, s2[m]);
         }
       }
-      float* p1 = red0 + (4 * w + g) * kHeadDim + 8 * j;
-      float* p2 = red1 + (4 * w + g) * kHeadDim + 8 * j;
+      float* p1 = red0 + (4 * w + g) * kHeadDim + 4 * j;
+      float* p2 = red1 + (4 * w + g) * kHeadDim + 4 * j;
       *reinterpret_cast<qt_f32x4*>(p1) = qt_f32x4{s1[0], s1[1], s1[2], s1[3]};
-      *reinterpret_cast<qt_f32x4*>(p1 + 4) = qt_f32x4{s1[4], s1[5], s1[6], s1[7]};
+      *reinterpret_cast<qt_f32x4*>(p1 + 64) = qt_f32x4{s1[4], s1[5], s1[6], s1[7]};
       *reinterpret_cast<qt_f32x4*>(p2) = qt_f32x4{s2[0], s2[1], s2[2], s2[3]};
-      *reinterpret_cast<qt_f32x4*>(p2 + 4) = qt_f32x4{s2[4], s2[5], s2[6], s2[7]};
+      *reinterpret_cast<qt_f32x4*>(p2 + 64) = qt_f32x4{s2[4], s2[5], s2[6], s2[7]};
     }
     __syncthreads();
     for (int i = tid; i < kHeadDim; i += NT) {   // lane-order index i: channel (i >> 3) + 16 (i & 7)
       float S1 = 0.f, S2 = 0.f;
+      const int at = 64 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);   // its place in a row of partials
 #pragma unroll
       for (int row = 0; row < T / 8; ++row) {
-        S1 += red0[row * kHeadDim + i];
-        S2 += red1[row * kHeadDim + i];
+        S1 += red0[row * kHeadDim + at];
+        S2 += red1[row * kHeadDim + at];
       }
       // copies of row 0 each added row 0's own shifted value rho (the fma
       // residual of the shift); take them out
@@ -319,18 +325,18 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         t1[q] = x1;
         t2[q] = x2;
       }
-      *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(0)]) = qt_f32x4{t1[0], t1[1], t1[2], t1[3]};
-      *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(4)]) = qt_f32x4{t1[4], t1[5], t1[6], t1[7]};
-      *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(0)]) = qt_f32x4{t2[0], t2[1], t2[2], t2[3]};
-      *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(4)]) = qt_f32x4{t2[4], t2[5], t2[6], t2[7]};
+      *reinterpret_cast<qt_f32x4*>(&red0[j * kRedStride<T> + tok(0)]) = qt_f32x4{t1[0], t1[1], t1[2], t1[3]};
+      *reinterpret_cast<qt_f32x4*>(&red0[j * kRedStride<T> + tok(4)]) = qt_f32x4{t1[4], t1[5], t1[6], t1[7]};
+      *reinterpret_cast<qt_f32x4*>(&red1[j * kRedStride<T> + tok(0)]) = qt_f32x4{t2[0], t2[1], t2[2], t2[3]};
+      *reinterpret_cast<qt_f32x4*>(&red1[j * kRedStride<T> + tok(4)]) = qt_f32x4{t2[4], t2[5], t2[6], t2[7]};
     }
     __syncthreads();
     if (tid < T) {
       float T1 = 0.f, T2 = 0.f;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        T1 += red0[jj * T + tid];
-        T2 += red1[jj * T + tid];
+        T1 += red0[jj * kRedStride<T> + tid];
+        T2 += red1[jj * kRedStride<T> + tid];
       }
       const float mn = T1 * (1.0f / kHeadDim);
       const float var = fmaxf(__builtin_fmaf(-mn, mn, T2 * (1.0f / kHeadDim)), 0.f);
@@ -367,10 +373,10 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
       zmin[q] = mn;
       zmax[q] = mx;
     }
-    *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(0)]) = qt_f32x4{zmin[0], zmin[1], zmin[2], zmin[3]};
-    *reinterpret_cast<qt_f32x4*>(&red0[j * T + tok(4)]) = qt_f32x4{zmin[4], zmin[5], zmin[6], zmin[7]};
-    *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(0)]) = qt_f32x4{zmax[0], zmax[1], zmax[2], zmax[3]};
-    *reinterpret_cast<qt_f32x4*>(&red1[j * T + tok(4)]) = qt_f32x4{zmax[4], zmax[5], zmax[6], zmax[7]};
+    *reinterpret_cast<qt_f32x4*>(&red0[j * kRedStride<T> + tok(0)]) = qt_f32x4{zmin[0], zmin[1], zmin[2], zmin[3]};
+    *reinterpret_cast<qt_f32x4*>(&red0[j * kRedStride<T> + tok(4)]) = qt_f32x4{zmin[4], zmin[5], zmin[6], zmin[7]};
+    *reinterpret_cast<qt_f32x4*>(&red1[j * kRedStride<T> + tok(0)]) = qt_f32x4{zmax[0], zmax[1], zmax[2], zmax[3]};
+    *reinterpret_cast<qt_f32x4*>(&red1[j * kRedStride<T> + tok(4)]) = qt_f32x4{zmax[4], zmax[5], zmax[6], zmax[7]};
   }
   __syncthreads();
 
@@ -391,8 +397,8 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     float mn = red0[tid], mx = red1[tid];
 #pragma unroll
     for (int jj = 1; jj < 16; ++jj) {
-      mn = fminf(mn, red0[jj * T + tid]);
-      mx = fmaxf(mx, red1[jj * T + tid]);
+      mn = fminf(mn, red0[jj * kRedStride<T> + tid]);
+      mx = fmaxf(mx, red1[jj * kRedStride<T> + tid]);
     }
     float step = 0.f, off = 0.f, inv = 0.f, nmi = 0.f;
     if (tid < n_valid) {
