@@ -449,6 +449,14 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     }
   }
 
+  // the slots of the lane's two pages (its tokens 32 w + 16 bb + ...), taken
+  // once: the byte stores below could alias the block table, so an address
+  // formed per store would reload the page id from memory each time
+  uint8_t* lane_slot[2] = {nullptr, nullptr};
+  if (MODE != kDense) {
+    lane_slot[0] = slot_ptr(2 * w);
+    lane_slot[1] = slot_ptr(2 * w + 1);
+  }
   if (MODE == kDense || !VLAYOUT) {
     // unit j of each of the lane's tokens: field m <- channel j + 16 m
     // (a unit is BITS bytes: half a word at 2 bits, a word at 4, two words at 8)
@@ -459,7 +467,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
       uint8_t* dst;
       if (MODE == kDense) dst = A.codes + ((size_t)(t0 + t) * H + head) * (kHeadDim * BITS / 8) + BITS * j;
       else   // K slot: 4 blocks of 4 units (4 BITS bytes per token), token after token
-        dst = slot_ptr(t / kPage) + (j >> 2) * (kPage * 4 * BITS) + (t % kPage) * (4 * BITS) + BITS * (j & 3);
+        dst = lane_slot[q >> 2] + (j >> 2) * (kPage * 4 * BITS) + (t % kPage) * (4 * BITS) + BITS * (j & 3);
       if constexpr (BITS == 8) {
         const float lo[4] = {R[q][0], R[q][1], R[q][2], R[q][3]};
         const float hi[4] = {R[q][4], R[q][5], R[q][6], R[q][7]};
@@ -475,7 +483,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     // channel half h, field (r >> 1) + 2 (r & 1) for token 4g + r
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      uint8_t* slot = slot_ptr(2 * w + bb);
+      uint8_t* slot = lane_slot[bb];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         unsigned wd[2];
@@ -498,7 +506,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     constexpr int F = 32 / BITS;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      uint8_t* slot = slot_ptr(2 * w + bb);
+      uint8_t* slot = lane_slot[bb];
       unsigned part[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
