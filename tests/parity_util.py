@@ -78,7 +78,9 @@ def assert_dequant(gpu, ref, what="", rtol=DEQ_RTOL):
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {int(bad.sum())} restored values off, e.g. {tuple(i)} "
                              f"gpu {gpu[tuple(i)]} ref {ref[tuple(i)]}")
-    return float((np.abs(gpu - ref) / np.maximum(np.abs(ref), rms)).max())
+    den = np.broadcast_to(np.maximum(np.abs(ref), rms), ref.shape)
+    ratio = np.divide(np.abs(gpu - ref), den, out=np.zeros(ref.shape), where=den > 0)   # all-zero rows: exact
+    return float(ratio.max()) if ratio.size else 0.0
 
 
 def attn_tol(scale=None):

@@ -783,3 +783,71 @@ def test_full_size_mixed_64_seqs_1k_32k_sampled():
                                        orc.dequantize_tile, f"mixed-64 last tile s{s} h{h} {role}")
     _sampled_decode_checks(wl, q, table, lens + 1, gpk, gpv, got,
                            [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 5), (37, 7)], "mixed-64 decode")
+
+
+def _degenerate_inputs(wl):
+    """K and V with the method's degenerate tiles in sequence 1 (tile 64):
+    tile 0 all zero, tile 1 one row repeated, tile 2 rows constant across
+    channels, tile 3 a channel riding on an offset 100x its spread, tile 4 one
+    row 1000x the others; sequence 0 is empty and sequence 2 random."""
+    k, v = inputs.gen_kv(wl, "K").astype(np.float64), inputs.gen_kv(wl, "V").astype(np.float64)
+    cu = wl.cu_seqlens()
+    rng = np.random.default_rng(7)
+    for x in (k, v):
+        b = cu[1]
+        x[b:b + 64] = 0.0
+        x[b + 64:b + 128] = x[b + 64]
+        x[b + 128:b + 192] = rng.standard_normal((64, x.shape[1], 1))
+        x[b + 192:b + 256, :, 5] += 100.0
+        x[b + 300] *= 1000.0
+    return np.clip(k, -65504, 65504).astype(np.float16), np.clip(v, -65504, 65504).astype(np.float16)
+
+
+def test_degenerate_tiles_and_empty_sequence():
+    wl = _paged_workload(2, (0, 320, 77), 2, 8, 64, 4, 4, 3)
+    k, v = _degenerate_inputs(wl)
+    table, npages = inputs.block_table(wl)
+    cfg = api.config(64, 4, 4, 3)
+    cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+    cache.quantize_prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                           torch.from_numpy(wl.cu_seqlens()).cuda(), max(wl.seq_lens))
+    torch.cuda.synchronize()
+    ref_pk, ref_pv = orc.new_pool(npages, wl.hkv, 4, 64), orc.new_pool(npages, wl.hkv, 4, 64)
+    stg_k = np.zeros((wl.num_seqs, 64, wl.hkv, 128), np.float16)
+    stg_v = np.zeros_like(stg_k)
+    pre = orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, 64, 4, 4, 3, ref_pk, ref_pv, stg_k, stg_v)
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    tot = [0, 0, 0]
+    for s in (1, 2):
+        for h in range(wl.hkv):
+            for role, bits, gp, rp in (("K", 4, gpk, ref_pk), ("V", 4, gpv, ref_pv)):
+                n = wl.seq_lens[s]
+                _, gc, ga, gs, go = orc.read_sequence(gp, table[s], n, h, role, bits, 64)
+                _, rc, ra, rs, ro = orc.read_sequence(rp, table[s], n, h, role, bits, 64)
+                c = pu.compare_codes(gc, rc, pre[(s, h, role)], f"degenerate s{s} h{h} {role}")
+                tot = [a + b for a, b in zip(tot, c)]
+                for j in range(ga.shape[0]):
+                    sl = slice(j * 64, min(n, (j + 1) * 64))
+                    pu.check_tile_metadata(rc[sl], ga[j], gs[sl], go[sl], ra[j], rs[sl], ro[sl],
+                                           orc.dequantize_tile, f"degenerate s{s} h{h} {role} tile{j}")
+    _report("degenerate tiles", tot)
+    # the all-zero tile stores zero codes, zero scales and offsets and unit channel factors
+    _, zc, za, zs, zo = orc.read_sequence(gpk, table[1], 64, 0, "K", 4, 64)
+    assert not zc.any() and not zs.any() and not zo.any() and np.all(za == 1.0)
+    # decode: the empty sequence gives a zero row, the others match the oracle
+    lens = np.array(wl.seq_lens, np.int32)
+    q = inputs.gen_q(wl)
+    out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(lens).cuda(), max(wl.seq_lens)).cpu().numpy()
+    assert not out[0].any()
+    ref, sc = orc.paged_decode_attn(q[1:], table[1:], lens[1:], gpk, gpv, 64, 4, 4, return_scale=True)
+    pu.assert_attn(out[1:], ref, "degenerate decode", sc)
+    # one fused append + decode step: the empty sequence now holds one token
+    kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
+    out1 = cache.append_decode(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens).cuda(),
+                               torch.from_numpy(q).cuda(), max(wl.seq_lens) + 1).cpu().numpy()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    ref1, sc1 = orc.paged_decode_attn(q, table, lens + 1, gpk, gpv, 64, 4, 4, return_scale=True)
+    pu.assert_attn(out1, ref1, "degenerate fused step", sc1)
+    one = orc.quantize_tile(kn[0, 0][None], 4, 3)
+    _, gc, ga, gs, go = orc.read_sequence(gpk, table[0], 1, 0, "K", 4, 64)
+    pu.compare_codes(gc, one.codes, one.pre, "appended token of the empty sequence")
