@@ -46,6 +46,7 @@ DENSE_CASES = [
     (64, 8, 3, 1000, 2, 2),     # 8-bit codes, ragged tail
     (32, 8, 5, 77, 3, 5),       # 8-bit, heavy-tailed K
     (128, 8, 0, 129, 1, 2),     # 8-bit, no normalization, one-row last tile
+    (64, 4, 16, 200, 2, 5),     # the largest iteration count, heavy-tailed K
 ]
 
 
