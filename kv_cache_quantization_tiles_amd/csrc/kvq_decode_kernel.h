@@ -171,22 +171,37 @@ __device__ __forceinline__ void split_grid(float x0, float x1, float m0, float m
 }
 constexpr float kGrid = 12582912.f;   // 1.5 * 2^23
 
+// Another lane's value through a DPP permutation of the VALU operand (no LDS
+// round trip): quad_perm [1,0,3,2] is lane ^ 1 and [2,3,0,1] lane ^ 2;
+// row_half_mirror is 7 - lane within each 8, row_mirror 15 - lane within each
+// 16 (on values already equal within each quad, resp. each 8, these pair the
+// same groups as lane ^ 4 and lane ^ 8); row_ror:n is lane - n within each 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140, kRor4 = 0x124, kRor8 = 0x128;
+
 __device__ __forceinline__ float wave_max(float v) {
-  v = vmax(v, lane_xor<1>(v));
-  v = vmax(v, lane_xor<2>(v));
-  v = vmax(v, lane_xor<4>(v));
-  v = vmax(v, lane_xor<8>(v));
+  v = vmax(v, dpp<kXor1>(v));
+  v = vmax(v, dpp<kXor2>(v));
+  v = vmax(v, dpp<kHalfMirror>(v));
+  v = vmax(v, dpp<kMirror>(v));
   return group_max(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-  v += lane_xor<1>(v);
-  v += lane_xor<2>(v);
-  v += lane_xor<4>(v);
-  v += lane_xor<8>(v);
+  v += dpp<kXor1>(v);
+  v += dpp<kXor2>(v);
+  v += dpp<kHalfMirror>(v);
+  v += dpp<kMirror>(v);
   return group_sum(v);
 }
 // Sum / max over the lanes of one MFMA row index i = lane & 3 within groups of
-// NB blocks (NB = 8: each 32-lane half; NB = 16: the wave).
+// NB blocks (NB = 8: each 32-lane half; NB = 16: the wave).  The sum keeps the
+// xor pairing (lane ^ 4, then ^ 8, ^ 16, ^ 32): the query sum it forms meets a
+// term it nearly cancels in short heavy-tailed tiles, where a different
+// association of the same terms was measurably less accurate.  The max is
+// exact in any order: two rotations cover the 4 lanes of the class in each 16.
 template <int NB>
 __device__ __forceinline__ float blocks_sum(float v) {
   v += lane_xor<4>(v);
@@ -197,10 +212,10 @@ __device__ __forceinline__ float blocks_sum(float v) {
 }
 template <int NB>
 __device__ __forceinline__ float blocks_max(float v) {
-  v = vmax(v, lane_xor<4>(v));
-  v = vmax(v, lane_xor<8>(v));
-  v = vmax(v, lane_xor<16>(v));
-  if (NB == 16) v = vmax(v, xor32(v));
+  v = vmax(v, dpp<kRor4>(v));
+  v = vmax(v, dpp<kRor8>(v));
+  v = max16(v);
+  if (NB == 16) v = max32(v);
   return v;
 }
 
