@@ -316,6 +316,61 @@ def burst_leg():
                     "slot bytes at the middle step's lengths"}
 
 
+def mixed_leg(n_iter: int = 10):
+    """The mixed-precision stress workload: 64 sequences of 1K-32K tokens
+    (seeded lengths), 8 kv / 64 query heads, heavy-tailed K (Student-t(3) times
+    log-uniform channel scales), tile 32, 4-bit K / 2-bit V, 5 iterations:
+    quantize the prefill, then one fused append + decode step.  Inputs drawn on
+    the device."""
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+
+    wl = inputs.workload(5)
+    dev = torch.device("cuda:0")
+    table, npages = inputs.block_table(wl)
+    max_len = max(wl.seq_lens)
+    cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+    k = inputs.gen_kv_device(wl, "K", device=dev)
+    v = inputs.gen_kv_device(wl, "V", device=dev)
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(2)]
+    kn = torch.from_numpy(inputs.gen_decode_kv(wl, "K", 0)).to(dev)
+    vn = torch.from_numpy(inputs.gen_decode_kv(wl, "V", 0)).to(dev)
+    q = torch.from_numpy(inputs.gen_q(wl)).to(dev)
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+    ws = caches[0].workspace(wl.hq, max_len + 1)
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    q_ms = timed(lambda i: caches[i % 2].quantize_prefill(k, v, cu, max_len), 4)
+    for c in caches:
+        c.quantize_prefill(k, v, cu, max_len)
+    # the append re-quantizes the same tile each time (lengths are not advanced)
+    d_ms = timed(lambda i: caches[i % 2].append_decode(kn, vn, lens, q, max_len + 1, out=out, workspace=ws), n_iter)
+    th = wl.total_tokens * wl.hkv
+    qbytes = quantize_bytes(th, wl.bits_k, wl.tile_tokens) + quantize_bytes(th, wl.bits_v, wl.tile_tokens)
+    dbytes = decode_bytes(wl, [l + 1 for l in wl.seq_lens])
+    del caches, k, v
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "num_seqs": wl.num_seqs, "tokens": wl.total_tokens, "kv_heads": wl.hkv,
+            "q_heads": wl.hq, "tile_tokens": wl.tile_tokens, "bits_k": wl.bits_k, "bits_v": wl.bits_v,
+            "iters": wl.iters,
+            "quantize_prefill_ms": round(q_ms, 4), "quantize_GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            "quantize_hbm_frac": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "decode_step_ms": round(d_ms, 4), "decode_tok_per_s": round(wl.num_seqs / (d_ms * 1e-3), 1),
+            "decode_slot_GBps": round(dbytes / (d_ms * 1e-3) / 1e9, 1),
+            "decode_hbm_frac": round(dbytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 # ----------------------------------------------------------------------------- GPU leg
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -326,7 +381,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the fp16 / fp8 / 4-bit / 2-bit comparison at 6 x 128K and the 32 x 16K burst")
+                    help="skip the fp16 / fp8 / 4-bit / 2-bit comparison at 6 x 128K, the 32 x 16K burst and the mixed-length leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards "
@@ -560,6 +615,7 @@ def main():
     torch.cuda.empty_cache()
     rec["long_context"] = None if args.no_long_context else long_context_leg()
     rec["burst_32x16k"] = None if args.no_long_context else burst_leg()
+    rec["mixed_64seq"] = None if args.no_long_context else mixed_leg()
     print(json.dumps(rec), flush=True)
 
 
