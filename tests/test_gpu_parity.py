@@ -852,3 +852,22 @@ def test_degenerate_tiles_and_empty_sequence():
     one = orc.quantize_tile(kn[0, 0][None], 4, 3)
     _, gc, ga, gs, go = orc.read_sequence(gpk, table[0], 1, 0, "K", 4, 64)
     pu.compare_codes(gc, one.codes, one.pre, "appended token of the empty sequence")
+
+
+@pytest.mark.parametrize("case", [(2, (300, 97, 33), 2, 8, 64, 4, 4, 3, 5, 4), (5, (200, 70), 1, 8, 32, 4, 2, 5, 3, 5)])
+def test_multi_query_with_randomized_rotation(case):
+    """Several causal queries per sequence over pages quantized with a random
+    sign mask: the query takes the signs before H and the output after it."""
+    recipe, lens, hkv, hq, tile, bk, bv, iters, n_q, seed = case
+    mask = inputs.hadamard_signs(seed)
+    wl = _paged_workload(recipe, lens, hkv, hq, tile, bk, bv, iters)
+    _, _, table, _, cache = _gpu_prefill(wl, signs=mask)
+    q = inputs.gen_q_multi(wl, n_q)
+    seq_lens = np.array(wl.seq_lens, np.int32)
+    out = cache.multi_query(torch.from_numpy(q).cuda(), torch.from_numpy(seq_lens).cuda(), max(lens)).cpu().numpy()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    ref, sc = orc.paged_multi_query_attn(q, table, seq_lens, gpk, gpv, tile, bk, bv, return_scale=True, signs=mask)
+    err = pu.assert_attn(out, ref, f"signed multi-query {case}", sc)
+    plain = orc.paged_multi_query_attn(q, table, seq_lens, gpk, gpv, tile, bk, bv)
+    assert np.abs(plain - ref).max() > 1e-2   # the mask is in effect
+    print(f"[attn] signed multi-query {case}: max abs err {err:.2e}", flush=True)
