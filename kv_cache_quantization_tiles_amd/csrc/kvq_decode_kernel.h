@@ -317,6 +317,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
   const int c_begin = part * A.tiles_per_part;
   const int c_end = min(nchunks, c_begin + A.tiles_per_part);
   if (c_begin >= c_end) return;  // uniform over the workgroup
+  // the query rows wave 0 folds below, loaded first so that their memory
+  // latency overlaps that of the block table and the first chunk
+  u32x4 qraw[4];
+  if (wave == 0) {
+    const int n16 = lane & 15, grp = lane >> 4;
+    const bool real = n16 < nrows;
+    size_t qix;
+    if constexpr (MQ) {
+      const int r = r0 + (real ? n16 : 0);
+      qix = ((size_t)seq * A.n_q + r / G) * A.q_heads + kvh * G + r % G;
+    } else {
+      qix = (size_t)seq * A.q_heads + kvh * G + (real ? n16 : 0);
+    }
+    const uint16_t* qrow = A.q + qix * kHeadDim + 32 * grp;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      qraw[v] = real ? *reinterpret_cast<const u32x4*>(qrow + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+  }
   // MQ: tokens visible to row h (causal: up to its query's position)
   int vis[MQ ? NH : 1];
   if constexpr (MQ) {
@@ -446,19 +464,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
   // stored divided by the weight of channel c's K code field (a power of two)
   if (wave == 0) {
     const int n16 = lane & 15, grp = lane >> 4;
-    const bool real = n16 < nrows;
     float hq[32];
-    size_t qix;
-    if constexpr (MQ) {
-      const int r = r0 + (real ? n16 : 0);
-      qix = ((size_t)seq * A.n_q + r / G) * A.q_heads + kvh * G + r % G;
-    } else {
-      qix = (size_t)seq * A.q_heads + kvh * G + (real ? n16 : 0);
-    }
-    const uint16_t* qrow = A.q + qix * kHeadDim + 32 * grp;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      u32x4 w = real ? *reinterpret_cast<const u32x4*>(qrow + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 w = qraw[v];
       // randomized rotation: q's channels take the signs before H (keys are H s k)
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] ^= sign_pair_mask(A.signs, 32 * grp + 8 * v, i);
