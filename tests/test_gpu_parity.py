@@ -633,6 +633,8 @@ MQ_CASES = [
     (2, (700, 100), 2, 8, 64, 8, 8, 3, 4),               # 8-bit codes
     (2, (400, 300), 1, 4, 64, 4, 4, 3, 70),              # a 70-token chunk: the mask spans two chunks
     (2, (100, 3), 1, 4, 64, 4, 4, 3, 6),                 # a sequence shorter than n_q: zero rows
+    (2, (900, 300), 1, 16, 128, 8, 8, 3, 2),             # 8-bit, tile 128, G = 16: 32 rows in 4 blocks
+    (5, (300, 65), 2, 8, 32, 8, 8, 5, 5),                # 8-bit, tile 32, heavy-tailed K, 20 rows
 ]
 
 
