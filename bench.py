@@ -371,6 +371,73 @@ def mixed_leg(n_iter: int = 10):
             "decode_hbm_frac": round(dbytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def context_sweep(contexts=(1024, 4096, 16384, 65536, 131072), num_seqs=6, n_iter=10):
+    """Decode-attention time against context length for one layer of the
+    Qwen3-4B-shaped long-context workload (8 kv / 32 query heads, tile 128):
+    fp16 and fp8 pages, and 4-, 2- and 8-bit quantized pages filled from the
+    same inputs.  One JSON line per context."""
+    import dataclasses
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+
+    dev = torch.device("cuda:0")
+    out_lines = []
+    for ctx in contexts:
+        wl = dataclasses.replace(inputs.workload(4), seq_lens=(ctx,) * num_seqs, layers=1)
+        table, npages = inputs.block_table(wl, capacity_tokens=ctx)
+        lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+        cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+        q = torch.from_numpy(inputs.gen_q(wl)).to(dev)
+        out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+        k = inputs.gen_kv_device(wl, "K", device=dev)
+        v = inputs.gen_kv_device(wl, "V", device=dev)
+        copies = max(2, int(math.ceil(1.0e9 / (wl.total_tokens * wl.hkv * 512))))   # >= 1 GB of fp16 pools
+        rec = {"context": ctx, "num_seqs": num_seqs, "modes": {}}
+        for name in ("fp16", "fp8", "kvq4", "kvq2", "kvq8"):
+            if name in ("fp16", "fp8"):
+                fp8 = name == "fp8"
+                ks = float(k.abs().max()) / 448.0 if fp8 else 1.0
+                vs = float(v.abs().max()) / 448.0 if fp8 else 1.0
+                caches = [api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs, fp8, ks, vs)
+                          for _ in range(copies)]
+                for c in caches:
+                    c.fill(k, v, cu, ctx)
+                per_tok = 2 * 128 * (1 if fp8 else 2)
+            else:
+                bits = int(name[3:])
+                cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
+                caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+                          for _ in range(copies)]
+                for c in caches:
+                    c.quantize_prefill(k, v, cu, ctx)
+                per_tok = 2 * slot_bytes_per_token(bits, wl.tile_tokens)
+            ws = caches[0].workspace(wl.hq, ctx)
+            for i in range(2):
+                caches[i % copies].decode(q, lens, ctx, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(n_iter):
+                caches[i % copies].decode(q, lens, ctx, out=out, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n_iter
+            byts = wl.total_tokens * wl.hkv * per_tok
+            rec["modes"][name] = {"decode_attn_us": round(ms * 1e3, 2),
+                                  "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                                  "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            del caches, ws
+            torch.cuda.empty_cache()
+        base = rec["modes"]["fp16"]["decode_attn_us"]
+        for m in rec["modes"].values():
+            m["speedup_vs_fp16"] = round(base / m["decode_attn_us"], 3)
+        del k, v
+        torch.cuda.empty_cache()
+        print(json.dumps(rec), flush=True)
+        out_lines.append(rec)
+    return out_lines
+
+
 # ----------------------------------------------------------------------------- GPU leg
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -382,11 +449,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the fp16 / fp8 / 4-bit / 2-bit comparison at 6 x 128K, the 32 x 16K burst and the mixed-length leg")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print decode-attention time against context length (fp16, fp8, 4-, 2-, 8-bit pages) "
+                         "instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards "
               "without communication, see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        import torch
+        torch.cuda.set_device(0)
+        context_sweep()
+        return
     wl = inputs.workload(args.workload)
     if wl.layers != 1:
         raise SystemExit("multi-layer workloads are not bench lines")
