@@ -258,7 +258,7 @@ struct alignas(16) DecodeSmemU {
   static constexpr int QG = FUSED ? (64 * kWaves) / (2 * T) : 0;
   union {
     DecodeSmem<T, HG> dec;
-    Smem<T> q[QG > 0 ? QG : 1];
+    std::conditional_t<FUSED, TileSmem<T>, char> q[QG > 0 ? QG : 1];   // (the append's buffers)
   };
 };
 
@@ -348,15 +348,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, Quant
         constexpr int QG = DecodeSmemU<T, HG, FUSED>::QG;
         const int g = threadIdx.x / (2 * T), tid = threadIdx.x % (2 * T);
         if constexpr (QG == 1) {
-          quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[0], 0, kvh, seq, tile_idx, tid);
+          quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[0].f, &smu.q[0].s, 0, kvh, seq, tile_idx, tid);
           __syncthreads();
-          quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[0], 1, kvh, seq, tile_idx, tid);
+          quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[0].f, &smu.q[0].s, 1, kvh, seq, tile_idx, tid);
         } else {
           // groups 2j and 2j + 1 quantize K and V; with 4 groups (tile 32) the
           // second pair repeats the first, writing the same bytes, so that every
           // wave meets the quantizer's barriers
-          if ((g & 1) == 0) quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[g], 0, kvh, seq, tile_idx, tid);
-          else quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[g], 1, kvh, seq, tile_idx, tid);
+          if ((g & 1) == 0)
+            quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[g].f, &smu.q[g].s, 0, kvh, seq, tile_idx, tid);
+          else quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[g].f, &smu.q[g].s, 1, kvh, seq, tile_idx, tid);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

@@ -12,6 +12,7 @@ constexpr int kPage = 16;
 // A channel (token) whose spread is at most 1e-2 of its RMS keeps factor 1:
 // var > kGuard2 * meansq  <=>  std > 1e-2 * rms.
 constexpr float kGuard2 = 1e-4f;
+constexpr double kGuard = 1e-2;   // the same test in float64: std > kGuard * rms
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 
 __host__ __device__ constexpr int slot_code_bytes(int bits) { return kPage * kHeadDim * bits / 8; }

@@ -1,32 +1,17 @@
-// Tile quantizer kernels for gfx950: Hadamard rotation along channels, then
-// Sinkhorn-like alternating channel/token variance normalization, then
-// per-token asymmetric round-to-nearest to packed 2- or 4-bit codes.
+// Tile quantizer kernels for gfx950 (the tile body is in kvq_tile.h):
+// Hadamard rotation along channels (one v_mfma_f32_16x16x32_f16 per 16-token
+// block, 32-channel group and sign for channel bits 0..4, a register
+// butterfly for bits 5, 6), Sinkhorn-like alternating channel/token variance
+// normalization on one-pass shifted sums, per-token asymmetric round-to-
+// nearest to packed 2-, 4- or 8-bit codes stored in unit order (dense codes,
+// K slots) or as V runs; tiles of fewer than 16 tokens in float64.  Also the
+// dense restore, the restore into fp16 pages and a copy kernel that
+// calibrates bandwidth and byte counters.
 //
 // Method: page "Huawei's KVarN boosts vLLM KV-cache capacity by 5x without
 // accuracy loss" (axbrief.com), section "기존 방식과 달라진 지점" (the
 // four-step tile quantizer); restore: page "화웨이가 공개한 KVarN" (ttj.kr),
 // section "양자화로 캐시를 다이어트시킨다".
-//
-// One workgroup quantizes one tile of T tokens x 128 channels with 2T
-// threads.  Thread (tq, cg) holds the 4 tokens 4tq..4tq+3 and the 16
-// channels 8cg+j and 64+8cg+j (j < 8) in registers for the whole kernel:
-//   * the fp16 rows are read once (two 16-byte loads per token, the 8 cg
-//     threads of a token covering its 256-byte row);
-//   * the Hadamard butterfly runs 4 stages in registers (channel bits 0,1,2,6)
-//     and 3 stages across the 8 cg lanes with ds_swizzle (channel bits 3,4,5);
-//     it is left unnormalized and the 1/sqrt(128) is folded into the factors;
-//   * the normalization never rewrites the tile: with weights b = 1/beta and
-//     a = 1/alpha, the channel step needs the spread over t of u = b_t R_tc
-//     and the token step that over c of u = a_c R_tc.  Each is one pass of
-//     d = u - ref (ref: the first token's, resp. channel 0's, value of u),
-//     sum d and sum d^2 (three VALU ops per element); the shift keeps
-//     E[d^2] - E[d]^2 accurate when a mean dwarfs the spread.  Partial sums
-//     go through LDS and one thread per channel (token) finalizes the
-//     variance, the guard and the reciprocal std;
-//   * the last token step is skipped: its factor cancels exactly in the
-//     stored scale, offset and codes (rounding is per token row);
-//   * codes: z = R * a, per-row min/max through LDS, v = (z - min) / step,
-//     round half to even, packed and stored straight into the output layout.
 #include "kvq_tile.h"
 
 namespace kvq {
@@ -39,7 +24,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int T, int BITS>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void quantize_dense_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
-  quantize_tile_body<T, BITS, false, kDense>(A, sm, 0, blockIdx.y, 0, blockIdx.x, threadIdx.x);
+  quantize_tile_body<T, BITS, false, kDense>(A, sm, nullptr, 0, blockIdx.y, 0, blockIdx.x, threadIdx.x);
+}
+
+// the last tile of each head's run when it holds fewer than 16 tokens (float64 path)
+template <int T, int BITS>
+__global__ __launch_bounds__(2 * T) void quantize_dense_short_kernel(QuantArgs A) {
+  __shared__ TileSmem<T> sm;
+  quantize_tile_body<T, BITS, false, kDense, kPathShort>(A, sm.f, &sm.s, 0, blockIdx.x, 0, (A.n_tokens - 1) / T,
+                                                         threadIdx.x);
 }
 
 // grid: x = tile index in the sequence, y = head + Hkv * role (0 K, 1 V), z = sequence
@@ -51,19 +44,35 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void
   if ((int)blockIdx.x * T >= len) return;
   const int role = blockIdx.y / A.kv_heads;
   const int head = blockIdx.y % A.kv_heads;
-  if (role == 0) quantize_tile_body<T, BK, false, kPaged>(A, sm, 0, head, seq, blockIdx.x, threadIdx.x);
-  else quantize_tile_body<T, BV, true, kPaged>(A, sm, 1, head, seq, blockIdx.x, threadIdx.x);
+  if (role == 0) quantize_tile_body<T, BK, false, kPaged>(A, sm, nullptr, 0, head, seq, blockIdx.x, threadIdx.x);
+  else quantize_tile_body<T, BV, true, kPaged>(A, sm, nullptr, 1, head, seq, blockIdx.x, threadIdx.x);
+}
+
+// grid: x = head + Hkv * role, y = sequence: the sequence's last tile when it
+// holds fewer than 16 tokens (float64 path)
+template <int T, int BK, int BV>
+__global__ __launch_bounds__(2 * T) void quantize_paged_short_kernel(QuantArgs A) {
+  __shared__ TileSmem<T> sm;
+  const int seq = blockIdx.y;
+  const int len = A.cu_seqlens[seq + 1] - A.cu_seqlens[seq];
+  if (len <= 0) return;
+  const int role = blockIdx.x / A.kv_heads;
+  const int head = blockIdx.x % A.kv_heads;
+  const int tile = (len - 1) / T;
+  if (role == 0) quantize_tile_body<T, BK, false, kPaged, kPathShort>(A, sm.f, &sm.s, 0, head, seq, tile, threadIdx.x);
+  else quantize_tile_body<T, BV, true, kPaged, kPathShort>(A, sm.f, &sm.s, 1, head, seq, tile, threadIdx.x);
 }
 
 // grid: x = head, y = role, z = sequence
 template <int T, int BK, int BV>
-__global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void append_kernel(QuantArgs A) {
-  __shared__ Smem<T> sm;
+__global__ __launch_bounds__(2 * T) void append_kernel(QuantArgs A) {
+  __shared__ TileSmem<T> sm;
   const int seq = blockIdx.z;
   const int tile_idx = A.lens_before[seq] / T;
   if ((tile_idx + 1) * (T / kPage) > A.max_blocks) return;  // no page for this tile
-  if (blockIdx.y == 0) quantize_tile_body<T, BK, false, kAppend>(A, sm, 0, blockIdx.x, seq, tile_idx, threadIdx.x);
-  else quantize_tile_body<T, BV, true, kAppend>(A, sm, 1, blockIdx.x, seq, tile_idx, threadIdx.x);
+  if (blockIdx.y == 0)
+    quantize_tile_body<T, BK, false, kAppend>(A, sm.f, &sm.s, 0, blockIdx.x, seq, tile_idx, threadIdx.x);
+  else quantize_tile_body<T, BV, true, kAppend>(A, sm.f, &sm.s, 1, blockIdx.x, seq, tile_idx, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- dequantize (dense)
@@ -380,6 +389,9 @@ hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStre
     return by_bits(bits, [&](auto B) {
       dim3 grid((a.n_tokens + T() - 1) / T(), a.heads);
       hipLaunchKernelGGL((quantize_dense_kernel<T(), B()>), grid, dim3(2 * T()), 0, s, a);
+      const int tail = a.n_tokens % T();
+      if (tail > 0 && tail < kShortTile)
+        hipLaunchKernelGGL((quantize_dense_short_kernel<T(), B()>), dim3(a.heads), dim3(2 * T()), 0, s, a);
       return hipGetLastError();
     });
   });
@@ -391,6 +403,8 @@ hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int b
     return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
       dim3 grid((max_seq_len + T() - 1) / T(), 2 * a.kv_heads, num_seqs);
       hipLaunchKernelGGL((quantize_paged_kernel<T(), BK(), BV()>), grid, dim3(2 * T()), 0, s, a);
+      hipLaunchKernelGGL((quantize_paged_short_kernel<T(), BK(), BV()>), dim3(2 * a.kv_heads, num_seqs),
+                         dim3(2 * T()), 0, s, a);
       return hipGetLastError();
     });
   });

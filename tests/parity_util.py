@@ -1,29 +1,34 @@
 """Comparison rules of the GPU parity tests (GPU output vs the CPU oracle).
 
 * Codes: bit-exact, except elements whose oracle pre-rounding value lies
-  within WINDOW of a rounding boundary k + 1/2 (the oracle decides in float64,
-  the kernel in float32).  Every mismatch must be in that window; the number of
+  within WINDOW of a rounding boundary k + 1/2 (the oracle decides in float64;
+  the kernel decides in fp32 on tiles of 16 or more tokens and in float64 on
+  shorter ones).  Every mismatch must be in that window; the number of
   elements in the window and the number of mismatches are reported.
-* Channel factors, token scales and offsets: relative error <= META_RTOL.
-  The kernel works in fp32 (eps 6e-8); a spread computed over values whose
-  mean-square is m times their variance carries ~eps*m relative error, and
-  the guard admits m up to 1e4 (spread down to 1% of RMS), so near-degenerate
-  channels of short tiles reach ~1e-4.  Tiles of fewer than SHORT_TILE tokens
-  are worse conditioned still (their spread comes from 1..15 values, and
-  errors compound over the iterations), so their metadata is checked through
-  its effect instead: the oracle's codes restored with the GPU metadata must
-  match the same codes restored with the oracle's metadata within DEQ_RTOL
-  (SHORT_DEQ_RTOL for short tiles: a spread from 2 heavy-tailed values over
-  5 iterations has measured up to ~1e-3 in fp32).
-  The codes check above is the binding one: it fails if a metadata error
-  moves any code outside the window.
+* Channel factors, token scales and offsets: relative error <= META_RTOL on
+  every tile.  On tiles of 16 or more tokens the kernel works in fp32 (eps
+  6e-8); a spread computed over values whose mean-square is m times their
+  variance carries ~eps*m relative error, and the guard admits m up to 1e4
+  (spread down to 1% of RMS), so near-degenerate channels reach ~1e-4.
+  Shorter tiles are quantized in float64 by the kernel, so their metadata
+  agree to fp32 rounding.  The metadata are also checked through their
+  effect: the oracle's codes restored with the GPU metadata must match the
+  same codes restored with the oracle's metadata within DEQ_RTOL.  The codes
+  check above is the binding one: it fails if a metadata error moves any code
+  outside the window.
 * Restored values: |gpu - ref| <= DEQ_RTOL * max(|ref|, rms of the token row).
 * Attention outputs: absolute error <= ATTN_ATOL (fp32 accumulation), plus
-  ATTN_ULPS units of 2^-24 times the output's own scale max_c sum_t p_t |v_t,c|
-  where the oracle supplies it.  For outputs of unit size the second term is
-  negligible; for heavy-tailed values (|v| ~ 1e4, where 2e-3 is about two fp32
-  ulps and plain fp32 attention over the same restored pages already errs by
-  ~1.4e-3) it admits a fixed number of fp32 roundings of that scale.
+  ATTN_ULPS units of 2^-24 times the output's own scale
+  max_c sum_t p_t |v_t,c| over the restored values, where the oracle supplies
+  it.  For outputs of unit size the second term is negligible (~1e-6).  It
+  matters where the method itself restores large values: a tile of two
+  tokens put through 5 normalization iterations and 2-bit rounding (a tail
+  tile of the heavy-tailed workload, one token after the append) restores
+  N(0, 1) values of size ~3 as values up to ~1.5e4 (the oracle's own
+  restore), so attention outputs there reach ~1.3e4 in the oracle itself,
+  where 2e-3 is two fp32 ulps of the output; the kernel, summing fp32 terms
+  of that size, measured 3.1e-3.  The term admits a fixed number of fp32
+  roundings of that scale (0.014 at 1.5e4).
 """
 import numpy as np
 
@@ -32,8 +37,6 @@ META_RTOL = 1e-4
 DEQ_RTOL = 1e-3
 ATTN_ATOL = 2e-3
 ATTN_ULPS = 16
-SHORT_TILE = 16
-SHORT_DEQ_RTOL = 1e-2
 
 
 def near_boundary(pre: np.ndarray) -> np.ndarray:
@@ -84,7 +87,7 @@ def assert_dequant(gpu, ref, what="", rtol=DEQ_RTOL):
 
 
 def attn_tol(scale=None):
-    """Per-row attention tolerance; scale [..., ] as from the oracle's
+    """Per-row attention tolerance; scale [...] as from the oracle's
     attention_abs_scale (None: the absolute bar alone)."""
     if scale is None:
         return ATTN_ATOL
@@ -104,10 +107,8 @@ def assert_attn(gpu, ref, what="", scale=None):
 def check_tile_metadata(codes_ref, ga, gs, go, ra, rs, ro, restore, what=""):
     """Metadata of one tile (alpha [128], scale/offset [n]) per the rules above.
     `restore(codes, alpha, scale, offset)` is the oracle's restore."""
-    n = codes_ref.shape[0]
-    if n >= SHORT_TILE:
-        assert_rel(ga, ra, META_RTOL, f"{what} alpha")
-        assert_rel(gs, rs, META_RTOL, f"{what} scale")
-        assert_rel(go, ro, META_RTOL, f"{what} offset")
+    assert_rel(ga, ra, META_RTOL, f"{what} alpha")
+    assert_rel(gs, rs, META_RTOL, f"{what} scale")
+    assert_rel(go, ro, META_RTOL, f"{what} offset")
     assert_dequant(restore(codes_ref, ga, gs, go), restore(codes_ref, ra, rs, ro), f"{what} metadata effect",
-                   DEQ_RTOL if n >= SHORT_TILE else SHORT_DEQ_RTOL)
+                   DEQ_RTOL)

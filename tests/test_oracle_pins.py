@@ -16,6 +16,7 @@ import scipy.special
 import torch
 
 import oracle as orc
+from oracle import kvq_oracle as orc_impl
 from kv_cache_quantization_tiles_amd import inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -142,6 +143,19 @@ def test_guard_on_repeated_and_zero_rows():
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(alpha)) and np.all(np.isfinite(beta))
     np.testing.assert_array_equal(y[3], 0.0)
     assert beta[3] == 1.0
+
+
+def test_guard_threshold_hand_example():
+    """The guard at 0.5% and 2% of RMS and exactly at the 1% threshold
+    (strictly above keeps the std; at the threshold the factor stays 1)."""
+    g = _golden("guard_threshold.json")
+    r = np.array(g["columns"]["R"], float)
+    _, alpha, _ = orc.sinkhorn(r, 1)
+    np.testing.assert_array_equal(alpha, g["columns"]["alpha"])
+    for case in g["rows"]:
+        _, alpha, beta = orc.sinkhorn(np.array(case["R"], float), 1)
+        np.testing.assert_array_equal(alpha, 1.0)
+        np.testing.assert_array_equal(beta, case["beta"])
 
 
 # ---------------------------------------------------------------- rounding
@@ -321,6 +335,34 @@ def test_slot_sizes(tile):
     assert orc.slot_bytes(8, tile) == 2048 + 128 + 4 * (16 * 128 // tile)
 
 
+def test_slot_metadata_byte_positions_hand_examples():
+    """Scale, offset and channel-factor slice at the byte positions worked by
+    hand (tests/golden/slot_metadata_positions.json), written through the
+    oracle's tile store: the page with index j in its tile holds the slice
+    alpha[j L : (j + 1) L]."""
+    import struct
+    for c in _golden("slot_metadata_positions.json")["cases"]:
+        bits, tile = c["bits"], c["tile"]
+        assert orc.slot_bytes(bits, tile) == c["total"]
+        ppt = tile // 16
+        tq = orc.TileQuant(codes=np.zeros((tile, 128), np.uint8),
+                           alpha=(3000.0 + np.arange(128)).astype(np.float32),
+                           scale=(1000.0 + np.arange(tile)).astype(np.float32),
+                           offset=(2000.0 + np.arange(tile)).astype(np.float32),
+                           pre=None, rotated=None, normalized=None, beta=None)
+        pool = orc.new_pool(ppt + 3, 1, bits, tile)
+        pages = np.array([ppt + 2 - j for j in range(ppt)], np.int32)   # reversed page ids
+        orc_impl._store_tile(pool, pages, 0, "K", bits, tile, 0, tq)
+        for j in range(ppt):
+            raw = pool[pages[j], 0].tobytes()
+            ts, to = c["scale_token"], c["offset_token"]
+            assert struct.unpack_from("<f", raw, c["scale_byte"])[0] == 1000.0 + 16 * j + ts
+            assert struct.unpack_from("<f", raw, c["offset_byte"])[0] == 2000.0 + 16 * j + to
+            for i in (0, c["alpha_len"] - 1):
+                assert struct.unpack_from("<f", raw, c["alpha_byte"] + 4 * i)[0] == 3000.0 + c["alpha_len"] * j + i
+            assert c["alpha_byte"] + 4 * c["alpha_len"] == len(raw)
+
+
 def test_pages_hold_the_same_values_as_dense_layout():
     wl = inputs.workload(1).scaled(seq_len=200)          # ragged: 3 full tiles + 8 rows
     k = inputs.gen_kv(wl, "K")
@@ -395,6 +437,27 @@ def test_attention_degenerate_cases():
     np.testing.assert_allclose(orc.attention(q, rng.standard_normal((1, 128)), v[:1], 0.1), v[0])
     same = np.repeat(rng.standard_normal((1, 128)), 5, axis=0)
     np.testing.assert_allclose(orc.attention(q, same, v, 0.1), v.mean(0), atol=1e-14)
+
+
+def test_two_token_tile_restores_large_values_after_five_iterations():
+    """The premise of the attention bar's ulp term: the method itself (not a
+    kernel) restores a 2-token tile of N(0, 1) values, put through 5
+    normalization iterations and 2-bit rounding, as values tens to thousands
+    of times the data (here up to ~1.4e3; 1.5e4 in the fused-step GPU case),
+    so attention outputs over such a tail tile reach that size and fp32
+    resolves them to ~1e-3.  Inputs: V rows of the heavy-tailed workload's
+    recipe, 2 tokens per tile."""
+    wl = inputs.workload(5).scaled(num_seqs=3, seq_len=98)
+    v = inputs.gen_kv(wl, "V")
+    big = 0.0
+    for s_ in range(wl.num_seqs):
+        for h in range(wl.hkv):
+            x = v[98 * s_ + 96:98 * s_ + 98, h]
+            tq = orc.quantize_tile(x, 2, 5)
+            r = orc.dequantize_tile(tq.codes, tq.alpha, tq.scale, tq.offset)
+            assert np.abs(x.astype(float)).max() < 6.0
+            big = max(big, float(np.abs(r).max()))
+    assert big > 1e3
 
 
 def test_attention_abs_scale_special_cases():
