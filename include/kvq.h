@@ -49,7 +49,9 @@
  *     `cfg` and scalar arguments live on the host.
  *   - The caller owns and allocates every buffer.  The library allocates
  *     nothing, keeps no state between calls except a thread-local error
- *     message, and never synchronizes: each call enqueues its kernels on
+ *     message (and, for kvq_append_and_decode_noalloc, its static device
+ *     scratch and each device's address of it), and never synchronizes: each
+ *     call enqueues its kernels on
  *     `stream` (a hipStream_t passed as void*, NULL = default stream) and
  *     returns.
  *   - Arguments are validated on the host before any launch.  On a non-OK
@@ -246,6 +248,33 @@ kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, c
                                  int32_t max_blocks, void* pool_k, void* pool_v, const kvq_half* q,
                                  int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_append_and_decode_noalloc - kvq_append_and_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors as kvq_append_and_decode (bit-identical pages, staging rows and
+ * output), without the workspace arguments: the partition partials go to a
+ * static device array of the library, KVQ_NOALLOC_SCRATCH_BYTES per GPU,
+ * which each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing.
+ *   - The stream must belong to the current device (KVQ_ERR_ARG otherwise);
+ *     the first call on a device looks up that device's copy of the array.
+ *   - KVQ_ERR_WORKSPACE if kvq_decode_workspace_bytes() of these sizes
+ *     exceeds KVQ_NOALLOC_SCRATCH_BYTES (checked on the host before any
+ *     device call).
+ *   - All calls on one GPU share its array: calls that overlap on one GPU
+ *     (on different streams, or from several threads without ordering)
+ *     race on it.  Calls ordered on one stream are safe; each leaves its
+ *     partials behind, and none needs the array cleared.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvq_status kvq_append_and_decode_noalloc(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                         const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                         kvq_half* staging_k, kvq_half* staging_v, const int32_t* block_table,
+                                         int32_t max_blocks, void* pool_k, void* pool_v, const kvq_half* q,
+                                         int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
+                                         void* stream);
 
 /* Bytes of workspace kvq_paged_multi_query_attn needs for these sizes (0 for
  * invalid sizes, n_q > max_seq_len included). */

@@ -21,8 +21,10 @@ EXPORTED = (
     "kvq_paged_decode_attn", "kvq_bandwidth_probe", "kvq_baseline_page_bytes", "kvq_fill_pages_fp16",
     "kvq_fill_pages_fp8", "kvq_baseline_workspace_bytes", "kvq_paged_decode_attn_fp16",
     "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages",
-    "kvq_multi_query_workspace_bytes", "kvq_paged_multi_query_attn",
+    "kvq_multi_query_workspace_bytes", "kvq_paged_multi_query_attn", "kvq_append_and_decode_noalloc",
 )
+
+KVQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class KvqConfig(ctypes.Structure):
@@ -82,6 +84,8 @@ def load():
     _F = ctypes.c_float
     lib.kvq_append_and_decode.argtypes = [_CFG, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I, _F, _P,
                                           _P, ctypes.c_size_t, _P]
+    lib.kvq_append_and_decode_noalloc.argtypes = [_CFG, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I,
+                                                  _F, _P, _P]
     lib.kvq_rematerialize_fp16_pages.argtypes = [_CFG, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P]
     lib.kvq_baseline_page_bytes.argtypes = [_I]
     lib.kvq_baseline_page_bytes.restype = ctypes.c_size_t
@@ -97,7 +101,7 @@ def load():
                  "kvq_append_and_requant", "kvq_paged_decode_attn", "kvq_bandwidth_probe",
                  "kvq_fill_pages_fp16", "kvq_fill_pages_fp8", "kvq_paged_decode_attn_fp16",
                  "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages",
-                 "kvq_paged_multi_query_attn"):
+                 "kvq_paged_multi_query_attn", "kvq_append_and_decode_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -250,3 +254,14 @@ def kvq_append_and_decode(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads
                                         max_blocks, _ptr(pool_k), _ptr(pool_v), _ptr(q), q_heads, max_seq_len,
                                         float(sm_scale), _ptr(out), _ptr(workspace), workspace_bytes,
                                         _stream(stream)))
+
+
+
+def kvq_append_and_decode_noalloc(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, staging_k, staging_v,
+                                  block_table, max_blocks, pool_k, pool_v, q, q_heads, max_seq_len, sm_scale, out,
+                                  stream=None):
+    _check(load().kvq_append_and_decode_noalloc(ctypes.byref(cfg), _ptr(k_new), _ptr(v_new),
+                                                _ptr(seq_lens_before), num_seqs, kv_heads, _ptr(staging_k),
+                                                _ptr(staging_v), _ptr(block_table), max_blocks, _ptr(pool_k),
+                                                _ptr(pool_v), _ptr(q), q_heads, max_seq_len, float(sm_scale),
+                                                _ptr(out), _stream(stream)))

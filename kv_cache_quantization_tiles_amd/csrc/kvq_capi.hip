@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
@@ -93,6 +94,45 @@ int chunks_per_partition(int num_seqs, int kv_heads, int max_seq_len, int tile) 
 template <class Args>
 void set_signs(Args& a, const kvq_config* cfg) {
   for (int i = 0; i < 4; ++i) a.signs[i] = cfg->hadamard_signs[i];
+}
+
+// Static scratch of kvq_append_and_decode_noalloc: the decode's partition
+// partials ([S][Hq][P][128] accumulators, then [S][Hq][P][2] (max, sum)),
+// for callers that cannot allocate.  Every GPU the library runs on holds its
+// own copy (KVQ_NOALLOC_SCRATCH_BYTES) until the process ends.  In host code
+// `scratch` is only a stand-in for the device array: its device address is
+// taken once per device with hipGetSymbolAddress, with that device current,
+// and only that address is passed to kernels.  Nothing in it needs to start
+// at zero (the merge reads exactly the partitions the decode wrote), and
+// calls that overlap on one GPU race on it.
+__device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+kvq_status scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(KVQ_ERR_ARG, "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return KVQ_OK;
 }
 
 }  // namespace
@@ -376,12 +416,12 @@ kvq_status kvq_paged_multi_query_attn(const kvq_config* cfg, const kvq_half* q, 
                   "kvq_paged_multi_query_attn");
 }
 
-kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+static kvq_status append_and_decode_impl(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
                                  const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
                                  kvq_half* staging_k, kvq_half* staging_v, const int32_t* block_table,
                                  int32_t max_blocks, void* pool_k, void* pool_v, const kvq_half* q,
                                  int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   KVQ_TRY(check_config(cfg, true));
   KVQ_NONNULL(k_new);
   KVQ_NONNULL(v_new);
@@ -393,7 +433,7 @@ kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, c
   KVQ_NONNULL(pool_v);
   KVQ_NONNULL(q);
   KVQ_NONNULL(out);
-  KVQ_NONNULL(workspace);
+  if (!noalloc) KVQ_NONNULL(workspace);
   if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
     return fail(KVQ_ERR_ARG, "num_seqs, q_heads, kv_heads, max_seq_len and max_blocks must be > 0");
   if (q_heads % kv_heads != 0)
@@ -407,12 +447,18 @@ kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, c
   if (need_blocks > max_blocks)
     return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens in whole tiles", max_blocks, max_seq_len);
   const size_t need = kvq_decode_workspace_bytes(cfg, num_seqs, q_heads, kv_heads, max_seq_len);
-  if (workspace_bytes < need)
+  if (noalloc && need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES)
+    return fail(KVQ_ERR_WORKSPACE,
+                "these sizes need %zu bytes of partition partials, beyond the %zu bytes of the library's "
+                "static scratch (use kvq_append_and_decode with a workspace)", need,
+                (size_t)KVQ_NOALLOC_SCRATCH_BYTES);
+  if (!noalloc && workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const int tpp = chunks_per_partition(num_seqs, kv_heads, max_seq_len, tile);
   const int parts = max_partitions(max_seq_len, 64, tpp);
   if (tpp > 64 || parts > 1024)
     return fail(KVQ_ERR_UNSUPPORTED, "max_seq_len %d is beyond 65536 chunks of 64 tokens", max_seq_len);
+  if (noalloc) KVQ_TRY(scratch_of_current_device((hipStream_t)stream, &workspace));
   kvq::DecodeArgs a{};
   a.q = q;
   a.block_table = block_table;
@@ -449,7 +495,29 @@ kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, c
   set_signs(a, cfg);
   set_signs(qa, cfg);
   return launched(kvq::launch_append_decode(a, qa, tile, cfg->bits_k, cfg->bits_v, (hipStream_t)stream),
-                  "kvq_append_and_decode");
+                  noalloc ? "kvq_append_and_decode_noalloc" : "kvq_append_and_decode");
+}
+
+kvq_status kvq_append_and_decode(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                 const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                 kvq_half* staging_k, kvq_half* staging_v, const int32_t* block_table,
+                                 int32_t max_blocks, void* pool_k, void* pool_v, const kvq_half* q,
+                                 int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return append_and_decode_impl(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, staging_k, staging_v,
+                                block_table, max_blocks, pool_k, pool_v, q, q_heads, max_seq_len, sm_scale, out,
+                                workspace, workspace_bytes, stream, false);
+}
+
+kvq_status kvq_append_and_decode_noalloc(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                         const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                         kvq_half* staging_k, kvq_half* staging_v, const int32_t* block_table,
+                                         int32_t max_blocks, void* pool_k, void* pool_v, const kvq_half* q,
+                                         int32_t q_heads, int32_t max_seq_len, float sm_scale, float* out,
+                                         void* stream) {
+  return append_and_decode_impl(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, staging_k, staging_v,
+                                block_table, max_blocks, pool_k, pool_v, q, q_heads, max_seq_len, sm_scale, out,
+                                nullptr, 0, stream, true);
 }
 
 size_t kvq_baseline_page_bytes(int32_t fp8) { return (size_t)kvq::kPage * kvq::kHeadDim * (fp8 ? 1 : 2); }

@@ -150,3 +150,20 @@ def test_multi_query_validation(lib):
     # NULL output
     assert lib.kvq_paged_multi_query_attn(c, 16, 4, 4, 32, 8, 16, 1028, 16, 16388, 16, 16, 0.1, None, 16, need,
                                           None) == L.KVQ_ERR_ARG
+
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch_on_the_host(lib):
+    """kvq_append_and_decode_noalloc checks the partials' size against its
+    static scratch before any device call (so this runs without a GPU)."""
+    cfg = L.config(32, 4, 2, 5)
+    # 512 sequences x 64K tokens x 64 query heads: far beyond 32 MiB of partials
+    need = L.kvq_decode_workspace_bytes(cfg, 512, 64, 8, 65536)
+    assert need > L.KVQ_NOALLOC_SCRATCH_BYTES
+    p = 256
+    st = lib.kvq_append_and_decode_noalloc(ctypes.byref(cfg), p, p, p, 512, 8, p, p, p, 8192, p, p, p, 64,
+                                           65536, 0.088, p, None)
+    assert st == L.KVQ_ERR_WORKSPACE
+    assert "static scratch" in L.kvq_last_error()
+    st = lib.kvq_append_and_decode_noalloc(ctypes.byref(cfg), p, p, p, 512, 8, p, p, p, 8192, p, p, None, 64,
+                                           65536, 0.088, p, None)
+    assert st == L.KVQ_ERR_ARG
