@@ -5,7 +5,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 namespace {

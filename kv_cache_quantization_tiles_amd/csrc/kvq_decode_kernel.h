@@ -276,8 +276,11 @@ struct alignas(16) DecodeSmemU {
 // MQ: several queries per sequence (A.n_q of them, the newest cached tokens);
 // row blocks of NH rows, row r = query r / G, head r % G, and query i sees
 // the tokens before L - n_q + i + 1.
+// Groups of up to 8 heads keep 2 waves per SIMD (at most 256 registers in all,
+// VGPRs and AGPRs); 16 heads need more registers and run 1 wave per SIMD.
 template <int T, int BK, int BV, int HG, bool FUSED, bool MQ = false>
-__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs A, QuantArgs Q) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(HG <= 2 ? 2 : 1)))
+void decode_kernel(DecodeArgs A, QuantArgs Q) {
   constexpr int NH = 4 * HG;
   constexpr int SETS = (T == 32) ? 4 : 2;        // QK A register sets
   constexpr int BLK = 32 / SETS;                 // steps per set = blocks per broadcast group

@@ -200,19 +200,16 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
     }
     __syncthreads();
     for (int c = tid; c < kHeadDim; c += NT) {
-      double v[kShortTile];
       double s1 = 0.0, s2 = 0.0;
-#pragma unroll
-      for (int r = 0; r < kShortTile; ++r) {
-        v[r] = (r < n) ? sh.col[r][c] : 0.0;
-        s1 += v[r];
-        s2 = __builtin_fma(v[r], v[r], s2);
+      for (int r = 0; r < n; ++r) {
+        const double v = sh.col[r][c];
+        s1 += v;
+        s2 = __builtin_fma(v, v, s2);
       }
       const double mean = s1 / dn;
       double c2 = 0.0;
-#pragma unroll
-      for (int r = 0; r < kShortTile; ++r) {
-        const double d = (r < n) ? v[r] - mean : 0.0;
+      for (int r = 0; r < n; ++r) {
+        const double d = sh.col[r][c] - mean;
         c2 = __builtin_fma(d, d, c2);
       }
       const double sd = __builtin_sqrt(c2 / dn), rms = __builtin_sqrt(s2 / dn);
