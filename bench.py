@@ -157,10 +157,12 @@ def cpu_baseline(wl, max_seqs: int):
     qb = quantize_bytes(ntok_heads, wl.bits_k, wl.tile_tokens) + quantize_bytes(ntok_heads, wl.bits_v, wl.tile_tokens)
     db = decode_bytes(wl, [wl.seq_lens[s] for s in seqs])
     unit_bytes = quantize_bytes(wl.seq_lens[0], wl.bits_k, wl.tile_tokens)
+    ntok = sum(wl.seq_lens[s] for s in seqs)
     return {"value": round((qb + db) / (tq + td) / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(seqs)} of {wl.num_seqs} sequences x {wl.seq_lens[0]} tokens, all {wl.hkv} kv heads: "
+            "sample": f"{wl.name}: {len(seqs)} of {wl.num_seqs} sequences ({ntok} tokens), all {wl.hkv} kv heads: "
                       f"quantize K and V to pages, then one decode step (fp64 NumPy oracle, "
                       f"{cores} worker processes)",
+            "decode_tok_per_s": round(len(seqs) / td, 3),
             "quantize_s": round(tq, 3), "decode_s": round(td, 3),
             "single_core_quantize_GBps": round(unit_bytes / t_unit / 1e9, 6),
             "single_core_unit": f"quantize one (sequence, kv head) of K, {wl.seq_lens[0]} tokens: {t_unit:.3f} s",
@@ -257,6 +259,180 @@ def long_context_leg(n_iter: int = 10):
             "modes": modes,
             "pages_context": "A100-80GB, whole Qwen3-4B at 128K: 66.6 / 105.0 / 140.9 tok/s for "
                              "fp16 / fp8 / compressed KV (other hardware, end-to-end; context only)"}
+
+
+def cpu_baseline_legs():
+    """The oracle beside the other workloads, each on a bounded sample (its
+    first sequences; one layer of the long-context one), same byte formulas."""
+    out = {}
+    for idx, nseq in ((1, 1), (3, 2), (5, 2), (4, 1)):
+        wl = inputs.workload(idx)
+        if wl.layers > 1:
+            wl = dataclasses.replace(wl, layers=1)
+        r = cpu_baseline(wl, nseq)
+        r["sample"] += " (one layer)" if idx == 4 else ""
+        out[wl.name] = r
+    return out
+
+
+def latency_leg(n: int = 50):
+    """The single-head 1024-token correctness workload as a latency line:
+    quantize its prefill, then one fused append + decode step (8 query heads),
+    each launch timed alone (events around one call, inputs resident)."""
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+    wl = inputs.workload(1)
+    dev = torch.device("cuda:0")
+    table, npages = inputs.block_table(wl)
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+    k = torch.from_numpy(inputs.gen_kv(wl, "K")).to(dev)
+    v = torch.from_numpy(inputs.gen_kv(wl, "V")).to(dev)
+    cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+    kn = torch.from_numpy(inputs.gen_decode_kv(wl, "K", 0)).to(dev)
+    vn = torch.from_numpy(inputs.gen_decode_kv(wl, "V", 0)).to(dev)
+    q = torch.from_numpy(inputs.gen_q(wl)).to(dev)
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+    ws = cache.workspace(wl.hq, max(wl.seq_lens) + 1)
+
+    def one(fn):
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+    tq = one(lambda: cache.quantize_prefill(k, v, cu, max(wl.seq_lens)))
+    td = one(lambda: cache.append_decode(kn, vn, lens, q, max(wl.seq_lens) + 1, out=out, workspace=ws))
+    return {"workload": wl.name, "tokens": wl.total_tokens, "kv_heads": wl.hkv, "q_heads": wl.hq,
+            "quantize_latency_us": round(tq, 2), "decode_step_latency_us": round(td, 2),
+            "note": "median of single launches (bulk + short-tile quantize; fused decode + merge); launch-bound"}
+
+
+def rematerialize_leg(idx: int, n_iter: int = 20):
+    """The read path the direct decode avoids, on a 16K workload: restore every
+    page to fp16 pages, then the fp16 decode, against the direct decode of the
+    same quantized pages (both timed as back-to-back batches over rotated
+    pools)."""
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+    wl = inputs.workload(idx)
+    dev = torch.device("cuda:0")
+    table, npages = inputs.block_table(wl)
+    max_len = max(wl.seq_lens)
+    cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+    k = inputs.gen_kv_device(wl, "K", device=dev)
+    v = inputs.gen_kv_device(wl, "V", device=dev)
+    cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
+    pool_bytes = npages * wl.hkv * (api.kvq_slot_bytes(cfg, False) + api.kvq_slot_bytes(cfg, True))
+    nc = max(2, int(math.ceil(1.0e9 / pool_bytes)))
+    caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(nc)]
+    for c in caches:
+        c.quantize_prefill(k, v, cu, max_len)
+    del k, v
+    base = [api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(2)]
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    q = torch.from_numpy(inputs.gen_q(wl)).to(dev)
+    out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+    ws = caches[0].workspace(wl.hq, max_len)
+    ws16 = base[0].workspace(wl.hq, max_len)
+
+    def batch(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for j in range(n_iter):
+            fn(j)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_iter
+    direct = batch(lambda j: caches[j % nc].decode(q, lens, max_len, out=out, workspace=ws))
+    remat = batch(lambda j: (caches[j % nc].rematerialize_into(base[j % 2], lens, max_len),
+                             base[j % 2].decode(q, lens, max_len, out=out, workspace=ws16)))
+    del caches, base
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "direct_decode_ms": round(direct, 4), "rematerialize_then_fp16_decode_ms": round(remat, 4),
+            "ratio": round(remat / direct, 2)}
+
+
+def long_context_decode_phase(n_steps: int = 1024):
+    """The long-context workload's decode phase on one layer: 6 sequences of
+    131072 tokens, 8 kv / 32 query heads, then 1024 decode steps, each an
+    append of one token per sequence and the attention that includes it:
+    fused append + re-quantize + attend for the 4- and 2-bit pages (tile 128:
+    the steps cross 8 tile boundaries), append + decode for the fp16 and fp8
+    pages.  The 1024 steps run back to back between two events; per-step
+    tokens and queries are resident before timing."""
+    import torch
+    from kv_cache_quantization_tiles_amd import api
+    wl = dataclasses.replace(inputs.workload(4), layers=1, decode_steps=n_steps)
+    dev = torch.device("cuda:0")
+    table, npages = inputs.block_table(wl)
+    max_len = max(wl.seq_lens)
+    cu = torch.from_numpy(wl.cu_seqlens()).to(dev)
+    k = inputs.gen_kv_device(wl, "K", device=dev)
+    v = inputs.gen_kv_device(wl, "V", device=dev)
+    kd = torch.from_numpy(np.stack([inputs.gen_decode_kv(wl, "K", i) for i in range(n_steps)])).to(dev)
+    vd = torch.from_numpy(np.stack([inputs.gen_decode_kv(wl, "V", i) for i in range(n_steps)])).to(dev)
+    qd = torch.from_numpy(np.stack([inputs.gen_q(wl, i) for i in range(n_steps)])).to(dev)
+    lens0 = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
+    lens = [lens0 + i for i in range(n_steps)]
+    out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
+    res = {}
+    for name in ("fp16", "fp8", "kvq4", "kvq2"):
+        if name in ("fp16", "fp8"):
+            fp8 = name == "fp8"
+            ks = max(float(k.abs().max()), float(kd.abs().max())) / 448.0 if fp8 else 1.0
+            vs = max(float(v.abs().max()), float(vd.abs().max())) / 448.0 if fp8 else 1.0
+            cache = api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs, fp8, ks, vs)
+            cache.fill(k, v, cu, max_len)
+            ws = cache.workspace(wl.hq, max_len + n_steps)
+
+            def step(i):
+                cache.append(kd[i], vd[i], lens[i])
+                cache.decode(qd[i], lens[i] + 1, max_len + n_steps, out=out, workspace=ws)
+            per_tok = 2 * 128 * (1 if fp8 else 2)
+        else:
+            bits = int(name[3:])
+            cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
+            cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+            cache.quantize_prefill(k, v, cu, max_len)
+            ws = cache.workspace(wl.hq, max_len + n_steps)
+
+            def step(i):
+                cache.append_decode(kd[i], vd[i], lens[i], qd[i], max_len + n_steps, out=out, workspace=ws)
+            per_tok = 2 * slot_bytes_per_token(bits, wl.tile_tokens)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n_steps
+        mid = max_len + n_steps // 2
+        rb = wl.num_seqs * wl.hkv * per_tok * (mid if name in ("fp16", "fp8") else
+                                               math.ceil(mid / wl.tile_tokens) * wl.tile_tokens)
+        res[name] = {"step_ms": round(ms, 4), "tok_per_s_per_layer": round(wl.num_seqs / (ms * 1e-3), 1),
+                     "tok_per_s_36_layers_extrapolated": round(wl.num_seqs / (36 * ms * 1e-3), 1),
+                     "read_GBps": round(rb / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(rb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del cache, ws
+        torch.cuda.empty_cache()
+    del k, v, kd, vd, qd
+    torch.cuda.empty_cache()
+    base = res["fp16"]["step_ms"]
+    for m in res.values():
+        m["speedup_vs_fp16"] = round(base / m["step_ms"], 3)
+    return {"workload": f"{wl.name}, one layer, {n_steps} decode steps", "num_seqs": wl.num_seqs,
+            "context_start": max_len, "tile_tokens": wl.tile_tokens, "modes": res,
+            "note": "step = append of one token per sequence + attention over every cached token (+ merge); "
+                    "read GB/s at the middle step's length; 36-layer figures are this layer's time x 36"}
 
 
 def burst_leg():
@@ -467,6 +643,7 @@ def main():
         raise SystemExit("multi-layer workloads are not bench lines")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seqs)  # before any GPU call
+    cpu_legs = None if (args.no_cpu_baseline or args.no_long_context) else cpu_baseline_legs()
 
     import torch
     from kv_cache_quantization_tiles_amd import api
@@ -709,7 +886,11 @@ def main():
     }
     del caches, ks, vs, src, dst
     torch.cuda.empty_cache()
+    rec["cpu_baseline_legs"] = cpu_legs
+    rec["latency_1x1024"] = latency_leg()
     rec["long_context"] = None if args.no_long_context else long_context_leg()
+    rec["long_context_decode_phase"] = None if args.no_long_context else long_context_decode_phase()
+    rec["rematerialize_16k"] = None if args.no_long_context else [rematerialize_leg(2), rematerialize_leg(3)]
     rec["burst_32x16k"] = None if args.no_long_context else burst_leg()
     rec["mixed_64seq"] = None if args.no_long_context else mixed_leg()
     print(json.dumps(rec), flush=True)

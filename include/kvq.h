@@ -341,6 +341,22 @@ kvq_status kvq_fill_pages_fp8(const kvq_config* cfg, const kvq_half* k, const kv
                               int32_t kv_heads, const int32_t* block_table, int32_t max_blocks,
                               void* pool_k, void* pool_v, float k_scale, float v_scale, void* stream);
 
+/* Append one decode token per sequence to fp16 (resp. E4M3) pools: k_new,
+ * v_new fp16 [num_seqs][kv_heads][128] go to position seq_lens_before[s]
+ * (device int32 [num_seqs]) of sequence s, K as row p % 16 of the page
+ * holding p, V as column p % 16, encoded as the fills encode (E4M3: x / scale
+ * rounded to nearest, ties to even; |x| / scale must stay within 448).  The
+ * page must exist in the block table (a position past max_blocks pages is
+ * skipped).  The caller advances its lengths afterwards.  Errors as the fills. */
+kvq_status kvq_append_pages_fp16(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                 const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                 const int32_t* block_table, int32_t max_blocks, void* pool_k, void* pool_v,
+                                 void* stream);
+kvq_status kvq_append_pages_fp8(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                const int32_t* block_table, int32_t max_blocks, void* pool_k, void* pool_v,
+                                float k_scale, float v_scale, void* stream);
+
 /* Workspace bytes of the two baseline decode functions. */
 size_t kvq_baseline_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t q_heads,
                                     int32_t kv_heads, int32_t max_seq_len);

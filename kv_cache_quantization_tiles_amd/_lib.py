@@ -22,6 +22,7 @@ EXPORTED = (
     "kvq_fill_pages_fp8", "kvq_baseline_workspace_bytes", "kvq_paged_decode_attn_fp16",
     "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages",
     "kvq_multi_query_workspace_bytes", "kvq_paged_multi_query_attn", "kvq_append_and_decode_noalloc",
+    "kvq_append_pages_fp16", "kvq_append_pages_fp8",
 )
 
 KVQ_NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -91,6 +92,8 @@ def load():
     lib.kvq_baseline_page_bytes.restype = ctypes.c_size_t
     lib.kvq_fill_pages_fp16.argtypes = [_CFG, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _P]
     lib.kvq_fill_pages_fp8.argtypes = [_CFG, _P, _P, _P, _I, _I, _I, _P, _I, _P, _P, _F, _F, _P]
+    lib.kvq_append_pages_fp16.argtypes = [_CFG, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P]
+    lib.kvq_append_pages_fp8.argtypes = [_CFG, _P, _P, _P, _I, _I, _P, _I, _P, _P, _F, _F, _P]
     lib.kvq_baseline_workspace_bytes.argtypes = [_CFG, _I, _I, _I, _I]
     lib.kvq_baseline_workspace_bytes.restype = ctypes.c_size_t
     lib.kvq_paged_decode_attn_fp16.argtypes = [_CFG, _P, _I, _I, _I, _P, _I, _P, _I, _P, _P, _F, _P, _P,
@@ -101,7 +104,8 @@ def load():
                  "kvq_append_and_requant", "kvq_paged_decode_attn", "kvq_bandwidth_probe",
                  "kvq_fill_pages_fp16", "kvq_fill_pages_fp8", "kvq_paged_decode_attn_fp16",
                  "kvq_paged_decode_attn_fp8", "kvq_append_and_decode", "kvq_rematerialize_fp16_pages",
-                 "kvq_paged_multi_query_attn", "kvq_append_and_decode_noalloc"):
+                 "kvq_paged_multi_query_attn", "kvq_append_and_decode_noalloc", "kvq_append_pages_fp16",
+                 "kvq_append_pages_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -265,3 +269,17 @@ def kvq_append_and_decode_noalloc(cfg, k_new, v_new, seq_lens_before, num_seqs, 
                                                 _ptr(staging_v), _ptr(block_table), max_blocks, _ptr(pool_k),
                                                 _ptr(pool_v), _ptr(q), q_heads, max_seq_len, float(sm_scale),
                                                 _ptr(out), _stream(stream)))
+
+
+def kvq_append_pages_fp16(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, block_table, max_blocks, pool_k,
+                          pool_v, stream=None):
+    _check(load().kvq_append_pages_fp16(ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(seq_lens_before),
+                                        num_seqs, kv_heads, _ptr(block_table), max_blocks, _ptr(pool_k),
+                                        _ptr(pool_v), _stream(stream)))
+
+
+def kvq_append_pages_fp8(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, block_table, max_blocks, pool_k,
+                         pool_v, k_scale, v_scale, stream=None):
+    _check(load().kvq_append_pages_fp8(ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(seq_lens_before),
+                                       num_seqs, kv_heads, _ptr(block_table), max_blocks, _ptr(pool_k),
+                                       _ptr(pool_v), float(k_scale), float(v_scale), _stream(stream)))

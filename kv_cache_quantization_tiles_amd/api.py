@@ -13,7 +13,8 @@ import torch
 from . import _lib
 from ._lib import (config, kvq_append_and_decode, kvq_append_and_requant, kvq_baseline_page_bytes,  # noqa: F401
                    kvq_baseline_workspace_bytes, kvq_decode_workspace_bytes, kvq_dequantize,
-                   kvq_fill_pages_fp8, kvq_fill_pages_fp16, kvq_multi_query_workspace_bytes,
+                   kvq_append_pages_fp8, kvq_append_pages_fp16, kvq_fill_pages_fp8,
+                   kvq_fill_pages_fp16, kvq_multi_query_workspace_bytes,
                    kvq_paged_decode_attn, kvq_paged_multi_query_attn,
                    kvq_paged_decode_attn_fp8, kvq_paged_decode_attn_fp16, kvq_quantize_tiles,
                    kvq_quantize_to_pages, kvq_rematerialize_fp16_pages, kvq_slot_bytes)
@@ -163,6 +164,16 @@ class BaselineCache:
             kvq_fill_pages_fp8(*args, self.k_scale, self.v_scale)
         else:
             kvq_fill_pages_fp16(*args)
+
+    def append(self, k_new, v_new, lens_before):
+        """Write one token per sequence at position lens_before[s]."""
+        _require_cuda(k_new, v_new, lens_before)
+        args = (self.cfg, k_new.contiguous(), v_new.contiguous(), lens_before, self.num_seqs, self.kv_heads,
+                self.block_table, self.max_blocks, self.pool_k, self.pool_v)
+        if self.fp8:
+            kvq_append_pages_fp8(*args, self.k_scale, self.v_scale)
+        else:
+            kvq_append_pages_fp16(*args)
 
     def workspace(self, q_heads, max_seq_len):
         nbytes = kvq_baseline_workspace_bytes(self.cfg, self.num_seqs, q_heads, self.kv_heads, int(max_seq_len))

@@ -132,6 +132,31 @@ __global__ __launch_bounds__(256) void fill_kernel(BaseFillArgs A) {
   }
 }
 
+// ---------------------------------------------------------------- append
+// One decode token per sequence written into its page (K row p % 16, V
+// column p % 16 of the page holding position p = lens_before[s]), encoded as
+// the fill encodes.  grid: x = kv head, y = sequence; 128 threads = channels.
+template <bool FP8>
+__global__ __launch_bounds__(128) void append_base_kernel(BaseFillArgs A, const int32_t* lens_before) {
+  const int head = blockIdx.x, seq = blockIdx.y, c = threadIdx.x;
+  const int p = lens_before[seq];
+  if (p / kPage >= A.max_blocks) return;   // no page for this position
+  const int H = A.kv_heads;
+  const size_t page = (size_t)A.block_table[(size_t)seq * A.max_blocks + p / kPage] * H + head;
+  const int r = p % kPage;
+  const size_t src = ((size_t)seq * H + head) * kHeadDim + c;
+  const uint16_t kh = A.k[src], vh = A.v[src];
+  if (!FP8) {
+    reinterpret_cast<uint16_t*>(A.pool_k)[page * (kPage * kHeadDim) + r * kHeadDim + c] = kh;
+    reinterpret_cast<uint16_t*>(A.pool_v)[page * (kPage * kHeadDim) + c * kPage + r] = vh;
+  } else {
+    const unsigned kb = __builtin_amdgcn_cvt_pk_fp8_f32(half_bits_to_float(kh) / A.k_scale, 0.f, 0u, false);
+    const unsigned vb = __builtin_amdgcn_cvt_pk_fp8_f32(half_bits_to_float(vh) / A.v_scale, 0.f, 0u, false);
+    A.pool_k[page * (kPage * kHeadDim) + r * kHeadDim + c] = (uint8_t)(kb & 0xFFu);
+    A.pool_v[page * (kPage * kHeadDim) + c * kPage + r] = (uint8_t)(vb & 0xFFu);
+  }
+}
+
 // ---------------------------------------------------------------- decode
 struct alignas(16) BaseSmem {
   int32_t pages[kMaxBlocksPerPart * kPagesPerBlock];
@@ -317,6 +342,14 @@ hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, i
   dim3 grid((max_seq_len + kPage - 1) / kPage, a.kv_heads, num_seqs);
   if (fp8) hipLaunchKernelGGL(fill_kernel<true>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(fill_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_baseline(const BaseFillArgs& a, const int32_t* lens_before, bool fp8, int num_seqs,
+                                  hipStream_t s) {
+  dim3 grid(a.kv_heads, num_seqs);
+  if (fp8) hipLaunchKernelGGL(append_base_kernel<true>, grid, dim3(128), 0, s, a, lens_before);
+  else hipLaunchKernelGGL(append_base_kernel<false>, grid, dim3(128), 0, s, a, lens_before);
   return hipGetLastError();
 }
 

@@ -586,6 +586,42 @@ kvq_status kvq_fill_pages_fp8(const kvq_config* cfg, const kvq_half* k, const kv
                        pool_k, pool_v, true, k_scale, v_scale, stream, "kvq_fill_pages_fp8");
 }
 
+static kvq_status append_baseline(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                  const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                  const int32_t* block_table, int32_t max_blocks, void* pool_k, void* pool_v,
+                                  bool fp8, float k_scale, float v_scale, void* stream, const char* what) {
+  KVQ_TRY(check_config(cfg, false));
+  KVQ_NONNULL(k_new);
+  KVQ_NONNULL(v_new);
+  KVQ_NONNULL(seq_lens_before);
+  KVQ_NONNULL(block_table);
+  KVQ_NONNULL(pool_k);
+  KVQ_NONNULL(pool_v);
+  if (num_seqs <= 0 || kv_heads <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, kv_heads and max_blocks must be > 0");
+  if (kv_heads > 65535 || num_seqs > 65535) return fail(KVQ_ERR_ARG, "too many heads or sequences");
+  if (fp8 && !(k_scale > 0.f && v_scale > 0.f)) return fail(KVQ_ERR_ARG, "fp8 scales must be > 0");
+  kvq::BaseFillArgs a{k_new, v_new, nullptr, block_table, max_blocks, kv_heads, (uint8_t*)pool_k, (uint8_t*)pool_v,
+                      k_scale, v_scale};
+  return launched(kvq::launch_append_baseline(a, seq_lens_before, fp8, num_seqs, (hipStream_t)stream), what);
+}
+
+kvq_status kvq_append_pages_fp16(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                 const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                 const int32_t* block_table, int32_t max_blocks, void* pool_k, void* pool_v,
+                                 void* stream) {
+  return append_baseline(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, block_table, max_blocks, pool_k,
+                         pool_v, false, 1.f, 1.f, stream, "kvq_append_pages_fp16");
+}
+
+kvq_status kvq_append_pages_fp8(const kvq_config* cfg, const kvq_half* k_new, const kvq_half* v_new,
+                                const int32_t* seq_lens_before, int32_t num_seqs, int32_t kv_heads,
+                                const int32_t* block_table, int32_t max_blocks, void* pool_k, void* pool_v,
+                                float k_scale, float v_scale, void* stream) {
+  return append_baseline(cfg, k_new, v_new, seq_lens_before, num_seqs, kv_heads, block_table, max_blocks, pool_k,
+                         pool_v, true, k_scale, v_scale, stream, "kvq_append_pages_fp8");
+}
+
 size_t kvq_baseline_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t q_heads,
                                     int32_t kv_heads, int32_t max_seq_len) {
   if (check_config(cfg, false) != KVQ_OK) return 0;

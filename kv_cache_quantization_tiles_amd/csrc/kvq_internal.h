@@ -121,6 +121,8 @@ hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int til
                                 hipStream_t s);
 hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, int max_seq_len, hipStream_t s);
 hipError_t launch_decode_baseline(const DecodeArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_append_baseline(const BaseFillArgs& a, const int32_t* lens_before, bool fp8, int num_seqs,
+                                  hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
 

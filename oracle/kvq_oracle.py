@@ -651,6 +651,24 @@ def fill_pages_baseline(k, v, cu_seqlens, table, pool_k, pool_v, fp8=False, k_sc
                     pool_v[page, h] = vt.reshape(-1)
 
 
+def append_pages_baseline(k_new, v_new, lens_before, table, pool_k, pool_v, fp8=False, k_scale=1.0, v_scale=1.0):
+    """One decode token per sequence written at position lens_before[s] of
+    fp16 or fp8 pools (in place), encoded as fill_pages_baseline encodes: K
+    row p % 16 of the page holding p, V column p % 16 of it."""
+    for s in range(k_new.shape[0]):
+        p = int(lens_before[s])
+        page, r = int(table[s][p // PAGE_TOKENS]), p % PAGE_TOKENS
+        for h in range(k_new.shape[1]):
+            kp = pool_k[page, h].reshape(PAGE_TOKENS, HEAD_DIM)
+            vp = pool_v[page, h].reshape(HEAD_DIM, PAGE_TOKENS)
+            if fp8:
+                kp[r] = fp8_encode(k_new[s, h], k_scale)
+                vp[:, r] = fp8_encode(v_new[s, h], v_scale)
+            else:
+                kp[r] = k_new[s, h]
+                vp[:, r] = v_new[s, h]
+
+
 def read_baseline_sequence(pool, table_row, seq_len, head, role, fp8=False, scale=1.0):
     """Restored tokens float64 [L, 128] of one (sequence, kv head)."""
     out = np.zeros((seq_len, HEAD_DIM))

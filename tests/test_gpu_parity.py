@@ -306,6 +306,38 @@ def test_baseline_fill_and_decode_parity(case, fp8):
     print(f"[attn] baseline {'fp8' if fp8 else 'fp16'} {case}: max abs err {err:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["fp16", "fp8"])
+def test_baseline_append_and_decode_parity(fp8):
+    """Decode tokens appended to fp16 / fp8 pages one step at a time: pages
+    byte-exact against the oracle's appends, attention within the bar."""
+    wl = _paged_workload(2, (200, 63, 16, 1), 2, 8, 64, 4, 4, 3, decode_steps=40)
+    k, v = inputs.gen_kv(wl, "K"), inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    kd = [inputs.gen_decode_kv(wl, "K", i) for i in range(40)]
+    vd = [inputs.gen_decode_kv(wl, "V", i) for i in range(40)]
+    ks = max(orc.fp8_scale(k), orc.fp8_scale(np.stack(kd))) if fp8 else 1.0
+    vs = max(orc.fp8_scale(v), orc.fp8_scale(np.stack(vd))) if fp8 else 1.0
+    cache = api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs, fp8, ks, vs)
+    cache.fill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(wl.cu_seqlens()).cuda(),
+               max(wl.seq_lens))
+    rk, rv = orc.new_baseline_pool(npages, wl.hkv, fp8), orc.new_baseline_pool(npages, wl.hkv, fp8)
+    orc.fill_pages_baseline(k, v, wl.cu_seqlens(), table, rk, rv, fp8, ks, vs)
+    lens = np.array(wl.seq_lens, np.int32)
+    for i in range(40):
+        cache.append(torch.from_numpy(kd[i]).cuda(), torch.from_numpy(vd[i]).cuda(), torch.from_numpy(lens).cuda())
+        orc.append_pages_baseline(kd[i], vd[i], lens, table, rk, rv, fp8, ks, vs)
+        lens = lens + 1
+    gk, gv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    view = np.uint8 if fp8 else np.float16
+    np.testing.assert_array_equal(gk.view(view), rk.view(view))
+    np.testing.assert_array_equal(gv.view(view), rv.view(view))
+    q = inputs.gen_q(wl, 40)
+    out = cache.decode(torch.from_numpy(q).cuda(), torch.from_numpy(lens).cuda(), int(lens.max())).cpu().numpy()
+    ref = orc.paged_decode_attn_baseline(q, table, lens, gk, gv, fp8, ks, vs)
+    err = pu.assert_attn(out, ref, f"baseline append {'fp8' if fp8 else 'fp16'}")
+    print(f"[attn] baseline append + decode {'fp8' if fp8 else 'fp16'}: max abs err {err:.2e}", flush=True)
+
+
 def test_baseline_decode_is_deterministic_and_order_free():
     wl = _paged_workload(2, (700, 513, 64, 1), 2, 8, 64, 4, 4, 3)
     q = torch.from_numpy(inputs.gen_q(wl)).cuda()

@@ -548,6 +548,39 @@ def test_baseline_pages_round_trip_and_attention():
         np.testing.assert_allclose(out[1, :4], ref, rtol=1e-10, atol=1e-12)
 
 
+def test_baseline_appends_one_by_one_equal_the_fill_of_the_longer_sequences():
+    """Appending decode tokens one at a time to fp16 / fp8 pages gives the
+    same bytes as filling the extended sequences at once (independent paths:
+    per-row writes vs whole-page writes)."""
+    import dataclasses
+    wl = dataclasses.replace(inputs.workload(2), seq_lens=(30, 17, 1), hkv=2, hq=8, tile_tokens=64, decode_steps=20)
+    k, v = inputs.gen_kv(wl, "K"), inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    steps = [(inputs.gen_decode_kv(wl, "K", i), inputs.gen_decode_kv(wl, "V", i)) for i in range(20)]
+    longer = dataclasses.replace(wl, seq_lens=tuple(l + 20 for l in wl.seq_lens))
+    cu_l = longer.cu_seqlens()
+    kl = np.zeros((cu_l[-1], 2, 128), np.float16)
+    vl = np.zeros_like(kl)
+    cu = wl.cu_seqlens()
+    for s_ in range(3):
+        n = wl.seq_lens[s_]
+        kl[cu_l[s_]:cu_l[s_] + n], vl[cu_l[s_]:cu_l[s_] + n] = k[cu[s_]:cu[s_ + 1]], v[cu[s_]:cu[s_ + 1]]
+        for i, (kn, vn) in enumerate(steps):
+            kl[cu_l[s_] + n + i], vl[cu_l[s_] + n + i] = kn[s_], vn[s_]
+    for fp8 in (False, True):
+        ks, vs = (orc.fp8_scale(kl), orc.fp8_scale(vl)) if fp8 else (1.0, 1.0)
+        pk, pv = orc.new_baseline_pool(npages, 2, fp8), orc.new_baseline_pool(npages, 2, fp8)
+        orc.fill_pages_baseline(k, v, cu, table, pk, pv, fp8, ks, vs)
+        lens = np.array(wl.seq_lens)
+        for kn, vn in steps:
+            orc.append_pages_baseline(kn, vn, lens, table, pk, pv, fp8, ks, vs)
+            lens = lens + 1
+        rk, rv = orc.new_baseline_pool(npages, 2, fp8), orc.new_baseline_pool(npages, 2, fp8)
+        orc.fill_pages_baseline(kl, vl, cu_l, table, rk, rv, fp8, ks, vs)
+        np.testing.assert_array_equal(pk, rk)
+        np.testing.assert_array_equal(pv, rv)
+
+
 def test_rematerialized_pages_hold_the_restored_tokens():
     """Restoring quantized pages into fp16 pages: each token equals the dense
     restore of the same tile rounded to fp16, rows past the end are 0, and fp16
