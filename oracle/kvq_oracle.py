@@ -56,6 +56,11 @@ Readings where the pages are silent (each is a documented parameter or choice):
   is alpha * (S * code + O) and the restored token is that row rotated back.
 * Tiles are aligned to the start of each sequence; the last one may be
   partial, and its statistics use only its valid rows.
+* Metadata precision: fp32 by default; the fp16 slot variant (meta16) moves
+  one power of two per tile from the scales and offsets into the channel
+  factors (see meta_fp16) and rounds all three to fp16 (nearest even).  Codes
+  are decided before the metadata are rounded, so they are the same in both
+  variants.
 
 "parity unpinned" applies to nothing here: every function is pinned by the
 tests in tests/test_oracle_pins.py.
@@ -184,6 +189,9 @@ class TileQuant:
     rotated: np.ndarray   # float64 [n, d]
     normalized: np.ndarray  # float64 [n, d]
     beta: np.ndarray      # float64 [n]
+    alpha64: np.ndarray = None   # float64 [d]: the channel factors before rounding
+    scale64: np.ndarray = None   # float64 [n]
+    offset64: np.ndarray = None  # float64 [n]
 
 
 def quantize_tile(x: np.ndarray, bits: int, iters: int, signs=None) -> TileQuant:
@@ -198,6 +206,7 @@ def quantize_tile(x: np.ndarray, bits: int, iters: int, signs=None) -> TileQuant
     return TileQuant(codes=codes, alpha=alpha.astype(np.float32),
                      scale=(beta * step).astype(np.float32),
                      offset=(beta * zero).astype(np.float32),
+                     alpha64=alpha, scale64=beta * step, offset64=beta * zero,
                      pre=pre, rotated=r, normalized=y, beta=beta)
 
 
@@ -313,15 +322,41 @@ def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits:
 # Rows of a page past the sequence's end hold code 0, scale 0 and offset 0.
 # ----------------------------------------------------------------------------
 
-def slot_layout(bits: int, tile_tokens: int, d: int = HEAD_DIM, page: int = PAGE_TOKENS):
+def slot_layout(bits: int, tile_tokens: int, meta16: bool = False, d: int = HEAD_DIM, page: int = PAGE_TOKENS):
+    """Byte layout of a slot; meta16: scale, offset and channel factors stored
+    as fp16 (2 bytes each) instead of fp32."""
+    me = 2 if meta16 else 4
     codes = page * d * bits // 8
     alpha_len = page * d // tile_tokens
-    return dict(codes=codes, scale=codes, offset=codes + 4 * page, alpha=codes + 8 * page,
-                alpha_len=alpha_len, total=codes + 8 * page + 4 * alpha_len)
+    return dict(codes=codes, scale=codes, offset=codes + me * page, alpha=codes + 2 * me * page,
+                alpha_len=alpha_len, total=codes + 2 * me * page + me * alpha_len, meta_dtype="<f2" if meta16 else "<f4")
 
 
-def slot_bytes(bits: int, tile_tokens: int) -> int:
-    return slot_layout(bits, tile_tokens)["total"]
+def slot_bytes(bits: int, tile_tokens: int, meta16: bool = False) -> int:
+    return slot_layout(bits, tile_tokens, meta16)["total"]
+
+
+FP16_MAX = 65504.0
+
+
+def meta_fp16(tq: TileQuant):
+    """The tile's metadata as fp16 slots store it.  A power of two moves from
+    the per-token scale and offset into the channel factors (exactly: the
+    restore alpha * (S * code + O) only sees their product): with M the largest
+    |S_t|, |O_t| of the tile, e = floor(log2 M) - 10 (0 if M = 0) and the
+    stored values are alpha * 2^e, S * 2^-e, O * 2^-e, each rounded to fp16
+    (nearest even; magnitudes beyond the fp16 range saturate at 65504).  This
+    keeps S and O within [2^10, 2^11) at the top, far from fp16 overflow, even
+    for tiles whose token factors grow large.  Returns (e, alpha16, scale16,
+    offset16, alpha, scale, offset) with the last three the scaled float64
+    values before rounding."""
+    m = float(max(np.abs(tq.scale64).max(), np.abs(tq.offset64).max())) if tq.scale64.size else 0.0
+    e = (math.frexp(m)[1] - 1) - 10 if m > 0 else 0
+    a, sc, of = tq.alpha64 * 2.0 ** e, tq.scale64 * 2.0 ** -e, tq.offset64 * 2.0 ** -e
+
+    def r16(x):
+        return np.clip(x, -FP16_MAX, FP16_MAX).astype(np.float16)
+    return e, r16(a), r16(sc), r16(of), a, sc, of
 
 
 def k_codes_to_bytes(codes: np.ndarray, bits: int) -> np.ndarray:
@@ -388,36 +423,41 @@ def bytes_to_v_codes(raw: np.ndarray, bits: int) -> np.ndarray:
     return ((words[word] >> shift) & ((1 << bits) - 1)).astype(np.uint8)
 
 
-def new_pool(num_pages: int, kv_heads: int, bits: int, tile_tokens: int) -> np.ndarray:
-    return np.zeros((num_pages, kv_heads, slot_bytes(bits, tile_tokens)), np.uint8)
+def new_pool(num_pages: int, kv_heads: int, bits: int, tile_tokens: int, meta16: bool = False) -> np.ndarray:
+    return np.zeros((num_pages, kv_heads, slot_bytes(bits, tile_tokens, meta16)), np.uint8)
 
 
-def write_slot(pool, page, head, role, bits, tile_tokens, codes16, scale16, offset16, alpha_slice):
-    lay = slot_layout(bits, tile_tokens)
+def write_slot(pool, page, head, role, bits, tile_tokens, codes16, scale16, offset16, alpha_slice, meta16=False):
+    lay = slot_layout(bits, tile_tokens, meta16)
+    dt = lay["meta_dtype"]
     enc = k_codes_to_bytes if role == "K" else v_codes_to_bytes
     slot = pool[page, head]
     slot[:lay["codes"]] = enc(codes16, bits)
-    slot[lay["scale"]:lay["offset"]] = np.asarray(scale16, "<f4").view(np.uint8)
-    slot[lay["offset"]:lay["alpha"]] = np.asarray(offset16, "<f4").view(np.uint8)
-    slot[lay["alpha"]:lay["total"]] = np.asarray(alpha_slice, "<f4").view(np.uint8)
+    slot[lay["scale"]:lay["offset"]] = np.asarray(scale16, dt).view(np.uint8)
+    slot[lay["offset"]:lay["alpha"]] = np.asarray(offset16, dt).view(np.uint8)
+    slot[lay["alpha"]:lay["total"]] = np.asarray(alpha_slice, dt).view(np.uint8)
 
 
-def read_slot(pool, page, head, role, bits, tile_tokens):
-    lay = slot_layout(bits, tile_tokens)
+def read_slot(pool, page, head, role, bits, tile_tokens, meta16=False):
+    lay = slot_layout(bits, tile_tokens, meta16)
+    dt = lay["meta_dtype"]
     slot = np.ascontiguousarray(pool[page, head])
     dec = bytes_to_k_codes if role == "K" else bytes_to_v_codes
     codes = dec(slot[:lay["codes"]], bits)
-    scale = slot[lay["scale"]:lay["offset"]].view("<f4").copy()
-    offset = slot[lay["offset"]:lay["alpha"]].view("<f4").copy()
-    alpha = slot[lay["alpha"]:lay["total"]].view("<f4").copy()
+    scale = slot[lay["scale"]:lay["offset"]].view(dt).astype(np.float32)
+    offset = slot[lay["offset"]:lay["alpha"]].view(dt).astype(np.float32)
+    alpha = slot[lay["alpha"]:lay["total"]].view(dt).astype(np.float32)
     return codes, scale, offset, alpha
 
 
-def _store_tile(pool, table_row, head, role, bits, tile_tokens, tile_index, tq: TileQuant):
+def _store_tile(pool, table_row, head, role, bits, tile_tokens, tile_index, tq: TileQuant, meta16=False):
     """Write one (possibly partial) quantized tile into its pages."""
     ppt = tile_tokens // PAGE_TOKENS
     alen = PAGE_TOKENS * HEAD_DIM // tile_tokens
     n = tq.codes.shape[0]
+    alpha, scale, offset = tq.alpha, tq.scale, tq.offset
+    if meta16:
+        _, alpha, scale, offset, _, _, _ = meta_fp16(tq)
     for j in range(ppt):
         page = int(table_row[tile_index * ppt + j])
         if page < 0:
@@ -428,14 +468,14 @@ def _store_tile(pool, table_row, head, role, bits, tile_tokens, tile_index, tq: 
         a, b = j * PAGE_TOKENS, min(n, (j + 1) * PAGE_TOKENS)
         if b > a:
             codes16[:b - a] = tq.codes[a:b]
-            scale16[:b - a] = tq.scale[a:b]
-            offset16[:b - a] = tq.offset[a:b]
+            scale16[:b - a] = scale[a:b]
+            offset16[:b - a] = offset[a:b]
         write_slot(pool, page, head, role, bits, tile_tokens, codes16, scale16, offset16,
-                   tq.alpha[j * alen:(j + 1) * alen])
+                   alpha[j * alen:(j + 1) * alen], meta16)
 
 
 def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iters,
-                      pool_k, pool_v, staging_k=None, staging_v=None, signs=None):
+                      pool_k, pool_v, staging_k=None, staging_v=None, signs=None, meta16=False):
     """Quantize every tile of every sequence into the page pools (in place).
 
     k, v: fp16 [total_tokens, Hkv, d]; table: int32 [S, max_blocks].  A tail
@@ -455,7 +495,7 @@ def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iter
                     a, b = j * tile_tokens, min(n, (j + 1) * tile_tokens)
                     tq = quantize_tile(x[a0 + a:a0 + b, h, :], bits, iters, signs)
                     pre_rows[a:b] = tq.pre
-                    _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq)
+                    _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq, meta16)
                 pre[(s, h, role)] = pre_rows
             tail = n % tile_tokens
             if stg is not None and tail:
@@ -464,7 +504,7 @@ def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iter
 
 
 def append_and_requant(k_new, v_new, lens_before, table, tile_tokens, bits_k, bits_v, iters,
-                       pool_k, pool_v, staging_k, staging_v, signs=None):
+                       pool_k, pool_v, staging_k, staging_v, signs=None, meta16=False):
     """Append one token per sequence and re-quantize its (partial) tile from the
     fp16 staging rows.  k_new, v_new fp16 [S, Hkv, d].  Returns pre-rounding
     values per (seq, head, role) of the re-quantized tile rows."""
@@ -478,12 +518,12 @@ def append_and_requant(k_new, v_new, lens_before, table, tile_tokens, bits_k, bi
         for role, stg, pool, bits in (("K", staging_k, pool_k, bits_k), ("V", staging_v, pool_v, bits_v)):
             for h in range(heads):
                 tq = quantize_tile(stg[s, :r + 1, h, :], bits, iters, signs)
-                _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq)
+                _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq, meta16)
                 pre[(s, h, role)] = tq.pre
     return pre
 
 
-def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens, signs=None):
+def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens, signs=None, meta16=False):
     """Decode one (sequence, kv head) from the pages with this module's own
     reader: returns (restored tokens float64 [L, d], codes [L, d], alpha per
     tile [ntiles, d], scale [L], offset [L])."""
@@ -497,7 +537,7 @@ def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens, signs
     for j in range(ntiles):
         for p in range(ppt):
             page = int(table_row[j * ppt + p])
-            c16, s16, o16, a = read_slot(pool, page, head, role, bits, tile_tokens)
+            c16, s16, o16, a = read_slot(pool, page, head, role, bits, tile_tokens, meta16)
             t0 = j * tile_tokens + p * PAGE_TOKENS
             codes[t0:t0 + PAGE_TOKENS] = c16
             scale[t0:t0 + PAGE_TOKENS] = s16
@@ -535,7 +575,7 @@ def attention_abs_scale(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_
 
 
 def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
-                      sm_scale=None, return_scale=False, signs=None):
+                      sm_scale=None, return_scale=False, signs=None, meta16=False):
     """q fp16 [S, Hq, d]; seq_lens count every cached token (the newest included).
     Query head h reads kv head h // (Hq / Hkv).  Returns float64 [S, Hq, d]
     (and, with return_scale, attention_abs_scale per [S, Hq])."""
@@ -547,8 +587,8 @@ def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, b
     scale = np.zeros((s_n, hq))
     for s in range(s_n):
         for kh in range(hkv):
-            kx = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens, signs)[0]
-            vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens, signs)[0]
+            kx = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens, signs, meta16)[0]
+            vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens, signs, meta16)[0]
             for h in range(kh * g, (kh + 1) * g):
                 out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
                 if return_scale:
@@ -557,7 +597,7 @@ def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, b
 
 
 def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
-                           sm_scale=None, return_scale=False, signs=None):
+                           sm_scale=None, return_scale=False, signs=None, meta16=False):
     """Several queries per sequence over the same compressed pages (the read
     path of [aitrends §TL;DR], with a causal mask): q fp16 [S, n_q, Hq, d]
     holds the n_q newest tokens of each sequence, already in the cache, so
@@ -576,8 +616,8 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
     for s in range(s_n):
         n = int(seq_lens[s])
         for kh in range(hkv):
-            kx = read_sequence(pool_k, table[s], n, kh, "K", bits_k, tile_tokens, signs)[0]
-            vx = read_sequence(pool_v, table[s], n, kh, "V", bits_v, tile_tokens, signs)[0]
+            kx = read_sequence(pool_k, table[s], n, kh, "K", bits_k, tile_tokens, signs, meta16)[0]
+            vx = read_sequence(pool_v, table[s], n, kh, "V", bits_v, tile_tokens, signs, meta16)[0]
             for i in range(n_q):
                 visible = n - n_q + i + 1
                 if visible <= 0:
@@ -682,7 +722,7 @@ def read_baseline_sequence(pool, table_row, seq_len, head, role, fp8=False, scal
 
 
 def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bits_v, base_k, base_v,
-                        signs=None):
+                        signs=None, meta16=False):
     """The re-materializing read path's first half: every cached token restored
     from the quantized pages (read_sequence, float64) and written, rounded to
     fp16, into fp16 baseline pools with the same block table (in place).  Pages
@@ -693,9 +733,9 @@ def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bi
         n = int(seq_lens[s])
         if n == 0:
             continue
-        kx = np.stack([read_sequence(pool_k, table[s], n, h, "K", bits_k, tile_tokens, signs)[0]
+        kx = np.stack([read_sequence(pool_k, table[s], n, h, "K", bits_k, tile_tokens, signs, meta16)[0]
                        for h in range(heads)], 1)
-        vx = np.stack([read_sequence(pool_v, table[s], n, h, "V", bits_v, tile_tokens, signs)[0]
+        vx = np.stack([read_sequence(pool_v, table[s], n, h, "V", bits_v, tile_tokens, signs, meta16)[0]
                        for h in range(heads)], 1)
         fill_pages_baseline(kx.astype(np.float16), vx.astype(np.float16), np.array([0, n]), table[s:s + 1],
                             base_k, base_v)

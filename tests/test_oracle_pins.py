@@ -363,6 +363,79 @@ def test_slot_metadata_byte_positions_hand_examples():
             assert c["alpha_byte"] + 4 * c["alpha_len"] == len(raw)
 
 
+def test_fp16_slot_metadata_byte_positions_hand_examples():
+    """fp16-metadata slots: scale, offset and channel-factor slice at the byte
+    positions worked by hand (2 bytes per value; 72 bytes per token at 4 bits,
+    tile 64)."""
+    import struct
+    for c in _golden("slot_metadata_positions.json")["cases_fp16"]:
+        bits, tile = c["bits"], c["tile"]
+        assert orc.slot_bytes(bits, tile, meta16=True) == c["total"]
+        ppt = tile // 16
+        n = tile
+        tq = orc.TileQuant(codes=np.zeros((n, 128), np.uint8), alpha=None, scale=None, offset=None, pre=None,
+                           rotated=None, normalized=None, beta=None,
+                           alpha64=(1.0 + np.arange(128)).astype(np.float64),
+                           scale64=(2.0 ** -3) * (1 + np.arange(n)).astype(np.float64),
+                           offset64=-(2.0 ** -4) * (1 + np.arange(n)).astype(np.float64))
+        e = orc.meta_fp16(tq)[0]
+        pool = orc.new_pool(ppt + 1, 1, bits, tile, meta16=True)
+        pages = np.array([ppt - j for j in range(ppt)], np.int32)
+        orc_impl._store_tile(pool, pages, 0, "K", bits, tile, 0, tq, meta16=True)
+        for j in range(ppt):
+            raw = pool[pages[j], 0].tobytes()
+            ts, to = c["scale_token"], c["offset_token"]
+            assert struct.unpack_from("<e", raw, c["scale_byte"])[0] == 2.0 ** -3 * (1 + 16 * j + ts) * 2.0 ** -e
+            assert struct.unpack_from("<e", raw, c["offset_byte"])[0] == -(2.0 ** -4) * (1 + 16 * j + to) * 2.0 ** -e
+            for i in (0, c["alpha_len"] - 1):
+                assert struct.unpack_from("<e", raw, c["alpha_byte"] + 2 * i)[0] == (1.0 + c["alpha_len"] * j + i) * 2.0 ** e
+            assert c["alpha_byte"] + 2 * c["alpha_len"] == len(raw)
+
+
+def test_fp16_metadata_rebalancing_hand_examples():
+    for c in _golden("meta_fp16.json")["cases"]:
+        tq = orc.TileQuant(codes=None, alpha=None, scale=None, offset=None, pre=None, rotated=None, normalized=None,
+                           beta=None, alpha64=np.array(c["alpha"], float), scale64=np.array(c["S"], float),
+                           offset64=np.array(c["O"], float))
+        e, a16, s16, o16, _, _, _ = orc.meta_fp16(tq)
+        assert e == c["e"]
+        np.testing.assert_array_equal(a16.astype(float), c["alpha16"])
+        np.testing.assert_array_equal(s16.astype(float), c["S16"])
+        np.testing.assert_array_equal(o16.astype(float), c["O16"])
+
+
+@pytest.mark.parametrize("recipe,tile,bits,iters", [(2, 64, 4, 3), (5, 32, 2, 5), (2, 128, 2, 3)])
+def test_fp16_metadata_pages_restore_within_their_rounding_bound(recipe, tile, bits, iters):
+    """The same codes as fp32-metadata pages, and restores that differ from
+    theirs by no more than the fp16 rounding of alpha, S and O allows:
+    |alpha'(S' q + O') - alpha (S q + O)| <= 2^-11 (3 |alpha S q| + 2 |alpha O|)
+    per rotated element (plus the fp32 rounding of the reference)."""
+    import dataclasses
+    wl = dataclasses.replace(inputs.workload(recipe).scaled(num_seqs=2, seq_len=3 * tile + 5), tile_tokens=tile)
+    k, v = inputs.gen_kv(wl, "K"), inputs.gen_kv(wl, "V")
+    table, npages = inputs.block_table(wl)
+    pk32, pv32 = orc.new_pool(npages, wl.hkv, bits, tile), orc.new_pool(npages, wl.hkv, bits, tile)
+    pk16 = orc.new_pool(npages, wl.hkv, bits, tile, meta16=True)
+    pv16 = orc.new_pool(npages, wl.hkv, bits, tile, meta16=True)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, tile, bits, bits, iters, pk32, pv32)
+    orc.quantize_to_pages(k, v, wl.cu_seqlens(), table, tile, bits, bits, iters, pk16, pv16, meta16=True)
+    n = wl.seq_lens[0]
+    for h in range(wl.hkv):
+        for p32, p16, role in ((pk32, pk16, "K"), (pv32, pv16, "V")):
+            _, c32, a32, s32, o32 = orc.read_sequence(p32, table[0], n, h, role, bits, tile)
+            _, c16, a16, s16, o16 = orc.read_sequence(p16, table[0], n, h, role, bits, tile, meta16=True)
+            np.testing.assert_array_equal(c16, c32)
+            for j in range(a32.shape[0]):
+                sl = slice(j * tile, min(n, (j + 1) * tile))
+                q = c32[sl].astype(float)
+                r32 = a32[j].astype(float)[None] * (s32[sl, None] * q + o32[sl, None])
+                r16 = a16[j].astype(float)[None] * (s16[sl, None] * q + o16[sl, None])
+                sq = np.abs(a32[j].astype(float)[None] * s32[sl, None] * q)
+                so = np.abs(a32[j].astype(float)[None] * o32[sl, None])
+                bound = 2.0 ** -11 * (3 * sq + 2 * so) + 1e-6 * (sq + so) + 1e-30
+                assert np.all(np.abs(r16 - r32) <= bound), (role, h, j, float(np.abs(r16 - r32).max()))
+
+
 def test_pages_hold_the_same_values_as_dense_layout():
     wl = inputs.workload(1).scaled(seq_len=200)          # ragged: 3 full tiles + 8 rows
     k = inputs.gen_kv(wl, "K")
