@@ -71,21 +71,22 @@ QUANTIZE_SOURCES = ("kvq_quantize.hip", "kvq_tile.h", "kvq_internal.h")
 
 
 # ----------------------------------------------------------------------------- byte model
-def quantize_bytes(n_token_heads: int, bits: int, tile: int) -> float:
+def quantize_bytes(n_token_heads: int, bits: int, tile: int, meta16: bool = False) -> float:
     """Algorithmic bytes of quantizing n token-heads of K or V: fp16 read,
     codes + scale + offset written, and the tile's channel factors."""
-    return n_token_heads * (2 * D + D * bits / 8 + 8 + 4 * D / tile)
+    return n_token_heads * (2 * D + slot_bytes_per_token(bits, tile, meta16))
 
 
-def slot_bytes_per_token(bits: int, tile: int) -> float:
-    return D * bits / 8 + 8 + 4 * D / tile
+def slot_bytes_per_token(bits: int, tile: int, meta16: bool = False) -> float:
+    m = 2 if meta16 else 4   # bytes per metadata value (fp16 or fp32)
+    return D * bits / 8 + 2 * m + m * D / tile
 
 
-def decode_bytes(wl, lens) -> float:
+def decode_bytes(wl, lens, meta16: bool = False) -> float:
     """Slot bytes of every page read by one decode step (whole tiles)."""
     t = wl.tile_tokens
     tok = sum(int(math.ceil(l / t)) * t for l in lens) * wl.hkv
-    return tok * (slot_bytes_per_token(wl.bits_k, t) + slot_bytes_per_token(wl.bits_v, t))
+    return tok * (slot_bytes_per_token(wl.bits_k, t, meta16) + slot_bytes_per_token(wl.bits_v, t, meta16))
 
 
 def append_bytes(wl, lens_before) -> float:
@@ -206,7 +207,7 @@ def long_context_leg(n_iter: int = 10):
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     modes = {}
-    for name in ("fp16", "fp8", "kvq4", "kvq2", "kvq8"):
+    for name in ("fp16", "fp8", "kvq4", "kvq2", "kvq8", "kvq4_meta16", "kvq2_meta16"):
         if name in ("fp16", "fp8"):
             fp8 = name == "fp8"
             ks = float(k.abs().max()) / 448.0 if fp8 else 1.0
@@ -216,12 +217,12 @@ def long_context_leg(n_iter: int = 10):
             per_token_head = 2 * 128 * (1 if fp8 else 2)
             fill_bytes = token_heads * (2 * 2 * D + per_token_head)
         else:
-            bits = int(name[3:])
-            cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
+            bits, m16 = int(name[3]), name.endswith("meta16")
+            cfg = api.config(wl.tile_tokens, bits, bits, wl.iters, meta_fp16=m16)
             cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
             fill_ms = timed(lambda: cache.quantize_prefill(k, v, cu, max_len), 3)
-            per_token_head = 2 * slot_bytes_per_token(bits, wl.tile_tokens)
-            fill_bytes = 2 * quantize_bytes(token_heads, bits, wl.tile_tokens)
+            per_token_head = 2 * slot_bytes_per_token(bits, wl.tile_tokens, m16)
+            fill_bytes = 2 * quantize_bytes(token_heads, bits, wl.tile_tokens, m16)
         ws = cache.workspace(wl.hq, max_len)
         dec_ms = timed(lambda: cache.decode(q, lens, max_len, out=out, workspace=ws), n_iter)
         dbytes = token_heads * per_token_head
@@ -254,6 +255,8 @@ def long_context_leg(n_iter: int = 10):
     base = modes["fp16"]["decode_attn_ms"]
     for m in modes.values():
         m["speedup_vs_fp16"] = round(base / m["decode_attn_ms"], 3)
+    for m in modes.values():
+        m["bytes_per_token_head"] = round(m["kv_bytes_per_layer_GB"] * 1e9 / token_heads, 2)
     return {"workload": f"{wl.name}, one layer of {wl.layers}", "num_seqs": wl.num_seqs, "context": max_len,
             "kv_heads": wl.hkv, "q_heads": wl.hq, "tile_tokens": wl.tile_tokens, "iters": n_iter,
             "modes": modes,
@@ -754,6 +757,18 @@ def main():
     q8_ms = q8_batch[0].elapsed_time(q8_batch[1]) / q8_batch[2]
     d8_ms = d8_batch[0].elapsed_time(d8_batch[1]) / d8_batch[2]
     del caches_8
+    # fp16 metadata slots (same codes; S, O and the channel factors in fp16)
+    cfg_h = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, meta_fp16=True)
+    caches_h = [api.PagedCache(cfg_h, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
+    qh_batch = batch_ms(lambda j: caches_h[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
+    dh_batch = batch_ms(lambda j: caches_h[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
+    adh_batch = batch_ms(lambda j: caches_h[j % n_pools].append_decode(kn, vn, lens_before, q, max_len + 1, out=out,
+                                                                      workspace=ws), n_q)
+    torch.cuda.synchronize()
+    qh_ms = qh_batch[0].elapsed_time(qh_batch[1]) / qh_batch[2]
+    dh_ms = dh_batch[0].elapsed_time(dh_batch[1]) / dh_batch[2]
+    adh_ms = adh_batch[0].elapsed_time(adh_batch[1]) / adh_batch[2]
+    del caches_h
     # several queries per sequence (a speculative verify of 4 and of 16 draft
     # tokens) over the same pages: tokens past the appended one are stale
     # pool bytes (timing only; parity is in the tests)
@@ -857,6 +872,14 @@ def main():
         "dense_entry_points": dense,
         "randomized_rotation": {"quantize_kernel_ms": round(qs_ms, 4), "decode_attn_ms": round(ds_ms, 4),
                                 "quantize_GBps": round(qbytes / (qs_ms * 1e-3) / 1e9, 1)},
+        "meta_fp16": {"bytes_per_token_head_k": slot_bytes_per_token(wl.bits_k, wl.tile_tokens, True),
+                      "bytes_per_token_head_k_fp32_meta": slot_bytes_per_token(wl.bits_k, wl.tile_tokens),
+                      "quantize_kernel_ms": round(qh_ms, 4), "decode_attn_ms": round(dh_ms, 4),
+                      "decode_step_ms": round(adh_ms, 4),
+                      "quantize_GBps": round(2 * quantize_bytes(ntok_heads, wl.bits_k, wl.tile_tokens, True)
+                                             / (qh_ms * 1e-3) / 1e9, 1),
+                      "decode_attn_GBps": round(decode_bytes(wl, [l + 1 for l in wl.seq_lens], True)
+                                                / (dh_ms * 1e-3) / 1e9, 1)},
         "codes_8bit": {"quantize_kernel_ms": round(q8_ms, 4), "decode_attn_ms": round(d8_ms, 4),
                        "quantize_GBps": round(q8_bytes / (q8_ms * 1e-3) / 1e9, 1),
                        "decode_attn_GBps": round(d8_bytes / (d8_ms * 1e-3) / 1e9, 1)},

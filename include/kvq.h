@@ -93,6 +93,9 @@ typedef struct {
   uint32_t hadamard_signs[4]; /* randomized rotation: bit c mod 32 of word c/32
                                  set = channel c negated before the Hadamard
                                  (and after the inverse); all 0 = plain H */
+  int32_t meta_fp16;      /* 0: slot metadata (scale, offset, channel factors)
+                             in fp32; 1: in fp16 (2- and 4-bit codes only), see
+                             the page-pool layout */
 } kvq_config;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -109,6 +112,13 @@ const char* kvq_version(void);
  *   offset: float32[16]   per token O   (0 for rows past the sequence end)
  *   alpha : float32[16*128/tile_tokens] the slice j*L..(j+1)*L-1 (L = 2048/T)
  *           of the tile's channel factors, j = the page's index in its tile.
+ * With cfg->meta_fp16 = 1 the three metadata arrays hold IEEE fp16 (2 bytes
+ *   each, same order; 72 bytes per token at 4 bits, tile 64, against 80), and
+ *   one power of two per tile moves from S and O into alpha: with M the
+ *   largest |S|, |O| of the tile's tokens, e = floor(log2 M) - 10 (0 if M is 0),
+ *   the slots hold S*2^-e, O*2^-e and alpha*2^e rounded to nearest even (the
+ *   restore alpha*(S*code + O) only sees their products).  Codes are the same
+ *   as with fp32 metadata.
  * Unit order of a token's 128 codes (dense codes and K slots): 16 units of
  *   8 fields, a unit being 8*bits bits (a little-endian 32-bit word at 4
  *   bits, a 16-bit half at 2 bits, a little-endian 64-bit pair of words at 8), unit u at bit 8*bits*u of the token's

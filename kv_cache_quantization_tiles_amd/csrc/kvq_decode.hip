@@ -85,36 +85,15 @@ hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hip
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
-  return by_tile(tile, [&](auto T) {
-    return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
-        dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
-        const QuantArgs q{};
-        if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false>), grid, dim3(64 * kWaves), 0, s, a, q);
-        else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false>), grid, dim3(64 * kWaves), 0, s, a, q);
-        else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, false>), grid, dim3(64 * kWaves), 0, s, a, q);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_combine(a, kChunk, true, s);
-    });
-  });
+hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s) {
+  if (m16) return launch_decode_m16(a, tile, bits_k, bits_v, s);
+  return launch_decode_fmt<false>(a, tile, bits_k, bits_v, s);
 }
 
 hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
-                                hipStream_t s) {
-  return by_tile(tile, [&](auto T) {
-    return by_bits_pair(bits_k, bits_v, [&](auto BK, auto BV) {
-        dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
-        if (a.group <= 4) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, true>), grid, dim3(64 * kWaves), 0, s, a, q);
-        else if (a.group <= 8) hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, true>), grid, dim3(64 * kWaves), 0, s, a, q);
-        else hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, true>), grid, dim3(64 * kWaves), 0, s, a, q);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        DecodeArgs b = a;
-        b.seq_lens_plus_one = 1;
-        return launch_combine(b, kChunk, true, s);
-    });
-  });
+                                bool m16, hipStream_t s) {
+  if (m16) return launch_append_decode_m16(a, q, tile, bits_k, bits_v, s);
+  return launch_append_decode_fmt<false>(a, q, tile, bits_k, bits_v, s);
 }
 
 }  // namespace kvq

@@ -278,7 +278,9 @@ struct alignas(16) DecodeSmemU {
 // the tokens before L - n_q + i + 1.
 // Groups of up to 8 heads keep 2 waves per SIMD (at most 256 registers in all,
 // VGPRs and AGPRs); 16 heads need more registers and run 1 wave per SIMD.
-template <int T, int BK, int BV, int HG, bool FUSED, bool MQ = false>
+// M16: slots with fp16 metadata (scales, offsets and channel factors read as
+// fp16 and widened to fp32; the arithmetic is the same).
+template <int T, int BK, int BV, int HG, bool FUSED, bool MQ = false, bool M16 = false>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(HG <= 2 ? 2 : 1)))
 void decode_kernel(DecodeArgs A, QuantArgs Q) {
   constexpr int NH = 4 * HG;
@@ -287,8 +289,10 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   constexpr int CB = (T == 32) ? 3 : 4;          // CBSZ of the QK broadcast
   constexpr int TPC = (T == 32) ? 2 : 1;         // tiles per chunk
   constexpr int PPT = T / kPage;                 // pages per tile
-  constexpr int SLOT_K = slot_bytes(BK, T), SLOT_V = slot_bytes(BV, T);
+  constexpr int SLOT_K = slot_bytes(BK, T, M16), SLOT_V = slot_bytes(BV, T, M16);
   constexpr int CODE_K = slot_code_bytes(BK), CODE_V = slot_code_bytes(BV);
+  constexpr int OFF_K = slot_offset_at(BK, M16), OFF_V = slot_offset_at(BV, M16);
+  constexpr int ALPHA_K = slot_alpha_at(BK, M16), ALPHA_V = slot_alpha_at(BV, M16);
   constexpr int AL = slot_alpha_len(T);
   // V fields of tokens 2 and 3 of a quad weigh kTok times those of tokens 0, 1;
   // their probabilities enter the MFMA divided by kTok.
@@ -351,16 +355,16 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         constexpr int QG = DecodeSmemU<T, HG, FUSED>::QG;
         const int g = threadIdx.x / (2 * T), tid = threadIdx.x % (2 * T);
         if constexpr (QG == 1) {
-          quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[0].f, &smu.q[0].s, 0, kvh, seq, tile_idx, tid);
+          quantize_tile_body<T, BK, false, kAppend, M16>(Q, smu.q[0].f, &smu.q[0].s, 0, kvh, seq, tile_idx, tid);
           __syncthreads();
-          quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[0].f, &smu.q[0].s, 1, kvh, seq, tile_idx, tid);
+          quantize_tile_body<T, BV, true, kAppend, M16>(Q, smu.q[0].f, &smu.q[0].s, 1, kvh, seq, tile_idx, tid);
         } else {
           // groups 2j and 2j + 1 quantize K and V; with 4 groups (tile 32) the
           // second pair repeats the first, writing the same bytes, so that every
           // wave meets the quantizer's barriers
           if ((g & 1) == 0)
-            quantize_tile_body<T, BK, false, kAppend>(Q, smu.q[g].f, &smu.q[g].s, 0, kvh, seq, tile_idx, tid);
-          else quantize_tile_body<T, BV, true, kAppend>(Q, smu.q[g].f, &smu.q[g].s, 1, kvh, seq, tile_idx, tid);
+            quantize_tile_body<T, BK, false, kAppend, M16>(Q, smu.q[g].f, &smu.q[g].s, 0, kvh, seq, tile_idx, tid);
+          else quantize_tile_body<T, BV, true, kAppend, M16>(Q, smu.q[g].f, &smu.q[g].s, 1, kvh, seq, tile_idx, tid);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -409,8 +413,8 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       } else if (BK == 4) kq[blk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sl + 256 * blk + 16 * (lane & 15)));
       else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 128 * blk + 8 * (lane & 15))); kq[blk] = u32x4{x[0], x[1], 0u, 0u}; }
     }
-    sk = __builtin_nontemporal_load(reinterpret_cast<const float*>(sl + CODE_K) + (lane & 15));
-    ok = __builtin_nontemporal_load(reinterpret_cast<const float*>(sl + CODE_K + 64) + (lane & 15));
+    sk = load_meta<M16>(sl + CODE_K, lane & 15);
+    ok = load_meta<M16>(sl + OFF_K, lane & 15);
   };
   auto load_v = [&](int c) {
 #pragma unroll
@@ -423,8 +427,17 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 8 * lane)); vq[p] = u32x4{x[0], x[1], 0u, 0u}; }
     }
     const uint8_t* sl = vslot(4 * c + (bq >> 2));
-    svq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 16 * (bq & 3)));
-    ovq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 64 + 16 * (bq & 3)));
+    if constexpr (M16) {
+      const u32x2 sw = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + CODE_V + 8 * (bq & 3)));
+      const u32x2 ow = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + OFF_V + 8 * (bq & 3)));
+      svq = f32x4{half_bits_to_float((uint16_t)sw[0]), half_bits_to_float((uint16_t)(sw[0] >> 16)),
+                  half_bits_to_float((uint16_t)sw[1]), half_bits_to_float((uint16_t)(sw[1] >> 16))};
+      ovq = f32x4{half_bits_to_float((uint16_t)ow[0]), half_bits_to_float((uint16_t)(ow[0] >> 16)),
+                  half_bits_to_float((uint16_t)ow[1]), half_bits_to_float((uint16_t)(ow[1] >> 16))};
+    } else {
+      svq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + CODE_V + 16 * (bq & 3)));
+      ovq = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sl + OFF_V + 16 * (bq & 3)));
+    }
   };
   auto load_alpha = [&](int c) {
     // QK steps of this lane: s = BLK st + bq % BLK; element k is channel qk_channel(s, k)
@@ -435,7 +448,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int ch = qk_channel<BK>(s, k);
-        ak[st][k] = reinterpret_cast<const float*>(kslot(tp + ch / AL) + CODE_K + 128)[ch % AL];
+        ak[st][k] = load_meta<M16>(kslot(tp + ch / AL) + ALPHA_K, ch % AL);
       }
     }
   };
@@ -446,7 +459,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int ch = lane + 64 * h;
-        av[tt][h] = reinterpret_cast<const float*>(vslot(tpv + ch / AL) + CODE_V + 128)[ch % AL];
+        av[tt][h] = load_meta<M16>(vslot(tpv + ch / AL) + ALPHA_V, ch % AL);
       }
     }
   };
@@ -845,6 +858,22 @@ hipError_t by_tile(int tile, F&& f) {
   }
   return hipErrorInvalidValue;
 }
+// Slot formats with fp32 metadata (M16 false: code widths 2 and 4 in any
+// pairing, 8 for both) or fp16 metadata (M16 true: 2 and 4 only).
+template <bool M16, typename F>
+hipError_t by_format(int bits_k, int bits_v, F&& f) {
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  if constexpr (!M16) {
+    if (bits_k == 8 && bits_v == 8) return f(I8{}, I8{});
+  }
+  if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{});
+  if (bits_k == 4 && bits_v == 2) return f(I4{}, I2{});
+  if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{});
+  if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{});
+  return hipErrorInvalidValue;
+}
 // K and V code widths: 2 and 4 in any pairing, 8 for both
 template <typename F>
 hipError_t by_bits_pair(int bits_k, int bits_v, F&& f) {
@@ -857,6 +886,72 @@ hipError_t by_bits_pair(int bits_k, int bits_v, F&& f) {
   if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{});
   if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{});
   return hipErrorInvalidValue;
+}
+
+// Launchers of the decode kernel for one metadata format (each translation
+// unit instantiates one format); the partition merge follows.
+template <bool M16>
+hipError_t launch_decode_fmt(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_format<M16>(bits_k, bits_v, [&](auto BK, auto BV) {
+      dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
+      const QuantArgs q{};
+      if (a.group <= 4)
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      else if (a.group <= 8)
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      else
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, false, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_combine(a, kChunk, true, s);
+    });
+  });
+}
+
+template <bool M16>
+hipError_t launch_append_decode_fmt(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
+                                    hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_format<M16>(bits_k, bits_v, [&](auto BK, auto BV) {
+      dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
+      if (a.group <= 4)
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, true, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      else if (a.group <= 8)
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, true, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      else
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, true, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      DecodeArgs b = a;
+      b.seq_lens_plus_one = 1;
+      return launch_combine(b, kChunk, true, s);
+    });
+  });
+}
+
+// Several queries per sequence: rows beyond 4 run in blocks of 8 (two groups
+// of 4 heads); blocks of 16 read the pages once but measured slower (a
+// 4-token verify at 4 x 16K, 8 kv / 32 query heads: 97 us against 67 us), as
+// did blocks of 4 (88 us).
+template <bool M16>
+hipError_t launch_multi_query_fmt(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
+  return by_tile(tile, [&](auto T) {
+    return by_format<M16>(bits_k, bits_v, [&](auto BK, auto BV) {
+      const int rows = a.n_q * a.group;
+      const QuantArgs q{};
+      if (rows <= 4) {
+        dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false, true, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      } else {
+        dim3 grid(a.kv_heads * ((rows + 7) / 8) * a.num_seqs, a.max_parts);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false, true, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_combine(a, 64, true, s);
+    });
+  });
 }
 
 }  // namespace

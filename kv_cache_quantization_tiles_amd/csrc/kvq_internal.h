@@ -15,10 +15,19 @@ constexpr float kGuard2 = 1e-4f;
 constexpr double kGuard = 1e-2;   // the same test in float64: std > kGuard * rms
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 
+// Slot layout: codes | scale[16] | offset[16] | alpha slice[2048 / T], the
+// metadata fp32 (4 bytes each) or, with fp16 metadata (M16), fp16 (2 bytes).
 __host__ __device__ constexpr int slot_code_bytes(int bits) { return kPage * kHeadDim * bits / 8; }
 __host__ __device__ constexpr int slot_alpha_len(int tile) { return kPage * kHeadDim / tile; }
-__host__ __device__ constexpr int slot_bytes(int bits, int tile) {
-  return slot_code_bytes(bits) + 8 * kPage + 4 * slot_alpha_len(tile);
+__host__ __device__ constexpr int meta_bytes(bool m16) { return m16 ? 2 : 4; }
+__host__ __device__ constexpr int slot_bytes(int bits, int tile, bool m16 = false) {
+  return slot_code_bytes(bits) + meta_bytes(m16) * (2 * kPage + slot_alpha_len(tile));
+}
+__host__ __device__ constexpr int slot_offset_at(int bits, bool m16) {   // byte of offset[0]
+  return slot_code_bytes(bits) + meta_bytes(m16) * kPage;
+}
+__host__ __device__ constexpr int slot_alpha_at(int bits, bool m16) {    // byte of alpha slice[0]
+  return slot_code_bytes(bits) + meta_bytes(m16) * 2 * kPage;
 }
 
 // Arguments of the tile-quantizer kernels (dense, paged prefill, append).
@@ -106,19 +115,23 @@ struct RematArgs {
 };
 
 hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s);
-hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v,
+hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16,
                                  int num_seqs, int max_seq_len, hipStream_t s);
-hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
+hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16, int num_seqs,
                          hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream_t s);
-hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, int num_seqs,
+hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, bool m16, int num_seqs,
                                 int max_seq_len, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s);
+hipError_t launch_decode_m16(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s);
-hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
+hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s);
+hipError_t launch_multi_query_m16(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
-                                hipStream_t s);
+                                bool m16, hipStream_t s);
+hipError_t launch_append_decode_m16(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
+                                    hipStream_t s);
 hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, int max_seq_len, hipStream_t s);
 hipError_t launch_decode_baseline(const DecodeArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_append_baseline(const BaseFillArgs& a, const int32_t* lens_before, bool fp8, int num_seqs,
@@ -137,14 +150,6 @@ __device__ __forceinline__ bool any_sign(const uint32_t* signs) {
   return (signs[0] | signs[1] | signs[2] | signs[3]) != 0u;
 }
 
-// Value of lane (lane ^ M) for M in {1, 2, 4, 8, 16} (ds_swizzle bit mode,
-// within each group of 32 lanes).
-template <int M>
-__device__ __forceinline__ float lane_xor(float v) {
-  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16, "xor within 32 lanes");
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
-}
-
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   _Float16 f;
   __builtin_memcpy(&f, &h, 2);
@@ -157,5 +162,39 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float x) {
   __builtin_memcpy(&h, &f, 2);
   return h;
 }
+
+// One metadata value (scale, offset or channel factor) at element i of an
+// array starting at byte pointer p: fp32, or fp16 with M16 (read as fp32).
+template <bool M16>
+__device__ __forceinline__ float load_meta(const uint8_t* p, int i) {
+  if constexpr (M16) return half_bits_to_float(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p) + i));
+  else return __builtin_nontemporal_load(reinterpret_cast<const float*>(p) + i);
+}
+template <bool M16>
+__device__ __forceinline__ void store_meta(uint8_t* p, int i, float v) {
+  if constexpr (M16) reinterpret_cast<uint16_t*>(p)[i] = float_to_half_bits(v);
+  else reinterpret_cast<float*>(p)[i] = v;
+}
+
+// fp16 metadata keep one power of two per tile out of the scales and offsets:
+// with M the largest |S|, |O| of the tile's tokens, e = floor(log2 M) - 10
+// (0 for M = 0 or not normal); S and O are stored times 2^-e and the channel
+// factors times 2^e (their products, all the restore uses, are unchanged).
+__device__ __forceinline__ int meta_exponent(float m) {
+  const int ex = (int)((__float_as_uint(m) >> 23) & 0xFFu);
+  return (ex == 0 || ex == 0xFF) ? 0 : ex - 127 - 10;
+}
+__device__ __forceinline__ float pow2f(int e) {   // 2^e for |e| < 127
+  return __uint_as_float((unsigned)(127 + e) << 23);
+}
+
+// Value of lane (lane ^ M) for M in {1, 2, 4, 8, 16} (ds_swizzle bit mode,
+// within each group of 32 lanes).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16, "xor within 32 lanes");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
+}
+
 
 }  // namespace kvq

@@ -128,7 +128,7 @@ __device__ __forceinline__ double quad_dpp(double v) {
 // offsets and channel factors, and leaves in R the integer codes of the
 // lane's rows in the fp32 path's layout (zeros past the tile's end), ready
 // for the code store.
-template <int T, int BITS, int MODE>
+template <int T, int BITS, int MODE, bool M16>
 __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, int role, int head, int seq,
                                            int t0, int n, const uint16_t* rows_base, size_t row_stride,
                                            int r_new, int tid, float (&R)[8][8], uint8_t* pool,
@@ -137,7 +137,8 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
   constexpr int NT = 2 * T;
   constexpr int CODE_BYTES = slot_code_bytes(BITS);
   constexpr int AL = slot_alpha_len(T);
-  constexpr int SLOT = slot_bytes(BITS, T);
+  constexpr int SLOT = slot_bytes(BITS, T, M16);
+  constexpr int OFF_AT = slot_offset_at(BITS, M16), ALPHA_AT = slot_alpha_at(BITS, M16);
   constexpr double kInvSqrtD64 = 0.088388347648318440550;   // 1/sqrt(128)
   const int H = (MODE == kDense) ? A.heads : A.kv_heads;
   const bool act = tid < 64;
@@ -283,8 +284,20 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
     cw[v] = w;
   }
   // scales and offsets: S = beta * step, O = beta * min (0 past the tile's end)
-  const float S = real ? (float)(beta * step) : 0.f;
-  const float O = real ? (float)(beta * mn) : 0.f;
+  double bs = real ? beta * step : 0.0, bo = real ? beta * mn : 0.0;
+  double ea = 1.0;   // fp16 metadata: the power of two moved into the channel factors
+  if constexpr (M16) {
+    double m = (k == 0) ? fmax(fabs(bs), fabs(bo)) : 0.0;   // the tile's largest |S|, |O| (wave 0 holds it)
+#pragma unroll
+    for (int sb = 1; sb < 64; sb <<= 1) m = fmax(m, __shfl_xor(m, sb));
+    const int ex = (int)((__double_as_longlong(m) >> 52) & 0x7FF);
+    const int e = (ex == 0 || ex == 0x7FF) ? 0 : ex - 1023 - 10;
+    ea = __longlong_as_double((long long)(1023 + e) << 52);
+    bs /= ea;
+    bo /= ea;
+    if (tid == 0) sh.inv_g[0] = ea;   // for the channel factors' writers (after the barrier below)
+  }
+  const float S = (float)bs, O = (float)bo;
   if (MODE == kDense) {
     if (act && k == 0 && t < n) {
       A.scale[(size_t)(t0 + t) * H + head] = S;
@@ -292,12 +305,17 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
     }
   } else {
     if (act && k == 0) {
-      reinterpret_cast<float*>(page_slot(0) + CODE_BYTES)[t] = S;
-      reinterpret_cast<float*>(page_slot(0) + CODE_BYTES + 4 * kPage)[t] = O;
+      if constexpr (M16) {
+        store_meta<true>(page_slot(0) + CODE_BYTES, t, (float)(_Float16)bs);
+        store_meta<true>(page_slot(0) + OFF_AT, t, (float)(_Float16)bo);
+      } else {
+        store_meta<false>(page_slot(0) + CODE_BYTES, t, S);
+        store_meta<false>(page_slot(0) + OFF_AT, t, O);
+      }
     }
     if (tid >= kShortTile && tid < T) {   // rows of the tile's later pages
-      reinterpret_cast<float*>(page_slot(tid / kPage) + CODE_BYTES)[tid % kPage] = 0.f;
-      reinterpret_cast<float*>(page_slot(tid / kPage) + CODE_BYTES + 4 * kPage)[tid % kPage] = 0.f;
+      store_meta<M16>(page_slot(tid / kPage) + CODE_BYTES, tid % kPage, 0.f);
+      store_meta<M16>(page_slot(tid / kPage) + OFF_AT, tid % kPage, 0.f);
     }
   }
   // codes to the fp32 path's register layout through LDS ([token][channel] bytes over col)
@@ -307,10 +325,11 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
     *reinterpret_cast<qt_u32x4*>(code8 + kHeadDim * t + 32 * k) = qt_u32x4{cw[0], cw[1], cw[2], cw[3]};
     *reinterpret_cast<qt_u32x4*>(code8 + kHeadDim * t + 32 * k + 16) = qt_u32x4{cw[4], cw[5], cw[6], cw[7]};
   }
+  if constexpr (M16) ea = sh.inv_g[0];
   for (int c = tid; c < kHeadDim; c += NT) {
-    const float al = (float)sh.alpha[c];
-    if (MODE == kDense) A.alpha[((size_t)(t0 / T) * H + head) * kHeadDim + c] = al;
-    else reinterpret_cast<float*>(page_slot(c / AL) + CODE_BYTES + 8 * kPage)[c % AL] = al;
+    if (MODE == kDense) A.alpha[((size_t)(t0 / T) * H + head) * kHeadDim + c] = (float)sh.alpha[c];
+    else if constexpr (M16) store_meta<true>(page_slot(c / AL) + ALPHA_AT, c % AL, (float)(_Float16)(sh.alpha[c] * ea));
+    else store_meta<false>(page_slot(c / AL) + ALPHA_AT, c % AL, (float)sh.alpha[c]);
   }
   __syncthreads();
   const int lane = tid & 63, w = tid >> 6, j = lane & 15, g = lane >> 4;
@@ -327,7 +346,8 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
 // over the sequences' last tiles), or both by a runtime branch (appends).
 enum TilePath { kPathFp32 = 0, kPathShort = 1, kPathBoth = 2 };
 
-template <int T, int BITS, bool VLAYOUT, int MODE, int PATH = (MODE == kAppend) ? kPathBoth : kPathFp32>
+template <int T, int BITS, bool VLAYOUT, int MODE, bool M16 = false,
+          int PATH = (MODE == kAppend) ? kPathBoth : kPathFp32>
 __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& sm, ShortSmem* sh, int role,
                                                    int head, int seq, int tile_idx, int tid) {
   constexpr int NT = 2 * T;
@@ -406,8 +426,9 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
   // Output addressing (paged): the tile's pages.
   uint8_t* pool = nullptr;
   const int32_t* pages = nullptr;
-  constexpr int SLOT = slot_bytes(BITS, T);
+  constexpr int SLOT = slot_bytes(BITS, T, M16);
   constexpr int CODE_BYTES = slot_code_bytes(BITS);
+  constexpr int OFF_AT = slot_offset_at(BITS, M16), ALPHA_AT = slot_alpha_at(BITS, M16);
   if (MODE != kDense) {
     pool = A.pool[role];
     pages = A.block_table + (size_t)seq * A.max_blocks + (t0 / kPage);
@@ -418,7 +439,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
 
   float R[8][8];   // [q = 4 bb + r][m = sigma + 2 p']: token tok(q), channel j + 16 m
   if (PATH != kPathFp32 && (PATH == kPathShort || n_valid < kShortTile)) {   // uniform over the group
-    short_tile<T, BITS, MODE>(A, *sh, role, head, seq, t0, n_valid, rows_base, row_stride, r_new, tid, R, pool,
+    short_tile<T, BITS, MODE, M16>(A, *sh, role, head, seq, t0, n_valid, rows_base, row_stride, r_new, tid, R, pool,
                               pages);
   } else {
     // ---------------------------------------------------------------- Hadamard (unnormalized)
@@ -642,6 +663,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     }
     __syncthreads();
 
+    float step = 0.f, off = 0.f;
     if (tid < T) {
       float mn = red0[tid], mx = red1[tid];
 #pragma unroll
@@ -649,7 +671,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         mn = fminf(mn, red0[jj * kRedStride<T> + tid]);
         mx = fmaxf(mx, red1[jj * kRedStride<T> + tid]);
       }
-      float step = 0.f, off = 0.f, inv = 0.f, nmi = 0.f;
+      float inv = 0.f, nmi = 0.f;
       if (tid < n_valid) {
         const float range = mx - mn;
         step = range * (1.0f / LEVELS);
@@ -666,10 +688,27 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
           A.scale[(size_t)(t0 + tid) * H + head] = step;
           A.offset[(size_t)(t0 + tid) * H + head] = off;
         }
-      } else {
+      } else if (!M16) {
         uint8_t* slot = slot_ptr(tid / kPage);
-        reinterpret_cast<float*>(slot + CODE_BYTES)[tid % kPage] = step;
-        reinterpret_cast<float*>(slot + CODE_BYTES + 4 * kPage)[tid % kPage] = off;
+        store_meta<false>(slot + CODE_BYTES, tid % kPage, step);
+        store_meta<false>(slot + OFF_AT, tid % kPage, off);
+      }
+    }
+    float ea = 1.f;   // fp16 metadata: the power of two moved into the channel factors
+    if constexpr (M16 && MODE != kDense) {
+      float m = fmaxf(fabsf(step), fabsf(off));   // the tile's largest |S|, |O| (0 past its end)
+#pragma unroll
+      for (int sb = 1; sb < 64; sb <<= 1) m = fmaxf(m, __shfl_xor(m, sb));
+      if (lane == 0) sm.ref_t[w] = m;   // (the token-step references are no longer needed)
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NT / 64; ++i) m = fmaxf(m, sm.ref_t[i]);
+      const int e = meta_exponent(m);
+      ea = pow2f(e);
+      if (tid < T) {
+        uint8_t* slot = slot_ptr(tid / kPage);
+        store_meta<true>(slot + CODE_BYTES, tid % kPage, step * pow2f(-e));
+        store_meta<true>(slot + OFF_AT, tid % kPage, off * pow2f(-e));
       }
     }
     for (int c = tid; c < kHeadDim; c += NT) {
@@ -678,7 +717,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         A.alpha[((size_t)tile_idx * H + head) * kHeadDim + c] = al;
       } else {
         constexpr int AL = slot_alpha_len(T);
-        reinterpret_cast<float*>(slot_ptr(c / AL) + CODE_BYTES + 8 * kPage)[c % AL] = al;
+        store_meta<M16>(slot_ptr(c / AL) + ALPHA_AT, c % AL, al * ea);
       }
     }
     __syncthreads();

@@ -565,20 +565,54 @@ def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: flo
     return p @ values.astype(np.float64)
 
 
-def attention_abs_scale(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: float) -> float:
-    """max over channels of sum_t p_t |v_t| for the attention above: the size
-    of the terms an output channel sums (its rounding scale in fp32)."""
+def attention_abs_scale(q: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: float,
+                        key_terms=None) -> float:
+    """The size of the terms an attention output is made of (its rounding
+    scale in fp32): max over channels c of sum_t p_t |v_t,c| (what the output
+    channel sums), plus, with key_terms, max over c of
+    sum_t p_t |v_t,c - o_c| sm_scale key_terms_t: the output moves by
+    p_t (v_t,c - o_c) per unit of score t, and a score evaluated in fp32
+    carries a rounding proportional to the terms it is summed from
+    (key_score_terms below), not to its own value."""
     s = sm_scale * (keys.astype(np.float64) @ np.asarray(q, np.float64))
     p = np.exp(s - s.max())
     p = p / p.sum()
-    return float((p @ np.abs(values.astype(np.float64))).max())
+    vals = values.astype(np.float64)
+    out = float((p @ np.abs(vals)).max())
+    if key_terms is not None:
+        o = p @ vals
+        out += float(((p * sm_scale * np.asarray(key_terms, np.float64)) @ np.abs(vals - o[None])).max())
+    return out
+
+
+def key_score_parts(q, codes, alpha, scale, offset, tile_tokens, signs=None):
+    """The two terms each cached token's score q . k is the sum of.  The
+    restored key is D H (alpha * (S code + O)) [ttj §quant], so with
+    qt = alpha * H D q (rotated query times the channel factors) the score is
+    S sum_c qt_c code_c + O sum_c qt_c.  Returns the two terms per token
+    (float64 [L] each); alpha per tile [ntiles, d] (read_sequence's layout)."""
+    hq = fwht(np.asarray(q, np.float64) * signs_from_mask(signs))
+    n = len(scale)
+    qt = hq[None] * np.asarray(alpha, np.float64)[np.arange(n) // tile_tokens]
+    return (np.asarray(scale, np.float64) * (qt * np.asarray(codes, np.float64)).sum(1),
+            np.asarray(offset, np.float64) * qt.sum(1))
+
+
+def key_score_terms(q, codes, alpha, scale, offset, tile_tokens, signs=None) -> np.ndarray:
+    """|first| + |second| of key_score_parts per token: in tiles whose per-token
+    factors are large (S and O of 1e4 and more in tiles of a few tokens) the
+    two terms nearly cancel, and a score evaluated in fp32 carries a rounding
+    proportional to them, not to its own value."""
+    a, b = key_score_parts(q, codes, alpha, scale, offset, tile_tokens, signs)
+    return np.abs(a) + np.abs(b)
 
 
 def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
                       sm_scale=None, return_scale=False, signs=None, meta16=False):
     """q fp16 [S, Hq, d]; seq_lens count every cached token (the newest included).
     Query head h reads kv head h // (Hq / Hkv).  Returns float64 [S, Hq, d]
-    (and, with return_scale, attention_abs_scale per [S, Hq])."""
+    (and, with return_scale, attention_abs_scale per [S, Hq], score terms
+    included)."""
     s_n, hq, d = q.shape
     hkv = pool_k.shape[1]
     g = hq // hkv
@@ -587,12 +621,14 @@ def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, b
     scale = np.zeros((s_n, hq))
     for s in range(s_n):
         for kh in range(hkv):
-            kx = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens, signs, meta16)[0]
+            kx, kc, ka, ks, ko = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens,
+                                               signs, meta16)
             vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens, signs, meta16)[0]
             for h in range(kh * g, (kh + 1) * g):
                 out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
                 if return_scale:
-                    scale[s, h] = attention_abs_scale(q[s, h], kx, vx, sm)
+                    terms = key_score_terms(q[s, h], kc, ka, ks, ko, tile_tokens, signs)
+                    scale[s, h] = attention_abs_scale(q[s, h], kx, vx, sm, terms)
     return (out, scale) if return_scale else out
 
 
@@ -606,7 +642,7 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
     step.  A query at a negative position (a sequence shorter than n_q) sees
     no token: its output row is zero, as the library defines it.  Returns
     float64 [S, n_q, Hq, d] (and, with return_scale, attention_abs_scale per
-    [S, n_q, Hq])."""
+    [S, n_q, Hq], score terms included)."""
     s_n, n_q, hq, d = q.shape
     hkv = pool_k.shape[1]
     g = hq // hkv
@@ -616,7 +652,7 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
     for s in range(s_n):
         n = int(seq_lens[s])
         for kh in range(hkv):
-            kx = read_sequence(pool_k, table[s], n, kh, "K", bits_k, tile_tokens, signs, meta16)[0]
+            kx, kc, ka, ks, ko = read_sequence(pool_k, table[s], n, kh, "K", bits_k, tile_tokens, signs, meta16)
             vx = read_sequence(pool_v, table[s], n, kh, "V", bits_v, tile_tokens, signs, meta16)[0]
             for i in range(n_q):
                 visible = n - n_q + i + 1
@@ -626,7 +662,8 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
                     qv = q[s, i, h].astype(np.float64)
                     out[s, i, h] = attention(qv, kx[:visible], vx[:visible], sm)
                     if return_scale:
-                        scale[s, i, h] = attention_abs_scale(qv, kx[:visible], vx[:visible], sm)
+                        terms = key_score_terms(qv, kc[:visible], ka, ks[:visible], ko[:visible], tile_tokens, signs)
+                        scale[s, i, h] = attention_abs_scale(qv, kx[:visible], vx[:visible], sm, terms)
     return (out, scale) if return_scale else out
 
 

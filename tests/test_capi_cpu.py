@@ -40,6 +40,13 @@ def test_version_and_slot_sizes_match_oracle_layout(lib):
             cfg = L.config(tile, bk, bv, 3)
             assert L.kvq_slot_bytes(cfg, False) == orc.slot_bytes(bk, tile)
             assert L.kvq_slot_bytes(cfg, True) == orc.slot_bytes(bv, tile)
+            cfg16 = L.config(tile, bk, bv, 3, meta_fp16=True)
+            if bk == 8:
+                assert L.kvq_slot_bytes(cfg16, False) == 0   # fp16 metadata take 2- and 4-bit codes only
+            else:
+                assert L.kvq_slot_bytes(cfg16, False) == orc.slot_bytes(bk, tile, meta16=True)
+                assert L.kvq_slot_bytes(cfg16, True) == orc.slot_bytes(bv, tile, meta16=True)
+    assert L.kvq_slot_bytes(L.config(64, 4, 4, 3, meta_fp16=True), False) == 72 * 16
 
 
 @pytest.mark.parametrize("field,value,status", [

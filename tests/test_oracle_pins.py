@@ -839,3 +839,30 @@ def test_multi_query_rows_before_the_sequence_start_are_zero():
     for i in range(3, n_q):
         dec = orc.paged_decode_attn(q[1:, i], table[1:], np.array([i - 2]), pk, pv, 32, 4, 2)
         np.testing.assert_array_equal(out[1, i], dec[0])
+
+
+def test_key_score_parts_sum_to_the_score_on_the_restored_keys():
+    """The two score terms (S sum qt code, O sum qt) add up to q . k with k the
+    oracle's own restore, for the plain and the randomized rotation, and
+    their magnitudes bound |q . k|."""
+    rng = np.random.default_rng(11)
+    for tile, bits, mask in ((64, 4, None), (32, 2, np.array([0x12345678, 0xFFFF0000, 7, 0x80000001], np.uint32))):
+        x = rng.standard_normal((2 * tile + 5, 128)) * np.exp(rng.uniform(-2, 2, 128))
+        x = x.astype(np.float16)
+        q = rng.standard_normal(128).astype(np.float16)
+        n = x.shape[0]
+        codes = np.zeros((n, 128))
+        scale, offset = np.zeros(n), np.zeros(n)
+        alpha = np.zeros(((n + tile - 1) // tile, 128))
+        keys = np.zeros((n, 128))
+        for j in range(alpha.shape[0]):
+            sl = slice(j * tile, min(n, (j + 1) * tile))
+            tq = orc.quantize_tile(x[sl], bits, 3, signs=mask)
+            codes[sl], scale[sl], offset[sl], alpha[j] = tq.codes, tq.scale64, tq.offset64, tq.alpha64
+            keys[sl] = orc.dequantize_tile(tq.codes, tq.alpha64, tq.scale64, tq.offset64, mask)
+        a, b = orc.key_score_parts(q, codes, alpha, scale, offset, tile, mask)
+        dot = keys @ q.astype(np.float64)
+        np.testing.assert_allclose(a + b, dot, rtol=1e-9, atol=1e-9 * np.abs(a).max())
+        terms = orc.key_score_terms(q, codes, alpha, scale, offset, tile, mask)
+        assert (np.abs(dot) <= terms * (1 + 1e-12)).all()
+        assert (terms > 10 * np.abs(dot)).any()    # the terms cancel: asymmetric codes carry an offset
