@@ -220,7 +220,7 @@ def long_context_leg(n_iter: int = 10):
             bits, m16 = int(name[3]), name.endswith("meta16")
             cfg = api.config(wl.tile_tokens, bits, bits, wl.iters, meta_fp16=m16)
             cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
-            fill_ms = timed(lambda: cache.quantize_prefill(k, v, cu, max_len), 3)
+            fill_ms = timed(lambda: cache.quantize_prefill(k, v, cu), 3)
             per_token_head = 2 * slot_bytes_per_token(bits, wl.tile_tokens, m16)
             fill_bytes = 2 * quantize_bytes(token_heads, bits, wl.tile_tokens, m16)
         ws = cache.workspace(wl.hq, max_len)
@@ -309,7 +309,7 @@ def latency_leg(n: int = 50):
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b) * 1e3)
         return float(np.median(ts))
-    tq = one(lambda: cache.quantize_prefill(k, v, cu, max(wl.seq_lens)))
+    tq = one(lambda: cache.quantize_prefill(k, v, cu))
     td = one(lambda: cache.append_decode(kn, vn, lens, q, max(wl.seq_lens) + 1, out=out, workspace=ws))
     return {"workload": wl.name, "tokens": wl.total_tokens, "kv_heads": wl.hkv, "q_heads": wl.hq,
             "quantize_latency_us": round(tq, 2), "decode_step_latency_us": round(td, 2),
@@ -335,7 +335,7 @@ def rematerialize_leg(idx: int, n_iter: int = 20):
     nc = max(2, int(math.ceil(1.0e9 / pool_bytes)))
     caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(nc)]
     for c in caches:
-        c.quantize_prefill(k, v, cu, max_len)
+        c.quantize_prefill(k, v, cu)
     del k, v
     base = [api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(2)]
     lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=dev)
@@ -404,7 +404,7 @@ def long_context_decode_phase(n_steps: int = 1024):
             bits = int(name[3:])
             cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
             cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
-            cache.quantize_prefill(k, v, cu, max_len)
+            cache.quantize_prefill(k, v, cu)
             ws = cache.workspace(wl.hq, max_len + n_steps)
 
             def step(i):
@@ -465,12 +465,12 @@ def burst_leg():
     out = torch.empty((wl.num_seqs, wl.hq, D), dtype=torch.float32, device=dev)
     caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(2)]
     ws = caches[0].workspace(wl.hq, max_len + steps)
-    caches[1].quantize_prefill(k, v, cu, max_len)   # warm-up
+    caches[1].quantize_prefill(k, v, cu)   # warm-up
     torch.cuda.synchronize()
     c = caches[0]
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     e[0].record()
-    c.quantize_prefill(k, v, cu, max_len)
+    c.quantize_prefill(k, v, cu)
     e[1].record()
     for i in range(steps):
         c.append_decode(kn[i], vn[i], lens[i], qs[i], max_len + steps, out=out, workspace=ws)
@@ -530,9 +530,9 @@ def mixed_leg(n_iter: int = 10):
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
-    q_ms = timed(lambda i: caches[i % 2].quantize_prefill(k, v, cu, max_len), 4)
+    q_ms = timed(lambda i: caches[i % 2].quantize_prefill(k, v, cu), 4)
     for c in caches:
-        c.quantize_prefill(k, v, cu, max_len)
+        c.quantize_prefill(k, v, cu)
     # the append re-quantizes the same tile each time (lengths are not advanced)
     d_ms = timed(lambda i: caches[i % 2].append_decode(kn, vn, lens, q, max_len + 1, out=out, workspace=ws), n_iter)
     th = wl.total_tokens * wl.hkv
@@ -588,7 +588,7 @@ def context_sweep(contexts=(1024, 4096, 16384, 65536, 131072), num_seqs=6, n_ite
                 caches = [api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
                           for _ in range(copies)]
                 for c in caches:
-                    c.quantize_prefill(k, v, cu, ctx)
+                    c.quantize_prefill(k, v, cu)
                 per_tok = 2 * slot_bytes_per_token(bits, wl.tile_tokens)
             ws = caches[0].workspace(wl.hq, ctx)
             for i in range(2):
@@ -677,7 +677,7 @@ def main():
         c = caches[i % n_pools]
         if ev is not None:
             ev[0].record()
-        c.quantize_prefill(ks[i % n_in], vs[i % n_in], cu, max_len)
+        c.quantize_prefill(ks[i % n_in], vs[i % n_in], cu)
         if ev is not None:
             ev[1].record()
         c.append_decode(kn, vn, lens_before, q, max_len + 1, out=out, workspace=ws)
@@ -724,7 +724,7 @@ def main():
         b1.record()
         return b0, b1, n
     n_q = max(20, args.steps)
-    q_batch = batch_ms(lambda j: caches[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
+    q_batch = batch_ms(lambda j: caches[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu), n_q)
     d_batch = batch_ms(lambda j: caches[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
     # the fused decode step alone (append + re-quantize + attend, then the merge), back to back
     ad_batch = batch_ms(lambda j: caches[j % n_pools].append_decode(kn, vn, lens_before, q, max_len + 1, out=out,
@@ -744,14 +744,14 @@ def main():
     # the randomized rotation (a seeded +-1 diagonal before H): same kernels, signs on
     cfg_s = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, hadamard_signs=inputs.hadamard_signs(1))
     caches_s = [api.PagedCache(cfg_s, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
-    qs_batch = batch_ms(lambda j: caches_s[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
+    qs_batch = batch_ms(lambda j: caches_s[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu), n_q)
     ds_batch = batch_ms(lambda j: caches_s[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
     torch.cuda.synchronize()
     del caches_s
     # 8-bit codes for K and V: same kernels at the wider width
     cfg_8 = api.config(wl.tile_tokens, 8, 8, wl.iters)
     caches_8 = [api.PagedCache(cfg_8, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
-    q8_batch = batch_ms(lambda j: caches_8[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
+    q8_batch = batch_ms(lambda j: caches_8[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu), n_q)
     d8_batch = batch_ms(lambda j: caches_8[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
     torch.cuda.synchronize()
     q8_ms = q8_batch[0].elapsed_time(q8_batch[1]) / q8_batch[2]
@@ -760,7 +760,7 @@ def main():
     # fp16 metadata slots (same codes; S, O and the channel factors in fp16)
     cfg_h = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, meta_fp16=True)
     caches_h = [api.PagedCache(cfg_h, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
-    qh_batch = batch_ms(lambda j: caches_h[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu, max_len), n_q)
+    qh_batch = batch_ms(lambda j: caches_h[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu), n_q)
     dh_batch = batch_ms(lambda j: caches_h[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
     adh_batch = batch_ms(lambda j: caches_h[j % n_pools].append_decode(kn, vn, lens_before, q, max_len + 1, out=out,
                                                                       workspace=ws), n_q)

@@ -172,9 +172,13 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const uint8_t* codes, const flo
  * kvq_quantize_to_pages - quantize a prefill of K and V into the page pools.
  *   k, v         fp16 [total_tokens][kv_heads][128], sequences packed back to
  *                back; sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1.
- *   cu_seqlens   int32 [num_seqs+1], device.
- *   max_seq_len  host upper bound of every sequence length (sizes the grid).
- *   block_table  int32 [num_seqs][max_blocks], device.
+ *   cu_seqlens   int32 [num_seqs+1], device, non-decreasing.
+ *   total_tokens host: cu_seqlens[num_seqs] (or more); the launch covers
+ *                total_tokens / T + num_seqs tile slots, which hold every
+ *                tile of any length mix with at most one idle slot per
+ *                sequence (a smaller value leaves the last tiles unwritten).
+ *   block_table  int32 [num_seqs][max_blocks], device; a tile whose pages
+ *                would lie past max_blocks is not written.
  *   pool_k/pool_v  K and V pools (layout above; bits from cfg).
  *   staging_k/staging_v  fp16 [num_seqs][T][kv_heads][128] or NULL: rows
  *                of a last tile that is not full are copied there (needed
@@ -183,7 +187,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const uint8_t* codes, const flo
  */
 kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
                                  const int32_t* cu_seqlens, int32_t num_seqs,
-                                 int32_t max_seq_len, int32_t kv_heads,
+                                 int32_t total_tokens, int32_t kv_heads,
                                  const int32_t* block_table, int32_t max_blocks, void* pool_k,
                                  void* pool_v, kvq_half* staging_k, kvq_half* staging_v,
                                  void* stream);

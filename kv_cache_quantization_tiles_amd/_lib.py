@@ -154,10 +154,10 @@ def kvq_dequantize(cfg, codes, alpha, tok_scale, tok_offset, n_tokens, heads, bi
                                  _ptr(tok_offset), n_tokens, heads, bits, _ptr(out), _stream(stream)))
 
 
-def kvq_quantize_to_pages(cfg, k, v, cu_seqlens, num_seqs, max_seq_len, kv_heads, block_table,
+def kvq_quantize_to_pages(cfg, k, v, cu_seqlens, num_seqs, total_tokens, kv_heads, block_table,
                           max_blocks, pool_k, pool_v, staging_k=None, staging_v=None, stream=None):
     _check(load().kvq_quantize_to_pages(ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs,
-                                        max_seq_len, kv_heads, _ptr(block_table), max_blocks,
+                                        total_tokens, kv_heads, _ptr(block_table), max_blocks,
                                         _ptr(pool_k), _ptr(pool_v), _ptr(staging_k), _ptr(staging_v),
                                         _stream(stream)))
 

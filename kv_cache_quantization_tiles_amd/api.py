@@ -69,9 +69,11 @@ class PagedCache:
         self.staging_k = torch.zeros((num_seqs, t, kv_heads, HEAD_DIM), dtype=torch.float16, device=device)
         self.staging_v = torch.zeros_like(self.staging_k)
 
-    def quantize_prefill(self, k, v, cu_seqlens, max_seq_len):
+    def quantize_prefill(self, k, v, cu_seqlens):
+        """k, v fp16 [total_tokens, kv_heads, 128] (sequences back to back),
+        cu_seqlens int32 [num_seqs + 1] on the device."""
         _require_cuda(k, v, cu_seqlens)
-        kvq_quantize_to_pages(self.cfg, k, v, cu_seqlens, self.num_seqs, int(max_seq_len), self.kv_heads,
+        kvq_quantize_to_pages(self.cfg, k, v, cu_seqlens, self.num_seqs, int(k.shape[0]), self.kv_heads,
                               self.block_table, self.max_blocks, self.pool_k, self.pool_v,
                               self.staging_k, self.staging_v)
 

@@ -197,7 +197,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const uint8_t* codes, const flo
 
 kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const kvq_half* v,
                                  const int32_t* cu_seqlens, int32_t num_seqs,
-                                 int32_t max_seq_len, int32_t kv_heads,
+                                 int32_t total_tokens, int32_t kv_heads,
                                  const int32_t* block_table, int32_t max_blocks, void* pool_k,
                                  void* pool_v, kvq_half* staging_k, kvq_half* staging_v,
                                  void* stream) {
@@ -210,14 +210,12 @@ kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const
   KVQ_NONNULL(pool_v);
   if ((staging_k == nullptr) != (staging_v == nullptr))
     return fail(KVQ_ERR_ARG, "staging_k and staging_v must both be set or both be NULL");
-  if (num_seqs <= 0 || kv_heads <= 0 || max_seq_len <= 0 || max_blocks <= 0)
-    return fail(KVQ_ERR_ARG, "num_seqs, kv_heads, max_seq_len and max_blocks must be > 0");
+  if (num_seqs <= 0 || kv_heads <= 0 || total_tokens <= 0 || max_blocks <= 0)
+    return fail(KVQ_ERR_ARG, "num_seqs, kv_heads, total_tokens and max_blocks must be > 0");
   if (2 * kv_heads > 65535 || num_seqs > 65535) return fail(KVQ_ERR_ARG, "too many heads or sequences");
   const int tile = cfg->tile_tokens;
-  const long need_blocks = (long)((max_seq_len + tile - 1) / tile) * (tile / kvq::kPage);
-  if (need_blocks > max_blocks)
-    return fail(KVQ_ERR_ARG, "max_blocks %d cannot hold %d tokens in whole tiles (%ld pages)", max_blocks,
-                max_seq_len, need_blocks);
+  if (max_blocks < tile / kvq::kPage)
+    return fail(KVQ_ERR_ARG, "max_blocks %d is smaller than one tile", max_blocks);
   kvq::QuantArgs a{};
   a.src[0] = k;
   a.src[1] = v;
@@ -226,12 +224,13 @@ kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const
   a.staging[0] = staging_k;
   a.staging[1] = staging_v;
   a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
   a.block_table = block_table;
   a.max_blocks = max_blocks;
   a.kv_heads = kv_heads;
   a.iters = cfg->sinkhorn_iters;
   set_signs(a, cfg);
-  return launched(kvq::launch_quantize_paged(a, tile, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0, num_seqs, max_seq_len,
+  return launched(kvq::launch_quantize_paged(a, tile, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0, num_seqs, total_tokens,
                                              (hipStream_t)stream),
                   "kvq_quantize_to_pages");
 }

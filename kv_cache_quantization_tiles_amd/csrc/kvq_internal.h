@@ -45,6 +45,7 @@ struct QuantArgs {
   uint8_t* pool[2];
   uint16_t* staging[2];       // [S][T][Hkv][D] or null
   const int32_t* cu_seqlens;  // prefill
+  int num_seqs;               // prefill: sequences in cu_seqlens
   const int32_t* lens_before; // append
   const int32_t* block_table;
   int max_blocks;
@@ -116,7 +117,7 @@ struct RematArgs {
 
 hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s);
 hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16,
-                                 int num_seqs, int max_seq_len, hipStream_t s);
+                                 int num_seqs, int total_tokens, hipStream_t s);
 hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16, int num_seqs,
                          hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream_t s);

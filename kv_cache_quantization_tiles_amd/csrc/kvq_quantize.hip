@@ -35,17 +35,45 @@ __global__ __launch_bounds__(2 * T) void quantize_dense_short_kernel(QuantArgs A
                                                          threadIdx.x);
 }
 
-// grid: x = tile index in the sequence, y = head + Hkv * role (0 K, 1 V), z = sequence
+// grid: x = tile slot, y = head + Hkv * role (0 K, 1 V).  Sequence s owns
+// the slots from floor(cu[s] / T) + s up to the next sequence's start; the
+// starts rise by at least ceil(len / T) (and at most one more), so
+// total_tokens / T + num_seqs slots hold every tile
+// of any length mix with at most one idle slot per sequence (a grid sized by
+// the longest sequence leaves most workgroups idle when lengths vary).  A
+// wave finds its sequence with one load of cu_seqlens per 64 sequences and
+// a ballot: the starts increase, so the sequences starting at or before the
+// slot are a prefix and the last one holds it.
 template <int T, int BK, int BV, bool M16>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void quantize_paged_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
-  const int seq = blockIdx.z;
-  const int len = A.cu_seqlens[seq + 1] - A.cu_seqlens[seq];
-  if ((int)blockIdx.x * T >= len) return;
+  const int f = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  int seq = -1, a0 = 0, a1 = 0;
+  for (int b = 0; b < A.num_seqs; b += 64) {   // uniform
+    const int i = b + lane;
+    int c0 = 0, c1 = 0;
+    bool before = false;
+    if (i < A.num_seqs) {
+      c0 = A.cu_seqlens[i];
+      c1 = A.cu_seqlens[i + 1];
+      before = c0 / T + i <= f;
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(before);
+    if (m != 0) {
+      const int l = 63 - __builtin_clzll(m);
+      seq = b + l;
+      a0 = __builtin_amdgcn_readlane(c0, l);
+      a1 = __builtin_amdgcn_readlane(c1, l);
+    }
+  }
+  if (seq < 0) return;   // uniform over the workgroup from here on
+  const int tile = f - (a0 / T + seq);
+  if (tile * T >= a1 - a0 || (tile + 1) * (T / kPage) > A.max_blocks) return;
   const int role = blockIdx.y / A.kv_heads;
   const int head = blockIdx.y % A.kv_heads;
-  if (role == 0) quantize_tile_body<T, BK, false, kPaged, M16>(A, sm, nullptr, 0, head, seq, blockIdx.x, threadIdx.x);
-  else quantize_tile_body<T, BV, true, kPaged, M16>(A, sm, nullptr, 1, head, seq, blockIdx.x, threadIdx.x);
+  if (role == 0) quantize_tile_body<T, BK, false, kPaged, M16>(A, sm, nullptr, 0, head, seq, tile, threadIdx.x);
+  else quantize_tile_body<T, BV, true, kPaged, M16>(A, sm, nullptr, 1, head, seq, tile, threadIdx.x);
 }
 
 // grid: x = head + Hkv * role, y = sequence: the sequence's last tile when it
@@ -59,6 +87,7 @@ __global__ __launch_bounds__(2 * T) void quantize_paged_short_kernel(QuantArgs A
   const int role = blockIdx.x / A.kv_heads;
   const int head = blockIdx.x % A.kv_heads;
   const int tile = (len - 1) / T;
+  if ((tile + 1) * (T / kPage) > A.max_blocks) return;   // no pages for this tile
   if (role == 0) quantize_tile_body<T, BK, false, kPaged, M16, kPathShort>(A, sm.f, &sm.s, 0, head, seq, tile, threadIdx.x);
   else quantize_tile_body<T, BV, true, kPaged, M16, kPathShort>(A, sm.f, &sm.s, 1, head, seq, tile, threadIdx.x);
 }
@@ -400,10 +429,10 @@ hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStre
 }
 
 hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16,
-                                 int num_seqs, int max_seq_len, hipStream_t s) {
+                                 int num_seqs, int total_tokens, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
     return by_format(bits_k, bits_v, m16, [&](auto BK, auto BV, auto M) {
-      dim3 grid((max_seq_len + T() - 1) / T(), 2 * a.kv_heads, num_seqs);
+      dim3 grid(total_tokens / T() + num_seqs, 2 * a.kv_heads);
       hipLaunchKernelGGL((quantize_paged_kernel<T(), BK(), BV(), M()>), grid, dim3(2 * T()), 0, s, a);
       hipLaunchKernelGGL((quantize_paged_short_kernel<T(), BK(), BV(), M()>), dim3(2 * a.kv_heads, num_seqs),
                          dim3(2 * T()), 0, s, a);

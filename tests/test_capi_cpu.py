@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle as orc
@@ -75,8 +76,9 @@ def test_null_and_size_errors(lib):
     assert lib.kvq_dequantize(cfg, 16, 16, 16, None, 8, 1, 4, 16, None) == L.KVQ_ERR_ARG
     # staging must be both or neither
     assert lib.kvq_quantize_to_pages(cfg, 16, 16, 16, 1, 64, 1, 16, 4, 16, 16, 16, None, None) == L.KVQ_ERR_ARG
-    # block table too narrow for whole tiles of max_seq_len
-    assert lib.kvq_quantize_to_pages(cfg, 16, 16, 16, 1, 65, 1, 16, 4, 16, 16, None, None, None) == L.KVQ_ERR_ARG
+    # block table narrower than one tile, no tokens
+    assert lib.kvq_quantize_to_pages(cfg, 16, 16, 16, 1, 64, 1, 16, 3, 16, 16, None, None, None) == L.KVQ_ERR_ARG
+    assert lib.kvq_quantize_to_pages(cfg, 16, 16, 16, 1, 0, 1, 16, 4, 16, 16, None, None, None) == L.KVQ_ERR_ARG
     assert lib.kvq_append_and_requant(cfg, 16, 16, 16, 1, 1, None, 16, 16, 4, 16, 16, None) == L.KVQ_ERR_ARG
 
 
@@ -174,3 +176,36 @@ def test_noalloc_decode_rejects_sizes_beyond_its_scratch_on_the_host(lib):
     st = lib.kvq_append_and_decode_noalloc(ctypes.byref(cfg), p, p, p, 512, 8, p, p, p, 8192, p, p, None, 64,
                                            65536, 0.088, p, None)
     assert st == L.KVQ_ERR_ARG
+
+
+def test_tile_slots_of_the_paged_quantizer_cover_every_tile_once():
+    """The paged quantizer's grid: sequence s starts at slot cu[s] // T + s
+    and a slot belongs to the last sequence starting at or before it.  For
+    length mixes with empty, short, tile-aligned and long sequences (and a
+    first offset cu[0] > 0), total_tokens // T + num_seqs slots map onto
+    every (sequence, tile) exactly once, with at most one idle slot per
+    sequence."""
+    rng = np.random.default_rng(5)
+    for tile in (32, 64, 128):
+        for trial in range(200):
+            n = int(rng.integers(1, 70))
+            lens = rng.choice([0, 1, 15, 16, tile - 1, tile, tile + 1, 3 * tile, int(rng.integers(0, 5000))], n)
+            cu = np.concatenate([[int(rng.integers(0, 3)) * (trial % 2)], lens]).cumsum()
+            total = int(cu[-1])
+            start = cu[:-1] // tile + np.arange(n)
+            assert (np.diff(start) >= 1).all()
+            seen = {}
+            idle = np.zeros(n, int)
+            for f in range(total // tile + n):
+                s = int(np.searchsorted(start, f, side="right")) - 1
+                if s < 0:
+                    continue
+                j = f - int(start[s])
+                if j * tile >= lens[s]:
+                    idle[s] += 1
+                    continue
+                assert (s, j) not in seen
+                seen[(s, j)] = f
+            want = {(s, j) for s in range(n) for j in range(-(-int(lens[s]) // tile))}
+            assert set(seen) == want
+            assert idle.max(initial=0) <= 1

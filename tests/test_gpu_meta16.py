@@ -44,7 +44,7 @@ def _prefill(wl):
     cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, meta_fp16=True)
     cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
     cache.quantize_prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
-                           torch.from_numpy(wl.cu_seqlens()).cuda(), max(wl.seq_lens))
+                           torch.from_numpy(wl.cu_seqlens()).cuda())
     torch.cuda.synchronize()
     return k, v, table, npages, cache
 

@@ -107,7 +107,7 @@ def _gpu_prefill(wl, shuffled=True, signs=None):
     cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, hadamard_signs=signs)
     cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
     cu = torch.from_numpy(wl.cu_seqlens()).cuda()
-    cache.quantize_prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), cu, max(wl.seq_lens))
+    cache.quantize_prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), cu)
     torch.cuda.synchronize()
     return k, v, table, npages, cache
 
@@ -756,7 +756,7 @@ def test_full_size_long_context_layer_6x128k_sampled(bits):
     table, npages = inputs.block_table(wl, capacity_tokens=max_len + 1)
     cfg = api.config(wl.tile_tokens, bits, bits, wl.iters)
     cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
-    cache.quantize_prefill(k, v, torch.from_numpy(wl.cu_seqlens()).cuda(), max_len)
+    cache.quantize_prefill(k, v, torch.from_numpy(wl.cu_seqlens()).cuda())
     lens = np.array(wl.seq_lens, np.int32)
     kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
     q = inputs.gen_q(wl)
@@ -788,7 +788,7 @@ def test_full_size_mixed_64_seqs_1k_32k_sampled():
     table, npages = inputs.block_table(wl)
     cfg = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters)
     cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
-    cache.quantize_prefill(k, v, torch.from_numpy(wl.cu_seqlens()).cuda(), max_len)
+    cache.quantize_prefill(k, v, torch.from_numpy(wl.cu_seqlens()).cuda())
     lens = np.array(wl.seq_lens, np.int32)
     kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
     q = inputs.gen_q(wl)
@@ -845,7 +845,7 @@ def test_degenerate_tiles_and_empty_sequence():
     cfg = api.config(64, 4, 4, 3)
     cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
     cache.quantize_prefill(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
-                           torch.from_numpy(wl.cu_seqlens()).cuda(), max(wl.seq_lens))
+                           torch.from_numpy(wl.cu_seqlens()).cuda())
     torch.cuda.synchronize()
     ref_pk, ref_pv = orc.new_pool(npages, wl.hkv, 4, 64), orc.new_pool(npages, wl.hkv, 4, 64)
     stg_k = np.zeros((wl.num_seqs, 64, wl.hkv, 128), np.float16)
