@@ -59,6 +59,13 @@ __device__ __forceinline__ float vmax(float a, float b) {
   return r;
 }
 
+// max(|a|, |b|, c) as one v_max3_f32 with absolute-value operands
+__device__ __forceinline__ float vmax3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // v_permlane16_swap / v_permlane32_swap with both operands a copy of v return
 // a pair whose two members are v and the value of lane l^16 (resp. l^32) in
 // some order, so a symmetric op over the pair reduces over that lane pair in
@@ -155,19 +162,22 @@ __device__ __forceinline__ f16x4 as_f16x4(unsigned a, unsigned b) {
   return __builtin_bit_cast(f16x4, u32x2{a, b});
 }
 
-// fp32 pair -> fp16 pair hi, x rounded (nearest even) to a multiple of 1/w,
-// and the fp16 pair lo = x - hi (the subtraction is exact; lo is rounded).
-// m = 1.5 * 2^23 / w: adding it leaves 1/w as the ulp, so (x + m) - m is
-// the rounded x for |x| w < 2^22.  With w the code field's weight and
+// fp32 pair -> fp16 pair hi, x = v * s rounded (nearest even) to a multiple
+// of 1/w, and the fp16 pair lo = x - hi (the subtraction is exact; lo is
+// rounded).  m = 1.5 * 2^23 / w: adding it leaves 1/w as the ulp, so
+// (x + m) - m is the rounded x for |x| w < 2^22; the product v * s enters
+// both through an fma, unrounded.  With w the code field's weight and
 // |x| w <= 2^11, hi is exact in fp16 and every product hi * (code w 2^-24)
 // is an integer multiple of 2^-24: an MFMA chain over hi then sums exactly
 // (its partial sums stay below 2^24 units), where products of unrelated
 // exponents would lose low bits in the MFMA's adder.  lo runs in a chain of
 // its own, 2^-11 smaller.
-__device__ __forceinline__ void split_grid(float x0, float x1, float m0, float m1, unsigned& hi, unsigned& lo) {
-  const float h0 = (x0 + m0) - m0, h1 = (x1 + m1) - m1;
+__device__ __forceinline__ void split_grid(float v0, float v1, float s0, float s1, float m0, float m1, unsigned& hi,
+                                           unsigned& lo) {
+  const float h0 = __builtin_fmaf(v0, s0, m0) - m0, h1 = __builtin_fmaf(v1, s1, m1) - m1;
   hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{h0, h1}, f16x2));
-  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, f16x2));
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{__builtin_fmaf(v0, s0, -h0),
+                                                                  __builtin_fmaf(v1, s1, -h1)}, f16x2));
 }
 constexpr float kGrid = 12582912.f;   // 1.5 * 2^23
 
@@ -221,8 +231,12 @@ __device__ __forceinline__ float blocks_max(float v) {
 
 template <int T, int HG>
 struct alignas(16) DecodeSmem {
-  const uint8_t* kp[kMaxChunksPerPart * 4];      // the partition's K and V slots (this kv head)
-  const uint8_t* vp[kMaxChunksPerPart * 4];
+  // the partition's K and V slots (this kv head), kept as global-memory
+  // pointers: loads through them are global loads (a generic pointer read
+  // back from LDS would make every slot load a flat load, which also counts
+  // against the LDS counter and makes LDS waits wait for memory)
+  const __attribute__((address_space(1))) uint8_t* kp[kMaxChunksPerPart * 4];
+  const __attribute__((address_space(1))) uint8_t* vp[kMaxChunksPerPart * 4];
   union {
     struct {
       float hq[4 * HG][kHeadDim];                // (H q)_c / weight of c's K field, at qk_slot(c)
@@ -380,8 +394,8 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
     const int n = last - 4 * c_begin;
     for (int i = threadIdx.x; i < n; i += 64 * kWaves) {
       const size_t slot = (size_t)row[i] * H + kvh;
-      sm.kp[i] = A.pool_k + slot * SLOT_K;
-      sm.vp[i] = A.pool_v + slot * SLOT_V;
+      sm.kp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_k + slot * SLOT_K);
+      sm.vp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_v + slot * SLOT_V);
     }
   }
   __syncthreads();
@@ -389,8 +403,8 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   // was never started reads its first tile's pages instead (every token there
   // is past the end and masked)
   auto page_ix = [&](int pj) { return (pj < npages ? pj : pj - 2) - 4 * c_begin; };
-  auto kslot = [&](int pj) { return sm.kp[page_ix(pj)]; };   // K slot of page pj of the sequence
-  auto vslot = [&](int pj) { return sm.vp[page_ix(pj)]; };
+  auto kslot = [&](int pj) { return (const uint8_t*)sm.kp[page_ix(pj)]; };   // K slot of page pj of the sequence
+  auto vslot = [&](int pj) { return (const uint8_t*)sm.vp[page_ix(pj)]; };
 
   // ------------------------------------------------ per-chunk operands (loaded one chunk ahead,
   // each right after its last use in the current chunk)
@@ -550,16 +564,18 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       for (int hg = 0; hg < HG; ++hg) {
         const int hh = 4 * hg + iq;
         float x[SETS][4];
-        float qmax = 0.f, qsum = 0.f;
+        float qm0 = 0.f, qm1 = 0.f, qsum = 0.f;   // |x| maxima of the elements of weight w0 and w1
 #pragma unroll
         for (int st = 0; st < SETS; ++st) {
           const int s = BLK * st + (bq % BLK);
           const f32x4 hv = *reinterpret_cast<const f32x4*>(&sm.loop.hq[hh][4 * s]);
 #pragma unroll
           for (int k = 0; k < 4; ++k) x[st][k] = hv[k] * ak[st][k];
-          // the bound is on qt itself: x times the field weight
-          qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(x[st][0]), fabsf(x[st][1])) * w0, fmaxf(fabsf(x[st][2]), fabsf(x[st][3])) * w1));
+          qm0 = vmax3_abs(x[st][0], x[st][1], qm0);
+          qm1 = vmax3_abs(x[st][2], x[st][3], qm1);
         }
+        // the bound is on qt itself: x times the field weight
+        float qmax = vmax(qm0 * w0, qm1 * w1);
         qmax = blocks_max<BLK>(qmax);
         int ex = (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127;
         ex = min(max(ex, -100), 100);
@@ -571,24 +587,21 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         // in proportion to the restored key.  (With the exact sum it would leave
         // S sum_c err_c k_c against O sum_c qt_c, and in tiles of a few tokens,
         // where S and O reach 1e4..1e5 and nearly cancel, that costs ~1e-3.)
+        // The pairs enter the sum through v_dot2 (fp16 products with the field
+        // weights are exact in fp32).
         const float g0 = kGrid / w0, g1 = kGrid / w1;
+        const f16x2 wp0{(_Float16)w0, (_Float16)w0}, wp1{(_Float16)w1, (_Float16)w1};
 #pragma unroll
         for (int st = 0; st < SETS; ++st) {
           unsigned h01, l01, h23, l23;
-          split_grid(x[st][0] * qscale, x[st][1] * qscale, g0, g0, h01, l01);
-          split_grid(x[st][2] * qscale, x[st][3] * qscale, g1, g1, h23, l23);
+          split_grid(x[st][0], x[st][1], qscale, qscale, g0, g0, h01, l01);
+          split_grid(x[st][2], x[st][3], qscale, qscale, g1, g1, h23, l23);
           qa_hi[hg][st] = as_f16x4(h01, h23);
           qa_lo[hg][st] = as_f16x4(l01, l23);
-          const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, l01);
-          const f16x2 c = __builtin_bit_cast(f16x2, h23), e = __builtin_bit_cast(f16x2, l23);
-          qsum = __builtin_fmaf((float)a[0], w0, qsum);
-          qsum = __builtin_fmaf((float)b[0], w0, qsum);
-          qsum = __builtin_fmaf((float)a[1], w0, qsum);
-          qsum = __builtin_fmaf((float)b[1], w0, qsum);
-          qsum = __builtin_fmaf((float)c[0], w1, qsum);
-          qsum = __builtin_fmaf((float)e[0], w1, qsum);
-          qsum = __builtin_fmaf((float)c[1], w1, qsum);
-          qsum = __builtin_fmaf((float)e[1], w1, qsum);
+          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h01), wp0, qsum, false);
+          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, l01), wp0, qsum, false);
+          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h23), wp1, qsum, false);
+          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, l23), wp1, qsum, false);
         }
         qsum = blocks_sum<BLK>(qsum) * qunscale;
         cA[hg] = c0 * kTwo24 * qunscale;   // score = S D cA + O cB
@@ -707,8 +720,8 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       for (int hg = 0; hg < HG; ++hg) {
         const f32x4 p4 = *reinterpret_cast<const f32x4*>(&sm.loop.pt[wave][4 * hg + iq][4 * bq]);
         unsigned h01, l01, h23, l23;
-        split_grid(p4[0] * sw[0], p4[1] * sw[1], kGrid, kGrid, h01, l01);
-        split_grid(p4[2] * sw[2], p4[3] * sw[3], kGrid / kTok, kGrid / kTok, h23, l23);
+        split_grid(p4[0], p4[1], sw[0], sw[1], kGrid, kGrid, h01, l01);
+        split_grid(p4[2], p4[3], sw[2], sw[3], kGrid / kTok, kGrid / kTok, h23, l23);
         pa_hi[hg] = as_f16x4(h01, h23);
         pa_lo[hg] = as_f16x4(l01, l23);
         const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, l01);
