@@ -341,17 +341,13 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
 }
 
 // Row blocks of the multi-query kernel per (sequence, kv head): 8 rows each.
-static int mq_row_blocks(int n_q, int group) {
-  const long rows = (long)n_q * group;
-  return (int)((rows + 7) / 8);
-}
 
 size_t kvq_multi_query_workspace_bytes(const kvq_config* cfg, int32_t num_seqs, int32_t n_q, int32_t q_heads,
                                        int32_t kv_heads, int32_t max_seq_len) {
   if (check_config(cfg, true) != KVQ_OK) return 0;
   if (num_seqs <= 0 || n_q <= 0 || q_heads <= 0 || kv_heads <= 0 || max_seq_len <= 0) return 0;
   if (q_heads % kv_heads != 0 || n_q > max_seq_len) return 0;
-  const int rb = mq_row_blocks(n_q, q_heads / kv_heads);
+  const int rb = kvq::mq_row_blocks(n_q, q_heads / kv_heads);
   const int cpp = chunks_per_partition(num_seqs * rb, kv_heads, max_seq_len, cfg->tile_tokens);
   const int parts = max_partitions(max_seq_len, 64, cpp);
   return (size_t)num_seqs * n_q * q_heads * parts * (kvq::kHeadDim + 2) * sizeof(float);
@@ -378,7 +374,7 @@ kvq_status kvq_paged_multi_query_attn(const kvq_config* cfg, const kvq_half* q, 
     return fail(KVQ_ERR_ARG, "n_q %d exceeds max_seq_len %d (the queries are cached tokens)", n_q, max_seq_len);
   const int group = q_heads / kv_heads;
   if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d larger than 16", group);
-  const int rb = mq_row_blocks(n_q, group);
+  const int rb = kvq::mq_row_blocks(n_q, group);
   if (num_seqs > 65535 || (long)kv_heads * rb * num_seqs > 2147483647L ||
       (long)num_seqs * n_q * q_heads > 2147483647L)
     return fail(KVQ_ERR_ARG, "too many heads, queries or sequences");

@@ -127,6 +127,15 @@ hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, 
 hipError_t launch_decode_m16(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s);
+// Several queries per sequence: with at least 16 (query, head) rows per
+// sequence and kv head the 16-row MFMA kernel takes them in blocks of up to
+// 64 rows; fewer rows (and one query, which must equal the decode step bit
+// for bit) run on the decode kernel in blocks of up to 8.
+inline bool mq_dense(int n_q, int group) { return n_q > 1 && (long)n_q * group >= 16; }
+inline int mq_row_blocks(int n_q, int group) {
+  const long rows = (long)n_q * group;
+  return (int)(mq_dense(n_q, group) ? (rows + 63) / 64 : (rows + 7) / 8);
+}
 hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s);
 hipError_t launch_multi_query_m16(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,

@@ -3,15 +3,17 @@
 // cached tokens up to their own positions, reading the compressed pages
 // directly as the decode step does (aitrends.kr article 74976, TL;DR: the
 // attention backend reads compressed KV pages without re-materializing fp16).
-// It is the decode kernel with (query, head) rows in place of heads; rows come
-// in blocks of up to 8 per workgroup, and every block reads the partition's
-// pages (a block's re-read of the same pages is served mostly from cache).
-#include "kvq_decode_kernel.h"
+// With 16 or more (query, head) rows per sequence and kv head the rows go
+// to the 16-row MFMA kernel (kvq_mq_dense.h) in blocks of up to 64, each
+// block reading the partition's pages once; fewer rows run on the decode
+// kernel with (query, head) rows in place of heads, in blocks of up to 8.
+#include "kvq_mq_dense.h"
 
 namespace kvq {
 
 hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s) {
   if (m16) return launch_multi_query_m16(a, tile, bits_k, bits_v, s);
+  if (mq_dense(a.n_q, a.group)) return launch_mq_dense_fmt<false>(a, tile, bits_k, bits_v, s);
   return launch_multi_query_fmt<false>(a, tile, bits_k, bits_v, s);
 }
 
