@@ -360,11 +360,27 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
   auto process = [&](Ops& o, int chunk, int cn) {
     const int pg0 = 4 * chunk;
     const bool more = cn < c_end;
-    float* meta = sm.meta[wave];   // [4][64]: S_K, O_K, S_V, O_V by token of the chunk
+    // P = p S_V, scaled by 2^k per chunk so that it stays below 2^(PE+1)
+    const float smax = wave_max(vmax(o.sv, 0.f));
+    int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
+    pe = min(max(pe, -100), 100);
+    const float pk = (float)(PE - pe);
+    const float pinv = __uint_as_float((unsigned)(127 - PE + pe) << 23);   // 2^-k
+    // per token (lane = token of the chunk): the V scale the probabilities are
+    // multiplied by (a zero-range token, S = 0 and codes 0, takes 2^pe <= max S_V
+    // in place of S: its P then carries p to the offset term while its codes
+    // contribute nothing; tokens 2, 3 of a quad divided by kTok) and O over it,
+    // nearest (reciprocal refined by one Newton step)
+    float swt = o.sv > 0.f ? o.sv : __uint_as_float((unsigned)(127 + pe) << 23);
+    if ((lane & 3) >= 2) swt *= (1.f / kTok);
+    const float rct = __builtin_amdgcn_rcpf(swt);
+    const float z0t = o.ov * rct;
+    const float zrt = __builtin_fmaf(__builtin_fmaf(-swt, z0t, o.ov), rct, z0t);
+    float* meta = sm.meta[wave];   // [4][64]: S_K, O_K, sw, O / sw by token of the chunk
     meta[lane] = o.sk;
     meta[64 + lane] = o.ok;
-    meta[128 + lane] = o.sv;
-    meta[192 + lane] = o.ov;
+    meta[128 + lane] = swt;
+    meta[192 + lane] = zrt;
     asm volatile("" ::: "memory");   // the reads below see this wave's writes (LDS keeps order)
     if (more) load_meta_ops(o, cn);
     // alpha_V of the lane's channels 16 j + n for the chunk's tile(s), needed after the softmax
@@ -396,15 +412,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
       }
       const f32x4 sk = *reinterpret_cast<const f32x4*>(&meta[16 * tb + 4 * g]);
       const f32x4 ok = *reinterpret_cast<const f32x4*>(&meta[64 + 16 * tb + 4 * g]);
-      f32x4 d{0.f, 0.f, 0.f, 0.f}, dl{0.f, 0.f, 0.f, 0.f};
+      // the lo products go on top of the finished (exact) hi sum: one rounding per add
+      f32x4 d{0.f, 0.f, 0.f, 0.f};
+      f16x8 a[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const f16x8 a = mq_k_operand<BK>(o.kb[tb], ks);
-        d = mfma16(a, qhi[ks], d);
-        dl = mfma16(a, qlo[ks], dl);
+        a[ks] = mq_k_operand<BK>(o.kb[tb], ks);
+        d = mfma16(a[ks], qhi[ks], d);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[tb][i] = __builtin_fmaf(cA * sk[i], d[i] + dl[i], cB * ok[i]);
+      for (int ks = 0; ks < 4; ++ks) d = mfma16(a[ks], qlo[ks], d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[tb][i] = __builtin_fmaf(cA * sk[i], d[i], cB * ok[i]);
     }
     if (more) load_k_ops(o, cn);
     // causal and length mask, only where some row's limit falls inside the chunk
@@ -437,13 +456,6 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
         for (int j = 0; j < 8; ++j) acc[j][i] *= ci;
       }
     }
-    // P = p S_V, scaled by 2^k per chunk so that it stays below 2^(PE+1)
-    const float smax = wave_max(vmax(o.sv, 0.f));
-    int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
-    pe = min(max(pe, -100), 100);
-    const float pk = (float)(PE - pe);
-    const float pinv = __uint_as_float((unsigned)(127 - PE + pe) << 23);   // 2^-k
-    const float p2e = __uint_as_float((unsigned)(127 + pe) << 23);         // 2^pe <= max S_V
     float p[4][4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -462,27 +474,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const int tb = 2 * kb + q2;
-        // a zero-range token (S = 0, codes 0) takes the chunk's power of two in
-        // place of S: its P then carries p (times that scale) to the offset
-        // term while its codes contribute nothing
-        f32x4 sw = *reinterpret_cast<const f32x4*>(&meta[128 + 16 * tb + 4 * g]);
-        const f32x4 ov = *reinterpret_cast<const f32x4*>(&meta[192 + 16 * tb + 4 * g]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sw[k] = sw[k] > 0.f ? sw[k] : p2e;
-        sw[2] *= (1.f / kTok);
-        sw[3] *= (1.f / kTok);
+        const f32x4 sw = *reinterpret_cast<const f32x4*>(&meta[128 + 16 * tb + 4 * g]);
+        const f32x4 zr = *reinterpret_cast<const f32x4*>(&meta[192 + 16 * tb + 4 * g]);
         split_grid(p[tb][0], p[tb][1], sw[0], sw[1], kGrid, kGrid, ph[2 * q2], pl[2 * q2]);
         split_grid(p[tb][2], p[tb][3], sw[2], sw[3], kGrid / kTok, kGrid / kTok, ph[2 * q2 + 1], pl[2 * q2 + 1]);
         // offset term through the represented P: p_t O_t = P_t (O_t / sw_t)
         const f16x2 a = __builtin_bit_cast(f16x2, ph[2 * q2]), b = __builtin_bit_cast(f16x2, pl[2 * q2]);
         const f16x2 c = __builtin_bit_cast(f16x2, ph[2 * q2 + 1]), e = __builtin_bit_cast(f16x2, pl[2 * q2 + 1]);
-        float zr[4];   // O / sw, nearest (reciprocal refined by one Newton step)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float rc = __builtin_amdgcn_rcpf(sw[k]);
-          const float z0 = ov[k] * rc;
-          zr[k] = __builtin_fmaf(__builtin_fmaf(-sw[k], z0, ov[k]), rc, z0);
-        }
         float& q = po[kb];
         q = __builtin_fmaf((float)a[0], zr[0], q);
         q = __builtin_fmaf((float)b[0], zr[0], q);
@@ -512,16 +510,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     for (int jr = 0; jr < 4; ++jr) {
 #pragma unroll
       for (int sg = 0; sg < NSEG; ++sg) {
-        f32x4 vh[2], vl[2];   // [channel half]
+        constexpr int KB0 = 0, NKB = (NSEG == 2) ? 1 : 2;   // page pairs of the segment
+        f32x4 vh[2];   // [channel half]: the hi chain (exact), then the lo products on top
+        f16x8 bv[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           vh[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-          vl[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
 #pragma unroll
-        for (int kb = sg; kb < (NSEG == 2 ? sg + 1 : 2); ++kb) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
+          for (int kk = KB0; kk < NKB; ++kk) {
+            const int kb = (NSEG == 2) ? sg : kk;
             unsigned b[4];
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
@@ -529,21 +526,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
               if (BV == 2 && (g & 1)) x >>= 8;   // odd quads sit in bits 8..15 of each half
               mq_v_fields<BV>(x, BV == 8 ? o.vw[jr][2 * kb + q2][BV == 8 ? 1 : 0] : 0u, h, b[2 * q2], b[2 * q2 + 1]);
             }
-            const f16x8 bv = as_f16x8(b[0], b[1], b[2], b[3]);
-            vh[h] = mfma16(pah[kb], bv, vh[h]);
-            vl[h] = mfma16(pal[kb], bv, vl[h]);
+            bv[h][kk] = as_f16x8(b[0], b[1], b[2], b[3]);
+            vh[h] = mfma16(pah[kb], bv[h][kk], vh[h]);
           }
         }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int kk = KB0; kk < NKB; ++kk) vh[h] = mfma16(pal[(NSEG == 2) ? sg : kk], bv[h][kk], vh[h]);
         // acc += alpha_V (sum_t p_t S_t k_t + sum_t p_t O_t) over the segment
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int j = jr + 4 * h;
           const float cf = kTwo24 * pinv * ((BV == 2 && h == 1) ? (1.f / 16.f) : 1.f);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float y = __builtin_fmaf(vl[h][i], cf, __builtin_fmaf(vh[h][i], cf, so[sg][i]));
-            acc[j][i] = __builtin_fmaf(av[sg][j], y, acc[j][i]);
-          }
+          for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(av[sg][j], __builtin_fmaf(vh[h][i], cf, so[sg][i]), acc[j][i]);
         }
       }
     }
