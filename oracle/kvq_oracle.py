@@ -56,6 +56,16 @@ Readings where the pages are silent (each is a documented parameter or choice):
   is alpha * (S * code + O) and the restored token is that row rotated back.
 * Tiles are aligned to the start of each sequence; the last one may be
   partial, and its statistics use only its valid rows.
+* Per-channel rounding for K (kchan): the pages do not say over which axis
+  the asymmetric rounding runs.  The variant rounds each channel of a K tile
+  over the tile's valid tokens: zero-point = the channel's minimum of Y,
+  step = (max - min) / (2^bits - 1), ties to even.  The token factors beta
+  then stay per token and the channel factors merge with the rounding, so a
+  K slot stores beta per token and, per channel of the tile, the scale
+  A = alpha * step and the zero offset in code units M = min / step; the
+  restored rotated row is beta * A * (code + M).  A channel of zero range
+  stores A = alpha * min and M = 1 (its codes are 0).  V keeps per-token
+  rounding.
 * Metadata precision: fp32 by default; the fp16 slot variant (meta16) moves
   one power of two per tile from the scales and offsets into the channel
   factors (see meta_fp16) and rounds all three to fp16 (nearest even).  Codes
@@ -179,6 +189,14 @@ def rtn(y: np.ndarray, bits: int):
     return codes, step, zero, pre
 
 
+def rtn_channel(y: np.ndarray, bits: int):
+    """Per-channel asymmetric round-to-nearest over the tile's tokens: the
+    row rule above applied to each column.  Returns (codes uint8 [n, d],
+    step[d], zero[d], pre[n, d])."""
+    codes, step, zero, pre = rtn(np.asarray(y, np.float64).T, bits)
+    return codes.T.copy(), step, zero, pre.T.copy()
+
+
 @dataclasses.dataclass
 class TileQuant:
     codes: np.ndarray     # uint8 [n, d], one code per element
@@ -192,22 +210,46 @@ class TileQuant:
     alpha64: np.ndarray = None   # float64 [d]: the channel factors before rounding
     scale64: np.ndarray = None   # float64 [n]
     offset64: np.ndarray = None  # float64 [n]
+    # per-channel rounding (kchan): alpha holds A = alpha * step per channel,
+    # scale (and offset) beta per token, zp the zero offset M in code units
+    kchan: bool = False
+    zp: np.ndarray = None        # float32 [d]
+    zp64: np.ndarray = None      # float64 [d]
 
 
-def quantize_tile(x: np.ndarray, bits: int, iters: int, signs=None) -> TileQuant:
+def quantize_tile(x: np.ndarray, bits: int, iters: int, signs=None, kchan: bool = False) -> TileQuant:
     """The four steps on one tile of 1..T tokens: x fp16 [n, d] (signs: the
-    optional sign mask of the randomized rotation, see signs_from_mask)."""
+    optional sign mask of the randomized rotation, see signs_from_mask;
+    kchan: round per channel instead of per token, see the module notes)."""
     x = np.asarray(x)
     if x.ndim != 2 or x.shape[0] < 1:
         raise ValueError("tile must be [n>=1, d]")
     r = fwht(x.astype(np.float64) * signs_from_mask(signs)[None, :])
     y, alpha, beta = sinkhorn(r, iters)
+    if kchan:
+        codes, step, zero, pre = rtn_channel(y, bits)
+        flat = step == 0
+        a64 = np.where(flat, alpha * zero, alpha * step)
+        m64 = np.where(flat, 1.0, zero / np.where(flat, 1.0, step))
+        return TileQuant(codes=codes, alpha=a64.astype(np.float32), scale=beta.astype(np.float32),
+                         offset=beta.astype(np.float32), alpha64=a64, scale64=beta, offset64=beta,
+                         pre=pre, rotated=r, normalized=y, beta=beta, kchan=True,
+                         zp=m64.astype(np.float32), zp64=m64)
     codes, step, zero, pre = rtn(y, bits)
     return TileQuant(codes=codes, alpha=alpha.astype(np.float32),
                      scale=(beta * step).astype(np.float32),
                      offset=(beta * zero).astype(np.float32),
                      alpha64=alpha, scale64=beta * step, offset64=beta * zero,
                      pre=pre, rotated=r, normalized=y, beta=beta)
+
+
+def dequantize_tile_kchan(codes, chan_scale, zp, beta, signs=None) -> np.ndarray:
+    """Restore a per-channel-rounded K tile: rotated row beta * A * (code + M),
+    rotated back as in dequantize_tile.  float64 [n, d]."""
+    codes = np.asarray(codes, dtype=np.float64)
+    rot = np.asarray(beta, np.float64)[:, None] * np.asarray(chan_scale, np.float64)[None, :] * (
+        codes + np.asarray(zp, np.float64)[None, :])
+    return fwht(rot) * signs_from_mask(signs)[None, :]
 
 
 def dequantize_tile(codes, alpha, scale, offset, signs=None) -> np.ndarray:
@@ -322,18 +364,26 @@ def dequantize_dense(codes_packed, alpha, scale, offset, tile_tokens: int, bits:
 # Rows of a page past the sequence's end hold code 0, scale 0 and offset 0.
 # ----------------------------------------------------------------------------
 
-def slot_layout(bits: int, tile_tokens: int, meta16: bool = False, d: int = HEAD_DIM, page: int = PAGE_TOKENS):
+def slot_layout(bits: int, tile_tokens: int, meta16: bool = False, d: int = HEAD_DIM, page: int = PAGE_TOKENS,
+                kchan: bool = False):
     """Byte layout of a slot; meta16: scale, offset and channel factors stored
-    as fp16 (2 bytes each) instead of fp32."""
+    as fp16 (2 bytes each) instead of fp32.  kchan (K slots rounded per
+    channel): codes | beta fp32[16] | A slice fp32[16 d / T] | M slice fp32[16 d / T],
+    the page with index j in its tile holding channels j * 16d/T .. (j+1) * 16d/T - 1."""
     me = 2 if meta16 else 4
     codes = page * d * bits // 8
     alpha_len = page * d // tile_tokens
+    if kchan:
+        if meta16:
+            raise ValueError("per-channel K slots keep fp32 metadata")
+        return dict(codes=codes, scale=codes, alpha=codes + 4 * page, zp=codes + 4 * page + 4 * alpha_len,
+                    alpha_len=alpha_len, total=codes + 4 * page + 8 * alpha_len, meta_dtype="<f4")
     return dict(codes=codes, scale=codes, offset=codes + me * page, alpha=codes + 2 * me * page,
                 alpha_len=alpha_len, total=codes + 2 * me * page + me * alpha_len, meta_dtype="<f2" if meta16 else "<f4")
 
 
-def slot_bytes(bits: int, tile_tokens: int, meta16: bool = False) -> int:
-    return slot_layout(bits, tile_tokens, meta16)["total"]
+def slot_bytes(bits: int, tile_tokens: int, meta16: bool = False, kchan: bool = False) -> int:
+    return slot_layout(bits, tile_tokens, meta16, kchan=kchan)["total"]
 
 
 FP16_MAX = 65504.0
@@ -423,8 +473,27 @@ def bytes_to_v_codes(raw: np.ndarray, bits: int) -> np.ndarray:
     return ((words[word] >> shift) & ((1 << bits) - 1)).astype(np.uint8)
 
 
-def new_pool(num_pages: int, kv_heads: int, bits: int, tile_tokens: int, meta16: bool = False) -> np.ndarray:
-    return np.zeros((num_pages, kv_heads, slot_bytes(bits, tile_tokens, meta16)), np.uint8)
+def new_pool(num_pages: int, kv_heads: int, bits: int, tile_tokens: int, meta16: bool = False,
+             kchan: bool = False) -> np.ndarray:
+    return np.zeros((num_pages, kv_heads, slot_bytes(bits, tile_tokens, meta16, kchan)), np.uint8)
+
+
+def write_slot_kchan(pool, page, head, bits, tile_tokens, codes16, beta16, a_slice, m_slice):
+    lay = slot_layout(bits, tile_tokens, kchan=True)
+    slot = pool[page, head]
+    slot[:lay["codes"]] = k_codes_to_bytes(codes16, bits)
+    slot[lay["scale"]:lay["alpha"]] = np.asarray(beta16, "<f4").view(np.uint8)
+    slot[lay["alpha"]:lay["zp"]] = np.asarray(a_slice, "<f4").view(np.uint8)
+    slot[lay["zp"]:lay["total"]] = np.asarray(m_slice, "<f4").view(np.uint8)
+
+
+def read_slot_kchan(pool, page, head, bits, tile_tokens):
+    """(codes [16, d], beta [16], A slice, M slice) of a per-channel K slot."""
+    lay = slot_layout(bits, tile_tokens, kchan=True)
+    slot = np.ascontiguousarray(pool[page, head])
+    return (bytes_to_k_codes(slot[:lay["codes"]], bits), slot[lay["scale"]:lay["alpha"]].view("<f4").astype(np.float32),
+            slot[lay["alpha"]:lay["zp"]].view("<f4").astype(np.float32),
+            slot[lay["zp"]:lay["total"]].view("<f4").astype(np.float32))
 
 
 def write_slot(pool, page, head, role, bits, tile_tokens, codes16, scale16, offset16, alpha_slice, meta16=False):
@@ -455,6 +524,20 @@ def _store_tile(pool, table_row, head, role, bits, tile_tokens, tile_index, tq: 
     ppt = tile_tokens // PAGE_TOKENS
     alen = PAGE_TOKENS * HEAD_DIM // tile_tokens
     n = tq.codes.shape[0]
+    if tq.kchan:
+        for j in range(ppt):
+            page = int(table_row[tile_index * ppt + j])
+            if page < 0:
+                raise ValueError("block table has no page for a started tile")
+            codes16 = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
+            beta16 = np.zeros(PAGE_TOKENS, np.float32)
+            a, b = j * PAGE_TOKENS, min(n, (j + 1) * PAGE_TOKENS)
+            if b > a:
+                codes16[:b - a] = tq.codes[a:b]
+                beta16[:b - a] = tq.scale[a:b]
+            write_slot_kchan(pool, page, head, bits, tile_tokens, codes16, beta16,
+                             tq.alpha[j * alen:(j + 1) * alen], tq.zp[j * alen:(j + 1) * alen])
+        return
     alpha, scale, offset = tq.alpha, tq.scale, tq.offset
     if meta16:
         _, alpha, scale, offset, _, _, _ = meta_fp16(tq)
@@ -475,7 +558,7 @@ def _store_tile(pool, table_row, head, role, bits, tile_tokens, tile_index, tq: 
 
 
 def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iters,
-                      pool_k, pool_v, staging_k=None, staging_v=None, signs=None, meta16=False):
+                      pool_k, pool_v, staging_k=None, staging_v=None, signs=None, meta16=False, kchan=False):
     """Quantize every tile of every sequence into the page pools (in place).
 
     k, v: fp16 [total_tokens, Hkv, d]; table: int32 [S, max_blocks].  A tail
@@ -493,7 +576,7 @@ def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iter
                 pre_rows = np.zeros((n, HEAD_DIM))
                 for j in range((n + tile_tokens - 1) // tile_tokens):
                     a, b = j * tile_tokens, min(n, (j + 1) * tile_tokens)
-                    tq = quantize_tile(x[a0 + a:a0 + b, h, :], bits, iters, signs)
+                    tq = quantize_tile(x[a0 + a:a0 + b, h, :], bits, iters, signs, kchan and role == "K")
                     pre_rows[a:b] = tq.pre
                     _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq, meta16)
                 pre[(s, h, role)] = pre_rows
@@ -504,7 +587,7 @@ def quantize_to_pages(k, v, cu_seqlens, table, tile_tokens, bits_k, bits_v, iter
 
 
 def append_and_requant(k_new, v_new, lens_before, table, tile_tokens, bits_k, bits_v, iters,
-                       pool_k, pool_v, staging_k, staging_v, signs=None, meta16=False):
+                       pool_k, pool_v, staging_k, staging_v, signs=None, meta16=False, kchan=False):
     """Append one token per sequence and re-quantize its (partial) tile from the
     fp16 staging rows.  k_new, v_new fp16 [S, Hkv, d].  Returns pre-rounding
     values per (seq, head, role) of the re-quantized tile rows."""
@@ -517,18 +600,39 @@ def append_and_requant(k_new, v_new, lens_before, table, tile_tokens, bits_k, bi
         staging_v[s, r] = v_new[s]
         for role, stg, pool, bits in (("K", staging_k, pool_k, bits_k), ("V", staging_v, pool_v, bits_v)):
             for h in range(heads):
-                tq = quantize_tile(stg[s, :r + 1, h, :], bits, iters, signs)
+                tq = quantize_tile(stg[s, :r + 1, h, :], bits, iters, signs, kchan and role == "K")
                 _store_tile(pool, table[s], h, role, bits, tile_tokens, j, tq, meta16)
                 pre[(s, h, role)] = tq.pre
     return pre
 
 
-def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens, signs=None, meta16=False):
+def read_sequence(pool, table_row, seq_len, head, role, bits, tile_tokens, signs=None, meta16=False, kchan=False):
     """Decode one (sequence, kv head) from the pages with this module's own
     reader: returns (restored tokens float64 [L, d], codes [L, d], alpha per
-    tile [ntiles, d], scale [L], offset [L])."""
+    tile [ntiles, d], scale [L], offset [L]).  With kchan (K slots rounded
+    per channel): (restored, codes, A per tile [ntiles, d], beta [L], M per
+    tile [ntiles, d])."""
     ppt = tile_tokens // PAGE_TOKENS
     ntiles = (seq_len + tile_tokens - 1) // tile_tokens
+    if kchan and role == "K":
+        alen = PAGE_TOKENS * HEAD_DIM // tile_tokens
+        codes = np.zeros((ntiles * tile_tokens, HEAD_DIM), np.uint8)
+        beta = np.zeros(ntiles * tile_tokens, np.float32)
+        cs = np.zeros((ntiles, HEAD_DIM), np.float32)
+        zp = np.zeros((ntiles, HEAD_DIM), np.float32)
+        for j in range(ntiles):
+            for p in range(ppt):
+                c16, b16, a_sl, m_sl = read_slot_kchan(pool, int(table_row[j * ppt + p]), head, bits, tile_tokens)
+                t0 = j * tile_tokens + p * PAGE_TOKENS
+                codes[t0:t0 + PAGE_TOKENS] = c16
+                beta[t0:t0 + PAGE_TOKENS] = b16
+                cs[j, p * alen:(p + 1) * alen] = a_sl
+                zp[j, p * alen:(p + 1) * alen] = m_sl
+        out = np.zeros((seq_len, HEAD_DIM))
+        for j in range(ntiles):
+            a, b = j * tile_tokens, min(seq_len, (j + 1) * tile_tokens)
+            out[a:b] = dequantize_tile_kchan(codes[a:b], cs[j], zp[j], beta[a:b], signs)
+        return out, codes[:seq_len], cs, beta[:seq_len], zp
     codes = np.zeros((ntiles * tile_tokens, HEAD_DIM), np.uint8)
     scale = np.zeros(ntiles * tile_tokens, np.float32)
     offset = np.zeros(ntiles * tile_tokens, np.float32)
@@ -598,17 +702,30 @@ def key_score_parts(q, codes, alpha, scale, offset, tile_tokens, signs=None):
             np.asarray(offset, np.float64) * qt.sum(1))
 
 
-def key_score_terms(q, codes, alpha, scale, offset, tile_tokens, signs=None) -> np.ndarray:
+def key_score_parts_kchan(q, codes, chan_scale, beta, zp, tile_tokens, signs=None):
+    """key_score_parts for per-channel K tiles: the restored key is
+    D H (beta * A * (code + M)), so with qt = A * H D q the score is
+    beta sum_c qt_c code_c + beta sum_c qt_c M_c (A, M per tile [ntiles, d])."""
+    hq = fwht(np.asarray(q, np.float64) * signs_from_mask(signs))
+    n = len(beta)
+    tix = np.arange(n) // tile_tokens
+    qt = hq[None] * np.asarray(chan_scale, np.float64)[tix]
+    b = np.asarray(beta, np.float64)
+    return b * (qt * np.asarray(codes, np.float64)).sum(1), b * (qt * np.asarray(zp, np.float64)[tix]).sum(1)
+
+
+def key_score_terms(q, codes, alpha, scale, offset, tile_tokens, signs=None, kchan=False) -> np.ndarray:
     """|first| + |second| of key_score_parts per token: in tiles whose per-token
     factors are large (S and O of 1e4 and more in tiles of a few tokens) the
     two terms nearly cancel, and a score evaluated in fp32 carries a rounding
     proportional to them, not to its own value."""
-    a, b = key_score_parts(q, codes, alpha, scale, offset, tile_tokens, signs)
+    parts = key_score_parts_kchan if kchan else key_score_parts
+    a, b = parts(q, codes, alpha, scale, offset, tile_tokens, signs)
     return np.abs(a) + np.abs(b)
 
 
 def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
-                      sm_scale=None, return_scale=False, signs=None, meta16=False):
+                      sm_scale=None, return_scale=False, signs=None, meta16=False, kchan=False):
     """q fp16 [S, Hq, d]; seq_lens count every cached token (the newest included).
     Query head h reads kv head h // (Hq / Hkv).  Returns float64 [S, Hq, d]
     (and, with return_scale, attention_abs_scale per [S, Hq], score terms
@@ -622,18 +739,18 @@ def paged_decode_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, b
     for s in range(s_n):
         for kh in range(hkv):
             kx, kc, ka, ks, ko = read_sequence(pool_k, table[s], int(seq_lens[s]), kh, "K", bits_k, tile_tokens,
-                                               signs, meta16)
+                                               signs, meta16, kchan)
             vx = read_sequence(pool_v, table[s], int(seq_lens[s]), kh, "V", bits_v, tile_tokens, signs, meta16)[0]
             for h in range(kh * g, (kh + 1) * g):
                 out[s, h] = attention(q[s, h].astype(np.float64), kx, vx, sm)
                 if return_scale:
-                    terms = key_score_terms(q[s, h], kc, ka, ks, ko, tile_tokens, signs)
+                    terms = key_score_terms(q[s, h], kc, ka, ks, ko, tile_tokens, signs, kchan)
                     scale[s, h] = attention_abs_scale(q[s, h], kx, vx, sm, terms)
     return (out, scale) if return_scale else out
 
 
 def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits_k, bits_v,
-                           sm_scale=None, return_scale=False, signs=None, meta16=False):
+                           sm_scale=None, return_scale=False, signs=None, meta16=False, kchan=False):
     """Several queries per sequence over the same compressed pages (the read
     path of [aitrends §TL;DR], with a causal mask): q fp16 [S, n_q, Hq, d]
     holds the n_q newest tokens of each sequence, already in the cache, so
@@ -652,7 +769,7 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
     for s in range(s_n):
         n = int(seq_lens[s])
         for kh in range(hkv):
-            kx, kc, ka, ks, ko = read_sequence(pool_k, table[s], n, kh, "K", bits_k, tile_tokens, signs, meta16)
+            kx, kc, ka, ks, ko = read_sequence(pool_k, table[s], n, kh, "K", bits_k, tile_tokens, signs, meta16, kchan)
             vx = read_sequence(pool_v, table[s], n, kh, "V", bits_v, tile_tokens, signs, meta16)[0]
             for i in range(n_q):
                 visible = n - n_q + i + 1
@@ -662,7 +779,8 @@ def paged_multi_query_attn(q, table, seq_lens, pool_k, pool_v, tile_tokens, bits
                     qv = q[s, i, h].astype(np.float64)
                     out[s, i, h] = attention(qv, kx[:visible], vx[:visible], sm)
                     if return_scale:
-                        terms = key_score_terms(qv, kc[:visible], ka, ks[:visible], ko[:visible], tile_tokens, signs)
+                        terms = key_score_terms(qv, kc[:visible], ka, ks[:visible], ko if kchan else ko[:visible],
+                                                tile_tokens, signs, kchan)
                         scale[s, i, h] = attention_abs_scale(qv, kx[:visible], vx[:visible], sm, terms)
     return (out, scale) if return_scale else out
 
@@ -759,7 +877,7 @@ def read_baseline_sequence(pool, table_row, seq_len, head, role, fp8=False, scal
 
 
 def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bits_v, base_k, base_v,
-                        signs=None, meta16=False):
+                        signs=None, meta16=False, kchan=False):
     """The re-materializing read path's first half: every cached token restored
     from the quantized pages (read_sequence, float64) and written, rounded to
     fp16, into fp16 baseline pools with the same block table (in place).  Pages
@@ -770,7 +888,7 @@ def rematerialize_pages(pool_k, pool_v, table, seq_lens, tile_tokens, bits_k, bi
         n = int(seq_lens[s])
         if n == 0:
             continue
-        kx = np.stack([read_sequence(pool_k, table[s], n, h, "K", bits_k, tile_tokens, signs, meta16)[0]
+        kx = np.stack([read_sequence(pool_k, table[s], n, h, "K", bits_k, tile_tokens, signs, meta16, kchan)[0]
                        for h in range(heads)], 1)
         vx = np.stack([read_sequence(pool_v, table[s], n, h, "V", bits_v, tile_tokens, signs, meta16)[0]
                        for h in range(heads)], 1)

@@ -5,6 +5,7 @@ a closed form worked by hand (tests/golden/), an exact identity, brute force
 on tiny inputs, or an invariant that a plausible mistake (dropped term, wrong
 sign, wrong axis, transposed operand) would break.
 """
+import dataclasses
 import json
 import math
 import os
@@ -866,3 +867,111 @@ def test_key_score_parts_sum_to_the_score_on_the_restored_keys():
         terms = orc.key_score_terms(q, codes, alpha, scale, offset, tile, mask)
         assert (np.abs(dot) <= terms * (1 + 1e-12)).all()
         assert (terms > 10 * np.abs(dot)).any()    # the terms cancel: asymmetric codes carry an offset
+
+
+# ---------------------------------------------------------------- per-channel K rounding
+
+def test_channel_rtn_hand_example():
+    """Per-channel rounding of a hand-worked tile (tests/golden/kchan_rtn.json):
+    zero-points and steps per column, ties to even, a zero-range column."""
+    g = _golden("kchan_rtn.json")
+    codes, step, zero, pre = orc.rtn_channel(np.array(g["y"], np.float64), g["bits"])
+    np.testing.assert_array_equal(codes, np.array(g["codes"]))
+    np.testing.assert_array_equal(step, np.array(g["step"], np.float64))
+    np.testing.assert_array_equal(zero, np.array(g["zero"], np.float64))
+
+
+def test_channel_rtn_is_the_row_rule_on_the_transpose_and_brute_force_nearest():
+    rng = np.random.default_rng(21)
+    for bits in (2, 4, 8):
+        y = rng.standard_normal((37, 128)) * np.exp(rng.uniform(-3, 3, 128))[None]
+        codes, step, zero, pre = orc.rtn_channel(y, bits)
+        dist = np.abs(y[None] - zero[None, None] - step[None, None] * np.arange(1 << bits)[:, None, None])
+        best = dist.min(0)
+        mine = np.abs(y - zero[None] - step[None] * codes)
+        np.testing.assert_allclose(mine, best, rtol=0, atol=1e-12 * np.abs(y).max())
+        assert (mine <= step[None] / 2 * (1 + 1e-12)).all()
+        assert codes.min() == 0 and (codes.max(0) == (1 << bits) - 1).all()   # every column spans the levels
+
+
+def test_kchan_tile_restores_within_the_rounding_bound_and_one_token_tiles_exactly():
+    """A per-channel K tile restores each rotated element within half a step of
+    its channel, times the token factor (the rotated row is beta A (code + M)
+    with A = alpha step); a one-token tile has zero range in every channel and
+    restores exactly (A = alpha min, M = 1)."""
+    rng = np.random.default_rng(22)
+    for bits, n in ((4, 64), (2, 32), (4, 5)):
+        x = (rng.standard_normal((n, 128)) * np.exp(rng.uniform(-2, 2, 128))[None]).astype(np.float16)
+        tq = orc.quantize_tile(x, bits, 3, kchan=True)
+        rot_hat = tq.scale64[:, None] * tq.alpha64[None] * (tq.codes + tq.zp64[None])
+        _, step, zero, _ = orc.rtn_channel(tq.normalized, bits)
+        bound = np.abs(tq.scale64)[:, None] * np.abs(orc.sinkhorn(tq.rotated, 3)[1])[None] * step[None] / 2
+        assert (np.abs(rot_hat - tq.rotated) <= bound * (1 + 1e-9) + 1e-9).all()
+        np.testing.assert_allclose(orc.dequantize_tile_kchan(tq.codes, tq.alpha64, tq.zp64, tq.scale64),
+                                   orc.fwht(rot_hat), rtol=0, atol=1e-12 * np.abs(rot_hat).max())
+    x1 = (rng.standard_normal((1, 128)) * 3).astype(np.float16)
+    tq = orc.quantize_tile(x1, 4, 3, kchan=True)
+    assert (tq.codes == 0).all() and (tq.zp64 == 1.0).all()
+    np.testing.assert_allclose(orc.dequantize_tile_kchan(tq.codes, tq.alpha64, tq.zp64, tq.scale64),
+                               x1.astype(np.float64), rtol=0, atol=1e-12)
+
+
+def test_kchan_slot_byte_positions_hand_examples():
+    """beta, the channel-scale slice and the zero-offset slice of a per-channel
+    K slot at the byte positions worked by hand
+    (tests/golden/slot_metadata_positions.json, cases_kchan)."""
+    import struct
+    for c in _golden("slot_metadata_positions.json")["cases_kchan"]:
+        bits, tile = c["bits"], c["tile"]
+        assert orc.slot_bytes(bits, tile, kchan=True) == c["total"]
+        ppt = tile // 16
+        tq = orc.TileQuant(codes=np.zeros((tile, 128), np.uint8),
+                           alpha=(3000.0 + np.arange(128)).astype(np.float32),
+                           scale=(1000.0 + np.arange(tile)).astype(np.float32),
+                           offset=(1000.0 + np.arange(tile)).astype(np.float32),
+                           pre=None, rotated=None, normalized=None, beta=None, kchan=True,
+                           zp=(5000.0 + np.arange(128)).astype(np.float32))
+        pool = orc.new_pool(ppt + 3, 1, bits, tile, kchan=True)
+        pages = np.array([ppt + 2 - j for j in range(ppt)], np.int32)
+        orc_impl._store_tile(pool, pages, 0, "K", bits, tile, 0, tq)
+        for j in range(ppt):
+            raw = pool[pages[j], 0].tobytes()
+            assert struct.unpack_from("<f", raw, c["beta_byte"])[0] == 1000.0 + 16 * j + c["beta_token"]
+            for i in (0, c["len"] - 1):
+                assert struct.unpack_from("<f", raw, c["a_byte"] + 4 * i)[0] == 3000.0 + c["len"] * j + i
+                assert struct.unpack_from("<f", raw, c["m_byte"] + 4 * i)[0] == 5000.0 + c["len"] * j + i
+            assert c["m_byte"] + 4 * c["len"] == len(raw)
+
+
+def test_kchan_pages_appends_one_by_one_equal_prefill_and_attention():
+    """Per-channel K pages: appends one token at a time rebuild the prefill's
+    pages byte for byte; paged attention over them equals attention over the
+    tiles restored one by one; the two score terms sum to q . k."""
+    wl = inputs.workload(5).scaled(seq_len=70)
+    wl = dataclasses.replace(wl, hkv=1, hq=4, tile_tokens=32, bits_k=4, bits_v=2, iters=5)
+    k = inputs.gen_kv(wl, "K")[:, :1]
+    v = inputs.gen_kv(wl, "V")[:, :1]
+    wl = dataclasses.replace(wl, seq_lens=(70,))
+    table, npages = inputs.block_table(wl)
+    fk, fv = orc.new_pool(npages, 1, 4, 32, kchan=True), orc.new_pool(npages, 1, 2, 32)
+    orc.quantize_to_pages(k[:70], v[:70], np.array([0, 70]), table, 32, 4, 2, 5, fk, fv, kchan=True)
+    ak, av = orc.new_pool(npages, 1, 4, 32, kchan=True), orc.new_pool(npages, 1, 2, 32)
+    sk, sv = np.zeros((1, 32, 1, 128), np.float16), np.zeros((1, 32, 1, 128), np.float16)
+    for pos in range(70):
+        orc.append_and_requant(k[pos:pos + 1], v[pos:pos + 1], [pos], table, 32, 4, 2, 5, ak, av, sk, sv, kchan=True)
+    np.testing.assert_array_equal(ak, fk)
+    np.testing.assert_array_equal(av, fv)
+    kx, kc, ka, kb, km = orc.read_sequence(fk, table[0], 70, 0, "K", 4, 32, kchan=True)
+    for j in range(3):
+        a, b = 32 * j, min(70, 32 * (j + 1))
+        tq = orc.quantize_tile(k[a:b, 0], 4, 5, kchan=True)
+        np.testing.assert_array_equal(kc[a:b], tq.codes)
+        np.testing.assert_allclose(kx[a:b], orc.dequantize_tile_kchan(tq.codes, tq.alpha, tq.zp, tq.scale), rtol=1e-12)
+    q = inputs.gen_q(dataclasses.replace(wl, hq=4))[:1]
+    vx = orc.read_sequence(fv, table[0], 70, 0, "V", 2, 32)[0]
+    out = orc.paged_decode_attn(q, table, np.array([70]), fk, fv, 32, 4, 2, kchan=True)
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], orc.attention(q[0, h].astype(np.float64), kx, vx, 1 / np.sqrt(128)),
+                                   rtol=1e-12, atol=1e-12)
+        p1, p2 = orc.key_score_parts_kchan(q[0, h], kc, ka, kb, km, 32)
+        np.testing.assert_allclose(p1 + p2, kx @ q[0, h].astype(np.float64), rtol=1e-9, atol=1e-9 * np.abs(p1).max())
