@@ -96,6 +96,10 @@ typedef struct {
   int32_t meta_fp16;      /* 0: slot metadata (scale, offset, channel factors)
                              in fp32; 1: in fp16 (2- and 4-bit codes only), see
                              the page-pool layout */
+  int32_t k_per_channel;  /* 0: K rounded per token (as V); 1: K tiles rounded
+                             per channel over the tile's tokens (2- and 4-bit
+                             codes, fp32 metadata, paged entry points only),
+                             see the page-pool layout */
 } kvq_config;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -119,6 +123,15 @@ const char* kvq_version(void);
  *   the slots hold S*2^-e, O*2^-e and alpha*2^e rounded to nearest even (the
  *   restore alpha*(S*code + O) only sees their products).  Codes are the same
  *   as with fp32 metadata.
+ * With cfg->k_per_channel = 1 a K slot is
+ *   codes | beta: float32[16] per token (0 past the sequence end) |
+ *   A: float32[16*128/tile_tokens] | M: float32[16*128/tile_tokens]
+ *   (1344 bytes at 4 bits, tile 64): the tile is rounded per channel over
+ *   its valid tokens (zero-point min, step (max - min)/(2^bits - 1)), A is
+ *   the slice of the tile's channel scales alpha*step and M of its zero
+ *   offsets in code units min/step (a channel of zero range: A = alpha*min,
+ *   M = 1, codes 0), the same page-in-tile slicing as alpha; the restored
+ *   rotated row is beta*A*(code + M).  V slots are unchanged.
  * Unit order of a token's 128 codes (dense codes and K slots): 16 units of
  *   8 fields, a unit being 8*bits bits (a little-endian 32-bit word at 4
  *   bits, a 16-bit half at 2 bits, a little-endian 64-bit pair of words at 8), unit u at bit 8*bits*u of the token's

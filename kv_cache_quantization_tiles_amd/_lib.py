@@ -32,17 +32,20 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("bits_k", ctypes.c_int32),
                 ("bits_v", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32),
-                ("hadamard_signs", ctypes.c_uint32 * 4), ("meta_fp16", ctypes.c_int32)]
+                ("hadamard_signs", ctypes.c_uint32 * 4), ("meta_fp16", ctypes.c_int32),
+                ("k_per_channel", ctypes.c_int32)]
 
 
 def config(tile_tokens=64, bits_k=4, bits_v=4, sinkhorn_iters=3, head_dim=128, page_tokens=16,
-           hadamard_signs=None, meta_fp16=False):
+           hadamard_signs=None, meta_fp16=False, k_per_channel=False):
     """hadamard_signs: None (plain rotation) or 4 32-bit words, bit c mod 32 of
     word c // 32 set = channel c negated before the Hadamard.  meta_fp16: slot
-    metadata in fp16 instead of fp32."""
+    metadata in fp16 instead of fp32.  k_per_channel: K tiles rounded per
+    channel (page pools only)."""
     signs = (ctypes.c_uint32 * 4)(*[int(w) & 0xFFFFFFFF for w in (hadamard_signs if hadamard_signs is not None
                                                                    else (0, 0, 0, 0))])
-    return KvqConfig(head_dim, page_tokens, tile_tokens, bits_k, bits_v, sinkhorn_iters, signs, int(bool(meta_fp16)))
+    return KvqConfig(head_dim, page_tokens, tile_tokens, bits_k, bits_v, sinkhorn_iters, signs, int(bool(meta_fp16)),
+                     int(bool(k_per_channel)))
 
 
 class KvqError(RuntimeError):

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_m16.hip", "kvq_multi_query.hip",
+SOURCES = ["kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_m16.hip", "kvq_decode_kch.hip", "kvq_multi_query.hip",
            "kvq_multi_query_m16.hip", "kvq_baseline.hip", "kvq_capi.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of the generated code.

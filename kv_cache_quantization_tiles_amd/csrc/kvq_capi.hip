@@ -43,7 +43,21 @@ kvq_status check_config(const kvq_config* cfg, bool need_paged_bits) {
     return fail(KVQ_ERR_ARG, "meta_fp16 must be 0 or 1 (got %d)", cfg->meta_fp16);
   if (need_paged_bits && cfg->meta_fp16 && (cfg->bits_k == 8 || cfg->bits_v == 8))
     return fail(KVQ_ERR_UNSUPPORTED, "fp16 metadata slots take 2- and 4-bit codes only");
+  if (cfg->k_per_channel != 0 && cfg->k_per_channel != 1)
+    return fail(KVQ_ERR_ARG, "k_per_channel must be 0 or 1 (got %d)", cfg->k_per_channel);
+  if (cfg->k_per_channel) {
+    if (!need_paged_bits)
+      return fail(KVQ_ERR_UNSUPPORTED, "per-channel K rounding is a page-pool format (paged entry points only)");
+    if (cfg->meta_fp16) return fail(KVQ_ERR_UNSUPPORTED, "per-channel K slots keep fp32 metadata");
+    if (cfg->bits_k == 8 || cfg->bits_v == 8)
+      return fail(KVQ_ERR_UNSUPPORTED, "per-channel K slots take 2- and 4-bit codes only");
+  }
   return KVQ_OK;
+}
+
+// The slot format of the paged pools for this configuration.
+int slot_format(const kvq_config* cfg) {
+  return cfg->k_per_channel ? kvq::kFmtKch : (cfg->meta_fp16 ? kvq::kFmtM16 : kvq::kFmtFp32);
 }
 
 kvq_status check_bits(int bits) {
@@ -149,7 +163,8 @@ const char* kvq_version(void) { return "kvq 0.1 gfx950"; }
 
 size_t kvq_slot_bytes(const kvq_config* cfg, int32_t is_v) {
   if (check_config(cfg, true) != KVQ_OK) return 0;
-  return (size_t)kvq::slot_bytes(is_v ? cfg->bits_v : cfg->bits_k, cfg->tile_tokens, cfg->meta_fp16 != 0);
+  return (size_t)kvq::slot_bytes(is_v ? cfg->bits_v : cfg->bits_k, cfg->tile_tokens, cfg->meta_fp16 != 0,
+                                 !is_v && cfg->k_per_channel != 0);
 }
 
 kvq_status kvq_quantize_tiles(const kvq_config* cfg, const kvq_half* x, int32_t n_tokens,
@@ -230,7 +245,7 @@ kvq_status kvq_quantize_to_pages(const kvq_config* cfg, const kvq_half* k, const
   a.kv_heads = kv_heads;
   a.iters = cfg->sinkhorn_iters;
   set_signs(a, cfg);
-  return launched(kvq::launch_quantize_paged(a, tile, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0, num_seqs, total_tokens,
+  return launched(kvq::launch_quantize_paged(a, tile, cfg->bits_k, cfg->bits_v, slot_format(cfg), num_seqs, total_tokens,
                                              (hipStream_t)stream),
                   "kvq_quantize_to_pages");
 }
@@ -267,7 +282,7 @@ kvq_status kvq_append_and_requant(const kvq_config* cfg, const kvq_half* k_new,
   a.kv_heads = kv_heads;
   a.iters = cfg->sinkhorn_iters;
   set_signs(a, cfg);
-  return launched(kvq::launch_append(a, cfg->tile_tokens, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0, num_seqs,
+  return launched(kvq::launch_append(a, cfg->tile_tokens, cfg->bits_k, cfg->bits_v, slot_format(cfg), num_seqs,
                                      (hipStream_t)stream),
                   "kvq_append_and_requant");
 }
@@ -336,7 +351,7 @@ kvq_status kvq_paged_decode_attn(const kvq_config* cfg, const kvq_half* q, int32
   a.n_q = 1;
   a.out_scale = 1.0f;
   set_signs(a, cfg);
-  return launched(kvq::launch_decode(a, tile, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0, (hipStream_t)stream),
+  return launched(kvq::launch_decode(a, tile, cfg->bits_k, cfg->bits_v, slot_format(cfg), (hipStream_t)stream),
                   "kvq_paged_decode_attn");
 }
 
@@ -411,7 +426,7 @@ kvq_status kvq_paged_multi_query_attn(const kvq_config* cfg, const kvq_half* q, 
   a.n_q = n_q;
   a.out_scale = 1.0f;
   set_signs(a, cfg);
-  return launched(kvq::launch_multi_query(a, tile, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0, (hipStream_t)stream),
+  return launched(kvq::launch_multi_query(a, tile, cfg->bits_k, cfg->bits_v, slot_format(cfg), (hipStream_t)stream),
                   "kvq_paged_multi_query_attn");
 }
 
@@ -493,7 +508,7 @@ static kvq_status append_and_decode_impl(const kvq_config* cfg, const kvq_half* 
   qa.iters = cfg->sinkhorn_iters;
   set_signs(a, cfg);
   set_signs(qa, cfg);
-  return launched(kvq::launch_append_decode(a, qa, tile, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0,
+  return launched(kvq::launch_append_decode(a, qa, tile, cfg->bits_k, cfg->bits_v, slot_format(cfg),
                                            (hipStream_t)stream),
                   noalloc ? "kvq_append_and_decode_noalloc" : "kvq_append_and_decode");
 }
@@ -573,7 +588,7 @@ kvq_status kvq_rematerialize_fp16_pages(const kvq_config* cfg, const void* pool_
   kvq::RematArgs a{(const uint8_t*)pool_k, (const uint8_t*)pool_v, block_table, max_blocks, seq_lens, kv_heads,
                    base_k, base_v};
   set_signs(a, cfg);
-  return launched(kvq::launch_rematerialize(a, T, cfg->bits_k, cfg->bits_v, cfg->meta_fp16 != 0, num_seqs, max_seq_len,
+  return launched(kvq::launch_rematerialize(a, T, cfg->bits_k, cfg->bits_v, slot_format(cfg), num_seqs, max_seq_len,
                                             (hipStream_t)stream),
                   "kvq_rematerialize_fp16_pages");
 }

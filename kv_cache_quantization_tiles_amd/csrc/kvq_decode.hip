@@ -85,15 +85,17 @@ hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hip
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s) {
-  if (m16) return launch_decode_m16(a, tile, bits_k, bits_v, s);
-  return launch_decode_fmt<false>(a, tile, bits_k, bits_v, s);
+hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, int fmt, hipStream_t s) {
+  if (fmt == kFmtM16) return launch_decode_m16(a, tile, bits_k, bits_v, s);
+  if (fmt == kFmtKch) return launch_decode_kch(a, tile, bits_k, bits_v, s);
+  return launch_decode_fmt<kFmtFp32>(a, tile, bits_k, bits_v, s);
 }
 
 hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
-                                bool m16, hipStream_t s) {
-  if (m16) return launch_append_decode_m16(a, q, tile, bits_k, bits_v, s);
-  return launch_append_decode_fmt<false>(a, q, tile, bits_k, bits_v, s);
+                                int fmt, hipStream_t s) {
+  if (fmt == kFmtM16) return launch_append_decode_m16(a, q, tile, bits_k, bits_v, s);
+  if (fmt == kFmtKch) return launch_append_decode_kch(a, q, tile, bits_k, bits_v, s);
+  return launch_append_decode_fmt<kFmtFp32>(a, q, tile, bits_k, bits_v, s);
 }
 
 }  // namespace kvq

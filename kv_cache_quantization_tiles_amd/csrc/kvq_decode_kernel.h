@@ -294,7 +294,10 @@ struct alignas(16) DecodeSmemU {
 // VGPRs and AGPRs); 16 heads need more registers and run 1 wave per SIMD.
 // M16: slots with fp16 metadata (scales, offsets and channel factors read as
 // fp16 and widened to fp32; the arithmetic is the same).
-template <int T, int BK, int BV, int HG, bool FUSED, bool MQ = false, bool M16 = false>
+// KCH: K slots rounded per channel: the fold takes the channel scales A in
+// place of alpha_K, both per-token factors are beta, and the offset term is
+// sum_c qt_c M_c over the represented query (the zero offsets M of the tile).
+template <int T, int BK, int BV, int HG, bool FUSED, bool MQ = false, bool M16 = false, bool KCH = false>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(HG <= 2 ? 2 : 1)))
 void decode_kernel(DecodeArgs A, QuantArgs Q) {
   constexpr int NH = 4 * HG;
@@ -303,10 +306,11 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   constexpr int CB = (T == 32) ? 3 : 4;          // CBSZ of the QK broadcast
   constexpr int TPC = (T == 32) ? 2 : 1;         // tiles per chunk
   constexpr int PPT = T / kPage;                 // pages per tile
-  constexpr int SLOT_K = slot_bytes(BK, T, M16), SLOT_V = slot_bytes(BV, T, M16);
+  constexpr int SLOT_K = slot_bytes(BK, T, M16, KCH), SLOT_V = slot_bytes(BV, T, M16);
   constexpr int CODE_K = slot_code_bytes(BK), CODE_V = slot_code_bytes(BV);
   constexpr int OFF_K = slot_offset_at(BK, M16), OFF_V = slot_offset_at(BV, M16);
-  constexpr int ALPHA_K = slot_alpha_at(BK, M16), ALPHA_V = slot_alpha_at(BV, M16);
+  constexpr int ALPHA_K = KCH ? slot_chan_scale_at(BK) : slot_alpha_at(BK, M16), ALPHA_V = slot_alpha_at(BV, M16);
+  constexpr int ZP_K = slot_chan_zp_at(BK, T);
   constexpr int AL = slot_alpha_len(T);
   // V fields of tokens 2 and 3 of a quad weigh kTok times those of tokens 0, 1;
   // their probabilities enter the MFMA divided by kTok.
@@ -369,16 +373,17 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         constexpr int QG = DecodeSmemU<T, HG, FUSED>::QG;
         const int g = threadIdx.x / (2 * T), tid = threadIdx.x % (2 * T);
         if constexpr (QG == 1) {
-          quantize_tile_body<T, BK, false, kAppend, M16>(Q, smu.q[0].f, &smu.q[0].s, 0, kvh, seq, tile_idx, tid);
+          quantize_tile_body<T, BK, false, kAppend, M16, kPathBoth, KCH>(Q, smu.q[0].f, &smu.q[0].s, 0, kvh, seq, tile_idx, tid);
           __syncthreads();
           quantize_tile_body<T, BV, true, kAppend, M16>(Q, smu.q[0].f, &smu.q[0].s, 1, kvh, seq, tile_idx, tid);
         } else {
           // groups 2j and 2j + 1 quantize K and V; with 4 groups (tile 32) the
           // second pair repeats the first, writing the same bytes, so that every
-          // wave meets the quantizer's barriers
+          // wave meets the quantizer's barriers (with K rounded per channel the
+          // V body passes the K body's extra barriers too)
           if ((g & 1) == 0)
-            quantize_tile_body<T, BK, false, kAppend, M16>(Q, smu.q[g].f, &smu.q[g].s, 0, kvh, seq, tile_idx, tid);
-          else quantize_tile_body<T, BV, true, kAppend, M16>(Q, smu.q[g].f, &smu.q[g].s, 1, kvh, seq, tile_idx, tid);
+            quantize_tile_body<T, BK, false, kAppend, M16, kPathBoth, KCH>(Q, smu.q[g].f, &smu.q[g].s, 0, kvh, seq, tile_idx, tid);
+          else quantize_tile_body<T, BV, true, kAppend, M16, kPathBoth, false, KCH>(Q, smu.q[g].f, &smu.q[g].s, 1, kvh, seq, tile_idx, tid);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -413,6 +418,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   u32x4 vq[VQ];           // V codes of run `lane` (channels lane, 64 + lane), 4 pages
   f32x4 svq, ovq;         // V scale / offset of tokens 4 bq .. 4 bq + 3
   f32x4 ak[SETS];         // alpha_K of this lane's QK steps (fold layout)
+  f32x4 mk[KCH ? SETS : 1];   // KCH: the zero offsets M of the same channels
   float av[TPC][2];       // alpha_V of channels lane, 64 + lane
   auto tile_page = [&](int c, int tile_in_chunk) {   // first page (in the sequence) of a tile of chunk c
     return (T == 128) ? 4 * (c & ~1) : 4 * c + PPT * tile_in_chunk;
@@ -428,7 +434,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       else { const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sl + 128 * blk + 8 * (lane & 15))); kq[blk] = u32x4{x[0], x[1], 0u, 0u}; }
     }
     sk = load_meta<M16>(sl + CODE_K, lane & 15);
-    ok = load_meta<M16>(sl + OFF_K, lane & 15);
+    ok = KCH ? sk : load_meta<M16>(sl + OFF_K, lane & 15);   // KCH: beta for both
   };
   auto load_v = [&](int c) {
 #pragma unroll
@@ -463,6 +469,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       for (int k = 0; k < 4; ++k) {
         const int ch = qk_channel<BK>(s, k);
         ak[st][k] = load_meta<M16>(kslot(tp + ch / AL) + ALPHA_K, ch % AL);
+        if constexpr (KCH) mk[st][k] = load_meta<false>(kslot(tp + ch / AL) + ZP_K, ch % AL);
       }
     }
   };
@@ -598,10 +605,25 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
           split_grid(x[st][2], x[st][3], qscale, qscale, g1, g1, h23, l23);
           qa_hi[hg][st] = as_f16x4(h01, h23);
           qa_lo[hg][st] = as_f16x4(l01, l23);
-          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h01), wp0, qsum, false);
-          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, l01), wp0, qsum, false);
-          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h23), wp1, qsum, false);
-          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, l23), wp1, qsum, false);
+          if constexpr (KCH) {   // sum_c qt_c M_c over the represented query
+            const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, l01);
+            const f16x2 c = __builtin_bit_cast(f16x2, h23), e = __builtin_bit_cast(f16x2, l23);
+            const float z0 = w0 * mk[KCH ? st : 0][0], z1 = w0 * mk[KCH ? st : 0][1];
+            const float z2 = w1 * mk[KCH ? st : 0][2], z3 = w1 * mk[KCH ? st : 0][3];
+            qsum = __builtin_fmaf((float)a[0], z0, qsum);
+            qsum = __builtin_fmaf((float)b[0], z0, qsum);
+            qsum = __builtin_fmaf((float)a[1], z1, qsum);
+            qsum = __builtin_fmaf((float)b[1], z1, qsum);
+            qsum = __builtin_fmaf((float)c[0], z2, qsum);
+            qsum = __builtin_fmaf((float)e[0], z2, qsum);
+            qsum = __builtin_fmaf((float)c[1], z3, qsum);
+            qsum = __builtin_fmaf((float)e[1], z3, qsum);
+          } else {
+            qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h01), wp0, qsum, false);
+            qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, l01), wp0, qsum, false);
+            qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h23), wp1, qsum, false);
+            qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, l23), wp1, qsum, false);
+          }
         }
         qsum = blocks_sum<BLK>(qsum) * qunscale;
         cA[hg] = c0 * kTwo24 * qunscale;   // score = S D cA + O cB
@@ -871,14 +893,14 @@ hipError_t by_tile(int tile, F&& f) {
   }
   return hipErrorInvalidValue;
 }
-// Slot formats with fp32 metadata (M16 false: code widths 2 and 4 in any
-// pairing, 8 for both) or fp16 metadata (M16 true: 2 and 4 only).
-template <bool M16, typename F>
+// Slot formats: fp32 metadata (code widths 2 and 4 in any pairing, 8 for
+// both), fp16 metadata or K rounded per channel (2 and 4 only).
+template <int FMT, typename F>
 hipError_t by_format(int bits_k, int bits_v, F&& f) {
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   using I8 = std::integral_constant<int, 8>;
-  if constexpr (!M16) {
+  if constexpr (FMT == kFmtFp32) {
     if (bits_k == 8 && bits_v == 8) return f(I8{}, I8{});
   }
   if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{});
@@ -903,18 +925,19 @@ hipError_t by_bits_pair(int bits_k, int bits_v, F&& f) {
 
 // Launchers of the decode kernel for one metadata format (each translation
 // unit instantiates one format); the partition merge follows.
-template <bool M16>
+template <int FMT>
 hipError_t launch_decode_fmt(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_format<M16>(bits_k, bits_v, [&](auto BK, auto BV) {
+    return by_format<FMT>(bits_k, bits_v, [&](auto BK, auto BV) {
+      constexpr bool M16 = FMT == kFmtM16, KCH = FMT == kFmtKch;
       dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
       const QuantArgs q{};
       if (a.group <= 4)
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false, false, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       else if (a.group <= 8)
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false, false, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       else
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, false, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, false, false, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       return launch_combine(a, kChunk, true, s);
@@ -922,18 +945,19 @@ hipError_t launch_decode_fmt(const DecodeArgs& a, int tile, int bits_k, int bits
   });
 }
 
-template <bool M16>
+template <int FMT>
 hipError_t launch_append_decode_fmt(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
                                     hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_format<M16>(bits_k, bits_v, [&](auto BK, auto BV) {
+    return by_format<FMT>(bits_k, bits_v, [&](auto BK, auto BV) {
+      constexpr bool M16 = FMT == kFmtM16, KCH = FMT == kFmtKch;
       dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
       if (a.group <= 4)
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, true, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, true, false, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       else if (a.group <= 8)
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, true, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, true, false, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       else
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, true, false, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 4, true, false, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       DecodeArgs b = a;
@@ -947,18 +971,19 @@ hipError_t launch_append_decode_fmt(const DecodeArgs& a, const QuantArgs& q, int
 // of 4 heads); blocks of 16 read the pages once but measured slower (a
 // 4-token verify at 4 x 16K, 8 kv / 32 query heads: 97 us against 67 us), as
 // did blocks of 4 (88 us).
-template <bool M16>
+template <int FMT>
 hipError_t launch_multi_query_fmt(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_format<M16>(bits_k, bits_v, [&](auto BK, auto BV) {
+    return by_format<FMT>(bits_k, bits_v, [&](auto BK, auto BV) {
+      constexpr bool M16 = FMT == kFmtM16, KCH = FMT == kFmtKch;
       const int rows = a.n_q * a.group;
       const QuantArgs q{};
       if (rows <= 4) {
         dim3 grid(a.kv_heads * a.num_seqs, a.max_parts);
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false, true, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 1, false, true, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       } else {
         dim3 grid(a.kv_heads * ((rows + 7) / 8) * a.num_seqs, a.max_parts);
-        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false, true, M16>), grid, dim3(64 * kWaves), 0, s, a, q);
+        hipLaunchKernelGGL((decode_kernel<T(), BK(), BV(), 2, false, true, M16, KCH>), grid, dim3(64 * kWaves), 0, s, a, q);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

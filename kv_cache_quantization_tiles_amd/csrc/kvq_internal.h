@@ -20,8 +20,15 @@ constexpr float kInvSqrtD = 0.08838834764831845f;  // 1/sqrt(128)
 __host__ __device__ constexpr int slot_code_bytes(int bits) { return kPage * kHeadDim * bits / 8; }
 __host__ __device__ constexpr int slot_alpha_len(int tile) { return kPage * kHeadDim / tile; }
 __host__ __device__ constexpr int meta_bytes(bool m16) { return m16 ? 2 : 4; }
-__host__ __device__ constexpr int slot_bytes(int bits, int tile, bool m16 = false) {
-  return slot_code_bytes(bits) + meta_bytes(m16) * (2 * kPage + slot_alpha_len(tile));
+// K slots rounded per channel (KCH, fp32 metadata): codes | beta[16] |
+// channel-scale slice A[2048 / T] | zero-offset slice M[2048 / T].
+__host__ __device__ constexpr int slot_bytes(int bits, int tile, bool m16 = false, bool kch = false) {
+  return kch ? slot_code_bytes(bits) + 4 * kPage + 8 * slot_alpha_len(tile)
+             : slot_code_bytes(bits) + meta_bytes(m16) * (2 * kPage + slot_alpha_len(tile));
+}
+__host__ __device__ constexpr int slot_chan_scale_at(int bits) { return slot_code_bytes(bits) + 4 * kPage; }
+__host__ __device__ constexpr int slot_chan_zp_at(int bits, int tile) {
+  return slot_code_bytes(bits) + 4 * kPage + 4 * slot_alpha_len(tile);
 }
 __host__ __device__ constexpr int slot_offset_at(int bits, bool m16) {   // byte of offset[0]
   return slot_code_bytes(bits) + meta_bytes(m16) * kPage;
@@ -115,16 +122,21 @@ struct RematArgs {
   uint32_t signs[4];
 };
 
+// Slot formats of the paged pools: fp32 metadata, fp16 metadata, or K slots
+// rounded per channel (fp32 metadata; V as with kFmtFp32).
+constexpr int kFmtFp32 = 0, kFmtM16 = 1, kFmtKch = 2;
+
 hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStream_t s);
-hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16,
+hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v, int fmt,
                                  int num_seqs, int total_tokens, hipStream_t s);
-hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16, int num_seqs,
+hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, int fmt, int num_seqs,
                          hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream_t s);
-hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, bool m16, int num_seqs,
+hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, int fmt, int num_seqs,
                                 int max_seq_len, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int tile, int bits_k, int bits_v, int fmt, hipStream_t s);
 hipError_t launch_decode_m16(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
+hipError_t launch_decode_kch(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, int unit_tokens, bool rotate, hipStream_t s);
 // Several queries per sequence: with at least 16 (query, head) rows per
@@ -136,11 +148,14 @@ inline int mq_row_blocks(int n_q, int group) {
   const long rows = (long)n_q * group;
   return (int)(mq_dense(n_q, group) ? (rows + 63) / 64 : (rows + 7) / 8);
 }
-hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s);
+hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, int fmt, hipStream_t s);
 hipError_t launch_multi_query_m16(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
+hipError_t launch_multi_query_kch(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s);
 hipError_t launch_append_decode(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
-                                bool m16, hipStream_t s);
+                                int fmt, hipStream_t s);
 hipError_t launch_append_decode_m16(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
+                                    hipStream_t s);
+hipError_t launch_append_decode_kch(const DecodeArgs& a, const QuantArgs& q, int tile, int bits_k, int bits_v,
                                     hipStream_t s);
 hipError_t launch_fill_baseline(const BaseFillArgs& a, bool fp8, int num_seqs, int max_seq_len, hipStream_t s);
 hipError_t launch_decode_baseline(const DecodeArgs& a, bool fp8, hipStream_t s);

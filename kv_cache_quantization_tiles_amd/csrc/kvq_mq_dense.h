@@ -126,12 +126,15 @@ struct alignas(16) MqSmem {
   };
 };
 
-template <int T, int BK, int BV, bool M16>
+template <int T, int BK, int BV, bool M16, bool KCH>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T != 32 && BK != 8 && BV != 8) ? 2 : 1))) void mq_dense_kernel(DecodeArgs A) {
-  constexpr int SLOT_K = slot_bytes(BK, T, M16), SLOT_V = slot_bytes(BV, T, M16);
+  constexpr int SLOT_K = slot_bytes(BK, T, M16, KCH), SLOT_V = slot_bytes(BV, T, M16);
   constexpr int CODE_K = slot_code_bytes(BK), CODE_V = slot_code_bytes(BV);
   constexpr int OFF_K = slot_offset_at(BK, M16), OFF_V = slot_offset_at(BV, M16);
-  constexpr int ALPHA_K = slot_alpha_at(BK, M16), ALPHA_V = slot_alpha_at(BV, M16);
+  // KCH (K rounded per channel): the fold takes the channel scales A, both
+  // per-token factors are beta, and the offset term is sum_c qt_c M_c
+  constexpr int ALPHA_K = KCH ? slot_chan_scale_at(BK) : slot_alpha_at(BK, M16), ALPHA_V = slot_alpha_at(BV, M16);
+  constexpr int ZP_K = slot_chan_zp_at(BK, T);
   constexpr int AL = slot_alpha_len(T);   // channels of a tile's alpha per page
   constexpr int PPT = T / kPage;
   // V tokens 2, 3 of a quad weigh kTok times tokens 0, 1 (their probabilities
@@ -249,7 +252,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
   float cA = 0.f, cB = 0.f;
   // alpha_K of a tile for the lane's channels 16 m + 4 g + j, loaded ahead of its fold
   f32x4 akn[8];
+  int akn_page = 0;   // the tile of akn (KCH: its zero offsets are read at the fold)
   auto load_alpha_k = [&](int tile_page) {   // first page (in the sequence) of the tile
+    akn_page = tile_page;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int c = 16 * m + 4 * g;
@@ -257,6 +262,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     }
   };
   auto fold = [&]() {   // the tile whose alpha_K sits in akn
+    f32x4 mz[KCH ? 8 : 1];
+    if constexpr (KCH) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int c = 16 * m + 4 * g;
+        mz[m] = load_meta4<BK, false>(kslot(akn_page + c / AL) + ZP_K, c % AL);
+      }
+    }
     float x[8][4];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -285,9 +298,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
         constexpr int j0 = mq_off<BK>(ks, 2 * pp), j1 = mq_off<BK>(ks, 2 * pp + 1);
         constexpr float w = k_field_weight<BK>(16 * m0);   // the pair shares its weight
         split_grid(x[m0][j0], x[m1][j1], qscale, qscale, kGrid / w, kGrid / w, hw[pp], lw[pp]);
-        const f16x2 wp{(_Float16)w, (_Float16)w};
-        qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[pp]), wp, qsum, false);
-        qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lw[pp]), wp, qsum, false);
+        if constexpr (KCH) {   // sum_c qt_c M_c over the represented query
+          const f16x2 a = __builtin_bit_cast(f16x2, hw[pp]), b = __builtin_bit_cast(f16x2, lw[pp]);
+          const float z0 = w * mz[KCH ? m0 : 0][j0], z1 = w * mz[KCH ? m1 : 0][j1];
+          qsum = __builtin_fmaf((float)a[0], z0, qsum);
+          qsum = __builtin_fmaf((float)b[0], z0, qsum);
+          qsum = __builtin_fmaf((float)a[1], z1, qsum);
+          qsum = __builtin_fmaf((float)b[1], z1, qsum);
+        } else {
+          const f16x2 wp{(_Float16)w, (_Float16)w};
+          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hw[pp]), wp, qsum, false);
+          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lw[pp]), wp, qsum, false);
+        }
       });
       qhi[ks] = as_f16x8(hw[0], hw[1], hw[2], hw[3]);
       qlo[ks] = as_f16x8(lw[0], lw[1], lw[2], lw[3]);
@@ -350,7 +372,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     const uint8_t* ks = kslot(pg0 + (lane >> 4));
     const uint8_t* vs = vslot(pg0 + (lane >> 4));
     o.sk = load_meta<M16>(ks + CODE_K, lane & 15);
-    o.ok = load_meta<M16>(ks + OFF_K, lane & 15);
+    o.ok = KCH ? o.sk : load_meta<M16>(ks + OFF_K, lane & 15);   // KCH: beta for both
     o.sv = load_meta<M16>(vs + CODE_V, lane & 15);
     o.ov = load_meta<M16>(vs + OFF_V, lane & 15);
   };
@@ -606,13 +628,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
 
 // Multi-query attention with at least 16 rows ((query, head) pairs) per
 // sequence and kv head: workgroups of up to 64 rows, then the partition merge.
-template <bool M16>
+template <int FMT>
 hipError_t launch_mq_dense_fmt(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_format<M16>(bits_k, bits_v, [&](auto BK, auto BV) {
+    return by_format<FMT>(bits_k, bits_v, [&](auto BK, auto BV) {
+      constexpr bool M16 = FMT == kFmtM16, KCH = FMT == kFmtKch;
       const int rows = a.n_q * a.group;
       dim3 grid(a.kv_heads * ((rows + kMqBlockRows - 1) / kMqBlockRows) * a.num_seqs, a.max_parts);
-      hipLaunchKernelGGL((mq_dense_kernel<T(), BK(), BV(), M16>), grid, dim3(64 * kWaves), 0, s, a);
+      hipLaunchKernelGGL((mq_dense_kernel<T(), BK(), BV(), M16, KCH>), grid, dim3(64 * kWaves), 0, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       return launch_combine(a, 64, true, s);

@@ -11,10 +11,11 @@
 
 namespace kvq {
 
-hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, bool m16, hipStream_t s) {
-  if (m16) return launch_multi_query_m16(a, tile, bits_k, bits_v, s);
-  if (mq_dense(a.n_q, a.group)) return launch_mq_dense_fmt<false>(a, tile, bits_k, bits_v, s);
-  return launch_multi_query_fmt<false>(a, tile, bits_k, bits_v, s);
+hipError_t launch_multi_query(const DecodeArgs& a, int tile, int bits_k, int bits_v, int fmt, hipStream_t s) {
+  if (fmt == kFmtM16) return launch_multi_query_m16(a, tile, bits_k, bits_v, s);
+  if (fmt == kFmtKch) return launch_multi_query_kch(a, tile, bits_k, bits_v, s);
+  if (mq_dense(a.n_q, a.group)) return launch_mq_dense_fmt<kFmtFp32>(a, tile, bits_k, bits_v, s);
+  return launch_multi_query_fmt<kFmtFp32>(a, tile, bits_k, bits_v, s);
 }
 
 }  // namespace kvq

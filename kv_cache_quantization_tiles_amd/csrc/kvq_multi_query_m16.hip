@@ -5,8 +5,8 @@
 namespace kvq {
 
 hipError_t launch_multi_query_m16(const DecodeArgs& a, int tile, int bits_k, int bits_v, hipStream_t s) {
-  if (mq_dense(a.n_q, a.group)) return launch_mq_dense_fmt<true>(a, tile, bits_k, bits_v, s);
-  return launch_multi_query_fmt<true>(a, tile, bits_k, bits_v, s);
+  if (mq_dense(a.n_q, a.group)) return launch_mq_dense_fmt<kFmtM16>(a, tile, bits_k, bits_v, s);
+  return launch_multi_query_fmt<kFmtM16>(a, tile, bits_k, bits_v, s);
 }
 
 }  // namespace kvq

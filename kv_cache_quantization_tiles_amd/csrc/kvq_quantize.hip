@@ -44,7 +44,7 @@ __global__ __launch_bounds__(2 * T) void quantize_dense_short_kernel(QuantArgs A
 // wave finds its sequence with one load of cu_seqlens per 64 sequences and
 // a ballot: the starts increase, so the sequences starting at or before the
 // slot are a prefix and the last one holds it.
-template <int T, int BK, int BV, bool M16>
+template <int T, int BK, int BV, bool M16, bool KCH>
 __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void quantize_paged_kernel(QuantArgs A) {
   __shared__ Smem<T> sm;
   const int f = blockIdx.x;
@@ -72,13 +72,13 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(4))) void
   if (tile * T >= a1 - a0 || (tile + 1) * (T / kPage) > A.max_blocks) return;
   const int role = blockIdx.y / A.kv_heads;
   const int head = blockIdx.y % A.kv_heads;
-  if (role == 0) quantize_tile_body<T, BK, false, kPaged, M16>(A, sm, nullptr, 0, head, seq, tile, threadIdx.x);
+  if (role == 0) quantize_tile_body<T, BK, false, kPaged, M16, kPathFp32, KCH>(A, sm, nullptr, 0, head, seq, tile, threadIdx.x);
   else quantize_tile_body<T, BV, true, kPaged, M16>(A, sm, nullptr, 1, head, seq, tile, threadIdx.x);
 }
 
 // grid: x = head + Hkv * role, y = sequence: the sequence's last tile when it
 // holds fewer than 16 tokens (float64 path)
-template <int T, int BK, int BV, bool M16>
+template <int T, int BK, int BV, bool M16, bool KCH>
 __global__ __launch_bounds__(2 * T) void quantize_paged_short_kernel(QuantArgs A) {
   __shared__ TileSmem<T> sm;
   const int seq = blockIdx.y;
@@ -88,19 +88,19 @@ __global__ __launch_bounds__(2 * T) void quantize_paged_short_kernel(QuantArgs A
   const int head = blockIdx.x % A.kv_heads;
   const int tile = (len - 1) / T;
   if ((tile + 1) * (T / kPage) > A.max_blocks) return;   // no pages for this tile
-  if (role == 0) quantize_tile_body<T, BK, false, kPaged, M16, kPathShort>(A, sm.f, &sm.s, 0, head, seq, tile, threadIdx.x);
+  if (role == 0) quantize_tile_body<T, BK, false, kPaged, M16, kPathShort, KCH>(A, sm.f, &sm.s, 0, head, seq, tile, threadIdx.x);
   else quantize_tile_body<T, BV, true, kPaged, M16, kPathShort>(A, sm.f, &sm.s, 1, head, seq, tile, threadIdx.x);
 }
 
 // grid: x = head, y = role, z = sequence
-template <int T, int BK, int BV, bool M16>
+template <int T, int BK, int BV, bool M16, bool KCH>
 __global__ __launch_bounds__(2 * T) void append_kernel(QuantArgs A) {
   __shared__ TileSmem<T> sm;
   const int seq = blockIdx.z;
   const int tile_idx = A.lens_before[seq] / T;
   if ((tile_idx + 1) * (T / kPage) > A.max_blocks) return;  // no page for this tile
   if (blockIdx.y == 0)
-    quantize_tile_body<T, BK, false, kAppend, M16>(A, sm.f, &sm.s, 0, blockIdx.x, seq, tile_idx, threadIdx.x);
+    quantize_tile_body<T, BK, false, kAppend, M16, kPathBoth, KCH>(A, sm.f, &sm.s, 0, blockIdx.x, seq, tile_idx, threadIdx.x);
   else quantize_tile_body<T, BV, true, kAppend, M16>(A, sm.f, &sm.s, 1, blockIdx.x, seq, tile_idx, threadIdx.x);
 }
 
@@ -207,12 +207,15 @@ __global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
 // the fp16 pool's page of the same id (K token-major, V channel-major), as
 // kvq_fill_pages_fp16 lays them out.  128 threads = 16 tokens x 8 channel
 // groups, the dense restore's register layout and butterfly.
-template <int T, int BITS, bool VL, bool M16>
+template <int T, int BITS, bool VL, bool M16, bool KCH = false>
 __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj, int head, int n,
                                              uint16_t (*vt)[kPage + 2]) {
   constexpr int PPT = T / kPage, AL = slot_alpha_len(T);
-  constexpr int SLOT = slot_bytes(BITS, T, M16), CODE = slot_code_bytes(BITS);
-  constexpr int OFF_AT = slot_offset_at(BITS, M16), ALPHA_AT = slot_alpha_at(BITS, M16);
+  constexpr int SLOT = slot_bytes(BITS, T, M16, KCH), CODE = slot_code_bytes(BITS);
+  constexpr int OFF_AT = slot_offset_at(BITS, M16);
+  // KCH (K rounded per channel): the channel scales A stand where alpha does
+  // and the restore is beta A (code + M)
+  constexpr int ALPHA_AT = KCH ? slot_chan_scale_at(BITS) : slot_alpha_at(BITS, M16);
   constexpr unsigned MASK = (1u << BITS) - 1u;
   const int H = A.kv_heads;
   const int tid = threadIdx.x, t = tid >> 3, cg = tid & 7;
@@ -230,8 +233,18 @@ __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj
 #pragma unroll
     for (int i = 0; i < 8; ++i) al[8 * half + i] = load_meta<M16>(ap, c0 % AL + i);
   }
-  const float S = load_meta<M16>(slot + CODE, t);
-  const float O = load_meta<M16>(slot + OFF_AT, t);
+  float mz[KCH ? 16 : 1];   // KCH: the zero offsets of the lane's channels
+  if constexpr (KCH) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c0 = 64 * half + 8 * cg;
+      const uint8_t* zp = pool + ((size_t)row_tab[pt0 + c0 / AL] * H + head) * SLOT + slot_chan_zp_at(BITS, T);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mz[8 * half + i] = load_meta<false>(zp, c0 % AL + i);
+    }
+  }
+  const float S = load_meta<M16>(slot + CODE, t);   // KCH: beta
+  const float O = KCH ? 0.f : load_meta<M16>(slot + OFF_AT, t);
   float x[16];
   if (!VL) {
     // unit order: channel 64 half + 8 cg + j is field 4 half + (cg >> 1) of unit
@@ -269,7 +282,9 @@ __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj
       for (int j = 0; j < 8; ++j) {
         const unsigned u = (BITS == 8 && m >= 4) ? units8_hi[j] : units[j];
         const int mm = (BITS == 8) ? (m & 3) : m;
-        x[8 * half + j] = al[8 * half + j] * __builtin_fmaf(S, (float)((u >> (BITS * mm)) & MASK), O);
+        const float code = (float)((u >> (BITS * mm)) & MASK);
+        if constexpr (KCH) x[8 * half + j] = al[8 * half + j] * S * (code + mz[KCH ? 8 * half + j : 0]);
+        else x[8 * half + j] = al[8 * half + j] * __builtin_fmaf(S, code, O);
       }
     }
   } else {
@@ -349,7 +364,7 @@ __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj
 }
 
 // grid: x = page of the sequence, y = head + Hkv * role (0 K, 1 V), z = sequence
-template <int T, int BK, int BV, bool M16>
+template <int T, int BK, int BV, bool M16, bool KCH>
 __global__ __launch_bounds__(128) void rematerialize_kernel(RematArgs A) {
   __shared__ uint16_t vt[kHeadDim][kPage + 2];
   const int seq = blockIdx.z, pj = blockIdx.x;
@@ -357,7 +372,7 @@ __global__ __launch_bounds__(128) void rematerialize_kernel(RematArgs A) {
   const int L = A.seq_lens[seq];
   if (pj * kPage >= L) return;   // uniform over the workgroup
   const int n = min(kPage, L - pj * kPage);
-  if (role == 0) restore_page<T, BK, false, M16>(A, seq, pj, head, n, vt);
+  if (role == 0) restore_page<T, BK, false, M16, KCH>(A, seq, pj, head, n, vt);
   else restore_page<T, BV, true, M16>(A, seq, pj, head, n, vt);
 }
 
@@ -392,23 +407,28 @@ hipError_t by_bits(int bits, F&& f) {
 // Slot formats: K and V code widths 2 and 4 in any pairing, 8 for both; fp16
 // metadata (M16) with 2 and 4 only.
 template <typename F>
-hipError_t by_format(int bits_k, int bits_v, bool m16, F&& f) {
+hipError_t by_format(int bits_k, int bits_v, int fmt, F&& f) {
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   using I8 = std::integral_constant<int, 8>;
-  using M0 = std::integral_constant<bool, false>;
-  using M1 = std::integral_constant<bool, true>;
-  if (!m16) {
-    if (bits_k == 8 && bits_v == 8) return f(I8{}, I8{}, M0{});
-    if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{}, M0{});
-    if (bits_k == 4 && bits_v == 2) return f(I4{}, I2{}, M0{});
-    if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{}, M0{});
-    if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{}, M0{});
-  } else {
-    if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{}, M1{});
-    if (bits_k == 4 && bits_v == 2) return f(I4{}, I2{}, M1{});
-    if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{}, M1{});
-    if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{}, M1{});
+  using B0 = std::integral_constant<bool, false>;
+  using B1 = std::integral_constant<bool, true>;
+  if (fmt == kFmtFp32) {
+    if (bits_k == 8 && bits_v == 8) return f(I8{}, I8{}, B0{}, B0{});
+    if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{}, B0{}, B0{});
+    if (bits_k == 4 && bits_v == 2) return f(I4{}, I2{}, B0{}, B0{});
+    if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{}, B0{}, B0{});
+    if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{}, B0{}, B0{});
+  } else if (fmt == kFmtM16) {
+    if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{}, B1{}, B0{});
+    if (bits_k == 4 && bits_v == 2) return f(I4{}, I2{}, B1{}, B0{});
+    if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{}, B1{}, B0{});
+    if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{}, B1{}, B0{});
+  } else if (fmt == kFmtKch) {
+    if (bits_k == 4 && bits_v == 4) return f(I4{}, I4{}, B0{}, B1{});
+    if (bits_k == 4 && bits_v == 2) return f(I4{}, I2{}, B0{}, B1{});
+    if (bits_k == 2 && bits_v == 4) return f(I2{}, I4{}, B0{}, B1{});
+    if (bits_k == 2 && bits_v == 2) return f(I2{}, I2{}, B0{}, B1{});
   }
   return hipErrorInvalidValue;
 }
@@ -428,25 +448,25 @@ hipError_t launch_quantize_dense(const QuantArgs& a, int tile, int bits, hipStre
   });
 }
 
-hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16,
+hipError_t launch_quantize_paged(const QuantArgs& a, int tile, int bits_k, int bits_v, int fmt,
                                  int num_seqs, int total_tokens, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_format(bits_k, bits_v, m16, [&](auto BK, auto BV, auto M) {
+    return by_format(bits_k, bits_v, fmt, [&](auto BK, auto BV, auto M, auto KC) {
       dim3 grid(total_tokens / T() + num_seqs, 2 * a.kv_heads);
-      hipLaunchKernelGGL((quantize_paged_kernel<T(), BK(), BV(), M()>), grid, dim3(2 * T()), 0, s, a);
-      hipLaunchKernelGGL((quantize_paged_short_kernel<T(), BK(), BV(), M()>), dim3(2 * a.kv_heads, num_seqs),
+      hipLaunchKernelGGL((quantize_paged_kernel<T(), BK(), BV(), M(), KC()>), grid, dim3(2 * T()), 0, s, a);
+      hipLaunchKernelGGL((quantize_paged_short_kernel<T(), BK(), BV(), M(), KC()>), dim3(2 * a.kv_heads, num_seqs),
                          dim3(2 * T()), 0, s, a);
       return hipGetLastError();
     });
   });
 }
 
-hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, bool m16, int num_seqs,
+hipError_t launch_append(const QuantArgs& a, int tile, int bits_k, int bits_v, int fmt, int num_seqs,
                          hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_format(bits_k, bits_v, m16, [&](auto BK, auto BV, auto M) {
+    return by_format(bits_k, bits_v, fmt, [&](auto BK, auto BV, auto M, auto KC) {
       dim3 grid(a.kv_heads, 2, num_seqs);
-      hipLaunchKernelGGL((append_kernel<T(), BK(), BV(), M()>), grid, dim3(2 * T()), 0, s, a);
+      hipLaunchKernelGGL((append_kernel<T(), BK(), BV(), M(), KC()>), grid, dim3(2 * T()), 0, s, a);
       return hipGetLastError();
     });
   });
@@ -463,12 +483,12 @@ hipError_t launch_dequantize(const DequantArgs& a, int tile, int bits, hipStream
   });
 }
 
-hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, bool m16, int num_seqs,
+hipError_t launch_rematerialize(const RematArgs& a, int tile, int bits_k, int bits_v, int fmt, int num_seqs,
                                 int max_seq_len, hipStream_t s) {
   return by_tile(tile, [&](auto T) {
-    return by_format(bits_k, bits_v, m16, [&](auto BK, auto BV, auto M) {
+    return by_format(bits_k, bits_v, fmt, [&](auto BK, auto BV, auto M, auto KC) {
       dim3 grid((max_seq_len + kPage - 1) / kPage, 2 * a.kv_heads, num_seqs);
-      hipLaunchKernelGGL((rematerialize_kernel<T(), BK(), BV(), M()>), grid, dim3(128), 0, s, a);
+      hipLaunchKernelGGL((rematerialize_kernel<T(), BK(), BV(), M(), KC()>), grid, dim3(128), 0, s, a);
       return hipGetLastError();
     });
   });

@@ -83,8 +83,9 @@ struct alignas(16) Smem {
 constexpr int kShortTile = 16;
 struct alignas(16) ShortSmem {
   double col[kShortTile][kHeadDim + 2];   // the tile [token][channel]
-  double inv_g[kHeadDim];                 // 1 / (factor of the current channel step)
+  double inv_g[kHeadDim];                 // 1 / (factor of the current channel step); KCH: levels / range
   double alpha[kHeadDim];                 // channel factors
+  double zmin[kHeadDim];                  // KCH: each channel's minimum over the tile
 };
 template <int T>
 union TileSmem {
@@ -128,7 +129,7 @@ __device__ __forceinline__ double quad_dpp(double v) {
 // offsets and channel factors, and leaves in R the integer codes of the
 // lane's rows in the fp32 path's layout (zeros past the tile's end), ready
 // for the code store.
-template <int T, int BITS, int MODE, bool M16>
+template <int T, int BITS, int MODE, bool M16, bool KCH = false, bool PADK = false>
 __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, int role, int head, int seq,
                                            int t0, int n, const uint16_t* rows_base, size_t row_stride,
                                            int r_new, int tid, float (&R)[8][8], uint8_t* pool,
@@ -137,7 +138,7 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
   constexpr int NT = 2 * T;
   constexpr int CODE_BYTES = slot_code_bytes(BITS);
   constexpr int AL = slot_alpha_len(T);
-  constexpr int SLOT = slot_bytes(BITS, T, M16);
+  constexpr int SLOT = slot_bytes(BITS, T, M16, KCH);
   constexpr int OFF_AT = slot_offset_at(BITS, M16), ALPHA_AT = slot_alpha_at(BITS, M16);
   constexpr double kInvSqrtD64 = 0.088388347648318440550;   // 1/sqrt(128)
   const int H = (MODE == kDense) ? A.heads : A.kv_heads;
@@ -227,7 +228,9 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
         y[i + 1] *= ig.y;
       }
     }
-    if (it + 1 == iters) break;   // the final token step cancels in every stored value
+    // the final token step cancels in every stored value of a row-rounded
+    // tile; per-channel rounding needs it
+    if (it + 1 == iters && !KCH) break;
     // token step: mean, spread and RMS of each token over its 128 channels
     if (act) {
       double s1 = 0.0, s2 = 0.0;
@@ -256,6 +259,63 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
 #pragma unroll
       for (int i = 0; i < 32; ++i) y[i] *= ig;
     }
+  }
+
+  if constexpr (KCH) {
+    // rounding per channel over the n tokens: zero-point = min, step =
+    // range / levels, ties to even; the slot keeps beta per token, A = alpha
+    // step and M = min / step per channel (a zero-range channel: A = alpha min,
+    // M = 1, codes 0)
+    __syncthreads();   // every thread is done with the channel step's col reads
+    if (act && t < n) {
+#pragma unroll
+      for (int i = 0; i < 32; i += 2)
+        *reinterpret_cast<double2*>(&sh.col[t][32 * k + i]) = double2{y[i], y[i + 1]};
+    }
+    __syncthreads();
+    for (int c = tid; c < kHeadDim; c += NT) {
+      double lo = sh.col[0][c], hi = lo;
+      for (int r = 1; r < n; ++r) {
+        lo = fmin(lo, sh.col[r][c]);
+        hi = fmax(hi, sh.col[r][c]);
+      }
+      const double st = (hi - lo) / LEVELS;
+      sh.zmin[c] = lo;
+      sh.inv_g[c] = st > 0.0 ? 1.0 / st : 0.0;
+      const double al = sh.alpha[c];
+      uint8_t* slot = page_slot(c / AL);
+      store_meta<false>(slot + slot_chan_scale_at(BITS), c % AL, (float)(st > 0.0 ? al * st : al * lo));
+      store_meta<false>(slot + slot_chan_zp_at(BITS, T), c % AL, (float)(st > 0.0 ? lo / st : 1.0));
+    }
+    if (act && k == 0) store_meta<false>(page_slot(0) + CODE_BYTES, t, t < n ? (float)beta : 0.f);
+    if (tid >= kShortTile && tid < T) store_meta<false>(page_slot(tid / kPage) + CODE_BYTES, tid % kPage, 0.f);
+    __syncthreads();
+    unsigned cw[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      unsigned wd = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 32 * k + 4 * v + e;
+        const double cd = (act && t < n) ? fmin(fmax(__builtin_rint((y[4 * v + e] - sh.zmin[c]) * sh.inv_g[c]), 0.0), LEVELS) : 0.0;
+        wd |= (unsigned)cd << (8 * e);
+      }
+      cw[v] = wd;
+    }
+    __syncthreads();   // every thread is done reading col
+    uint8_t* code8 = reinterpret_cast<uint8_t*>(&sh.col[0][0]);
+    if (act) {
+      *reinterpret_cast<qt_u32x4*>(code8 + kHeadDim * t + 32 * k) = qt_u32x4{cw[0], cw[1], cw[2], cw[3]};
+      *reinterpret_cast<qt_u32x4*>(code8 + kHeadDim * t + 32 * k + 16) = qt_u32x4{cw[4], cw[5], cw[6], cw[7]};
+    }
+    __syncthreads();
+    const int lane = tid & 63, w = tid >> 6, j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        R[q][m] = (w == 0 && q < 4) ? (float)code8[kHeadDim * (4 * g + q) + j + 16 * m] : 0.f;
+    return;
   }
 
   // rounding: per token, zero-point = min, step = range / levels, ties to even
@@ -338,6 +398,11 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
 #pragma unroll
     for (int m = 0; m < 8; ++m)
       R[q][m] = (w == 0 && q < 4) ? (float)code8[kHeadDim * (4 * g + q) + j + 16 * m] : 0.f;
+  if constexpr (PADK) {   // the per-channel K body beside this one passes three more barriers
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
+  }
 }
 
 // Which tiles a quantizer instantiation handles: the fp32 path only (tiles of
@@ -346,10 +411,17 @@ __device__ __forceinline__ void short_tile(const QuantArgs& A, ShortSmem& sh, in
 // over the sequences' last tiles), or both by a runtime branch (appends).
 enum TilePath { kPathFp32 = 0, kPathShort = 1, kPathBoth = 2 };
 
+// KCH: a K tile rounded per channel (fp32 metadata, paged layouts): all
+// normalization half-steps run, and the slot takes beta per token and the
+// channel scales and zero offsets in place of S, O and alpha.
+// PADK: a body that runs beside a per-channel K body in one workgroup (the
+// fused append + decode) and passes the same number of workgroup barriers.
 template <int T, int BITS, bool VLAYOUT, int MODE, bool M16 = false,
-          int PATH = (MODE == kAppend) ? kPathBoth : kPathFp32>
+          int PATH = (MODE == kAppend) ? kPathBoth : kPathFp32, bool KCH = false, bool PADK = false>
 __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& sm, ShortSmem* sh, int role,
                                                    int head, int seq, int tile_idx, int tid) {
+  static_assert(!KCH || (!VLAYOUT && !M16 && MODE != kDense), "per-channel rounding: paged K slots, fp32 metadata");
+  static_assert(!(KCH && PADK), "a per-channel body is not padded");
   constexpr int NT = 2 * T;
   constexpr float LEVELS = (float)((1 << BITS) - 1);
   const int lane = tid & 63;
@@ -426,7 +498,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
   // Output addressing (paged): the tile's pages.
   uint8_t* pool = nullptr;
   const int32_t* pages = nullptr;
-  constexpr int SLOT = slot_bytes(BITS, T, M16);
+  constexpr int SLOT = slot_bytes(BITS, T, M16, KCH);
   constexpr int CODE_BYTES = slot_code_bytes(BITS);
   constexpr int OFF_AT = slot_offset_at(BITS, M16), ALPHA_AT = slot_alpha_at(BITS, M16);
   if (MODE != kDense) {
@@ -439,8 +511,8 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
 
   float R[8][8];   // [q = 4 bb + r][m = sigma + 2 p']: token tok(q), channel j + 16 m
   if (PATH != kPathFp32 && (PATH == kPathShort || n_valid < kShortTile)) {   // uniform over the group
-    short_tile<T, BITS, MODE, M16>(A, *sh, role, head, seq, t0, n_valid, rows_base, row_stride, r_new, tid, R, pool,
-                              pages);
+    short_tile<T, BITS, MODE, M16, KCH, PADK>(A, *sh, role, head, seq, t0, n_valid, rows_base, row_stride, r_new,
+                                              tid, R, pool, pages);
   } else {
     // ---------------------------------------------------------------- Hadamard (unnormalized)
     // B+ = [H16; H16], B- = [H16; -H16] in the MFMA B layout: lane (g, j) holds
@@ -582,7 +654,15 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
 #pragma unroll
         for (int i = 0; i < 4; ++i) { a[i] = lo[i]; a[4 + i] = hi[i]; }
       }
-      if (it + 1 == iters) break;  // the final token step cancels in every stored value
+      // the final token step cancels in every stored value of a row-rounded
+      // tile; per-channel rounding needs it
+      if (it + 1 == iters && !KCH) {
+        if constexpr (PADK) {   // the per-channel K body beside this one runs the token step's two barriers
+          __syncthreads();
+          __syncthreads();
+        }
+        break;
+      }
 
       // token step: spread over the 128 channels of u = a_c R_tc
       const float a0 = sm.a[0];   // channel 0
@@ -641,6 +721,65 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     }
 
     // ---------------------------------------------------------------- rounding
+    if constexpr (KCH) {
+      // per channel over the tile's tokens of y = R a b (copies of row 0 weigh
+      // as row 0 and leave the minima and maxima alone); the slot takes beta =
+      // 1 / b per token, A = alpha step and M = min / step per channel (a
+      // zero-range channel: A = alpha min, M = 1, codes 0)
+      float cmin[8], cmax[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        cmin[m] = INFINITY;
+        cmax[m] = -INFINITY;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          R[q][m] *= a[m] * b[q];
+          cmin[m] = fminf(cmin[m], R[q][m]);
+          cmax[m] = fmaxf(cmax[m], R[q][m]);
+        }
+      float* p1 = red0 + (4 * w + g) * kHeadDim + 8 * j;   // [row 4w + g][lane order]
+      float* p2 = red1 + (4 * w + g) * kHeadDim + 8 * j;
+      *reinterpret_cast<qt_f32x4*>(p1) = qt_f32x4{cmin[0], cmin[1], cmin[2], cmin[3]};
+      *reinterpret_cast<qt_f32x4*>(p1 + 4) = qt_f32x4{cmin[4], cmin[5], cmin[6], cmin[7]};
+      *reinterpret_cast<qt_f32x4*>(p2) = qt_f32x4{cmax[0], cmax[1], cmax[2], cmax[3]};
+      *reinterpret_cast<qt_f32x4*>(p2 + 4) = qt_f32x4{cmax[4], cmax[5], cmax[6], cmax[7]};
+      __syncthreads();
+      for (int i = tid; i < kHeadDim; i += NT) {   // lane-order index i: channel (i >> 3) + 16 (i & 7)
+        float mn = red0[i], mx = red1[i];
+#pragma unroll
+        for (int row = 1; row < T / 8; ++row) {
+          mn = fminf(mn, red0[row * kHeadDim + i]);
+          mx = fmaxf(mx, red1[row * kHeadDim + i]);
+        }
+        const float range = mx - mn;
+        const float inv = range > 0.f ? LEVELS * __builtin_amdgcn_rcpf(range) : 0.f;
+        sm.a[i] = inv;             // (the channel factors' reciprocals are in registers)
+        sm.ref_c[i] = -mn * inv;   // (the channel-step references are no longer needed)
+        const int c = (i >> 3) + 16 * (i & 7);
+        const float al = sm.alpha[c];
+        const float st = range * (1.0f / LEVELS);
+        constexpr int AL = slot_alpha_len(T);
+        uint8_t* slot = slot_ptr(c / AL);
+        store_meta<false>(slot + slot_chan_scale_at(BITS), c % AL, range > 0.f ? al * st : al * mn);
+        store_meta<false>(slot + slot_chan_zp_at(BITS, T), c % AL, range > 0.f ? mn / st : 1.f);
+      }
+      if (tid < T) store_meta<false>(slot_ptr(tid / kPage) + CODE_BYTES, tid % kPage, tid < n_valid ? 1.f / sm.b[tid] : 0.f);
+      __syncthreads();
+      const qt_f32x4 i0 = *reinterpret_cast<const qt_f32x4*>(&sm.a[8 * j]);
+      const qt_f32x4 i1 = *reinterpret_cast<const qt_f32x4*>(&sm.a[8 * j + 4]);
+      const qt_f32x4 n0 = *reinterpret_cast<const qt_f32x4*>(&sm.ref_c[8 * j]);
+      const qt_f32x4 n1 = *reinterpret_cast<const qt_f32x4*>(&sm.ref_c[8 * j + 4]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool real = tok(q) < n_valid;   // rows past the tile's end get code 0
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          R[q][m] = real ? __builtin_fmaf(R[q][m], m < 4 ? i0[m] : i1[m - 4], m < 4 ? n0[m] : n1[m - 4]) : 0.f;
+      }
+    } else {
     {
       float zmin[8], zmax[8];
 #pragma unroll
@@ -736,6 +875,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         for (int m = 0; m < 8; ++m) R[q][m] = __builtin_fmaf(R[q][m], iv, nm);
       }
     }
+    }   // per-token rounding
 
   }
 

@@ -151,3 +151,17 @@ def check_tile_metadata_fp16(tq, ga, gs, go, what=""):
             raise AssertionError(f"{what} {name}[{j}]: gpu {g[j]!r} oracle fp16 {r[j]!r} (unrounded {u[j]!r})")
     return int((ga != a16.astype(np.float64)).sum() + (gs != s16.astype(np.float64)).sum() +
                (go != o16.astype(np.float64)).sum())
+
+
+def check_tile_metadata_kchan(tq, ga, gb, gm, what=""):
+    """Per-channel K tile (oracle tile `tq`): the token factors beta within
+    META_RTOL; the channel scales A and zero offsets M through their effect:
+    the oracle's codes restored with the GPU's beta, A, M against the same
+    codes restored with the oracle's, within DEQ_RTOL.  (A = alpha step and
+    M = min / step are each ill-conditioned in a channel whose range is tiny
+    next to its minimum, while their product in the restore is not.)"""
+    import oracle as orc
+    assert_rel(gb, tq.scale64, META_RTOL, f"{what} beta")
+    assert_dequant(orc.dequantize_tile_kchan(tq.codes, ga, gm, gb),
+                   orc.dequantize_tile_kchan(tq.codes, tq.alpha64, tq.zp64, tq.scale64),
+                   f"{what} channel scale / zero offset effect")

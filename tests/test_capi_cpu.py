@@ -48,6 +48,14 @@ def test_version_and_slot_sizes_match_oracle_layout(lib):
                 assert L.kvq_slot_bytes(cfg16, False) == orc.slot_bytes(bk, tile, meta16=True)
                 assert L.kvq_slot_bytes(cfg16, True) == orc.slot_bytes(bv, tile, meta16=True)
     assert L.kvq_slot_bytes(L.config(64, 4, 4, 3, meta_fp16=True), False) == 72 * 16
+    for tile in (32, 64, 128):
+        for bk, bv in ((4, 4), (4, 2), (2, 4), (2, 2)):
+            c = L.config(tile, bk, bv, 3, k_per_channel=True)
+            assert L.kvq_slot_bytes(c, False) == orc.slot_bytes(bk, tile, kchan=True)
+            assert L.kvq_slot_bytes(c, True) == orc.slot_bytes(bv, tile)
+    assert L.kvq_slot_bytes(L.config(64, 4, 4, 3, k_per_channel=True), False) == 1344
+    for bad in (L.config(64, 8, 8, 3, k_per_channel=True), L.config(64, 4, 4, 3, meta_fp16=True, k_per_channel=True)):
+        assert L.kvq_slot_bytes(bad, False) == 0
 
 
 @pytest.mark.parametrize("field,value,status", [
