@@ -77,7 +77,9 @@ def quantize_bytes(n_token_heads: int, bits: int, tile: int, meta16: bool = Fals
     return n_token_heads * (2 * D + slot_bytes_per_token(bits, tile, meta16))
 
 
-def slot_bytes_per_token(bits: int, tile: int, meta16: bool = False) -> float:
+def slot_bytes_per_token(bits: int, tile: int, meta16: bool = False, kchan: bool = False) -> float:
+    if kchan:   # K rounded per channel: beta per token, channel scale and zero offset per channel of the tile
+        return D * bits / 8 + 4 + 8 * D / tile
     m = 2 if meta16 else 4   # bytes per metadata value (fp16 or fp32)
     return D * bits / 8 + 2 * m + m * D / tile
 
@@ -207,7 +209,7 @@ def long_context_leg(n_iter: int = 10):
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     modes = {}
-    for name in ("fp16", "fp8", "kvq4", "kvq2", "kvq8", "kvq4_meta16", "kvq2_meta16"):
+    for name in ("fp16", "fp8", "kvq4", "kvq2", "kvq8", "kvq4_meta16", "kvq2_meta16", "kvq4_kchan"):
         if name in ("fp16", "fp8"):
             fp8 = name == "fp8"
             ks = float(k.abs().max()) / 448.0 if fp8 else 1.0
@@ -217,12 +219,13 @@ def long_context_leg(n_iter: int = 10):
             per_token_head = 2 * 128 * (1 if fp8 else 2)
             fill_bytes = token_heads * (2 * 2 * D + per_token_head)
         else:
-            bits, m16 = int(name[3]), name.endswith("meta16")
-            cfg = api.config(wl.tile_tokens, bits, bits, wl.iters, meta_fp16=m16)
+            bits, m16, kch = int(name[3]), name.endswith("meta16"), name.endswith("kchan")
+            cfg = api.config(wl.tile_tokens, bits, bits, wl.iters, meta_fp16=m16, k_per_channel=kch)
             cache = api.PagedCache(cfg, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
             fill_ms = timed(lambda: cache.quantize_prefill(k, v, cu), 3)
-            per_token_head = 2 * slot_bytes_per_token(bits, wl.tile_tokens, m16)
-            fill_bytes = 2 * quantize_bytes(token_heads, bits, wl.tile_tokens, m16)
+            per_token_head = (slot_bytes_per_token(bits, wl.tile_tokens, m16, kch)
+                              + slot_bytes_per_token(bits, wl.tile_tokens, m16))
+            fill_bytes = token_heads * (4 * D + per_token_head)
         ws = cache.workspace(wl.hq, max_len)
         dec_ms = timed(lambda: cache.decode(q, lens, max_len, out=out, workspace=ws), n_iter)
         dbytes = token_heads * per_token_head
@@ -769,6 +772,32 @@ def main():
     dh_ms = dh_batch[0].elapsed_time(dh_batch[1]) / dh_batch[2]
     adh_ms = adh_batch[0].elapsed_time(adh_batch[1]) / adh_batch[2]
     del caches_h
+    # K rounded per channel (V per token as before)
+    cfg_c = api.config(wl.tile_tokens, wl.bits_k, wl.bits_v, wl.iters, k_per_channel=True)
+    caches_c = [api.PagedCache(cfg_c, npages, wl.hkv, torch.from_numpy(table), wl.num_seqs) for _ in range(n_pools)]
+    qc_batch = batch_ms(lambda j: caches_c[j % n_pools].quantize_prefill(ks[j % n_in], vs[j % n_in], cu), n_q)
+    dc_batch = batch_ms(lambda j: caches_c[j % n_pools].decode(q, lens_after, max_len + 1, out=out, workspace=ws), n_q)
+    adc_batch = batch_ms(lambda j: caches_c[j % n_pools].append_decode(kn, vn, lens_before, q, max_len + 1, out=out,
+                                                                      workspace=ws), n_q)
+    torch.cuda.synchronize()
+    qc_ms = qc_batch[0].elapsed_time(qc_batch[1]) / qc_batch[2]
+    dc_ms = dc_batch[0].elapsed_time(dc_batch[1]) / dc_batch[2]
+    adc_ms = adc_batch[0].elapsed_time(adc_batch[1]) / adc_batch[2]
+    # restore error of K (relative RMS over the layer, fp16 restore through the
+    # re-materialize path) for per-token and per-channel K pages
+    k_err = {}
+    for tag, cc in (("per_token", caches[0]), ("per_channel", caches_c[0])):
+        cc.quantize_prefill(ks[0], vs[0], cu)
+        b16 = api.BaselineCache(npages, wl.hkv, torch.from_numpy(table), wl.num_seqs)
+        cc.rematerialize_into(b16, lens_before, max_len)
+        tab = torch.from_numpy(table).to(dev).long()
+        tok = torch.arange(max_len, device=dev)
+        pages = tab[:, tok // 16]                                   # [S, L]
+        kr = b16.pool_k.view(npages, wl.hkv, 16, D)[pages, :, tok % 16]   # [S, L, Hkv, D]
+        kref = ks[0].view(wl.num_seqs, max_len, wl.hkv, D).float()
+        k_err[tag] = round(float(((kr.float() - kref) ** 2).mean().sqrt() / (kref ** 2).mean().sqrt()), 5)
+        del b16
+    del caches_c
     # several queries per sequence (a speculative verify of 4 and of 16 draft
     # tokens) over the same pages: tokens past the appended one are stale
     # pool bytes (timing only; parity is in the tests)
@@ -880,6 +909,12 @@ def main():
                                              / (qh_ms * 1e-3) / 1e9, 1),
                       "decode_attn_GBps": round(decode_bytes(wl, [l + 1 for l in wl.seq_lens], True)
                                                 / (dh_ms * 1e-3) / 1e9, 1)},
+        "k_per_channel": {"bytes_per_token_head_k": slot_bytes_per_token(wl.bits_k, wl.tile_tokens, kchan=True),
+                          "quantize_kernel_ms": round(qc_ms, 4), "decode_attn_ms": round(dc_ms, 4),
+                          "decode_step_ms": round(adc_ms, 4),
+                          "k_restore_rel_rms": k_err,
+                          "note": "K restore error over the layer (relative RMS of the fp16 restore against the "
+                                  "input K): per-token against per-channel rounding of K"},
         "codes_8bit": {"quantize_kernel_ms": round(q8_ms, 4), "decode_attn_ms": round(d8_ms, 4),
                        "quantize_GBps": round(q8_bytes / (q8_ms * 1e-3) / 1e9, 1),
                        "decode_attn_GBps": round(d8_bytes / (d8_ms * 1e-3) / 1e9, 1)},
