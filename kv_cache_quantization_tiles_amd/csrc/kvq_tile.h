@@ -111,6 +111,20 @@ __device__ __forceinline__ unsigned pack_fields(const float (&v)[N]) {
   return w;
 }
 
+// min / max of three floats as one v_min3_f32 / v_max3_f32 (fminf / fmaxf
+// add canonicalizing ops around values that may be signaling NaNs; the tile's
+// values are finite)
+__device__ __forceinline__ float vmin3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // A double's value in lane l ^ 1 (QX1) or l ^ 2 (QX2): DPP quad permutations
 // of its two halves (VALU, no LDS round trip).
 constexpr int kQuadX1 = 0xB1, kQuadX2 = 0x4E;
@@ -728,18 +742,14 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
       // zero-range channel: A = alpha min, M = 1, codes 0)
       float cmin[8], cmax[8];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        cmin[m] = INFINITY;
-        cmax[m] = -INFINITY;
-      }
-#pragma unroll
       for (int q = 0; q < 8; ++q)
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          R[q][m] *= a[m] * b[q];
-          cmin[m] = fminf(cmin[m], R[q][m]);
-          cmax[m] = fmaxf(cmax[m], R[q][m]);
-        }
+        for (int m = 0; m < 8; ++m) R[q][m] *= a[m] * b[q];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        cmin[m] = vmin3f(vmin3f(vmin3f(R[0][m], R[1][m], R[2][m]), R[3][m], R[4][m]), R[5][m], vmin3f(R[6][m], R[7][m], R[7][m]));
+        cmax[m] = vmax3f(vmax3f(vmax3f(R[0][m], R[1][m], R[2][m]), R[3][m], R[4][m]), R[5][m], vmax3f(R[6][m], R[7][m], R[7][m]));
+      }
       float* p1 = red0 + (4 * w + g) * kHeadDim + 8 * j;   // [row 4w + g][lane order]
       float* p2 = red1 + (4 * w + g) * kHeadDim + 8 * j;
       *reinterpret_cast<qt_f32x4*>(p1) = qt_f32x4{cmin[0], cmin[1], cmin[2], cmin[3]};
@@ -786,12 +796,13 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
       for (int q = 0; q < 8; ++q) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) R[q][m] *= a[m];
-        float mn = fminf(R[q][0], R[q][1]), mx = fmaxf(R[q][0], R[q][1]);
-#pragma unroll
-        for (int m = 2; m < 8; m += 2) {
-          mn = fminf(mn, fminf(R[q][m], R[q][m + 1]));
-          mx = fmaxf(mx, fmaxf(R[q][m], R[q][m + 1]));
-        }
+        float mn = vmin3f(R[q][0], R[q][1], R[q][2]), mx = vmax3f(R[q][0], R[q][1], R[q][2]);
+        mn = vmin3f(mn, R[q][3], R[q][4]);
+        mx = vmax3f(mx, R[q][3], R[q][4]);
+        mn = vmin3f(mn, R[q][5], R[q][6]);
+        mx = vmax3f(mx, R[q][5], R[q][6]);
+        mn = vmin3f(mn, R[q][7], R[q][7]);
+        mx = vmax3f(mx, R[q][7], R[q][7]);
         zmin[q] = mn;
         zmax[q] = mx;
       }
@@ -806,10 +817,12 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
     if (tid < T) {
       float mn = red0[tid], mx = red1[tid];
 #pragma unroll
-      for (int jj = 1; jj < 16; ++jj) {
-        mn = fminf(mn, red0[jj * kRedStride<T> + tid]);
-        mx = fmaxf(mx, red1[jj * kRedStride<T> + tid]);
+      for (int jj = 1; jj < 15; jj += 2) {
+        mn = vmin3f(mn, red0[jj * kRedStride<T> + tid], red0[(jj + 1) * kRedStride<T> + tid]);
+        mx = vmax3f(mx, red1[jj * kRedStride<T> + tid], red1[(jj + 1) * kRedStride<T> + tid]);
       }
+      mn = vmin3f(mn, red0[15 * kRedStride<T> + tid], red0[15 * kRedStride<T> + tid]);
+      mx = vmax3f(mx, red1[15 * kRedStride<T> + tid], red1[15 * kRedStride<T> + tid]);
       float inv = 0.f, nmi = 0.f;
       if (tid < n_valid) {
         const float range = mx - mn;
