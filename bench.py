@@ -918,7 +918,7 @@ def main():
         "codes_8bit": {"quantize_kernel_ms": round(q8_ms, 4), "decode_attn_ms": round(d8_ms, 4),
                        "quantize_GBps": round(q8_bytes / (q8_ms * 1e-3) / 1e9, 1),
                        "decode_attn_GBps": round(d8_bytes / (d8_ms * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "hbm", "kernel": f"quantize_paged_kernel<{wl.tile_tokens},{wl.bits_k},{wl.bits_v}>",
+        "roofline": {"bound": "hbm", "kernel": f"quantize_paged_kernel<{wl.tile_tokens},{wl.bits_k},{wl.bits_v},false,false>",
                      "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(QUANTIZE_SOURCES, f"traffic-quantize_paged_kernel-{wl.name}.json"),

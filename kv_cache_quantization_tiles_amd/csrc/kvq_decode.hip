@@ -8,70 +8,97 @@ namespace {
 // Merge the partitions of one (sequence, query, query head):
 // out = s H (sum_p w_p acc_p) / (sum_p w_p l_p), w_p = 2^(m_p - max m), with
 // the Hadamard H applied for pages quantized in the rotated basis (ROT) and
-// s = A.out_scale.
+// s = A.out_scale.  One wave per row; the row's partials are read with every
+// load in flight at once (16 partitions per round): lanes 32h + i take
+// channels 4i..4i+3 of the partitions of parity h and keep a running maximum
+// (rescaling their sums when it grows), and the two halves merge at the end.
+// The Hadamard then runs over channel bits 0, 1 in registers and bits 2..6
+// across the lanes.
 template <bool ROT>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
-  __shared__ float wts[1024];
-  const int lane = threadIdx.x;
+  constexpr int U = 8;   // float4 loads in flight per lane and round
+  const int lane = threadIdx.x, half = lane >> 5, c4 = lane & 31;
   const int seq = blockIdx.x / (A.q_heads * A.n_q);   // rows [S][n_q][Hq]
   const int L = A.seq_lens[seq] + A.seq_lens_plus_one;
   const int T = A.unit_tokens;
   const int ntiles = min((L + T - 1) / T, A.max_tiles);
   const int nparts = min((ntiles + A.tiles_per_part - 1) / A.tiles_per_part, A.max_parts);
   const size_t base = (size_t)blockIdx.x * A.max_parts;
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, A.ws_ml[2 * (base + p)]);
-  M = wave_max(M);
-  float den = 0.f;
-  for (int p = lane; p < nparts; p += 64) {
-    // a row that sees no token at all (M = -inf) gets zeros
-    const float w = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(A.ws_ml[2 * (base + p)] - M);
-    wts[p] = w;
-    den = __builtin_fmaf(w, A.ws_ml[2 * (base + p) + 1], den);
+  const float2* ml = reinterpret_cast<const float2*>(A.ws_ml) + base;
+  const f32x4* acc = reinterpret_cast<const f32x4*>(A.ws_acc) + base * (kHeadDim / 4);
+  float m = -INFINITY, den = 0.f;
+  f32x4 x{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < nparts; p0 += 2 * U) {
+    float2 s[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 2 * u + half;
+      const bool ok = p < nparts;
+      s[u] = ok ? ml[p] : float2{-INFINITY, 0.f};
+      v[u] = ok ? acc[(size_t)p * (kHeadDim / 4) + c4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mc = fmaxf(mc, s[u].x);
+    // a partition that sees no token (m = -inf) weighs 0
+    const float r = (mc == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mc);
+    den *= r;
+    x *= r;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = (s[u].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[u].x - mc);
+      den = __builtin_fmaf(w, s[u].y, den);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(w, v[u][e], x[e]);
+    }
+    m = mc;
   }
-  den = wave_sum(den);
-  __syncthreads();
-  float x0 = 0.f, x1 = 0.f;
-  const float* src = A.ws_acc + base * kHeadDim;
-  int p = 0;
-  for (; p + 4 <= nparts; p += 4) {
-    const float a0 = src[(p + 0) * kHeadDim + lane], b0 = src[(p + 0) * kHeadDim + lane + 64];
-    const float a1 = src[(p + 1) * kHeadDim + lane], b1 = src[(p + 1) * kHeadDim + lane + 64];
-    const float a2 = src[(p + 2) * kHeadDim + lane], b2 = src[(p + 2) * kHeadDim + lane + 64];
-    const float a3 = src[(p + 3) * kHeadDim + lane], b3 = src[(p + 3) * kHeadDim + lane + 64];
-    x0 = __builtin_fmaf(wts[p], a0, x0); x1 = __builtin_fmaf(wts[p], b0, x1);
-    x0 = __builtin_fmaf(wts[p + 1], a1, x0); x1 = __builtin_fmaf(wts[p + 1], b1, x1);
-    x0 = __builtin_fmaf(wts[p + 2], a2, x0); x1 = __builtin_fmaf(wts[p + 2], b2, x1);
-    x0 = __builtin_fmaf(wts[p + 3], a3, x0); x1 = __builtin_fmaf(wts[p + 3], b3, x1);
+  {   // the two halves (partitions of either parity)
+    const float mm = fmaxf(m, xor32(m));
+    const float r = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+    den *= r;
+    den += xor32(den);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] *= r;
+      x[e] += xor32(x[e]);
+    }
   }
-  for (; p < nparts; ++p) {
-    x0 = __builtin_fmaf(wts[p], src[p * kHeadDim + lane], x0);
-    x1 = __builtin_fmaf(wts[p], src[p * kHeadDim + lane + 64], x1);
-  }
-  float* o = A.out + (size_t)blockIdx.x * kHeadDim;
+  f32x4* o = reinterpret_cast<f32x4*>(A.out + (size_t)blockIdx.x * kHeadDim) + c4;
   if (!ROT) {
     const float inv = den > 0.f ? A.out_scale / den : 0.f;   // an empty sequence gives zeros
-    o[lane] = x0 * inv;
-    o[lane + 64] = x1 * inv;
+    if (half == 0) *o = x * inv;
     return;
   }
   const float inv = den > 0.f ? A.out_scale * kInvSqrtD / den : 0.f;
-  // channels lane (bit 6 = 0) and lane + 64 (bit 6 = 1)
-  float y0 = x0 + x1, y1 = x0 - x1;
+  // channel c = 4 c4 + e: bits 0, 1 in registers
+  float y[4];
+  {
+    const float a0 = x[0] + x[1], a1 = x[0] - x[1], a2 = x[2] + x[3], a3 = x[2] - x[3];
+    y[0] = a0 + a2;
+    y[2] = a0 - a2;
+    y[1] = a1 + a3;
+    y[3] = a1 - a3;
+  }
+  // bits 2..6 across lanes c4 ^ 1 .. c4 ^ 16
   auto stage = [&](float& v, float partner, int bit) {
-    v = __builtin_fmaf(v, (lane & bit) ? -1.f : 1.f, partner);
+    v = __builtin_fmaf(v, (c4 & bit) ? -1.f : 1.f, partner);
   };
-  stage(y0, lane_xor<1>(y0), 1);   stage(y1, lane_xor<1>(y1), 1);
-  stage(y0, lane_xor<2>(y0), 2);   stage(y1, lane_xor<2>(y1), 2);
-  stage(y0, lane_xor<4>(y0), 4);   stage(y1, lane_xor<4>(y1), 4);
-  stage(y0, lane_xor<8>(y0), 8);   stage(y1, lane_xor<8>(y1), 8);
-  stage(y0, lane_xor<16>(y0), 16); stage(y1, lane_xor<16>(y1), 16);
-  stage(y0, xor32(y0), 32);        stage(y1, xor32(y1), 32);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    stage(y[e], lane_xor<1>(y[e]), 1);
+    stage(y[e], lane_xor<2>(y[e]), 2);
+    stage(y[e], lane_xor<4>(y[e]), 4);
+    stage(y[e], lane_xor<8>(y[e]), 8);
+    stage(y[e], lane_xor<16>(y[e]), 16);
+  }
   // randomized rotation: the restore ends with the sign of each channel
-  const float s0 = ((A.signs[lane >> 5] >> (lane & 31)) & 1u) ? -inv : inv;
-  const float s1 = ((A.signs[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -inv : inv;
-  o[lane] = y0 * s0;
-  o[lane + 64] = y1 * s1;
+  const unsigned sg = (A.signs[c4 >> 3] >> (4 * (c4 & 7))) & 0xFu;
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = y[e] * (((sg >> e) & 1u) ? -inv : inv);
+  if (half == 0) *o = r;
 }
 
 }  // namespace
