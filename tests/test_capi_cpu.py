@@ -73,6 +73,28 @@ def test_bad_config_rejected(lib, field, value, status):
     assert L.kvq_slot_bytes(cfg, False) == 0
 
 
+def test_format_flags_rejected_where_they_do_not_apply(lib):
+    """The slot-format switches take 0 or 1; per-channel K rounding is a page
+    format of 2- and 4-bit codes with fp32 metadata, and fp16 metadata take 2-
+    and 4-bit codes (statuses as include/kvq.h documents them)."""
+    args = (16, 16, 16, 1, 64, 1, 16, 4, 16, 16, None, None, None)
+    for field, value in (("meta_fp16", 2), ("k_per_channel", 2), ("k_per_channel", -1)):
+        cfg = L.config(64, 4, 4, 3)
+        setattr(cfg, field, value)
+        assert lib.kvq_quantize_to_pages(ctypes.byref(cfg), *args) == L.KVQ_ERR_ARG
+        assert field in L.kvq_last_error()
+    for cfg in (L.config(64, 4, 4, 3, meta_fp16=True, k_per_channel=True), L.config(64, 8, 8, 3, k_per_channel=True),
+                L.config(64, 8, 8, 3, meta_fp16=True)):
+        assert lib.kvq_quantize_to_pages(ctypes.byref(cfg), *args) == L.KVQ_ERR_UNSUPPORTED
+    # the dense entry points have no per-channel layout
+    kc = ctypes.byref(L.config(64, 4, 4, 3, k_per_channel=True))
+    assert lib.kvq_quantize_tiles(kc, 16, 8, 1, 4, 16, 16, 16, 16, None) == L.KVQ_ERR_UNSUPPORTED
+    assert "page" in L.kvq_last_error()
+    # the paged entry points take it
+    assert lib.kvq_quantize_to_pages(kc, 16, 16, 16, 1, 64, 1, 16, 3, 16, 16, None, None, None) == L.KVQ_ERR_ARG
+    assert "max_blocks" in L.kvq_last_error() or "block" in L.kvq_last_error()
+
+
 def test_null_and_size_errors(lib):
     cfg = ctypes.byref(L.config(64, 4, 4, 3))
     assert lib.kvq_quantize_tiles(None, 16, 1, 1, 4, 16, 16, 16, 16, None) == L.KVQ_ERR_ARG
