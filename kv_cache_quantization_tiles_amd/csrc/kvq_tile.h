@@ -594,7 +594,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
       a[i] = kInvSqrtD;
       b[i] = 1.0f;
     }
-    const float inv_n = 1.0f / (float)n_valid;
+    const float inv_n = __builtin_amdgcn_rcpf((float)n_valid);   // the hardware reciprocal (within an ulp)
     const float n_copies = (float)(T - n_valid);  // rows that are copies of row 0
     const int iters = A.iters;
     float b0 = 1.0f;
@@ -658,7 +658,9 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         const float ms = __builtin_fmaf(mu, mu, var);                 // mean square of u
         if (var > kGuard2 * ms) {
           sm.a[i] = __builtin_amdgcn_rsqf(var);
-          sm.alpha[(i >> 3) + 16 * (i & 7)] = __builtin_sqrtf(var * (1.0f / kHeadDim));
+          // the stored factor only (codes use a): the hardware square root,
+          // within an ulp, in place of the correctly rounded expansion
+          sm.alpha[(i >> 3) + 16 * (i & 7)] = __builtin_amdgcn_sqrtf(var * (1.0f / kHeadDim));
         }
       }
       __syncthreads();
