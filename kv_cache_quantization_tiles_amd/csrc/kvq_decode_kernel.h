@@ -560,6 +560,9 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   // and w1 = 4 w0; a step's parity is bq's)
   const float w0 = (BK != 2) ? 1.f : ((bq & 1) ? 16.f : 1.f);
   const float w1 = (BK == 8) ? 1.f : (BK == 4) ? 16.f : w0 * 4.f;
+  // the split grids' constants kGrid / w (powers of two: exact products)
+  const float g0 = w0 == 1.f ? kGrid : kGrid * (1.f / 16.f);
+  const float g1 = (BK == 8) ? kGrid : (BK == 4) ? kGrid * (1.f / 16.f) : g0 * 0.25f;
 
   for (; chunk < c_end; chunk = next_chunk(chunk)) {
     const int next = next_chunk(chunk);
@@ -596,7 +599,6 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         // where S and O reach 1e4..1e5 and nearly cancel, that costs ~1e-3.)
         // The pairs enter the sum through v_dot2 (fp16 products with the field
         // weights are exact in fp32).
-        const float g0 = kGrid / w0, g1 = kGrid / w1;
         const f16x2 wp0{(_Float16)w0, (_Float16)w0}, wp1{(_Float16)w1, (_Float16)w1};
 #pragma unroll
         for (int st = 0; st < SETS; ++st) {

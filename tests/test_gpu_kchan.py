@@ -175,3 +175,45 @@ def test_kchan_fused_step_equals_append_then_decode(case):
         assert torch.equal(fused.pool_v, split.pool_v), step
         assert torch.equal(fused.staging_k, split.staging_k), step
         assert torch.equal(of, os_), (step, (of - os_).abs().max().item())
+
+
+def test_full_size_4x16k_layer_kchan_sampled():
+    """The 4 x 16K, 8/32-head layer with K rounded per channel in the launch
+    configuration the bench times: quantize every page, one fused append +
+    decode step; random whole tiles, every appended one-token tile and three
+    (sequence, kv head) attention outputs against the oracle."""
+    wl = inputs.workload(2)
+    k, v, table, npages, cache = _prefill(wl)
+    lens = np.array(wl.seq_lens, np.int32)
+    kn, vn = inputs.gen_decode_kv(wl, "K", 0), inputs.gen_decode_kv(wl, "V", 0)
+    q = inputs.gen_q(wl)
+    out = cache.append_decode(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), torch.from_numpy(lens).cuda(),
+                              torch.from_numpy(q).cuda(), int(lens.max()) + 1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gpk, gpv = cache.pool_k.cpu().numpy(), cache.pool_v.cpu().numpy()
+    cu, t = wl.cu_seqlens(), wl.tile_tokens
+    rng = np.random.default_rng(11)
+    tot = [0, 0, 0]
+    for _ in range(6):   # a sequence, then 2 whole tiles of it (every kv head, K and V)
+        s = int(rng.integers(wl.num_seqs))
+        tiles = sorted(int(x) for x in rng.choice(int(lens[s]) // t, 2, replace=False))
+        src = {"K": k[cu[s]:cu[s + 1]], "V": v[cu[s]:cu[s + 1]]}
+        c = _check_tiles(wl, table, s, int(lens[s]), lambda role, h: src[role][:, h], gpk, gpv, "kchan 4x16k",
+                         tiles=tiles)
+        tot = [a + b for a, b in zip(tot, c)]
+    for s in range(wl.num_seqs):   # the appended token opens a tile of one row
+        new = {"K": kn[s][None], "V": vn[s][None]}
+        j = int(lens[s]) // t
+        rows = lambda role, h, new=new, j=j: np.concatenate([np.zeros((j * t, 128), np.float16), new[role][:, h]])
+        c = _check_tiles(wl, table, s, int(lens[s]) + 1, rows, gpk, gpv, "kchan 4x16k append", tiles=[j])
+        tot = [a + b for a, b in zip(tot, c)]
+    print(f"[codes] kchan 4x16k sampled: {tot[0]} elements, {tot[1]} in window, {tot[2]} mismatches", flush=True)
+    g = wl.group
+    for s, kh in ((0, 0), (3, 7), (2, 3)):
+        ref, sc = orc.paged_decode_attn(q[s:s + 1, kh * g:(kh + 1) * g], table[s:s + 1], lens[s:s + 1] + 1,
+                                        gpk[:, kh:kh + 1], gpv[:, kh:kh + 1], t, wl.bits_k, wl.bits_v,
+                                        return_scale=True, kchan=True)
+        err = pu.assert_attn(got[s, kh * g:(kh + 1) * g], ref[0], f"kchan 4x16k s{s} kv head {kh}", sc[0])
+        print(f"[attn] kchan 4x16k s{s} kv head {kh}: max abs err {err:.2e}", flush=True)
+    assert np.isfinite(got).all()
