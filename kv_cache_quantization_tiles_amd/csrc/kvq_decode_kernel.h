@@ -567,6 +567,10 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   for (; chunk < c_end; chunk = next_chunk(chunk)) {
     const int next = next_chunk(chunk);
     const bool more = next < c_end;   // uniform
+    // the chunk whose operands load into the registers this one frees: the
+    // next, or (past the last) this one again, so that every load is issued
+    // unconditionally and no register copy at the loop's end waits for them
+    const int ld = more ? next : chunk;
 
     // -------------------------------------------- query fold (once per tile)
     if (new_tile(chunk)) {
@@ -632,7 +636,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         cB[hg] = c0 * qsum;
       }
     }
-    if (more && new_tile(next)) load_alpha(next);
+    load_alpha(ld);
 
     // -------------------------------------------- QK: lane = token, 4 heads per group
     f32x4 d[HG], dl[HG];   // hi chain (exact) and lo chain
@@ -682,7 +686,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         const bool masked = MQ ? tok >= vis[4 * hg + i] : past;
         sc[hg][i] = masked ? -INFINITY : __builtin_fmaf(fa * sk, d[hg][i] + dl[hg][i], fb * ok);
       }
-    if (more) load_k(next);
+    load_k(ld);
 
     // -------------------------------------------- online softmax (base 2), per head
     // the running max moves only when a chunk's scores pass it: a test in
@@ -829,9 +833,9 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       pv_fold(0);
       pv_tile(std::integral_constant<int, 1>{});
     }
-    if (more) load_v(next);
+    load_v(ld);
     pv_fold(TPC - 1);
-    if (more) load_av(next);
+    load_av(ld);
   }
 
   // ------------------------------------------------ merge the waves, write the partition's partial
