@@ -382,6 +382,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
   auto process = [&](Ops& o, int chunk, int cn) {
     const int pg0 = 4 * chunk;
     const bool more = cn < c_end;
+    // loads for the next chunk go out unconditionally (this chunk again past
+    // the last) so that the loop keeps no in-flight register to copy at its end
+    const int ld = more ? cn : chunk;
     // P = p S_V, scaled by 2^k per chunk so that it stays below 2^(PE+1)
     const float smax = wave_max(vmax(o.sv, 0.f));
     int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     meta[128 + lane] = swt;
     meta[192 + lane] = zrt;
     asm volatile("" ::: "memory");   // the reads below see this wave's writes (LDS keeps order)
-    if (more) load_meta_ops(o, cn);
+    load_meta_ops(o, ld);
     // alpha_V of the lane's channels 16 j + n for the chunk's tile(s), needed after the softmax
     float av[T == 32 ? 2 : 1][8];
 #pragma unroll
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     if (T == 64 || (T == 128 && (chunk & 1) == 0)) {
       fold();
       const int cn = (T == 128) ? next_chunk(next_chunk(chunk)) : next_chunk(chunk);   // the next tile's chunk
-      if (cn < c_end) load_alpha_k(4 * cn);
+      load_alpha_k(4 * (cn < c_end ? cn : chunk));
     }
     float s[4][4];   // [page][i]: token 64 chunk + 16 tb + 4 g + i, row n
 #pragma unroll
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
         fold();
         const int cn = next_chunk(chunk);
         if (tb == 0) load_alpha_k(pg0 + 2);
-        else if (cn < c_end) load_alpha_k(4 * cn);
+        else load_alpha_k(4 * (cn < c_end ? cn : chunk));
       }
       const f32x4 sk = *reinterpret_cast<const f32x4*>(&meta[16 * tb + 4 * g]);
       const f32x4 ok = *reinterpret_cast<const f32x4*>(&meta[64 + 16 * tb + 4 * g]);
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[tb][i] = __builtin_fmaf(cA * sk[i], d[i], cB * ok[i]);
     }
-    if (more) load_k_ops(o, cn);
+    load_k_ops(o, ld);
     // causal and length mask, only where some row's limit falls inside the chunk
     if (__builtin_amdgcn_ballot_w64(vis < kChunk * (chunk + 1)) != 0) {
 #pragma unroll
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
         }
       }
     }
-    if (more) load_v_ops(o, cn);
+    load_v_ops(o, ld);
   };
 
   if (active) {
