@@ -569,7 +569,11 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
     const bool more = next < c_end;   // uniform
     // the chunk whose operands load into the registers this one frees: the
     // next, or (past the last) this one again, so that every load is issued
-    // unconditionally and no register copy at the loop's end waits for them
+    // unconditionally and no register copy at the loop's end waits for them.
+    // At tile 128 (waves of 16 chunks and more, alpha_K once per two chunks)
+    // the loads stay conditional: there the extra loads cost more than the
+    // copy's wait (same-box A/B at 6 x 128K: 192.6 against 203.7 us).
+    constexpr bool UNCOND = (T != 128);
     const int ld = more ? next : chunk;
 
     // -------------------------------------------- query fold (once per tile)
@@ -636,7 +640,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         cB[hg] = c0 * qsum;
       }
     }
-    load_alpha(ld);
+    if (UNCOND || (more && new_tile(next))) load_alpha(ld);
 
     // -------------------------------------------- QK: lane = token, 4 heads per group
     f32x4 d[HG], dl[HG];   // hi chain (exact) and lo chain
@@ -686,7 +690,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
         const bool masked = MQ ? tok >= vis[4 * hg + i] : past;
         sc[hg][i] = masked ? -INFINITY : __builtin_fmaf(fa * sk, d[hg][i] + dl[hg][i], fb * ok);
       }
-    load_k(ld);
+    if (UNCOND || more) load_k(ld);
 
     // -------------------------------------------- online softmax (base 2), per head
     // the running max moves only when a chunk's scores pass it: a test in
@@ -833,9 +837,9 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
       pv_fold(0);
       pv_tile(std::integral_constant<int, 1>{});
     }
-    load_v(ld);
+    if (UNCOND || more) load_v(ld);
     pv_fold(TPC - 1);
-    load_av(ld);
+    if (UNCOND || more) load_av(ld);
   }
 
   // ------------------------------------------------ merge the waves, write the partition's partial
