@@ -94,6 +94,13 @@ __device__ __forceinline__ float group_sum(float v) { return sum32(sum16(v)); }
 constexpr int kWaves = 4;             // waves per decode workgroup
 constexpr int kChunk = 64;            // tokens per wave step (4 pages)
 constexpr int kMaxChunksPerPart = 64;
+// Slot pointers staged per partition: its pages, then those of one chunk past
+// any partition (the loads a wave issues after its last chunk read there).
+constexpr int kSlotEntries = 4 * kMaxChunksPerPart + 4;
+// A slot-sized block that those loads read in place of pool pages (the values
+// are never used; one small block stays in cache, where a reload of pool pages
+// would be fetched from memory again).
+static __device__ __align__(256) uint8_t g_spare_slot[4096];
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -235,8 +242,8 @@ struct alignas(16) DecodeSmem {
   // pointers: loads through them are global loads (a generic pointer read
   // back from LDS would make every slot load a flat load, which also counts
   // against the LDS counter and makes LDS waits wait for memory)
-  const __attribute__((address_space(1))) uint8_t* kp[kMaxChunksPerPart * 4];
-  const __attribute__((address_space(1))) uint8_t* vp[kMaxChunksPerPart * 4];
+  const __attribute__((address_space(1))) uint8_t* kp[kSlotEntries];
+  const __attribute__((address_space(1))) uint8_t* vp[kSlotEntries];
   union {
     struct {
       float hq[4 * HG][kHeadDim];                // (H q)_c / weight of c's K field, at qk_slot(c)
@@ -397,10 +404,16 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
     const int32_t* row = A.block_table + (size_t)seq * A.max_blocks + 4 * c_begin;
     const int last = min(npages, ((4 * c_end + PPT - 1) / PPT) * PPT);
     const int n = last - 4 * c_begin;
-    for (int i = threadIdx.x; i < n; i += 64 * kWaves) {
-      const size_t slot = (size_t)row[i] * H + kvh;
-      sm.kp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_k + slot * SLOT_K);
-      sm.vp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_v + slot * SLOT_V);
+    static_assert(SLOT_K <= (int)sizeof(g_spare_slot) && SLOT_V <= (int)sizeof(g_spare_slot), "spare slot size");
+    for (int i = threadIdx.x; i < kSlotEntries; i += 64 * kWaves) {
+      if (i < n) {
+        const size_t slot = (size_t)row[i] * H + kvh;
+        sm.kp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_k + slot * SLOT_K);
+        sm.vp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_v + slot * SLOT_V);
+      } else {
+        sm.kp[i] = (const __attribute__((address_space(1))) uint8_t*)g_spare_slot;
+        sm.vp[i] = (const __attribute__((address_space(1))) uint8_t*)g_spare_slot;
+      }
     }
   }
   __syncthreads();
@@ -568,13 +581,13 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
     const int next = next_chunk(chunk);
     const bool more = next < c_end;   // uniform
     // the chunk whose operands load into the registers this one frees: the
-    // next, or (past the last) this one again, so that every load is issued
+    // next, or past the last the spare slot, so that every load is issued
     // unconditionally and no register copy at the loop's end waits for them.
     // At tile 128 (waves of 16 chunks and more, alpha_K once per two chunks)
     // the loads stay conditional: there the extra loads cost more than the
     // copy's wait (same-box A/B at 6 x 128K: 192.6 against 203.7 us).
     constexpr bool UNCOND = (T != 128);
-    const int ld = more ? next : chunk;
+    const int ld = more ? next : c_begin + kMaxChunksPerPart;   // (past the last: the spare slot)
 
     // -------------------------------------------- query fold (once per tile)
     if (new_tile(chunk)) {
