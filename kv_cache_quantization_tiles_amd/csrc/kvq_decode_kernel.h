@@ -94,9 +94,10 @@ __device__ __forceinline__ float group_sum(float v) { return sum32(sum16(v)); }
 constexpr int kWaves = 4;             // waves per decode workgroup
 constexpr int kChunk = 64;            // tokens per wave step (4 pages)
 constexpr int kMaxChunksPerPart = 64;
-// Slot pointers staged per partition: its pages, then those of one chunk past
-// any partition (the loads a wave issues after its last chunk read there).
-constexpr int kSlotEntries = 4 * kMaxChunksPerPart + 4;
+// Slot pointers staged per partition: its pages, then those of one 128-token
+// tile past any partition (the loads a wave issues after its last chunk read
+// there: chunk c_begin + kMaxChunksPerPart, pages up to 8 on).
+constexpr int kSlotEntries = 4 * kMaxChunksPerPart + 8;
 // A slot-sized block that those loads read in place of pool pages (the values
 // are never used; one small block stays in cache, where a reload of pool pages
 // would be fetched from memory again).

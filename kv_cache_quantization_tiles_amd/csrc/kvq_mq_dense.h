@@ -113,8 +113,8 @@ __device__ __forceinline__ f32x4 load_meta4(const uint8_t* p, int i) {   // elem
 }
 
 struct alignas(16) MqSmem {
-  const __attribute__((address_space(1))) uint8_t* kp[kMaxChunksPerPart * 4];
-  const __attribute__((address_space(1))) uint8_t* vp[kMaxChunksPerPart * 4];
+  const __attribute__((address_space(1))) uint8_t* kp[kSlotEntries];
+  const __attribute__((address_space(1))) uint8_t* vp[kSlotEntries];
   float meta[kWaves][4 * kChunk];   // per wave: the chunk's S_K, O_K, S_V, O_V by token
   union {
     float hq[kMqBlockRows][kHeadDim];   // (H q)_c / (weight of c's K field) per row
@@ -185,10 +185,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     const int32_t* trow = A.block_table + (size_t)seq * A.max_blocks + 4 * c_begin;
     const int last = min(npages, ((4 * c_end + PPT - 1) / PPT) * PPT);
     const int np = last - 4 * c_begin;
-    for (int i = threadIdx.x; i < np; i += 64 * kWaves) {
-      const size_t slot = (size_t)trow[i] * H + kvh;
-      sm.kp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_k + slot * SLOT_K);
-      sm.vp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_v + slot * SLOT_V);
+    // (entries past the partition's pages point at the spare slot: the loads
+    // issued after a wave's last chunk read there)
+    static_assert(SLOT_K <= (int)sizeof(g_spare_slot) && SLOT_V <= (int)sizeof(g_spare_slot), "spare slot size");
+    for (int i = threadIdx.x; i < kSlotEntries; i += 64 * kWaves) {
+      if (i < np) {
+        const size_t slot = (size_t)trow[i] * H + kvh;
+        sm.kp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_k + slot * SLOT_K);
+        sm.vp[i] = (const __attribute__((address_space(1))) uint8_t*)(A.pool_v + slot * SLOT_V);
+      } else {
+        sm.kp[i] = (const __attribute__((address_space(1))) uint8_t*)g_spare_slot;
+        sm.vp[i] = (const __attribute__((address_space(1))) uint8_t*)g_spare_slot;
+      }
     }
   }
   // H q of the row tile, stored divided by the weight of each channel's K field
@@ -382,9 +390,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
   auto process = [&](Ops& o, int chunk, int cn) {
     const int pg0 = 4 * chunk;
     const bool more = cn < c_end;
-    // loads for the next chunk go out unconditionally (this chunk again past
-    // the last) so that the loop keeps no in-flight register to copy at its end
-    const int ld = more ? cn : chunk;
+    // loads for the next chunk go out unconditionally (past the last they read
+    // the spare slot) so that the loop keeps no in-flight register to copy at
+    // its end
+    const int spare = c_begin + kMaxChunksPerPart;
+    const int ld = more ? cn : spare;
     // P = p S_V, scaled by 2^k per chunk so that it stays below 2^(PE+1)
     const float smax = wave_max(vmax(o.sv, 0.f));
     int pe = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127;
@@ -424,7 +434,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     if (T == 64 || (T == 128 && (chunk & 1) == 0)) {
       fold();
       const int cn = (T == 128) ? next_chunk(next_chunk(chunk)) : next_chunk(chunk);   // the next tile's chunk
-      load_alpha_k(4 * (cn < c_end ? cn : chunk));
+      load_alpha_k(4 * (cn < c_end ? cn : spare));
     }
     float s[4][4];   // [page][i]: token 64 chunk + 16 tb + 4 g + i, row n
 #pragma unroll
@@ -433,7 +443,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
         fold();
         const int cn = next_chunk(chunk);
         if (tb == 0) load_alpha_k(pg0 + 2);
-        else load_alpha_k(4 * (cn < c_end ? cn : chunk));
+        else load_alpha_k(4 * (cn < c_end ? cn : spare));
       }
       const f32x4 sk = *reinterpret_cast<const f32x4*>(&meta[16 * tb + 4 * g]);
       const f32x4 ok = *reinterpret_cast<const f32x4*>(&meta[64 + 16 * tb + 4 * g]);
