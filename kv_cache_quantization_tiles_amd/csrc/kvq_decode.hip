@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs A) {
     stage(y[e], lane_xor<16>(y[e]), 16);
   }
   // randomized rotation: the restore ends with the sign of each channel
-  const unsigned sg = (A.signs[c4 >> 3] >> (4 * (c4 & 7))) & 0xFu;
+  const unsigned sg = (sign_word(A.signs, c4 >> 3) >> (4 * (c4 & 7))) & 0xFu;
   f32x4 r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) r[e] = y[e] * (((sg >> e) & 1u) ? -inv : inv);

@@ -352,10 +352,13 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   if (c_begin >= c_end) return;  // uniform over the workgroup
   // the query rows wave 0 folds below, loaded first so that their memory
   // latency overlaps that of the block table and the first chunk
+  // (rows past the real ones load row 0 and are zeroed at the fold: no
+  // branch around the loads, so nothing has to wait for them before the fold)
   u32x4 qraw[4];
+  const bool q_real = (lane & 15) < nrows;
   if (wave == 0) {
     const int n16 = lane & 15, grp = lane >> 4;
-    const bool real = n16 < nrows;
+    const bool real = q_real;
     size_t qix;
     if constexpr (MQ) {
       const int r = r0 + (real ? n16 : 0);
@@ -365,8 +368,7 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
     }
     const uint16_t* qrow = A.q + qix * kHeadDim + 32 * grp;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      qraw[v] = real ? *reinterpret_cast<const u32x4*>(qrow + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < 4; ++v) qraw[v] = *reinterpret_cast<const u32x4*>(qrow + 8 * v);
   }
   // MQ: tokens visible to row h (causal: up to its query's position)
   int vis[MQ ? NH : 1];
@@ -517,12 +519,13 @@ void decode_kernel(DecodeArgs A, QuantArgs Q) {
   if (wave == 0) {
     const int n16 = lane & 15, grp = lane >> 4;
     float hq[32];
+    const unsigned sgw = sign_word(A.signs, grp);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      u32x4 w = qraw[v];
+      u32x4 w = q_real ? qraw[v] : u32x4{0u, 0u, 0u, 0u};
       // randomized rotation: q's channels take the signs before H (keys are H s k)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] ^= sign_pair_mask(A.signs, 32 * grp + 8 * v, i);
+      for (int i = 0; i < 4; ++i) w[i] ^= sign_pair_mask_w(sgw, 8 * v, i);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         hq[8 * v + 2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFF));

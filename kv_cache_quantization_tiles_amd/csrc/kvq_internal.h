@@ -171,6 +171,18 @@ __device__ __forceinline__ unsigned sign_pair_mask(const uint32_t* signs, int c0
   const unsigned b = (signs[c0 >> 5] >> (c0 & 31)) & 0xFFu;
   return ((b << (15 - 2 * w)) & 0x8000u) | ((b << (30 - 2 * w)) & 0x80000000u);
 }
+// The sign word of channels 32 k .. 32 k + 31 for a k (< 4) that varies by
+// lane, as selects among the four words (indexing the argument array by a
+// lane value would read it from memory), and sign_pair_mask of a word.
+__device__ __forceinline__ unsigned sign_word(const uint32_t (&signs)[4], int k) {
+  const unsigned lo = (k & 1) ? signs[1] : signs[0];
+  const unsigned hi = (k & 1) ? signs[3] : signs[2];
+  return (k & 2) ? hi : lo;
+}
+__device__ __forceinline__ unsigned sign_pair_mask_w(unsigned word, int bit0, int w) {
+  const unsigned b = (word >> bit0) & 0xFFu;
+  return ((b << (15 - 2 * w)) & 0x8000u) | ((b << (30 - 2 * w)) & 0x80000000u);
+}
 __device__ __forceinline__ bool any_sign(const uint32_t* signs) {
   return (signs[0] | signs[1] | signs[2] | signs[3]) != 0u;
 }

@@ -176,8 +176,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
     const size_t qix = ((size_t)seq * A.n_q + r / G) * A.q_heads + kvh * G + r % G;
     const uint16_t* qrow = A.q + qix * kHeadDim + 32 * g;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      qraw[v] = row_real ? *reinterpret_cast<const u32x4*>(qrow + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < 4; ++v) qraw[v] = *reinterpret_cast<const u32x4*>(qrow + 8 * v);   // (zeroed at use past the real rows)
   }
   // the partition's slots
   const int npages = ((L + T - 1) / T) * PPT;
@@ -202,11 +201,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu((T 
   // H q of the row tile, stored divided by the weight of each channel's K field
   if (hq_wave) {
     float hq[32];
+    const unsigned sgw = sign_word(A.signs, g);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      u32x4 w = qraw[v];
+      u32x4 w = row_real ? qraw[v] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] ^= sign_pair_mask(A.signs, 32 * g + 8 * v, i);
+      for (int i = 0; i < 4; ++i) w[i] ^= sign_pair_mask_w(sgw, 8 * v, i);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         hq[8 * v + 2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFF));

@@ -183,7 +183,7 @@ __global__ __launch_bounds__(128) void dequantize_kernel(DequantArgs A) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int c0 = 64 * half + 8 * cg;
-      const unsigned b = (A.signs[c0 >> 5] >> (c0 & 31)) & 0xFFu;
+      const unsigned b = (sign_word(A.signs, c0 >> 5) >> (c0 & 31)) & 0xFFu;
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[8 * half + j] = ((b >> j) & 1u) ? -x[8 * half + j] : x[8 * half + j];
     }
@@ -331,7 +331,7 @@ __device__ __forceinline__ void restore_page(const RematArgs& A, int seq, int pj
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int c0 = 64 * half + 8 * cg;
-      const unsigned b = (A.signs[c0 >> 5] >> (c0 & 31)) & 0xFFu;
+      const unsigned b = (sign_word(A.signs, c0 >> 5) >> (c0 & 31)) & 0xFFu;
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[8 * half + j] = ((b >> j) & 1u) ? -x[8 * half + j] : x[8 * half + j];
     }
