@@ -11,7 +11,8 @@ Default workload: a Qwen3-4B-shaped layer, 8 KV heads / 32 query heads,
 normalization iterations.
 
 Prints one JSON line.  `value` is the step's algorithmic bytes (quantize +
-append + decode) over the step time, in GB/s.
+append + decode) over the step time, in GB/s, the K timed steps replayed
+from one HIP graph (`value_eager`: the same steps launched call by call).
 """
 from __future__ import annotations
 
