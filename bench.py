@@ -756,6 +756,26 @@ def main():
     # the fused decode step alone (append + re-quantize + attend, then the merge), back to back
     ad_batch = batch_ms(lambda j: caches[j % n_pools].append_decode(kn, vn, lens_before, q, max_len + 1, out=out,
                                                                     workspace=ws), n_q)
+    # the same plain decode at a short context (same batch, heads, tile and
+    # widths): the difference to the full-context decode splits the decode's
+    # time into a fixed part (launches, the dependent loads before the first
+    # chunk, the partition merge) and the streaming of the pages
+    short_ctx = 1024
+    wl_s = dataclasses.replace(wl, seq_lens=(short_ctx,) * wl.num_seqs)
+    table_s, npages_s = inputs.block_table(wl_s)
+    cu_s = torch.from_numpy(wl_s.cu_seqlens()).to(dev)
+    k_s, v_s = inputs.gen_kv_device(wl_s, "K", device=dev), inputs.gen_kv_device(wl_s, "V", device=dev)
+    caches_short = [api.PagedCache(cfg, npages_s, wl.hkv, torch.from_numpy(table_s), wl.num_seqs)
+                    for _ in range(n_pools)]
+    for c in caches_short:
+        c.quantize_prefill(k_s, v_s, cu_s)
+    lens_s = torch.full((wl.num_seqs,), short_ctx, dtype=torch.int32, device=dev)
+    ws_s = caches_short[0].workspace(wl.hq, short_ctx)
+    caches_short[0].decode(q, lens_s, short_ctx, out=out, workspace=ws_s)
+    ds_short_batch = batch_ms(lambda j: caches_short[j % n_pools].decode(q, lens_s, short_ctx, out=out,
+                                                                       workspace=ws_s), n_q)
+    torch.cuda.synchronize()
+    del caches_short, k_s, v_s
     # bandwidth probe: plain copy of 1 GiB
     nb = 1 << 30
     src = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -879,6 +899,7 @@ def main():
     del dq, restored
     q_kernel_ms = q_batch[0].elapsed_time(q_batch[1]) / q_batch[2]
     td_cold = d_batch[0].elapsed_time(d_batch[1]) / d_batch[2]
+    td_short = ds_short_batch[0].elapsed_time(ds_short_batch[1]) / ds_short_batch[2]
     ad_kernel_ms = ad_batch[0].elapsed_time(ad_batch[1]) / ad_batch[2]
     qs_ms = qs_batch[0].elapsed_time(qs_batch[1]) / qs_batch[2]
     ds_ms = ds_batch[0].elapsed_time(ds_batch[1]) / ds_batch[2]
@@ -897,6 +918,9 @@ def main():
     n_elem = 2 * ntok_heads * D
     q_tops = n_elem * quantize_valu_ops_per_element(wl.iters) / (q_kernel_ms * 1e-3) / 1e12
     d_gbps_cold = dbytes / (td_cold * 1e-3) / 1e9
+    dbytes_short = decode_bytes(wl_s, wl_s.seq_lens)
+    d_marginal_gbps = (dbytes - dbytes_short) / max((td_cold - td_short) * 1e-3, 1e-9) / 1e9
+    d_fixed_us = (td_short * 1e-3 - dbytes_short / (d_marginal_gbps * 1e9)) * 1e6
     value = (qbytes + abytes + dbytes) / (ms_step * 1e-3) / 1e9
     rec = {
         "metric": "quantize GB/s + quantized decode-attn tokens/s at 16K; % of HBM peak",
@@ -967,7 +991,17 @@ def main():
                             "launch_us": round(ad_kernel_ms * 1e3, 2),
                             "timing": "HIP events around a back-to-back batch of fused decode steps "
                                       "(pools rotated); slot bytes of every cached token read plus the "
-                                      "re-quantized tile's staging rows and slots"},
+                                      "re-quantized tile's staging rows and slots",
+                            "fixed_and_streaming": {
+                                "short_context": short_ctx, "short_decode_us": round(td_short * 1e3, 2),
+                                "full_decode_us": round(td_cold * 1e3, 2),
+                                "marginal_GBps": round(d_marginal_gbps, 1),
+                                "marginal_frac": round(d_marginal_gbps / HBM_PEAK_GBPS, 4),
+                                "fixed_us": round(d_fixed_us, 2),
+                                "note": "plain decode (decode kernel + partition merge) at the full and at a "
+                                        "1024-token context, same batch and heads: the slot bytes the longer "
+                                        "context adds over the time it adds (marginal), and the time left at "
+                                        "zero bytes (fixed)"}},
         "cpu_baseline": cpu,
     }
     del caches, ks, vs, src, dst
