@@ -637,6 +637,10 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         *reinterpret_cast<qt_f32x4*>(p2 + 64) = qt_f32x4{s2[4], s2[5], s2[6], s2[7]};
       }
       __syncthreads();
+      // The finalize is a short dependent chain that the group's other waves
+      // wait for at the next barrier: its waves go first meanwhile (wave
+      // priority), the other workgroups' element passes fill the issue slots.
+      __builtin_amdgcn_s_setprio(2);
       for (int i = tid; i < kHeadDim; i += NT) {   // lane-order index i: channel (i >> 3) + 16 (i & 7)
         float S1 = 0.f, S2 = 0.f;
         const int at = 64 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);   // its place in a row of partials
@@ -663,6 +667,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
           sm.alpha[(i >> 3) + 16 * (i & 7)] = __builtin_amdgcn_sqrtf(var * (1.0f / kHeadDim));
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       {
         const qt_f32x4 lo = *reinterpret_cast<const qt_f32x4*>(&sm.a[8 * j]);
@@ -710,6 +715,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         *reinterpret_cast<qt_f32x4*>(&red1[j * kRedStride<T> + tok(4)]) = qt_f32x4{t2[4], t2[5], t2[6], t2[7]};
       }
       __syncthreads();
+      __builtin_amdgcn_s_setprio(2);   // (as in the channel step's finalize)
       if (tid < T) {
         float T1 = 0.f, T2 = 0.f;
 #pragma unroll
@@ -723,6 +729,7 @@ __device__ __forceinline__ void quantize_tile_body(const QuantArgs& A, Smem<T>& 
         const float ms = __builtin_fmaf(mu, mu, var);
         if (var > kGuard2 * ms) sm.b[tid] = __builtin_amdgcn_rsqf(var);
       }
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       {
         b0 = sm.b[0];
