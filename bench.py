@@ -637,8 +637,8 @@ def main():
                          "instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards "
-              "without communication, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each GPU would run "
+              "this path on its own share of sequences and kv heads, with no communication)", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
         import torch
