@@ -207,6 +207,9 @@ DECODE_CASES = [
     (2, (700, 513, 64, 1), 2, 8, 64, 8, 8, 3),       # 8-bit codes
     (5, (611, 33, 96), 2, 16, 32, 8, 8, 5),          # 8-bit, tile 32, G = 8
     (2, (900, 129), 1, 16, 128, 8, 8, 3),            # 8-bit, tile 128, G = 16
+    (2, (700, 130, 5), 1, 8, 128, 4, 4, 3),          # tile 128, G = 8 (two head groups)
+    (2, (500, 33, 64), 2, 8, 32, 4, 4, 3),           # tile 32, G = 4 (one head group)
+    (2, (300, 65), 2, 4, 64, 2, 4, 3),               # G = 2 (padded), K2 / V4
 ]
 
 
