@@ -535,6 +535,8 @@ FUSED_CASES = [
     (2, (700, 513, 64, 1), 2, 8, 32, 4, 4, 3),
     (2, (300, 97, 33), 2, 8, 64, 8, 8, 3),
     (5, (200, 64, 17), 1, 16, 32, 8, 8, 5),
+    (2, (300, 129, 5), 1, 8, 128, 4, 4, 3),    # tile 128, G = 8 (two head groups)
+    (2, (90, 200), 2, 4, 64, 2, 4, 3),         # G = 2 (padded), K2 / V4
 ]
 
 
